@@ -1,0 +1,228 @@
+"""Throughput of the batched fp32 FFT on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload w2]
+
+One step is one pass of the whole hot path over one batch: for the default
+workload (w2: 16384 rows of N = 4096 complex64, U[-1,1]) a forward transform
+followed by the inverse of its output, two kernel launches.  Inputs are
+resident in HBM before timing starts.  Prints ONE JSON line.
+
+value     = 5 N log2(N) * rows * directions / time  (GFLOP/s, the pages'
+            flop convention)
+roofline  = algorithmic HBM bytes of one launch (read + write of every
+            element once) / the average launch duration, timed with HIP events
+            on the stream the kernels run on, against the 8 TB/s HBM peak
+cpu_baseline = the f64 oracle (untuned reference) on a bounded sample of the
+            same workload on the host cores
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "batched C2C fp32 FFT GFLOP/s (5N log2N) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of the kernel sources; stored HBM-traffic counters are used only
+    while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fourier_transform_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hpp", ".hip")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key):
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def workload_spec(name):
+    from fourier_transform_amd import workloads as W
+    if name == "w1":
+        return dict(kind="c2c", n=W.W1["n"], batch=W.W1["batch"], dirs=(-1,), gen=W.workload1,
+                    passes=1, label="1D C2C fp32 forward N=1024 batch=8")
+    if name == "w2":
+        return dict(kind="c2c", n=W.W2["n"], batch=W.W2["batch"], dirs=(-1, 1), gen=W.workload2,
+                    passes=1, label="1D C2C fp32 forward+inverse N=4096 batch=16384")
+    if name == "w3":
+        return dict(kind="c2c", n=W.W3["n"], batch=W.W3["batch"], dirs=(-1,), gen=W.workload3,
+                    passes=2, label="1D C2C fp32 forward N=2^22 batch=32 (four-step)")
+    if name == "w5":
+        return dict(kind="2d", n=W.W5["ny"] * W.W5["nx"], ny=W.W5["ny"], nx=W.W5["nx"], batch=1,
+                    dirs=(-1,), gen=W.workload5, passes=2,
+                    label="2D C2C fp32 forward 8192x8192 with fused chessboard shift")
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(spec, x_host):
+    """Time the f64 oracle on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    n = spec["n"]
+    if spec["kind"] == "2d":
+        sample_rows = 1
+        xs = x_host.astype(np.complex128)
+        t0 = time.perf_counter()
+        for s in spec["dirs"]:
+            oracle.c2c_2d(xs, s)
+        dt = time.perf_counter() - t0
+        desc = f"whole {spec['ny']}x{spec['nx']} image, {len(spec['dirs'])} direction(s)"
+    else:
+        budget_rows = max(1, min(spec["batch"], (1 << 24) // n))   # <= 16M points
+        sample_rows = budget_rows
+        xs = x_host[:sample_rows].astype(np.complex128)
+        t0 = time.perf_counter()
+        for s in spec["dirs"]:
+            oracle.c2c(xs, s)
+        dt = time.perf_counter() - t0
+        desc = f"{sample_rows} of {spec['batch']} rows, {len(spec['dirs'])} direction(s)"
+    flops = 5.0 * n * math.log2(n) * sample_rows * len(spec["dirs"])
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(0),
+            "kind": "oracle", "sample": desc + f", {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the transforms are not sharded across devices", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from fourier_transform_amd import fft as F
+
+    if not torch.cuda.is_available():
+        raise SystemExit("no HIP device")
+    F.lib()  # fail loudly if the library is missing
+    spec = workload_spec(args.workload)
+    n, batch = spec["n"], spec["batch"]
+    x_host = spec["gen"]()
+    xd = torch.from_numpy(x_host).cuda()
+    bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
+    plans = []
+    for s in spec["dirs"]:
+        if spec["kind"] == "2d":
+            p = F.fft_plan_create_2d(spec["ny"], spec["nx"], batch, F.FFT_C2C, s)
+            F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
+        else:
+            p = F.fft_plan_create(n, batch, F.FFT_C2C, s)
+        plans.append(p)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        src = xd
+        for i, (p, dst) in enumerate(zip(plans, bufs)):
+            if events is not None:
+                events[i][0].record(stream)
+            F.fft_exec(p, src, dst, stream.cuda_stream)
+            if events is not None:
+                events[i][1].record(stream)
+            src = dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between two synchronisations; HIP events on the
+    # exec stream bracket every launch group
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in plans] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    exec_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    avg_exec_ms = sum(exec_ms) / len(exec_ms)
+
+    # correctness guard for the numbers: the round trip must return N x
+    check = None
+    if len(spec["dirs"]) == 2:
+        z = bufs[-1]
+        check = float(torch.linalg.vector_norm(z / n - xd) / torch.linalg.vector_norm(xd))
+
+    # attainable-bandwidth reference: a plain 512 MiB device-to-device copy
+    a = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * a.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+
+    ms_per_step = wall * 1e3 / args.steps
+    flops_step = 5.0 * n * math.log2(n) * batch * len(spec["dirs"])
+    value = flops_step / (ms_per_step * 1e-3) / 1e9
+    bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
+    achieved = bytes_per_exec / (avg_exec_ms * 1e-3) / 1e9
+    key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
+           "w5": "2d_8192x8192"}[args.workload]
+    traffic = stored_traffic(key)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec["label"], "n": n, "batch": batch,
+                   "directions": len(spec["dirs"]), "layout": "interleaved complex64"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": key,
+                     "avg_launch_ms": round(avg_exec_ms, 5),
+                     "algorithmic_bytes_per_launch": bytes_per_exec},
+        "copy_gbps": round(copy_gbps, 1),
+    }
+    if check is not None:
+        out["round_trip_rel_l2"] = check
+    for p in plans:
+        F.fft_plan_destroy(p)
+    del xd, bufs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, x_host)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,71 @@
+// launch.hpp -- host-side launchers of the transform kernels (internal API of
+// libfft_amd.so; the public C ABI is include/fft.h).
+//
+// Every launcher picks the kernel instantiated for the given length and sign,
+// checks that the length is one it was built for, launches it on `stream`
+// and returns the launch status.  Pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fftamd {
+
+// Whole rows of length n (contiguous), one transform per row.
+// shift_mode: 0 none; 1 multiply element j by (-1)^j; 2 multiply element j of
+// row r by (-1)^(r mod rows_per_image + j) (2D chessboard).
+struct RowsArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;  // single-pass stage table for n
+  int64_t rows;
+  int shift_mode;
+  int64_t rows_per_image;
+};
+hipError_t launch_c2c_rows(int n, int sign, const RowsArgs& a, hipStream_t stream);
+
+// Columns of [images][ny][nx]: transform of length ny over every column, with
+// element stride nx.  In place is allowed (in == out).
+struct ColsArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;  // single-pass stage table for ny
+  int64_t ny, nx, images;
+};
+hipError_t launch_c2c_cols(int ny, int sign, const ColsArgs& a, hipStream_t stream);
+
+// Real transforms of length n = 2h through one complex transform of length h.
+// R2C: in float [rows][2h] -> out complex, bins 0..mmax.
+// C2R: in complex bins 0..mmax -> out float [rows][2h].
+// Spectrum layout: mmajor = 0 -> [rows][mmax+1]; 1 -> [mmax+1][rows].
+struct RealArgs {
+  const void* in;
+  void* out;
+  const float2* tw;  // single-pass stage table for h
+  const float2* rt;  // e^{-2 pi i k/n}, k = 0..h
+  int64_t rows;
+  int mmax;
+  int mmajor;
+};
+hipError_t launch_r2c(int h, const RealArgs& a, hipStream_t stream);
+hipError_t launch_c2r(int h, const RealArgs& a, hipStream_t stream);
+
+// Four-step transform of length n = n1*n2 (element n1 + N1*n2 -> bin
+// k2 + N2*k1).  Pass 1 (columns): in -> scratch, length-n2 transforms over
+// stride n1, each output multiplied by W_n^{n1*k2}.  Pass 2 (rows): scratch ->
+// out, length-n1 transforms over contiguous rows, stored transposed.
+// W_n^e = thi[e >> bits] * tlo[e & (2^bits - 1)].
+struct FourStepArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;   // stage table (n2 for pass 1, n1 for pass 2)
+  const float2* thi;
+  const float2* tlo;
+  int64_t batch;
+  int n1, n2, bits;
+  int shift;  // pass 1 only: multiply element j by (-1)^j (1D chessboard)
+};
+hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream);
+hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream);
+
+}  // namespace fftamd

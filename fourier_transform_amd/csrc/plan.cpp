@@ -1,0 +1,343 @@
+// plan.cpp -- the C ABI of include/fft.h: argument checks, plan construction
+// (path choice, host-f64 twiddle tables, scratch) and the launch sequence.
+//
+// Every argument check runs on the host before the first HIP call, so each
+// error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fft.h"
+#include "launch.hpp"
+#include "stockham.hpp"
+
+using namespace fftamd;
+
+namespace {
+
+constexpr int kFourStepMaxLog = 2 * ilog2c(kMaxSinglePass);  // 2^28
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+
+// ---------------------------------------------------------------------------
+// thread-local error state
+// ---------------------------------------------------------------------------
+struct ErrorState {
+  int code = FFT_OK;
+  std::string msg = "ok";
+};
+thread_local ErrorState g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err.code = code;
+  g_err.msg = msg;
+  return code;
+}
+int ok() { return set_err(FFT_OK, "ok"); }
+int hip_err(hipError_t e, const char* what) {
+  return set_err(e == hipErrorOutOfMemory ? FFT_ENOMEM : FFT_EHIP,
+                 std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool is_pow2(int64_t n) { return n >= 1 && (n & (n - 1)) == 0; }
+
+// ---------------------------------------------------------------------------
+// twiddle tables, computed in f64 and rounded once to fp32 (round to nearest)
+// ---------------------------------------------------------------------------
+float2 root(int64_t e, int64_t len) {  // e^{-2 pi i e/len}, 0 <= e < len
+  const double a = kTwoPi * (double)e / (double)len;
+  return make_float2((float)std::cos(a), (float)-std::sin(a));
+}
+
+// stage table of the single-pass schedule for length n (layout: stockham.hpp)
+void append_stage_table(int n, std::vector<float2>& t) {
+  const int stages = sched_stages(n);
+  for (int s = 1; s < stages; ++s) {
+    const int R = sched_radix(n, s), NS = sched_ns(n, s);
+    for (int r = 1; r < R; ++r)
+      for (int j = 0; j < NS; ++j) t.push_back(root((int64_t)r * j, (int64_t)NS * R));
+  }
+  if (t.empty()) t.push_back(make_float2(1.f, 0.f));  // keep offsets valid
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+struct fft_plan {
+  int dims = 1;
+  int64_t n = 0, ny = 1, nx = 0, batch = 0;
+  int kind = FFT_C2C, sign = FFT_FORWARD;
+  int shift = 0;
+  int64_t mmax = 0;
+  int spec_layout = 0;
+  bool executed = false;
+  bool fourstep = false;
+  int device = 0;
+  // four-step split n = n1 * n2
+  int n1 = 0, n2 = 0, bits = 0;
+  // device resources
+  float2* tables = nullptr;
+  const float2* tw_a = nullptr;  // rows: n (1D), nx (2D), h (real), n1 (four-step rows)
+  const float2* tw_b = nullptr;  // cols: ny (2D), n2 (four-step cols)
+  const float2* rt = nullptr;    // real transforms: e^{-2 pi i k/n}, k = 0..n/2
+  const float2* thi = nullptr;
+  const float2* tlo = nullptr;
+  float2* scratch = nullptr;
+  hipEvent_t done = nullptr;
+};
+
+namespace {
+
+int check_kind_sign(int kind, int sign) {
+  if (kind != FFT_C2C && kind != FFT_R2C && kind != FFT_C2R)
+    return set_err(FFT_EINVAL, "kind must be FFT_C2C, FFT_R2C or FFT_C2R");
+  if (sign != FFT_FORWARD && sign != FFT_INVERSE)
+    return set_err(FFT_EINVAL, "sign must be FFT_FORWARD (-1) or FFT_INVERSE (+1)");
+  if (kind == FFT_R2C && sign != FFT_FORWARD)
+    return set_err(FFT_EINVAL, "FFT_R2C is a forward transform (sign must be -1)");
+  if (kind == FFT_C2R && sign != FFT_INVERSE)
+    return set_err(FFT_EINVAL, "FFT_C2R is an inverse transform (sign must be +1)");
+  return FFT_OK;
+}
+
+int check_total(int64_t a, int64_t b, int64_t c) {
+  // a*b*c*8 bytes must fit in int64
+  const int64_t lim = INT64_MAX / 8;
+  if (a > lim / b || a * b > lim / c) return set_err(FFT_EINVAL, "transform size overflows");
+  return FFT_OK;
+}
+
+void free_plan(fft_plan* p) {
+  if (!p) return;
+  if (p->done) (void)hipEventDestroy(p->done);
+  if (p->tables) (void)hipFree(p->tables);
+  if (p->scratch) (void)hipFree(p->scratch);
+  delete p;
+}
+
+// allocate and upload the tables (called after every argument check passed)
+int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
+                const std::vector<const float2**>& slots, size_t scratch_bytes) {
+  std::vector<float2> all;
+  std::vector<size_t> offs;
+  for (auto* v : parts) {
+    while (all.size() % 32) all.push_back(make_float2(0.f, 0.f));  // 256 B alignment
+    offs.push_back(all.size());
+    all.insert(all.end(), v->begin(), v->end());
+  }
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+  e = hipMalloc((void**)&p->tables, all.size() * sizeof(float2));
+  if (e != hipSuccess) return hip_err(e, "hipMalloc(twiddle tables)");
+  e = hipMemcpy(p->tables, all.data(), all.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_err(e, "hipMemcpy(twiddle tables)");
+  for (size_t i = 0; i < slots.size(); ++i) *slots[i] = p->tables + offs[i];
+  if (scratch_bytes) {
+    e = hipMalloc((void**)&p->scratch, scratch_bytes);
+    if (e != hipSuccess) return hip_err(e, "hipMalloc(scratch)");
+  }
+  e = hipEventCreateWithFlags(&p->done, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+  return FFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
+  if (n < 1) return set_err(FFT_EINVAL, "n must be >= 1"), nullptr;
+  if (batch < 1) return set_err(FFT_EINVAL, "batch must be >= 1"), nullptr;
+  if (check_kind_sign(kind, sign) != FFT_OK) return nullptr;
+  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n must be a power of two"), nullptr;
+  if (check_total(n, batch, 1) != FFT_OK) return nullptr;
+  const int64_t max_len = kind == FFT_C2C ? (int64_t(1) << kFourStepMaxLog) : 2 * (int64_t)kMaxSinglePass;
+  const int64_t min_len = kind == FFT_C2C ? 2 : 4;
+  if (n < min_len || n > max_len)
+    return set_err(FFT_ENOTSUP, "n out of range: C2C needs 2 <= n <= 2^28, R2C/C2R 4 <= n <= 32768"),
+           nullptr;
+
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->dims = 1;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = kind;
+  p->sign = sign;
+  p->mmax = n / 2;
+
+  std::vector<float2> ta, tb, trt, thi, tlo;
+  std::vector<std::vector<float2>*> parts;
+  std::vector<const float2**> slots;
+  size_t scratch = 0;
+  if (kind == FFT_C2C && n <= kMaxSinglePass) {
+    append_stage_table((int)n, ta);
+    parts = {&ta};
+    slots = {&p->tw_a};
+  } else if (kind == FFT_C2C) {
+    const int L = ilog2c(n);
+    p->fourstep = true;
+    p->n1 = 1 << (L / 2);
+    p->n2 = 1 << (L - L / 2);
+    p->bits = L - L / 2;
+    append_stage_table(p->n1, ta);
+    append_stage_table(p->n2, tb);
+    for (int64_t h = 0; h < (n >> p->bits); ++h) thi.push_back(root(h << p->bits, n));
+    for (int64_t l = 0; l < (int64_t(1) << p->bits); ++l) tlo.push_back(root(l, n));
+    parts = {&ta, &tb, &thi, &tlo};
+    slots = {&p->tw_a, &p->tw_b, &p->thi, &p->tlo};
+    scratch = (size_t)(n * batch) * sizeof(float2);
+  } else {
+    append_stage_table((int)(n / 2), ta);
+    for (int64_t k = 0; k <= n / 2; ++k) trt.push_back(root(k, n));
+    parts = {&ta, &trt};
+    slots = {&p->tw_a, &p->rt};
+  }
+  if (finish_plan(p, parts, slots, scratch) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
+fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, int sign) {
+  if (ny < 1 || nx < 1) return set_err(FFT_EINVAL, "ny and nx must be >= 1"), nullptr;
+  if (batch < 1) return set_err(FFT_EINVAL, "batch must be >= 1"), nullptr;
+  if (check_kind_sign(kind, sign) != FFT_OK) return nullptr;
+  if (kind != FFT_C2C) return set_err(FFT_ENOTSUP, "2D plans support FFT_C2C only"), nullptr;
+  if (!is_pow2(ny) || !is_pow2(nx))
+    return set_err(FFT_ENOTSUP, "ny and nx must be powers of two"), nullptr;
+  if (ny < 2 || nx < 2 || ny > kMaxSinglePass || nx > kMaxSinglePass)
+    return set_err(FFT_ENOTSUP, "2D sizes must lie in [2, 16384]"), nullptr;
+  if (check_total(ny, nx, batch) != FFT_OK) return nullptr;
+
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->dims = 2;
+  p->ny = ny;
+  p->nx = nx;
+  p->n = ny * nx;
+  p->batch = batch;
+  p->kind = kind;
+  p->sign = sign;
+  std::vector<float2> ta, tb;
+  append_stage_table((int)nx, ta);
+  append_stage_table((int)ny, tb);
+  if (finish_plan(p, {&ta, &tb}, {&p->tw_a, &p->tw_b}, 0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
+int fft_plan_set(fft_plan* p, int option, int64_t value) {
+  if (!p) return set_err(FFT_EINVAL, "plan is NULL");
+  if (p->executed) return set_err(FFT_ESTATE, "options must be set before the first fft_exec");
+  switch (option) {
+    case FFT_OPT_SHIFT:
+      if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0 or 1");
+      if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
+      if (value && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
+        return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
+      p->shift = (int)value;
+      return ok();
+    case FFT_OPT_MMAX:
+      if (p->kind == FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_MMAX applies to R2C/C2R plans only");
+      if (value < 0 || value > p->n / 2) return set_err(FFT_EINVAL, "mmax must satisfy 0 <= mmax <= n/2");
+      p->mmax = value;
+      return ok();
+    case FFT_OPT_SPEC_LAYOUT:
+      if (p->kind == FFT_C2C)
+        return set_err(FFT_EINVAL, "FFT_OPT_SPEC_LAYOUT applies to R2C/C2R plans only");
+      if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_SPEC_LAYOUT takes 0 or 1");
+      p->spec_layout = (int)value;
+      return ok();
+    default:
+      return set_err(FFT_EINVAL, "unknown option");
+  }
+}
+
+int fft_plan_get_sizes(const fft_plan* p, int64_t* in_bytes, int64_t* out_bytes) {
+  if (!p) return set_err(FFT_EINVAL, "plan is NULL");
+  const int64_t cplx = p->batch * p->n * 8;
+  const int64_t real = p->batch * p->n * 4;
+  const int64_t spec = p->batch * (p->mmax + 1) * 8;
+  int64_t i = cplx, o = cplx;
+  if (p->kind == FFT_R2C) i = real, o = spec;
+  if (p->kind == FFT_C2R) i = spec, o = real;
+  if (in_bytes) *in_bytes = i;
+  if (out_bytes) *out_bytes = o;
+  return ok();
+}
+
+int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
+  if (!p) return set_err(FFT_EINVAL, "plan is NULL");
+  if (!in || !out) return set_err(FFT_EINVAL, "in and out must be device pointers");
+  if (((uintptr_t)in & 7) || ((uintptr_t)out & 7)) return set_err(FFT_EINVAL, "buffers must be 8-byte aligned");
+  if (p->kind != FFT_C2C && in == out) return set_err(FFT_EINVAL, "R2C/C2R cannot run in place");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+  if (cur != p->device) {
+    e = hipSetDevice(p->device);
+    if (e != hipSuccess) return hip_err(e, "hipSetDevice");
+  }
+  p->executed = true;
+  const float2* src = static_cast<const float2*>(in);
+  float2* dst = static_cast<float2*>(out);
+  if (p->kind == FFT_C2C && p->dims == 1 && !p->fourstep) {
+    RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1};
+    e = launch_c2c_rows((int)p->n, p->sign, a, stream);
+  } else if (p->kind == FFT_C2C && p->dims == 1) {
+    FourStepArgs a{src, p->scratch, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, p->shift};
+    e = launch_fourstep_cols(p->n2, p->sign, a, stream);
+    if (e == hipSuccess) {
+      FourStepArgs b{p->scratch, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
+      e = launch_fourstep_rows(p->n1, p->sign, b, stream);
+    }
+  } else if (p->kind == FFT_C2C) {
+    RowsArgs a{src, dst, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny};
+    e = launch_c2c_rows((int)p->nx, p->sign, a, stream);
+    if (e == hipSuccess) {
+      ColsArgs c{dst, dst, p->tw_b, p->ny, p->nx, p->batch};
+      e = launch_c2c_cols((int)p->ny, p->sign, c, stream);
+    }
+  } else {
+    RealArgs a{in, out, p->tw_a, p->rt, p->batch, (int)p->mmax, p->spec_layout};
+    e = p->kind == FFT_R2C ? launch_r2c((int)(p->n / 2), a, stream) : launch_c2r((int)(p->n / 2), a, stream);
+  }
+  if (e == hipSuccess) e = hipEventRecord(p->done, stream);
+  if (cur != p->device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return hip_err(e, "kernel launch");
+  return ok();
+}
+
+void fft_plan_destroy(fft_plan* p) {
+  if (!p) {
+    ok();
+    return;
+  }
+  if (p->executed && p->done) (void)hipEventSynchronize(p->done);
+  free_plan(p);
+  ok();
+}
+
+int fft_last_error(const char** msg) {
+  if (msg) *msg = g_err.msg.c_str();
+  return g_err.code;
+}
+
+int64_t fft_max_single_pass_length(void) { return kMaxSinglePass; }
+
+}  // extern "C"

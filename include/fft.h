@@ -1,0 +1,141 @@
+/*
+ * fft.h -- C ABI of libfft_amd.so: batched fp32 FFTs for AMD Instinct MI355X
+ * (gfx950), natural order in and out (Stockham autosort).
+ *
+ * Conventions
+ * -----------
+ *  - Transform (DFT definition: "High Performance Fourier Transforms on GPUs
+ *    with GLSL", Mota, section 2.2, Equation 5):
+ *        y_k = sum_{j=0}^{n-1} x_j * exp(sign * 2*pi*i * j*k / n)
+ *    sign = FFT_FORWARD (-1) or FFT_INVERSE (+1).  Neither direction is
+ *    normalised (the WGSL Fourier-stage source, turing-sphere fourier.ts,
+ *    stockham(), does the same): a forward then an inverse transform returns
+ *    n * x.
+ *  - Data are fp32.  Complex values are interleaved (re, im) pairs: 8 bytes per
+ *    element ("complex64").  Rows are contiguous; batches follow each other.
+ *  - Sizes are powers of two.  Every other length is rejected with
+ *    FFT_ENOTSUP (fourier.ts refuses non-power-of-two lengths at plan time).
+ *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
+ *    aligned.  The plan owns its twiddle tables and scratch (allocated at
+ *    create, freed at destroy).
+ *  - Errors: every function records a code and a message, readable with
+ *    fft_last_error() from the same host thread.  All argument checks run on
+ *    the host before any HIP call.
+ *
+ * Layouts per kind
+ * ----------------
+ *  FFT_C2C  in, out: complex64 [batch][n]      (2D: [batch][ny][nx])
+ *           in == out (in place) is allowed.
+ *  FFT_R2C  in : float32  [batch][n]            (real rows)
+ *           out: complex64 [batch][mmax+1]      (row-major, default), or
+ *                complex64 [mmax+1][batch]      (m-major, FFT_OPT_SPEC_LAYOUT=1,
+ *                the spectrum layout of fourier.ts fftAnalysWGSL)
+ *           mmax defaults to n/2 (the full half spectrum, n/2+1 bins).
+ *           Only sign = FFT_FORWARD.  in == out is rejected.
+ *  FFT_C2R  in : the R2C spectrum layout above (bins 0..mmax)
+ *           out: float32 [batch][n]
+ *           Bins above mmax are taken as zero; Im of bin 0 (and of bin n/2
+ *           when mmax = n/2) is ignored, as fourier.ts fftSynthWGSL does.
+ *           Only sign = FFT_INVERSE.  in == out is rejected.
+ *           Real transforms follow fourier.ts fftAnalysRealWGSL /
+ *           fftSynthRealWGSL: one complex transform of length n/2 plus a
+ *           Hermitian pack/unpack, so n >= 4 is required.
+ */
+#ifndef FFT_AMD_FFT_H
+#define FFT_AMD_FFT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fft_plan fft_plan; /* opaque */
+
+/* hipStream_t is `struct ihipStream_t*`; 0 / NULL is the null stream. */
+typedef struct ihipStream_t* fft_stream_t;
+
+enum fft_kind { FFT_C2C = 0, FFT_R2C = 1, FFT_C2R = 2 };
+enum fft_sign { FFT_FORWARD = -1, FFT_INVERSE = +1 };
+
+enum fft_status {
+  FFT_OK = 0,
+  FFT_EINVAL = -1,  /* bad argument: NULL, size < 1, bad kind/sign/option, misaligned */
+  FFT_ENOTSUP = -2, /* valid but unsupported: length not a power of two, too long */
+  FFT_ENOMEM = -3,  /* device allocation failed */
+  FFT_EHIP = -4,    /* a HIP runtime call or kernel launch failed (message has details) */
+  FFT_ESTATE = -5   /* option set after the first fft_exec */
+};
+
+enum fft_option {
+  /* 1: multiply the input by (-1)^j in 1D, (-1)^(i+j) in 2D, while loading it,
+   * which moves the zero frequency to the middle of the output (the chessboard
+   * fftshift: "The 1D fftshift in CUDA by chessboard multiplication").  The
+   * factor is applied by flipping the sign bits of both parts, before any
+   * arithmetic, so the result is bitwise the transform of the negated input.
+   * C2C only; every shifted axis must have even length.  Default 0. */
+  FFT_OPT_SHIFT = 1,
+  /* R2C: keep bins 0..mmax; C2R: read bins 0..mmax.  0 <= mmax <= n/2
+   * (fourier.ts: band limit |m| <= mmax < nphi/2).  Default n/2. */
+  FFT_OPT_MMAX = 2,
+  /* R2C/C2R spectrum layout: 0 = row-major [batch][mmax+1] (default),
+   * 1 = m-major [mmax+1][batch]. */
+  FFT_OPT_SPEC_LAYOUT = 3
+};
+
+/*
+ * Create a plan for `batch` transforms of length n.
+ * n: power of two, n >= 2 (C2C) or n >= 4 (R2C/C2R).  batch >= 1.
+ * kind: FFT_C2C, FFT_R2C or FFT_C2R.  sign: FFT_FORWARD or FFT_INVERSE.
+ * Lengths up to 16384 run as one kernel (one workgroup per row, all stages in
+ * LDS); longer C2C lengths, up to 2^28, run as two passes (four-step: strided
+ * column transforms with the inter-pass twiddle fused into their store, then
+ * row transforms with a transposing store) and own a scratch buffer of
+ * batch*n*8 bytes.
+ * Uses the current HIP device.  Returns NULL on error (see fft_last_error).
+ */
+fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);
+
+/*
+ * 2D C2C plan over [batch][ny][nx] complex64: every row, then every column
+ * (Mota, section 2.7, Equation 19).  ny, nx: powers of two in [2, 16384].
+ * Only kind = FFT_C2C.  Returns NULL on error.
+ */
+fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind,
+                             int sign);
+
+/* Set an option (enum fft_option).  Only before the first fft_exec of the
+ * plan, else FFT_ESTATE.  Returns FFT_OK or an error code. */
+int fft_plan_set(fft_plan* plan, int option, int64_t value);
+
+/*
+ * Byte sizes the plan reads from `in` and writes to `out` (given its current
+ * options).  Either pointer may be NULL.  Returns FFT_OK or FFT_EINVAL.
+ */
+int fft_plan_get_sizes(const fft_plan* plan, int64_t* in_bytes,
+                       int64_t* out_bytes);
+
+/*
+ * Enqueue the transform on `stream` and return (asynchronous).  `in` is read,
+ * `out` written; out-of-place execution never writes `in`.  Calls of one plan
+ * on two streams at once are undefined (they share the plan's scratch).
+ * Returns FFT_OK, FFT_EINVAL (NULL plan or buffer, misaligned, in == out for
+ * R2C/C2R) or FFT_EHIP (launch failure).
+ */
+int fft_exec(fft_plan* plan, const void* in, void* out, fft_stream_t stream);
+
+/* Wait for the plan's enqueued work, then free it.  NULL is a no-op. */
+void fft_plan_destroy(fft_plan* plan);
+
+/* Code of the last call on this host thread; *msg (if msg is not NULL) points
+ * to a thread-local message valid until the next call. */
+int fft_last_error(const char** msg);
+
+/* Longest length run as a single kernel (one workgroup per row). */
+int64_t fft_max_single_pass_length(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFT_AMD_FFT_H */

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle.
+
+Tolerance: relative L2 error <= 1e-5 over the whole output of a case, for every
+length (single-pass, four-step, real and 2D).  Shift index work is checked
+bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fourier_transform_amd import fft as F
+from fourier_transform_amd import workloads as W
+
+from gpu_helpers import c2c, c2c_2d, c2r, dev, empty, host, negate_odd, r2c, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    F.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# workload 1: N = 1024, batch 8, forward; oracle and brute force
+# --------------------------------------------------------------------------
+def test_w1_forward_vs_oracle_and_brute_force():
+    say("w1 n=1024 batch=8 forward")
+    x = W.workload1()
+    y = c2c(x, -1)
+    assert rel_l2(y, oracle.c2c(x, -1)) <= TOL
+    for r in range(x.shape[0]):
+        assert rel_l2(y[r], oracle.dft_brute(x[r], -1)) <= TOL
+
+
+# --------------------------------------------------------------------------
+# every single-pass length, both directions, ragged batches
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("logn", range(1, 15))
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_c2c_single_pass_sweep(logn, sign):
+    n = 1 << logn
+    for batch in (1, 3, 37):
+        say(f"c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(logn * 100 + batch))
+        y = c2c(x, sign)
+        assert rel_l2(y, oracle.c2c(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n", [2, 64, 4096])
+def test_c2c_in_place(n):
+    say(f"c2c in place n={n}")
+    x = W.uniform_c64((5, n), np.random.default_rng(n))
+    assert rel_l2(c2c(x, -1, inplace=True), oracle.c2c(x, -1)) <= TOL
+
+
+# --------------------------------------------------------------------------
+# workload 2: N = 4096, batch 16384, forward then inverse (full size)
+# --------------------------------------------------------------------------
+def test_w2_forward_inverse_full():
+    import torch
+    say("w2 n=4096 batch=16384 forward+inverse")
+    x = W.workload2()
+    n, batch = W.W2["n"], W.W2["batch"]
+    pf = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    pi = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_INVERSE)
+    try:
+        xd = dev(x)
+        yd = torch.empty_like(xd)
+        zd = torch.empty_like(xd)
+        F.fft_exec(pf, xd, yd)
+        F.fft_exec(pi, yd, zd)
+        y, z = host(yd), host(zd)
+    finally:
+        F.fft_plan_destroy(pf)
+        F.fft_plan_destroy(pi)
+    e_fwd = rel_l2(y, oracle.c2c(x, -1))
+    e_inv = rel_l2(z, oracle.c2c(y, +1))
+    e_rt = rel_l2(z / n, x)
+    say(f"w2 rel_l2 forward={e_fwd:.3e} inverse={e_inv:.3e} round_trip={e_rt:.3e}")
+    assert e_fwd <= TOL and e_inv <= TOL and e_rt <= TOL
+
+
+def test_deterministic_repeat():
+    say("determinism n=4096 batch=512")
+    x = W.uniform_c64((512, 4096), np.random.default_rng(3))
+    a, b = c2c(x, -1), c2c(x, -1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# four-step (lengths beyond one workgroup)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("logn", [15, 16, 17, 20])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_fourstep_sweep(logn, sign):
+    n = 1 << logn
+    batch = 3 if logn < 20 else 2
+    say(f"four-step n=2^{logn} batch={batch} sign={sign}")
+    x = W.normal_c64((batch, n), np.random.default_rng(logn))
+    assert rel_l2(c2c(x, sign), oracle.c2c(x, sign)) <= TOL
+
+
+def test_fourstep_in_place():
+    say("four-step in place n=2^16")
+    x = W.normal_c64((2, 1 << 16), np.random.default_rng(7))
+    assert rel_l2(c2c(x, -1, inplace=True), oracle.c2c(x, -1)) <= TOL
+
+
+def test_w3_full_size_sampled_rows():
+    """Workload 3 at full size (32 x 2^22): every row is an independent
+    transform; rows 0, 17 and 31 are compared with the oracle in full."""
+    say("w3 n=2^22 batch=32 forward")
+    x = W.workload3()
+    y = c2c(x, -1)
+    rows = [0, 17, 31]
+    e = rel_l2(y[rows], oracle.c2c(x[rows], -1))
+    say(f"w3 rel_l2 rows {rows}: {e:.3e}")
+    assert e <= TOL
+    # Parseval on every row (a property at any size)
+    px = np.sum(np.abs(x.astype(np.complex128)) ** 2, axis=1) * x.shape[1]
+    py = np.sum(np.abs(y.astype(np.complex128)) ** 2, axis=1)
+    assert np.max(np.abs(py / px - 1)) < 1e-5
+
+
+# --------------------------------------------------------------------------
+# real transforms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("logn", range(2, 16))
+def test_real_sweep(logn):
+    n = 1 << logn
+    g = np.random.default_rng(logn)
+    for batch, mmax, mmajor in ((1, None, False), (5, n // 2 - 1, True), (19, max(0, n // 3), False),
+                                (6, 0, True)):
+        m = n // 2 if mmax is None else mmax
+        say(f"r2c/c2r n={n} batch={batch} mmax={m} mmajor={mmajor}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = r2c(x, m, mmajor)
+        Fo = oracle.r2c(x, m)
+        assert rel_l2(Fg.T if mmajor else Fg, Fo) <= TOL, (n, batch, m)
+        S = (g.normal(size=(batch, m + 1)) + 1j * g.normal(size=(batch, m + 1))).astype(np.complex64)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        xg = c2r(Sin, n, batch, m, mmajor)
+        assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
+
+
+def test_w4_synthesis_then_analysis():
+    """Workload 4: nlat=1024 rows, nphi=2048, mmax=682, m-major spectrum."""
+    p = W.W4
+    n, nlat, mmax = p["nphi"], p["nlat"], p["mmax"]
+    Fm = W.workload4_spectrum()                      # [683][1024] m-major
+    say("w4 C2R synthesis")
+    xg = c2r(Fm, n, nlat, mmax, mmajor=True)
+    xo = oracle.c2r(Fm.T, n, mmax)
+    e_syn = rel_l2(xg, xo)
+    say("w4 R2C analysis")
+    x32 = xo.astype(np.float32)                      # the oracle's rows, rounded
+    Fg = r2c(x32, mmax, mmajor=True)
+    e_ana = rel_l2(Fg.T, oracle.r2c(x32, mmax))
+    e_closed = rel_l2(Fg / n, Fm)                    # R2C(C2R(F)) = n F
+    say(f"w4 rel_l2 synthesis={e_syn:.3e} analysis={e_ana:.3e} closed_form={e_closed:.3e}")
+    assert e_syn <= TOL and e_ana <= TOL and e_closed <= TOL
+
+
+# --------------------------------------------------------------------------
+# 2D and the fused chessboard shift
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("ny,nx", [(2, 2), (4, 16), (16, 4), (32, 64), (256, 128), (128, 1024),
+                                   (2048, 16), (16, 16384)])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_2d_sweep(ny, nx, shift):
+    say(f"2d {ny}x{nx} shift={shift}")
+    x = W.normal_c64((2, ny, nx), np.random.default_rng(ny * 7 + nx))
+    y = c2c_2d(x, -1, shift)
+    want = oracle.c2c_2d(x, -1)
+    if shift:
+        want = oracle.fftshift_2d(want)
+    assert rel_l2(y, want) <= TOL
+    yi = c2c_2d(x, +1, shift, inplace=True)
+    want_i = oracle.c2c_2d(x, +1)
+    if shift:
+        want_i = oracle.fftshift_2d(want_i)
+    assert rel_l2(yi, want_i) <= TOL
+
+
+def test_shift_bit_exact_1d():
+    for n, batch in ((1024, 8), (4096, 3), (1 << 16, 2)):
+        say(f"shift bit-exact 1d n={n}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n))
+        ys = c2c(x, -1, shift=1)
+        xn = negate_odd(x, np.broadcast_to(np.arange(n), x.shape))
+        yr = c2c(xn, -1, shift=0)
+        assert np.array_equal(ys.view(np.uint32), yr.view(np.uint32))
+        # and the shift is the index rotation of the plain transform
+        assert rel_l2(ys, oracle.c2c(x, -1)[:, oracle.fftshift_index(n)]) <= TOL
+
+
+def test_shift_bit_exact_2d():
+    say("shift bit-exact 2d 256x512")
+    x = W.normal_c64((2, 256, 512), np.random.default_rng(11))
+    ys = c2c_2d(x, -1, shift=1)
+    ii, jj = np.meshgrid(np.arange(256), np.arange(512), indexing="ij")
+    xn = negate_odd(x, np.broadcast_to(ii + jj, x.shape))
+    yr = c2c_2d(xn, -1, shift=0)
+    assert np.array_equal(ys.view(np.uint32), yr.view(np.uint32))
+
+
+def test_w5_full_size():
+    """Workload 5: 8192 x 8192 image, 2D forward with the shift fused."""
+    p = W.W5
+    say("w5 generate")
+    x = W.workload5()
+    say("w5 2d 8192x8192 shift")
+    y = c2c_2d(x, -1, shift=1)
+    want = oracle.fftshift_2d(oracle.c2c_2d(x, -1))
+    e = rel_l2(y, want)
+    say(f"w5 rel_l2={e:.3e}")
+    assert e <= TOL
+    # the tones land on their shifted bins with height ny*nx*e^{i phase}
+    ky, kx, phase, _ = W.workload5_params()
+    ny, nx = p["ny"], p["nx"]
+    for s in range(p["tones"]):
+        i, j = (ky[s] + ny // 2) % ny, (kx[s] + nx // 2) % nx
+        want_peak = ny * nx * np.exp(1j * phase[s])
+        # other tones on the same bin add up; only check isolated ones
+        if np.sum((ky == ky[s]) & (kx == kx[s])) == 1:
+            assert abs(y[i, j] - want_peak) / abs(want_peak) < 1e-4
+
+
+# --------------------------------------------------------------------------
+# errors that need a live plan
+# --------------------------------------------------------------------------
+def test_exec_errors_and_state():
+    import torch
+    say("exec error paths")
+    plan = F.fft_plan_create(64, 4, F.FFT_R2C, F.FFT_FORWARD)
+    try:
+        x = torch.zeros(4 * 64, dtype=torch.float32, device="cuda")
+        lib = F.lib()
+        assert lib.fft_exec(plan, x.data_ptr(), x.data_ptr(), None) == F.FFT_EINVAL
+        assert lib.fft_exec(plan, x.data_ptr() + 4, x.data_ptr() + 1024, None) == F.FFT_EINVAL
+        assert lib.fft_exec(plan, None, x.data_ptr(), None) == F.FFT_EINVAL
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_MMAX, 33)
+        assert e.value.code == F.FFT_EINVAL
+        with pytest.raises(F.FFTError):
+            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)     # C2C only
+        y = empty((4, 33), torch.complex64)
+        F.fft_exec(plan, x, y)
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_MMAX, 3)
+        assert e.value.code == F.FFT_ESTATE
+        with pytest.raises(ValueError):
+            F.fft_exec(plan, x[:10], y)                   # too small for the plan
+        torch.cuda.synchronize()
+    finally:
+        F.fft_plan_destroy(plan)
+    assert F.fft_plan_get_sizes is not None
