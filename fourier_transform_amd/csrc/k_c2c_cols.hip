@@ -8,11 +8,11 @@ struct ColsOp {
   template <int N>
   struct At {
     static hipError_t run(const ColsArgs& a, hipStream_t st) {
-      constexpr int C = cols_per_wg(N);
+      constexpr int C = tile_lines(N, false);
       uint32_t grid;
       hipError_t e = grid_of(a.images * a.nx, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_c2c_cols<N, S, C>), dim3(grid), dim3(threads_per_line(N) * C), 0, st, a);
+      hipLaunchKernelGGL((k_c2c_cols<N, S>), dim3(grid), dim3(C * (N / tile_e(N, false))), 0, st, a);
       return hipGetLastError();
     }
   };

@@ -13,11 +13,11 @@ struct FsColsOp {
   template <int N2>
   struct At {
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
-      constexpr int C = cols_per_wg(N2);
+      constexpr int C = tile_lines(N2, false);
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_cols<N2, S, C>), dim3(grid), dim3(threads_per_line(N2) * C), 0, st, a);
+      hipLaunchKernelGGL((k_fs_cols<N2, S>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
       return hipGetLastError();
     }
   };
@@ -27,11 +27,11 @@ struct FsRowsOp {
   template <int N1>
   struct At {
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
-      constexpr int C = tposed_rows_per_wg(N1);
+      constexpr int C = tile_lines(N1, true);
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_rows<N1, S, C>), dim3(grid), dim3(threads_per_line(N1) * C), 0, st, a);
+      hipLaunchKernelGGL((k_fs_rows<N1, S>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
       return hipGetLastError();
     }
   };

@@ -3,34 +3,14 @@
 #pragma once
 
 #include "launch.hpp"
+#include "shapes.hpp"
 #include "stockham.hpp"
 
 namespace fftamd {
 
-// ---------------------------------------------------------------------------
-// workgroup shapes
-// ---------------------------------------------------------------------------
-constexpr int threads_per_line(int n) { return n / sched_e(n); }
-constexpr int row_lds_bytes(int n, int c) { return c * (n + (n >> 4) + 1) * 8; }
-constexpr int col_lds_bytes(int n, int c) { return (n * c + ((n * c) >> 4) + 1) * 8; }
+template <bool SPLIT>
+using lds_elem_t = typename std::conditional<SPLIT, float, float2>::type;
 
-// Row lanes: at least 256 threads per workgroup (several short rows share one).
-constexpr int rows_per_wg(int n) {
-  return threads_per_line(n) >= 256 ? 1 : 256 / threads_per_line(n);
-}
-// Column lanes: up to 16 adjacent lines (16 x 8 B = one 128 B segment per
-// element index) within the thread and LDS limits.
-constexpr int cols_per_wg(int n) {
-  int c = 16;
-  while (c > 1 && (c * threads_per_line(n) > kMaxThreads || col_lds_bytes(n, c) > kLdsBudgetBytes)) c /= 2;
-  return c;
-}
-// Row lanes with a transposing store (four-step pass 2): as many lines as fit.
-constexpr int tposed_rows_per_wg(int n) {
-  int c = 16;
-  while (c > 1 && (c * threads_per_line(n) > kMaxThreads || row_lds_bytes(n, c) > kLdsBudgetBytes)) c /= 2;
-  return c;
-}
 // Real transforms: whole rows, >= 8 rows per workgroup so that m-major
 // spectrum accesses form 64 B runs.
 constexpr int real_rows_per_wg(int h) {
@@ -53,13 +33,15 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2c_rows(RowsArgs a
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
-  const int64_t row = (int64_t)blockIdx.x * C + line;
+  const int64_t row0 = (int64_t)blockIdx.x * C;
+  const int64_t row = row0 + line;
   const bool valid = row < a.rows;
+  const uint32_t off = (uint32_t)(line * N + u);
   float2 v[E];
   if (valid) {
-    const float2* src = a.in + row * N;
+    const float2* src = a.in + row0 * N;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = src[u + T * m];
+    for (int m = 0; m < E; ++m) v[m] = gload(src, off + T * m);
     if (a.shift_mode) {
       const int par = a.shift_mode == 2 ? (int)(row & (a.rows_per_image - 1)) : 0;
 #pragma unroll
@@ -70,44 +52,59 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2c_rows(RowsArgs a
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N, S, WL, L>(v, lds, a.tw, u, line);
+  run_stages<N, E, S, WL, L, false>(v, lds, a.tw, u, line);
   if (valid) {
-    float2* dst = a.out + row * N;
+    float2* dst = a.out + row0 * N;
+    if (a.stream_store) {
 #pragma unroll
-    for (int m = 0; m < E; ++m) dst[u + T * m] = v[m];
+      for (int m = 0; m < E; ++m) gstore_nt(dst, off + T * m, v[m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < E; ++m) gstore(dst, off + T * m, v[m]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// C2C over columns of [images][N][nx] (2D column pass); in place allowed
+// C2C over columns of [images][N][nx] (2D column pass); in place allowed.
+// C adjacent columns per workgroup, consecutive threads on consecutive columns.
 // ---------------------------------------------------------------------------
-template <int N, int S, int C>
-__global__ __launch_bounds__(threads_per_line(N) * C) void k_c2c_cols(ColsArgs a) {
-  constexpr int E = sched_e(N);
+template <int N, int S>
+__global__ __launch_bounds__(tile_lines(N, false) * (N / tile_e(N, false))) void k_c2c_cols(ColsArgs a) {
+  constexpr int E = tile_e(N, false);
+  constexpr bool SPLIT = tile_split(N, false);
+  constexpr int C = tile_lines(N, false);
   constexpr int T = N / E;
   using L = ColLds<N, C>;
-  static_assert(col_lds_bytes(N, C) <= kLdsBudgetBytes, "LDS budget");
-  __shared__ float2 lds[L::size(C)];
+  __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
-  const int64_t g = (int64_t)blockIdx.x * C + line;
-  const bool valid = g < a.images * a.nx;
-  const int64_t img = g / a.nx, col = g - img * a.nx;
-  const float2* src = a.in + img * (int64_t)N * a.nx + col;
-  float2* dst = a.out + img * (int64_t)N * a.nx + col;
+  // the group's first column sets a uniform base; every element is then a
+  // 32-bit offset from it (a group spans several images only when nx < C)
+  const int64_t g0 = (int64_t)xcd_grouped_block(blockIdx.x, gridDim.x) * C;
+  const bool valid = g0 + line < a.images * a.nx;
+  const uint32_t nx = (uint32_t)a.nx;
+  const int64_t img0 = g0 / nx;
+  const uint32_t col0 = (uint32_t)(g0 - img0 * nx);
+  const int64_t base = img0 * (int64_t)N * nx + col0;
+  const uint32_t rel = (uint32_t)line + col0;
+  const uint32_t off = (rel / nx) * (uint32_t)N * nx + rel % nx - col0 + (uint32_t)u * nx;
+  const uint32_t step = (uint32_t)T * nx;
   float2 v[E];
   if (valid) {
+    const float2* src = a.in + base;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = src[(int64_t)(u + T * m) * a.nx];
+    for (int m = 0; m < E; ++m) v[m] = gload(src, off + step * m);
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N, S, false, L>(v, lds, a.tw, u, line);
+  run_stages<N, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
   if (valid) {
+    float2* dst = a.out + base;
 #pragma unroll
-    for (int m = 0; m < E; ++m) dst[(int64_t)(u + T * m) * a.nx] = v[m];
+    for (int m = 0; m < E; ++m) gstore(dst, off + step * m, v[m]);
   }
 }
 
@@ -139,7 +136,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<H, -1, WL, L>(v, lds, a.tw, u, line);
+  run_stages<H, E, -1, WL, L, false>(v, lds, a.tw, u, line);
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
@@ -234,7 +231,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
     v[m] = make_float2(s.x - b.y, s.y + b.x);
   }
   __syncthreads();
-  run_stages<H, +1, WL, L>(v, lds, a.tw, u, line);
+  run_stages<H, E, +1, WL, L, false>(v, lds, a.tw, u, line);
   if (valid) {
     float2* dst = static_cast<float2*>(a.out) + row * H;
 #pragma unroll
@@ -246,26 +243,31 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
 // Four-step pass 1: column transforms of length N2 over stride n1, each
 // output multiplied by W_n^{n1*k2}, stored in place of the column (to scratch)
 // ---------------------------------------------------------------------------
-template <int N2, int S, int C>
-__global__ __launch_bounds__(threads_per_line(N2) * C) void k_fs_cols(FourStepArgs a) {
-  constexpr int E = sched_e(N2);
+template <int N2, int S>
+__global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) void k_fs_cols(FourStepArgs a) {
+  constexpr int E = tile_e(N2, false);
+  constexpr bool SPLIT = tile_split(N2, false);
+  constexpr int C = tile_lines(N2, false);
   constexpr int T = N2 / E;
   using L = ColLds<N2, C>;
-  static_assert(col_lds_bytes(N2, C) <= kLdsBudgetBytes, "LDS budget");
-  __shared__ float2 lds[L::size(C)];
+  __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
-  const int64_t g = (int64_t)blockIdx.x * C + line;
-  const int64_t n1 = a.n1;
-  const bool valid = g < a.batch * n1;
-  const int64_t b = g / n1;
-  const int c1 = (int)(g - b * n1);
-  const int64_t base = b * n1 * N2 + c1;
+  // n1 >= 128 > C: the group's columns belong to one transform b
+  const int64_t g0 = (int64_t)xcd_grouped_block(blockIdx.x, gridDim.x) * C;
+  const uint32_t n1 = (uint32_t)a.n1;
+  const bool valid = g0 + line < a.batch * (int64_t)n1;
+  const int64_t b = g0 / n1;
+  const uint32_t c1 = (uint32_t)(g0 - b * n1) + line;
+  const int64_t base = b * (int64_t)n1 * N2 + (c1 - line);
+  const uint32_t off = (uint32_t)line + (uint32_t)u * n1;
+  const uint32_t step = (uint32_t)T * n1;
   float2 v[E];
   if (valid) {
+    const float2* src = a.in + base;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = a.in[base + (int64_t)(u + T * m) * n1];
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + step * m);
     if (a.shift && (c1 & 1)) {  // element index c1 + n1*k has the parity of c1 (n1 even)
 #pragma unroll
       for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
@@ -274,58 +276,104 @@ __global__ __launch_bounds__(threads_per_line(N2) * C) void k_fs_cols(FourStepAr
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N2, S, false, L>(v, lds, a.tw, u, line);
+  run_stages<N2, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
   if (valid) {
     const uint32_t mask = (1u << a.bits) - 1u;
+    float2* dst = a.out + base;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      const uint32_t e = (uint32_t)c1 * (uint32_t)(u + T * m);
-      const float2 w = cmul(a.thi[e >> a.bits], a.tlo[e & mask]);
-      a.out[base + (int64_t)(u + T * m) * n1] = apply_tw<S>(v[m], w);
+      const uint32_t e = c1 * (uint32_t)(u + T * m);
+      const float2 w = cmul(gload(a.thi, e >> a.bits), gload(a.tlo, e & mask));
+      gstore_nt(dst, off + step * m, apply_tw<S>(v[m], w));
+      if constexpr (E > 16) {
+        if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Four-step pass 2: row transforms of length N1 over contiguous rows k2,
-// element k1 stored at k2 + n2*k1 (through LDS so the stores are coalesced)
+// element k1 stored at k2 + n2*k1.  The results go through LDS once more and
+// come back out with consecutive threads on consecutive rows, so each store
+// is a run of C elements.
 // ---------------------------------------------------------------------------
-template <int N1, int S, int C>
-__global__ __launch_bounds__(threads_per_line(N1) * C) void k_fs_rows(FourStepArgs a) {
-  constexpr int E = sched_e(N1);
+template <int N1, int S>
+__global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) void k_fs_rows(FourStepArgs a) {
+  constexpr int E = tile_e(N1, true);
+  constexpr bool SPLIT = tile_split(N1, true);
+  constexpr int C = tile_lines(N1, true);
   constexpr int T = N1 / E;
+  constexpr int NT = C * T;
   constexpr bool WL = T <= 64;
   using L = RowLds<N1>;
-  static_assert(row_lds_bytes(N1, C) <= kLdsBudgetBytes, "LDS budget");
-  __shared__ float2 lds[L::size(C)];
+  __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
   const int64_t n2 = a.n2;
   const int64_t lines = a.batch * n2;
-  const int64_t g = (int64_t)blockIdx.x * C + line;
-  const bool valid = g < lines;
+  const int64_t g0 = (int64_t)xcd_grouped_block(blockIdx.x, gridDim.x) * C;
+  const int64_t g = g0 + line;
   float2 v[E];
-  if (valid) {
-    const float2* src = a.in + g * N1;  // row k2 of transform b is at (b*n2 + k2)*N1
+  if (g < lines) {
+    const float2* src = a.in + g0 * N1;  // row k2 of transform b is at (b*n2 + k2)*N1
+    const uint32_t off = (uint32_t)(line * N1 + u);
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = src[u + T * m];
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N1, S, WL, L>(v, lds, a.tw, u, line);
+  run_stages<N1, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
+  // transposed read-back: slot p of thread tid is q = tid + NT*p, i.e. line
+  // q % C, element q / C
   __syncthreads();
+  if constexpr (SPLIT) {
 #pragma unroll
-  for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
-  __syncthreads();
-  for (int q = tid; q < C * N1; q += C * T) {
-    const int ln = q % C, k1 = q / C;
-    const int64_t gg = (int64_t)blockIdx.x * C + ln;
-    if (gg >= lines) continue;
-    const int64_t b = gg / n2;
-    const int64_t k2 = gg - b * n2;
-    a.out[b * n2 * N1 + (int64_t)k1 * n2 + k2] = lds[L::at(ln, k1)];
+    for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m].x;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < E; ++p) {
+      const int q = tid + NT * p;
+      v[p].x = lds[L::at(q % C, q / C)];
+    }
+    __syncthreads();
+    int u2 = u, line2 = line, tid2 = tid;  // recompute addresses (see run_stage)
+    asm volatile("" : "+v"(u2), "+v"(line2), "+v"(tid2));
+#pragma unroll
+    for (int m = 0; m < E; ++m) lds[L::at(line2, u2 + T * m)] = v[m].y;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < E; ++p) {
+      const int q = tid2 + NT * p;
+      v[p].y = lds[L::at(q % C, q / C)];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < E; ++p) {
+      const int q = tid + NT * p;
+      v[p] = lds[L::at(q % C, q / C)];
+    }
+  }
+  const int ln = tid % C;  // the same line for every slot p (NT is a multiple of C)
+  if (g0 + ln < lines) {
+    // n2 >= 128 > C: the group's rows belong to one transform b
+    const int64_t b = g0 / n2;
+    const int64_t k20 = g0 - b * n2;
+    float2* dst = a.out + b * n2 * N1 + k20;
+    const uint32_t off = (uint32_t)ln + (uint32_t)(tid / C) * (uint32_t)n2;
+    const uint32_t step = (uint32_t)(NT / C) * (uint32_t)n2;
+#pragma unroll
+    for (int p = 0; p < E; ++p) {
+      gstore_nt(dst, off + step * p, v[p]);
+      if constexpr (E > 16) {
+        if ((p & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 }
 

@@ -21,6 +21,7 @@ struct RowsArgs {
   int64_t rows;
   int shift_mode;
   int64_t rows_per_image;
+  int stream_store;  // 1: non-temporal stores (output not re-read soon)
 };
 hipError_t launch_c2c_rows(int n, int sign, const RowsArgs& a, hipStream_t stream);
 

@@ -14,6 +14,7 @@
 
 #include "../../include/fft.h"
 #include "launch.hpp"
+#include "shapes.hpp"
 #include "stockham.hpp"
 
 using namespace fftamd;
@@ -53,11 +54,12 @@ float2 root(int64_t e, int64_t len) {  // e^{-2 pi i e/len}, 0 <= e < len
   return make_float2((float)std::cos(a), (float)-std::sin(a));
 }
 
-// stage table of the single-pass schedule for length n (layout: stockham.hpp)
-void append_stage_table(int n, std::vector<float2>& t) {
-  const int stages = sched_stages(n);
+// stage table of the radix schedule for length n with e values per thread
+// (layout: stockham.hpp, run_stage)
+void append_stage_table(int n, int e, std::vector<float2>& t) {
+  const int stages = sched_stages(n, e);
   for (int s = 1; s < stages; ++s) {
-    const int R = sched_radix(n, s), NS = sched_ns(n, s);
+    const int R = sched_radix(n, e, s), NS = sched_ns(n, e, s);
     for (int r = 1; r < R; ++r)
       for (int j = 0; j < NS; ++j) t.push_back(root((int64_t)r * j, (int64_t)NS * R));
   }
@@ -178,7 +180,7 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   std::vector<const float2**> slots;
   size_t scratch = 0;
   if (kind == FFT_C2C && n <= kMaxSinglePass) {
-    append_stage_table((int)n, ta);
+    append_stage_table((int)n, rows_values((int)n), ta);
     parts = {&ta};
     slots = {&p->tw_a};
   } else if (kind == FFT_C2C) {
@@ -187,15 +189,15 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     p->n1 = 1 << (L / 2);
     p->n2 = 1 << (L - L / 2);
     p->bits = L - L / 2;
-    append_stage_table(p->n1, ta);
-    append_stage_table(p->n2, tb);
+    append_stage_table(p->n1, tposed_values(p->n1), ta);
+    append_stage_table(p->n2, cols_values(p->n2), tb);
     for (int64_t h = 0; h < (n >> p->bits); ++h) thi.push_back(root(h << p->bits, n));
     for (int64_t l = 0; l < (int64_t(1) << p->bits); ++l) tlo.push_back(root(l, n));
     parts = {&ta, &tb, &thi, &tlo};
     slots = {&p->tw_a, &p->tw_b, &p->thi, &p->tlo};
     scratch = (size_t)(n * batch) * sizeof(float2);
   } else {
-    append_stage_table((int)(n / 2), ta);
+    append_stage_table((int)(n / 2), rows_values((int)(n / 2)), ta);
     for (int64_t k = 0; k <= n / 2; ++k) trt.push_back(root(k, n));
     parts = {&ta, &trt};
     slots = {&p->tw_a, &p->rt};
@@ -229,8 +231,8 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   p->kind = kind;
   p->sign = sign;
   std::vector<float2> ta, tb;
-  append_stage_table((int)nx, ta);
-  append_stage_table((int)ny, tb);
+  append_stage_table((int)nx, rows_values((int)nx), ta);
+  append_stage_table((int)ny, cols_values((int)ny), tb);
   if (finish_plan(p, {&ta, &tb}, {&p->tw_a, &p->tw_b}, 0) != FFT_OK) {
     free_plan(p);
     return nullptr;
@@ -297,7 +299,7 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
   if (p->kind == FFT_C2C && p->dims == 1 && !p->fourstep) {
-    RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1};
+    RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1, 1};
     e = launch_c2c_rows((int)p->n, p->sign, a, stream);
   } else if (p->kind == FFT_C2C && p->dims == 1) {
     FourStepArgs a{src, p->scratch, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, p->shift};
@@ -307,7 +309,7 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       e = launch_fourstep_rows(p->n1, p->sign, b, stream);
     }
   } else if (p->kind == FFT_C2C) {
-    RowsArgs a{src, dst, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny};
+    RowsArgs a{src, dst, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny, 0};
     e = launch_c2c_rows((int)p->nx, p->sign, a, stream);
     if (e == hipSuccess) {
       ColsArgs c{dst, dst, p->tw_b, p->ny, p->nx, p->batch};

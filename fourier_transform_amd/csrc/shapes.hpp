@@ -1,0 +1,54 @@
+// shapes.hpp -- workgroup shapes of the kernels (lines per workgroup, values
+// per thread, LDS exchange mode).  Shared by the kernels and by the host code
+// that builds each kernel's twiddle table, which depends on the values per
+// thread through the radix schedule.
+#pragma once
+
+#include "stockham.hpp"
+
+namespace fftamd {
+
+// ---------------------------------------------------------------------------
+// workgroup shapes
+// ---------------------------------------------------------------------------
+constexpr int threads_per_line(int n) { return n / sched_e(n); }
+constexpr int row_lds_bytes(int n, int c) { return c * (n + (n >> 4) + 1) * 8; }
+constexpr int col_lds_bytes(int n, int c) { return (n * c + ((n * c) >> 4) + 1) * 8; }
+
+// Row lanes: at least 256 threads per workgroup (several short rows share one).
+constexpr int rows_per_wg(int n) {
+  return threads_per_line(n) >= 256 ? 1 : 256 / threads_per_line(n);
+}
+// Workgroups whose lines are read with a stride (column lanes) or stored
+// transposed (row lanes + transposing store) hold up to 16 adjacent lines, so
+// every strided access is a run of 16 x 8 B = 128 B.  When 16 values per
+// thread with a complex LDS exchange cannot hold enough lines, 64 values per
+// thread (<= 512 threads, so up to 256 VGPRs per lane) with the exchange split
+// into real and imaginary halves (half the LDS per line) is used instead.
+constexpr int kSplitValues = 64;
+constexpr int tile_lds_elems(int n, int c, bool rowlanes) {
+  return rowlanes ? c * (n + (n >> 4) + 1) : n * c + ((n * c) >> 4) + 1;
+}
+constexpr bool tile_fits(int n, int e, int c, bool split, bool rowlanes) {
+  return e <= n && c * (n / e) <= kMaxThreads &&
+         tile_lds_elems(n, c, rowlanes) * (split ? 4 : 8) <= kLdsBudgetBytes;
+}
+constexpr int tile_c(int n, int e, bool split, bool rowlanes) {
+  int c = 16;
+  while (c > 1 && !tile_fits(n, e, c, split, rowlanes)) c /= 2;
+  return c;
+}
+constexpr bool tile_split(int n, bool rowlanes) {
+  return n >= 2 * kSplitValues &&
+         tile_c(n, kSplitValues, true, rowlanes) > tile_c(n, sched_e(n), false, rowlanes);
+}
+constexpr int tile_e(int n, bool rowlanes) { return tile_split(n, rowlanes) ? kSplitValues : sched_e(n); }
+constexpr int tile_lines(int n, bool rowlanes) {
+  return tile_c(n, tile_e(n, rowlanes), tile_split(n, rowlanes), rowlanes);
+}
+// values per thread of each kernel family (selects the radix schedule)
+constexpr int rows_values(int n) { return sched_e(n); }           // k_c2c_rows, k_r2c, k_c2r
+constexpr int cols_values(int n) { return tile_e(n, false); }     // k_c2c_cols, k_fs_cols
+constexpr int tposed_values(int n) { return tile_e(n, true); }    // k_fs_rows
+
+}  // namespace fftamd

@@ -35,25 +35,40 @@ constexpr int ilog2c(int64_t n) {
   while ((int64_t(1) << l) < n) ++l;
   return l;
 }
-// values held per thread
+// Default values held per thread (row kernels): 16.
 constexpr int sched_e(int n) { return n < 16 ? n : 16; }
-// number of radix-16 stages and the leftover radix (1 = none)
-constexpr int sched_n16(int n) { return n < 16 ? 0 : ilog2c(n) / 4; }
-constexpr int sched_rem(int n) { return n < 16 ? n : (1 << (ilog2c(n) % 4)); }
-constexpr int sched_stages(int n) { return sched_n16(n) + (sched_rem(n) > 1 ? 1 : 0); }
-constexpr int sched_radix(int n, int s) { return s < sched_n16(n) ? 16 : sched_rem(n); }
-constexpr int sched_ns(int n, int s) {
+// Radix schedule for E values per thread.  The first stage (no twiddles)
+// takes radix min(E, 64, n); later stages take radix min(E, 32) and the
+// leftover power of two comes last.  With E = 16 this is all radix 16; with
+// E = 64 a 2048-point line is 64 x 32, one LDS exchange.  A twiddled radix-64
+// stage would need more than 256 VGPRs, hence the cap of 32 after stage 0.
+constexpr int sched_r0(int n, int e) {
+  int r = e < 64 ? e : 64;
+  return r < n ? r : n;
+}
+constexpr int sched_rmax(int e) { return e < 32 ? e : 32; }
+constexpr int sched_nfull(int n, int e) {
+  return ilog2c(n / sched_r0(n, e)) / ilog2c(sched_rmax(e));
+}
+constexpr int sched_rem(int n, int e) {
+  return 1 << (ilog2c(n / sched_r0(n, e)) % ilog2c(sched_rmax(e)));
+}
+constexpr int sched_stages(int n, int e) { return 1 + sched_nfull(n, e) + (sched_rem(n, e) > 1 ? 1 : 0); }
+constexpr int sched_radix(int n, int e, int s) {
+  return s == 0 ? sched_r0(n, e) : (s - 1 < sched_nfull(n, e) ? sched_rmax(e) : sched_rem(n, e));
+}
+constexpr int sched_ns(int n, int e, int s) {
   int p = 1;
-  for (int t = 0; t < s; ++t) p *= sched_radix(n, t);
+  for (int t = 0; t < s; ++t) p *= sched_radix(n, e, t);
   return p;
 }
 // offset of stage s in the twiddle table (stage 0 needs none)
-constexpr int sched_tw_off(int n, int s) {
+constexpr int sched_tw_off(int n, int e, int s) {
   int o = 0;
-  for (int t = 1; t < s; ++t) o += (sched_radix(n, t) - 1) * sched_ns(n, t);
+  for (int t = 1; t < s; ++t) o += (sched_radix(n, e, t) - 1) * sched_ns(n, e, t);
   return o;
 }
-constexpr int sched_tw_size(int n) { return sched_tw_off(n, sched_stages(n)); }
+constexpr int sched_tw_size(int n, int e) { return sched_tw_off(n, e, sched_stages(n, e)); }
 
 // Longest line held in one workgroup: 16384 complex = 128 KiB (+1/16 padding)
 // of the 160 KiB of LDS a gfx950 workgroup may use.
@@ -86,6 +101,31 @@ __device__ __forceinline__ float2 apply_tw(float2 v, float2 w) {
   return S < 0 ? cmul(v, w) : cmulc(v, w);
 }
 
+// Global accesses as a wave-uniform base pointer plus an unsigned 32-bit
+// element offset: the compiler then uses the SGPR-base form of the global
+// memory instructions (one 32-bit VGPR per address instead of a 64-bit pair
+// built with 64-bit multiply-adds).  Offsets must stay below 2^29 elements.
+__device__ __forceinline__ float2 gload(const float2* __restrict__ base, uint32_t i) {
+  return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(base) + (i << 3));
+}
+__device__ __forceinline__ void gstore(float2* base, uint32_t i, float2 v) {
+  *reinterpret_cast<float2*>(reinterpret_cast<char*>(base) + (i << 3)) = v;
+}
+// Streaming variants (non-temporal hint) for data touched once.  Used where
+// measurement shows they help: stores of whole rows, and both directions of
+// the four-step passes.  Not for the 2D column pass, whose 32 B runs rely on
+// neighbouring workgroups meeting in L2.
+typedef float fftamd_v2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 gload_nt(const float2* __restrict__ base, uint32_t i) {
+  const fftamd_v2f w = __builtin_nontemporal_load(
+      reinterpret_cast<const fftamd_v2f*>(reinterpret_cast<const char*>(base) + (i << 3)));
+  return make_float2(w.x, w.y);
+}
+__device__ __forceinline__ void gstore_nt(float2* base, uint32_t i, float2 v) {
+  const fftamd_v2f w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<fftamd_v2f*>(reinterpret_cast<char*>(base) + (i << 3)));
+}
+
 // flip the sign bits of both parts: exact multiplication by -1
 __device__ __forceinline__ float2 negate_bits(float2 v) {
   return make_float2(__uint_as_float(__float_as_uint(v.x) ^ 0x80000000u),
@@ -93,55 +133,61 @@ __device__ __forceinline__ float2 negate_bits(float2 v) {
 }
 
 // ---------------------------------------------------------------------------
-// constant twiddles of the in-register DFTs (R <= 16), in units of 2*pi/16
-// cos(pi/4), cos(pi/8), sin(pi/8) written to 20 digits, rounded once to fp32
+// constant twiddles of the in-register DFTs (R <= 64), in units of 2*pi/64:
+// cos(pi*k/32), k = 0..16, written to 22 digits and rounded once to fp32
 // ---------------------------------------------------------------------------
-#define FFTAMD_C8 0.70710678118654752440f
-#define FFTAMD_C16 0.92387953251128675613f
-#define FFTAMD_S16 0.38268343236508977173f
-
-__host__ __device__ constexpr float cos16(int k) {
-  switch (k & 15) {
+__host__ __device__ constexpr float cos64_q(int k) {  // 0 <= k <= 16
+  switch (k) {
     case 0: return 1.0f;
-    case 1: return FFTAMD_C16;
-    case 2: return FFTAMD_C8;
-    case 3: return FFTAMD_S16;
-    case 4: return 0.0f;
-    case 5: return -FFTAMD_S16;
-    case 6: return -FFTAMD_C8;
-    case 7: return -FFTAMD_C16;
-    case 8: return -1.0f;
-    case 9: return -FFTAMD_C16;
-    case 10: return -FFTAMD_C8;
-    case 11: return -FFTAMD_S16;
-    case 12: return 0.0f;
-    case 13: return FFTAMD_S16;
-    case 14: return FFTAMD_C8;
-    default: return FFTAMD_C16;
+    case 1: return 0.9951847266721968862448f;
+    case 2: return 0.9807852804032304491262f;
+    case 3: return 0.9569403357322088649358f;
+    case 4: return 0.9238795325112867561282f;
+    case 5: return 0.8819212643483550297128f;
+    case 6: return 0.8314696123025452370788f;
+    case 7: return 0.7730104533627369608109f;
+    case 8: return 0.7071067811865475244008f;
+    case 9: return 0.6343932841636454982152f;
+    case 10: return 0.5555702330196022247428f;
+    case 11: return 0.4713967368259976485564f;
+    case 12: return 0.3826834323650897717285f;
+    case 13: return 0.2902846772544623676362f;
+    case 14: return 0.1950903220161282678483f;
+    case 15: return 0.0980171403295606019942f;
+    default: return 0.0f;
   }
 }
-__host__ __device__ constexpr float sin16(int k) { return cos16(k - 4); }
+// cos(2*pi*k/64) for any k, by the symmetries of the quarter wave
+__host__ __device__ constexpr float cos64(int k) {
+  k &= 63;
+  if (k <= 16) return cos64_q(k);
+  if (k <= 32) return -cos64_q(32 - k);
+  if (k <= 48) return -cos64_q(k - 32);
+  return cos64_q(64 - k);
+}
+__host__ __device__ constexpr float sin64(int k) { return cos64(k - 16); }
 
-// v * e^{S * 2*pi*i * K/R}, K and R compile-time, R | 16
+// v * e^{S * 2*pi*i * K/R}, K and R compile-time, R | 64
 template <int R, int K, int S>
 __device__ __forceinline__ float2 twc(float2 v) {
-  constexpr int k = ((K * (16 / R)) % 16 + 16) % 16;
+  constexpr int k = ((K * (64 / R)) % 64 + 64) % 64;
   if constexpr (k == 0) {
     return v;
-  } else if constexpr (k == 4) {
+  } else if constexpr (k == 16) {
     return mul_si<S>(v);
-  } else if constexpr (k == 8) {
+  } else if constexpr (k == 32) {
     return make_float2(-v.x, -v.y);
-  } else if constexpr (k == 12) {
+  } else if constexpr (k == 48) {
     return mul_si<-S>(v);
-  } else if constexpr ((k & 1) == 0) {
+  } else if constexpr ((k & 15) == 8) {
     // odd multiple of pi/4: both parts of the factor have magnitude cos(pi/4)
-    constexpr float sc = cos16(k) > 0 ? 1.0f : -1.0f;
-    constexpr float ss = (S > 0 ? 1.0f : -1.0f) * (sin16(k) > 0 ? 1.0f : -1.0f);
-    return make_float2(FFTAMD_C8 * (sc * v.x - ss * v.y), FFTAMD_C8 * (ss * v.x + sc * v.y));
+    constexpr float c8 = cos64_q(8);
+    constexpr float sc = cos64(k) > 0 ? 1.0f : -1.0f;
+    constexpr float ss = (S > 0 ? 1.0f : -1.0f) * (sin64(k) > 0 ? 1.0f : -1.0f);
+    return make_float2(c8 * (sc * v.x - ss * v.y), c8 * (ss * v.x + sc * v.y));
   } else {
-    constexpr float c = cos16(k);
-    constexpr float s = (S > 0 ? 1.0f : -1.0f) * sin16(k);
+    constexpr float c = cos64(k);
+    constexpr float s = (S > 0 ? 1.0f : -1.0f) * sin64(k);
     return make_float2(v.x * c - v.y * s, v.x * s + v.y * c);
   }
 }
@@ -157,7 +203,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // In-register R-point DFT, natural order in and out:
 // y_k = sum_j x_j e^{S 2 pi i jk/R}.  R = 2 and 4 are written out (Mota,
 // section 2.3, Equations 7-8); 8 and 16 split into even and odd halves
-// (section 2.3.1, Equation 9).
+// (section 2.3.1, Equation 9); 32 = 4 x 8 and 64 = 8 x 8 use the same
+// two-factor split as the four-step pass (transforms over the coarse index,
+// constant twiddles, transforms over the fine index), all indices compile-time.
 template <int R, int S>
 __device__ __forceinline__ void dft(float2* x) {
   if constexpr (R == 1) {
@@ -174,7 +222,7 @@ __device__ __forceinline__ void dft(float2* x) {
     x[1] = cadd(b, d);
     x[2] = csub(a, c);
     x[3] = csub(b, d);
-  } else {
+  } else if constexpr (R <= 16) {
     constexpr int H = R / 2;
     float2 e[H], o[H];
 #pragma unroll
@@ -189,6 +237,31 @@ __device__ __forceinline__ void dft(float2* x) {
       float2 t = twc<R, k, S>(o[k]);
       x[k] = cadd(e[k], t);
       x[k + H] = csub(e[k], t);
+    });
+  } else {
+    // R = A*B, input index a + A*b, output index kb + B*ka
+    constexpr int A = R == 32 ? 4 : 8;
+    constexpr int B = R / A;
+    float2 y[R];
+    static_for<0, A>([&](auto ac) {
+      constexpr int a = decltype(ac)::value;
+      float2 t[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) t[b] = x[a + A * b];
+      dft<B, S>(t);
+      static_for<0, B>([&](auto kc) {
+        constexpr int kb = decltype(kc)::value;
+        y[a + A * kb] = twc<R, a * kb, S>(t[kb]);
+      });
+    });
+    static_for<0, B>([&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      float2 t[A];
+#pragma unroll
+      for (int a = 0; a < A; ++a) t[a] = y[a + A * kb];
+      dft<A, S>(t);
+#pragma unroll
+      for (int ka = 0; ka < A; ++ka) x[kb + B * ka] = t[ka];
     });
   }
 }
@@ -230,53 +303,112 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// the stages.  On entry and exit v[m] holds element u + T*m of `line`.
+// the stages.  E values per thread (E a multiple of every radix, T = N/E
+// threads per line).  On entry and exit v[m] holds element u + T*m of `line`.
 // tw: forward twiddles of all stages (stage s, factor r, index j at
 // sched_tw_off(N,s) + (r-1)*NS + j holds e^{-2 pi i r j/(NS*R)}).
+// SPLIT = false: LDS holds float2 and one exchange is write, barrier, read.
+// SPLIT = true: LDS holds floats and the real parts are exchanged, then the
+// imaginary parts, so a workgroup can hold twice as many lines in the same
+// LDS; the butterfly outputs wait in v meanwhile, so no extra registers.
 // On return other threads may still be reading LDS: synchronise before
 // writing it again.
 // ---------------------------------------------------------------------------
-template <int N, int S, bool WAVE_LOCAL, class Lds>
-__device__ __forceinline__ void run_stages(float2* v, float2* lds, const float2* __restrict__ tw,
-                                           int u, int line) {
-  constexpr int E = sched_e(N);
+template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, int s, class LdsT>
+__device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __restrict__ tw, int u,
+                                          int line) {
+  static_assert(SPLIT == std::is_same<LdsT, float>::value, "LDS element type");
   constexpr int T = N / E;
-  constexpr int NST = sched_stages(N);
-  static_for<0, NST>([&](auto sc) {
-    constexpr int s = decltype(sc)::value;
-    constexpr int R = sched_radix(N, s);
-    constexpr int NS = sched_ns(N, s);
-    constexpr int KB = E / R;
-    constexpr bool last = (s == NST - 1);
-    constexpr int OFF = sched_tw_off(N, s);
+  constexpr int NST = sched_stages(N, E);
+  constexpr int R = sched_radix(N, E, s);
+  constexpr int NS = sched_ns(N, E, s);
+  constexpr int KB = E / R;
+  static_assert(KB * R == E, "radix must divide the values per thread");
+  constexpr bool last = (s == NST - 1);
+  constexpr int OFF = sched_tw_off(N, E, s);
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    float2 x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = v[k + r * KB];
+    const int b = u + T * k;
+    const int j = b & (NS - 1);
+    if constexpr (s > 0) {
+#pragma unroll
+      for (int r = 1; r < R; ++r) {
+        x[r] = apply_tw<S>(x[r], gload(tw, (uint32_t)(OFF + (r - 1) * NS + j)));
+        // bound the twiddle loads in flight for large radices (VGPR budget)
+        if constexpr (R > 16) {
+          if ((r & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    dft<R, S>(x);
+    if constexpr (last || SPLIT) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[k + r * KB] = x[r];
+    } else {
+      const int base = (b - j) * R + j;
+#pragma unroll
+      for (int r = 0; r < R; ++r) lds[Lds::at(line, base + r * NS)] = x[r];
+    }
+    // keep the scheduler from hoisting the next butterflies' twiddle loads
+    // above this one: with many values per thread that would exhaust VGPRs
+    if constexpr (KB > 1 && E > 16) __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!last && !SPLIT) {
+    lds_sync<WAVE_LOCAL>();
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = lds[Lds::at(line, u + T * m)];
+    if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
+  } else if constexpr (!last && SPLIT) {
+    // real parts
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      float2 x[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) x[r] = v[k + r * KB];
       const int b = u + T * k;
-      const int j = b & (NS - 1);
-      if constexpr (s > 0) {
+      const int base = (b - (b & (NS - 1))) * R + (b & (NS - 1));
 #pragma unroll
-        for (int r = 1; r < R; ++r) x[r] = apply_tw<S>(x[r], tw[OFF + (r - 1) * NS + j]);
-      }
-      dft<R, S>(x);
-      if constexpr (last) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) v[k + r * KB] = x[r];
-      } else {
-        const int base = (b - j) * R + j;
-#pragma unroll
-        for (int r = 0; r < R; ++r) lds[Lds::at(line, base + r * NS)] = x[r];
-      }
+      for (int r = 0; r < R; ++r) lds[Lds::at(line, base + r * NS)] = v[k + r * KB].x;
     }
-    if constexpr (!last) {
-      lds_sync<WAVE_LOCAL>();
+    lds_sync<WAVE_LOCAL>();
 #pragma unroll
-      for (int m = 0; m < E; ++m) v[m] = lds[Lds::at(line, u + T * m)];
-      if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
+    for (int m = 0; m < E; ++m) v[m].x = lds[Lds::at(line, u + T * m)];
+    lds_sync<WAVE_LOCAL>();
+    // imaginary parts (v[.].y still hold the butterfly outputs).  The empty
+    // asm hides that the indices are unchanged, so the padded LDS addresses
+    // are recomputed rather than kept live across the barriers (2*E VGPRs).
+    int u2 = u, line2 = line;
+    asm volatile("" : "+v"(u2), "+v"(line2));
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int b = u2 + T * k;
+      const int base = (b - (b & (NS - 1))) * R + (b & (NS - 1));
+#pragma unroll
+      for (int r = 0; r < R; ++r) lds[Lds::at(line2, base + r * NS)] = v[k + r * KB].y;
     }
+    lds_sync<WAVE_LOCAL>();
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m].y = lds[Lds::at(line2, u2 + T * m)];
+    if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
+  }
+}
+
+template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, class LdsT>
+__device__ __forceinline__ void run_stages(float2* v, LdsT* lds, const float2* __restrict__ tw,
+                                           int u, int line) {
+  static_for<0, sched_stages(N, E)>([&](auto sc) {
+    run_stage<N, E, S, WAVE_LOCAL, Lds, SPLIT, decltype(sc)::value>(v, lds, tw, u, line);
   });
+}
+
+// Blocks are dispatched to the 8 XCDs of the chip round-robin by index, and
+// each XCD has its own L2.  Renumber them so that the blocks one XCD runs at
+// the same time handle adjacent line groups: their short strided runs then
+// share L2 lines instead of being fetched separately by 8 XCDs.
+__device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t b, uint32_t nblocks) {
+  const uint32_t full = nblocks & ~7u;
+  if (b >= full) return b;
+  return (b & 7u) * (full >> 3) + (b >> 3);
 }
 
 }  // namespace fftamd
