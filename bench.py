@@ -67,6 +67,11 @@ def workload_spec(name):
     if name == "w3":
         return dict(kind="c2c", n=W.W3["n"], batch=W.W3["batch"], dirs=(-1,), gen=W.workload3,
                     passes=2, label="1D C2C fp32 forward N=2^22 batch=32 (four-step)")
+    if name == "w4":
+        return dict(kind="real", n=W.W4["nphi"], batch=W.W4["nlat"], mmax=W.W4["mmax"], dirs=(1, -1),
+                    gen=W.workload4_spectrum, passes=1,
+                    label="real rows nlat=1024 x nphi=2048, C2R synthesis then R2C analysis, "
+                          "mmax=682, m-major spectrum")
     if name == "w5":
         return dict(kind="2d", n=W.W5["ny"] * W.W5["nx"], ny=W.W5["ny"], nx=W.W5["nx"], batch=1,
                     dirs=(-1,), gen=W.workload5, passes=2,
@@ -74,31 +79,49 @@ def workload_spec(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def cpu_baseline(spec, x_host):
-    """Time the f64 oracle on a bounded sample of the workload."""
+def cpu_baseline(spec, x_host, reps=3):
+    """Time the f64 oracle (as it stands, untuned) on the host cores.
+
+    The sample is the whole workload when it is small enough, else its first
+    rows up to 2^27 points (a few seconds of work at most); the reported time
+    is the median of `reps` runs and excludes the fp32 -> f64 widening.
+    """
     import numpy as np
     import oracle
     n = spec["n"]
-    if spec["kind"] == "2d":
-        sample_rows = 1
+    if spec["kind"] == "real":
+        rows = spec["batch"]
+        xs = np.ascontiguousarray(x_host.T).astype(np.complex128)   # [rows][mmax+1]
+
+        def run():
+            oracle.r2c(oracle.c2r(xs, n, spec["mmax"]), spec["mmax"])
+        flops = 2.5 * n * math.log2(n) * rows * 2
+        desc = f"all {rows} rows, C2R then R2C"
+    elif spec["kind"] == "2d":
         xs = x_host.astype(np.complex128)
-        t0 = time.perf_counter()
-        for s in spec["dirs"]:
-            oracle.c2c_2d(xs, s)
-        dt = time.perf_counter() - t0
+
+        def run():
+            for s in spec["dirs"]:
+                oracle.c2c_2d(xs, s)
+        flops = 5.0 * n * math.log2(n) * len(spec["dirs"])
         desc = f"whole {spec['ny']}x{spec['nx']} image, {len(spec['dirs'])} direction(s)"
     else:
-        budget_rows = max(1, min(spec["batch"], (1 << 24) // n))   # <= 16M points
-        sample_rows = budget_rows
-        xs = x_host[:sample_rows].astype(np.complex128)
+        rows = max(1, min(spec["batch"], (1 << 27) // n))
+        xs = x_host[:rows].astype(np.complex128)
+
+        def run():
+            for s in spec["dirs"]:
+                oracle.c2c(xs, s)
+        flops = 5.0 * n * math.log2(n) * rows * len(spec["dirs"])
+        desc = f"{rows} of {spec['batch']} rows, {len(spec['dirs'])} direction(s)"
+    times = []
+    for _ in range(reps):
         t0 = time.perf_counter()
-        for s in spec["dirs"]:
-            oracle.c2c(xs, s)
-        dt = time.perf_counter() - t0
-        desc = f"{sample_rows} of {spec['batch']} rows, {len(spec['dirs'])} direction(s)"
-    flops = 5.0 * n * math.log2(n) * sample_rows * len(spec["dirs"])
+        run()
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(0),
-            "kind": "oracle", "sample": desc + f", {dt:.2f} s"}
+            "kind": "oracle", "sample": desc + f", median of {reps} runs, {dt:.3f} s each"}
 
 
 def main():
@@ -106,7 +129,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w5"])
+    ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w4", "w5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -125,10 +148,18 @@ def main():
     n, batch = spec["n"], spec["batch"]
     x_host = spec["gen"]()
     xd = torch.from_numpy(x_host).cuda()
-    bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
+    if spec["kind"] == "real":
+        # synthesis: m-major spectrum -> real rows; analysis: real rows -> spectrum
+        bufs = [torch.empty((batch, n), dtype=torch.float32, device="cuda"), torch.empty_like(xd)]
+    else:
+        bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
     plans = []
     for s in spec["dirs"]:
-        if spec["kind"] == "2d":
+        if spec["kind"] == "real":
+            p = F.fft_plan_create(n, batch, F.FFT_C2R if s > 0 else F.FFT_R2C, s)
+            F.fft_plan_set(p, F.FFT_OPT_MMAX, spec["mmax"])
+            F.fft_plan_set(p, F.FFT_OPT_SPEC_LAYOUT, 1)
+        elif spec["kind"] == "2d":
             p = F.fft_plan_create_2d(spec["ny"], spec["nx"], batch, F.FFT_C2C, s)
             F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
         else:
@@ -136,32 +167,30 @@ def main():
         plans.append(p)
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step():
         src = xd
-        for i, (p, dst) in enumerate(zip(plans, bufs)):
-            if events is not None:
-                events[i][0].record(stream)
+        for p, dst in zip(plans, bufs):
             F.fft_exec(p, src, dst, stream.cuda_stream)
-            if events is not None:
-                events[i][1].record(stream)
             src = dst
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps between two synchronisations; HIP events on the
-    # exec stream bracket every launch group
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in plans] for _ in range(args.steps)]
+    # timed region: K steps between two synchronisations, bracketed by HIP
+    # events on the stream the kernels are launched on (no events between
+    # launches, which would insert gaps)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    exec_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    avg_exec_ms = sum(exec_ms) / len(exec_ms)
+    avg_exec_ms = ev0.elapsed_time(ev1) / (args.steps * len(plans))
 
     # correctness guard for the numbers: the round trip must return N x
     check = None
@@ -184,12 +213,18 @@ def main():
     del a, b
 
     ms_per_step = wall * 1e3 / args.steps
-    flops_step = 5.0 * n * math.log2(n) * batch * len(spec["dirs"])
+    if spec["kind"] == "real":
+        # real transforms: 2.5 N log2 N per row and direction; bytes per exec:
+        # the real rows (4 B) once and the kept bins (8 B) once
+        flops_step = 2.5 * n * math.log2(n) * batch * len(spec["dirs"])
+        bytes_per_exec = batch * n * 4 + (spec["mmax"] + 1) * batch * 8
+    else:
+        flops_step = 5.0 * n * math.log2(n) * batch * len(spec["dirs"])
+        bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
     value = flops_step / (ms_per_step * 1e-3) / 1e9
-    bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
     achieved = bytes_per_exec / (avg_exec_ms * 1e-3) / 1e9
     key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
-           "w5": "2d_8192x8192"}[args.workload]
+           "w4": "real_2048", "w5": "2d_8192x8192"}[args.workload]
     traffic = stored_traffic(key)
     out = {
         "metric": METRIC,
@@ -205,7 +240,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": spec["label"], "n": n, "batch": batch,
-                   "directions": len(spec["dirs"]), "layout": "interleaved complex64"},
+                   "directions": len(spec["dirs"]),
+                   "layout": "float32 rows / m-major complex64 spectrum" if spec["kind"] == "real"
+                   else "interleaved complex64"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": key,

@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/fft.h"
+#include "fft.h"
 #include "launch.hpp"
 #include "shapes.hpp"
 #include "stockham.hpp"
@@ -91,7 +91,6 @@ struct fft_plan {
   const float2* thi = nullptr;
   const float2* tlo = nullptr;
   float2* scratch = nullptr;
-  hipEvent_t done = nullptr;
 };
 
 namespace {
@@ -117,7 +116,6 @@ int check_total(int64_t a, int64_t b, int64_t c) {
 
 void free_plan(fft_plan* p) {
   if (!p) return;
-  if (p->done) (void)hipEventDestroy(p->done);
   if (p->tables) (void)hipFree(p->tables);
   if (p->scratch) (void)hipFree(p->scratch);
   delete p;
@@ -144,8 +142,6 @@ int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
     e = hipMalloc((void**)&p->scratch, scratch_bytes);
     if (e != hipSuccess) return hip_err(e, "hipMalloc(scratch)");
   }
-  e = hipEventCreateWithFlags(&p->done, hipEventDisableTiming);
-  if (e != hipSuccess) return hip_err(e, "hipEventCreate");
   return FFT_OK;
 }
 
@@ -319,7 +315,6 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     RealArgs a{in, out, p->tw_a, p->rt, p->batch, (int)p->mmax, p->spec_layout};
     e = p->kind == FFT_R2C ? launch_r2c((int)(p->n / 2), a, stream) : launch_c2r((int)(p->n / 2), a, stream);
   }
-  if (e == hipSuccess) e = hipEventRecord(p->done, stream);
   if (cur != p->device) (void)hipSetDevice(cur);
   if (e != hipSuccess) return hip_err(e, "kernel launch");
   return ok();
@@ -330,7 +325,8 @@ void fft_plan_destroy(fft_plan* p) {
     ok();
     return;
   }
-  if (p->executed && p->done) (void)hipEventSynchronize(p->done);
+  // work enqueued with this plan may still read its tables and scratch
+  if (p->executed) (void)hipDeviceSynchronize();
   free_plan(p);
   ok();
 }

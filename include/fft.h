@@ -124,7 +124,9 @@ int fft_plan_get_sizes(const fft_plan* plan, int64_t* in_bytes,
  */
 int fft_exec(fft_plan* plan, const void* in, void* out, fft_stream_t stream);
 
-/* Wait for the plan's enqueued work, then free it.  NULL is a no-op. */
+/* Free the plan.  If it has been executed, first waits for all work on the
+ * device (hipDeviceSynchronize), since enqueued transforms may still read its
+ * tables and scratch.  NULL is a no-op. */
 void fft_plan_destroy(fft_plan* plan);
 
 /* Code of the last call on this host thread; *msg (if msg is not NULL) points
