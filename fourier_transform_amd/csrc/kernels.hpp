@@ -75,7 +75,8 @@ __global__ __launch_bounds__(tile_lines(N, false) * (N / tile_e(N, false))) void
   constexpr bool SPLIT = tile_split(N, false);
   constexpr int C = tile_lines(N, false);
   constexpr int T = N / E;
-  using L = ColLds<N, C>;
+  using L = ColLds<N, C, SPLIT>;
+  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
@@ -249,7 +250,8 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   constexpr bool SPLIT = tile_split(N2, false);
   constexpr int C = tile_lines(N2, false);
   constexpr int T = N2 / E;
-  using L = ColLds<N2, C>;
+  using L = ColLds<N2, C, SPLIT>;
+  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
@@ -306,7 +308,8 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr int T = N1 / E;
   constexpr int NT = C * T;
   constexpr bool WL = T <= 64;
-  using L = RowLds<N1>;
+  using L = RowLds<N1, SPLIT>;
+  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;

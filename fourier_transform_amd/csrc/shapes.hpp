@@ -12,8 +12,14 @@ namespace fftamd {
 // workgroup shapes
 // ---------------------------------------------------------------------------
 constexpr int threads_per_line(int n) { return n / sched_e(n); }
-constexpr int row_lds_bytes(int n, int c) { return c * (n + (n >> 4) + 1) * 8; }
-constexpr int col_lds_bytes(int n, int c) { return (n * c + ((n * c) >> 4) + 1) * 8; }
+// LDS bytes of c lines of length n (layouts: stockham.hpp RowLds / ColLds)
+constexpr int row_lds_bytes(int n, int c, bool split = false) {
+  return (split ? lds_pad<true, false>(c * (n + 1) - 1) : lds_pad<false, false>(c * (n + 1) - 1)) * (split ? 4 : 8) +
+         (split ? 4 : 8);
+}
+constexpr int col_lds_bytes(int n, int c, bool split = false) {
+  return (split ? lds_pad<true, true>(n * c - 1) : lds_pad<false, true>(n * c - 1)) * (split ? 4 : 8) + (split ? 4 : 8);
+}
 
 // Row lanes: at least 256 threads per workgroup (several short rows share one).
 constexpr int rows_per_wg(int n) {
@@ -26,12 +32,9 @@ constexpr int rows_per_wg(int n) {
 // thread (<= 512 threads, so up to 256 VGPRs per lane) with the exchange split
 // into real and imaginary halves (half the LDS per line) is used instead.
 constexpr int kSplitValues = 64;
-constexpr int tile_lds_elems(int n, int c, bool rowlanes) {
-  return rowlanes ? c * (n + (n >> 4) + 1) : n * c + ((n * c) >> 4) + 1;
-}
 constexpr bool tile_fits(int n, int e, int c, bool split, bool rowlanes) {
   return e <= n && c * (n / e) <= kMaxThreads &&
-         tile_lds_elems(n, c, rowlanes) * (split ? 4 : 8) <= kLdsBudgetBytes;
+         (rowlanes ? row_lds_bytes(n, c, split) : col_lds_bytes(n, c, split)) <= kLdsBudgetBytes;
 }
 constexpr int tile_c(int n, int e, bool split, bool rowlanes) {
   int c = 16;

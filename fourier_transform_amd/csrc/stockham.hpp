@@ -268,25 +268,34 @@ __device__ __forceinline__ void dft(float2* x) {
 
 // ---------------------------------------------------------------------------
 // LDS addressing.  Lines of one workgroup are stored either one after the
-// other (row lanes: consecutive threads walk along a line) or interleaved
-// (column lanes: consecutive threads walk across lines).  One float2 of
-// padding every 16 breaks the power-of-two strides of the Stockham writes
-// over the LDS banks; row-lane lines are also offset by one element from each
-// other so that reading across lines (transposing stores) does not collide.
+// other (row lanes: consecutive threads walk along a line; lines are N + 1
+// elements apart so that reading across lines, as the transposing store does,
+// changes bank) or interleaved (column lanes: consecutive threads walk across
+// lines).  The linear index a is then padded so that the power-of-two strides
+// of the Stockham writes, the slot reads and the transposed reads spread over
+// the banks.  The paddings were chosen with a bank model of every exchange
+// pattern used here (32 or 64 banks, 32- or 64-lane issue groups):
+//   row lanes:                a + a/32   (a/64 for 4-byte elements)
+//   column lanes, 8-byte:     a + a/32 + 8*(a/256)
+//   column lanes, 4-byte:     a + a/64
+// SPLIT: the exchange moves 4-byte halves (real, then imaginary parts).
 // ---------------------------------------------------------------------------
-template <int N>
+template <bool SPLIT, bool COL>
+__host__ __device__ constexpr int lds_pad(int a) {
+  if (COL && SPLIT) return a + (a >> 6);
+  if (COL) return a + (a >> 5) + ((a >> 8) << 3);
+  if (SPLIT) return a + (a >> 6);
+  return a + (a >> 5);
+}
+template <int N, bool SPLIT = false>
 struct RowLds {
-  static constexpr int kStride = N + (N >> 4) + 1;
-  __device__ __forceinline__ static int at(int line, int i) { return line * kStride + i + (i >> 4); }
-  static constexpr int size(int lines) { return lines * kStride; }
+  __device__ __forceinline__ static int at(int line, int i) { return lds_pad<SPLIT, false>(line * (N + 1) + i); }
+  static constexpr int size(int lines) { return lds_pad<SPLIT, false>(lines * (N + 1) - 1) + 1; }
 };
-template <int N, int C>
+template <int N, int C, bool SPLIT = false>
 struct ColLds {
-  __device__ __forceinline__ static int at(int line, int i) {
-    int a = i * C + line;
-    return a + (a >> 4);
-  }
-  static constexpr int size(int lines) { return N * C + ((N * C) >> 4) + 1; }
+  __device__ __forceinline__ static int at(int line, int i) { return lds_pad<SPLIT, true>(i * C + line); }
+  static constexpr int size(int lines) { return lds_pad<SPLIT, true>(N * C - 1) + 1; }
 };
 
 // Barrier between the LDS writes and reads of one exchange.  When every line
