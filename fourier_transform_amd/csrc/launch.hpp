@@ -69,4 +69,24 @@ struct FourStepArgs {
 hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream);
 hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream);
 
+// One step of a column transform split in two (2D column pass of tall images,
+// ny = na * nb; column row index i = ia + na*ib, output k = kb + nb*ka).
+// Lines c = 0 .. nlines-1 of each image; with q = c / nx and r = c % nx the
+// line's elements sit at q*a_in + r + t*s_in (t < L) and its results go to
+// q*a_out + r + k*s_out.  Step A (L = nb): q = ia, elements ia + na*ib, each
+// output multiplied by W_ny^{ia*kb} (wt[e] = e^{-2 pi i e/ny}), stored in
+// place.  Step B (L = na): q = kb, elements na*kb + ia, stored at row kb + nb*ka.
+struct ColStageArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;   // stage table for L
+  const float2* wt;   // W_ny table (step A only)
+  int64_t nlines;     // lines per image
+  int64_t image_stride;
+  int images;
+  uint32_t nx, log2nx;
+  uint32_t a_in, s_in, a_out, s_out;
+};
+hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
+
 }  // namespace fftamd

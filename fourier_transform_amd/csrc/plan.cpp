@@ -22,6 +22,10 @@ using namespace fftamd;
 namespace {
 
 constexpr int kFourStepMaxLog = 2 * ilog2c(kMaxSinglePass);  // 2^28
+// 2D images with at least this many rows split their column transform in two
+// steps (64 x ny/64), each with long runs (see ColStageArgs)
+constexpr int64_t kTallRows = 8192;
+constexpr int kTallSplit = 64;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 // ---------------------------------------------------------------------------
@@ -90,6 +94,11 @@ struct fft_plan {
   const float2* rt = nullptr;    // real transforms: e^{-2 pi i k/n}, k = 0..n/2
   const float2* thi = nullptr;
   const float2* tlo = nullptr;
+  // tall 2D images: column steps A (length ny/64) and B (length 64), W_ny table
+  bool tall = false;
+  const float2* tw_ca = nullptr;
+  const float2* tw_cb = nullptr;
+  const float2* wt = nullptr;
   float2* scratch = nullptr;
 };
 
@@ -216,6 +225,8 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   if (ny < 2 || nx < 2 || ny > kMaxSinglePass || nx > kMaxSinglePass)
     return set_err(FFT_ENOTSUP, "2D sizes must lie in [2, 16384]"), nullptr;
   if (check_total(ny, nx, batch) != FFT_OK) return nullptr;
+  if (ny >= kTallRows && batch > 65535)
+    return set_err(FFT_ENOTSUP, "2D plans with ny >= 8192 take at most 65535 images"), nullptr;
 
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
@@ -226,10 +237,22 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   p->batch = batch;
   p->kind = kind;
   p->sign = sign;
-  std::vector<float2> ta, tb;
+  std::vector<float2> ta, tb, tca, tcb, wt;
   append_stage_table((int)nx, rows_values((int)nx), ta);
-  append_stage_table((int)ny, cols_values((int)ny), tb);
-  if (finish_plan(p, {&ta, &tb}, {&p->tw_a, &p->tw_b}, 0) != FFT_OK) {
+  int rc;
+  if (ny >= kTallRows) {
+    p->tall = true;
+    const int nb = (int)(ny / kTallSplit);
+    append_stage_table(nb, colstage_values(nb), tca);
+    append_stage_table(kTallSplit, colstage_values(kTallSplit), tcb);
+    for (int64_t e = 0; e < ny; ++e) wt.push_back(root(e, ny));
+    rc = finish_plan(p, {&ta, &tca, &tcb, &wt}, {&p->tw_a, &p->tw_ca, &p->tw_cb, &p->wt},
+                     (size_t)(ny * nx * batch) * sizeof(float2));
+  } else {
+    append_stage_table((int)ny, cols_values((int)ny), tb);
+    rc = finish_plan(p, {&ta, &tb}, {&p->tw_a, &p->tw_b}, 0);
+  }
+  if (rc != FFT_OK) {
     free_plan(p);
     return nullptr;
   }
@@ -304,12 +327,27 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       FourStepArgs b{p->scratch, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
       e = launch_fourstep_rows(p->n1, p->sign, b, stream);
     }
-  } else if (p->kind == FFT_C2C) {
+  } else if (p->kind == FFT_C2C && !p->tall) {
     RowsArgs a{src, dst, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny, 0};
     e = launch_c2c_rows((int)p->nx, p->sign, a, stream);
     if (e == hipSuccess) {
       ColsArgs c{dst, dst, p->tw_b, p->ny, p->nx, p->batch};
       e = launch_c2c_cols((int)p->ny, p->sign, c, stream);
+    }
+  } else if (p->kind == FFT_C2C) {
+    // rows: in -> scratch; column step A in place on scratch; step B scratch -> out
+    const uint32_t nx = (uint32_t)p->nx, na = kTallSplit, nb = (uint32_t)(p->ny / kTallSplit);
+    RowsArgs a{src, p->scratch, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny, 0};
+    e = launch_c2c_rows((int)p->nx, p->sign, a, stream);
+    if (e == hipSuccess) {
+      ColStageArgs ca{p->scratch, p->scratch, p->tw_ca, p->wt, (int64_t)na * nx, p->ny * p->nx, (int)p->batch,
+                      nx, (uint32_t)ilog2c(nx), nx, na * nx, nx, na * nx};
+      e = launch_col_stage((int)nb, p->sign, true, ca, stream);
+    }
+    if (e == hipSuccess) {
+      ColStageArgs cb{p->scratch, dst, p->tw_cb, p->wt, (int64_t)nb * nx, p->ny * p->nx, (int)p->batch,
+                      nx, (uint32_t)ilog2c(nx), na * nx, nx, nx, nb * nx};
+      e = launch_col_stage((int)na, p->sign, false, cb, stream);
     }
   } else {
     RealArgs a{in, out, p->tw_a, p->rt, p->batch, (int)p->mmax, p->spec_layout};

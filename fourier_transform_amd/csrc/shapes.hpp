@@ -49,9 +49,20 @@ constexpr int tile_e(int n, bool rowlanes) { return tile_split(n, rowlanes) ? kS
 constexpr int tile_lines(int n, bool rowlanes) {
   return tile_c(n, tile_e(n, rowlanes), tile_split(n, rowlanes), rowlanes);
 }
+// Column-stage kernels (short columns, long runs): about 4096 elements per
+// workgroup, up to 64 adjacent lines (512 B runs), 16 values per thread.
+constexpr int colstage_lines(int n) {
+  int c = 4096 / n;
+  if (c > 64) c = 64;
+  if (c < 1) c = 1;
+  while (c > 1 && (c * threads_per_line(n) > kMaxThreads || col_lds_bytes(n, c) > kLdsBudgetBytes)) c /= 2;
+  return c;
+}
+
 // values per thread of each kernel family (selects the radix schedule)
 constexpr int rows_values(int n) { return sched_e(n); }           // k_c2c_rows, k_r2c, k_c2r
 constexpr int cols_values(int n) { return tile_e(n, false); }     // k_c2c_cols, k_fs_cols
 constexpr int tposed_values(int n) { return tile_e(n, true); }    // k_fs_rows
+constexpr int colstage_values(int n) { return sched_e(n); }       // k_col_stage
 
 }  // namespace fftamd

@@ -99,7 +99,10 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);
 /*
  * 2D C2C plan over [batch][ny][nx] complex64: every row, then every column
  * (Mota, section 2.7, Equation 19).  ny, nx: powers of two in [2, 16384].
- * Only kind = FFT_C2C.  Returns NULL on error.
+ * Only kind = FFT_C2C.  Images with ny >= 8192 rows run the column transform
+ * as two steps of 64 x ny/64 points (three passes in all, each with long
+ * contiguous runs), own a scratch buffer of batch*ny*nx*8 bytes and take at
+ * most 65535 images.  Returns NULL on error.
  */
 fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind,
                              int sign);

@@ -72,6 +72,7 @@ def test_create_rejects(lib, args, code):
     ((8, 32768, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((1, 8, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((8, 8, 1, F.FFT_C2C, 3), F.FFT_EINVAL),
+    ((8192, 2, 70000, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # tall images: at most 65535
 ])
 def test_create_2d_rejects(lib, args, code):
     assert err_of(F.fft_plan_create_2d, *args) == code

@@ -172,7 +172,7 @@ def test_w4_synthesis_then_analysis():
 # 2D and the fused chessboard shift
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("ny,nx", [(2, 2), (4, 16), (16, 4), (32, 64), (256, 128), (128, 1024),
-                                   (2048, 16), (16, 16384)])
+                                   (2048, 16), (16, 16384), (8192, 2), (8192, 16), (16384, 32)])
 @pytest.mark.parametrize("shift", [0, 1])
 def test_2d_sweep(ny, nx, shift):
     say(f"2d {ny}x{nx} shift={shift}")
