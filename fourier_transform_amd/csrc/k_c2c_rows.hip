@@ -8,11 +8,11 @@ struct RowsOp {
   template <int N>
   struct At {
     static hipError_t run(const RowsArgs& a, hipStream_t st) {
-      constexpr int C = rows_per_wg(N);
+      constexpr int C = rows_lines(N);
       uint32_t grid;
       hipError_t e = grid_of(a.rows, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_c2c_rows<N, S, C>), dim3(grid), dim3(threads_per_line(N) * C), 0, st, a);
+      hipLaunchKernelGGL((k_c2c_rows<N, S, C>), dim3(grid), dim3(rows_threads(N) * C), 0, st, a);
       return hipGetLastError();
     }
   };

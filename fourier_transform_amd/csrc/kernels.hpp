@@ -23,13 +23,14 @@ constexpr int real_rows_per_wg(int h) {
 // C2C over contiguous rows
 // ---------------------------------------------------------------------------
 template <int N, int S, int C>
-__global__ __launch_bounds__(threads_per_line(N) * C) void k_c2c_rows(RowsArgs a) {
-  constexpr int E = sched_e(N);
+__global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
+  constexpr int E = rows_values(N);
+  constexpr bool SPLIT = rows_split(N);
   constexpr int T = N / E;
   constexpr bool WL = T <= 64;  // every line inside one wavefront
-  using L = RowLds<N>;
-  static_assert(row_lds_bytes(N, C) <= kLdsBudgetBytes, "LDS budget");
-  __shared__ float2 lds[L::size(C)];
+  using L = RowLds<N, SPLIT>;
+  static_assert(row_lds_bytes(N, C, SPLIT) <= kLdsBudgetBytes, "LDS budget");
+  __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2c_rows(RowsArgs a
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N, E, S, WL, L, false>(v, lds, a.tw, u, line);
+  run_stages<N, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
   if (valid) {
     float2* dst = a.out + row0 * N;
     if (a.stream_store) {

@@ -202,7 +202,7 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     slots = {&p->tw_a, &p->tw_b, &p->thi, &p->tlo};
     scratch = (size_t)(n * batch) * sizeof(float2);
   } else {
-    append_stage_table((int)(n / 2), rows_values((int)(n / 2)), ta);
+    append_stage_table((int)(n / 2), real_values((int)(n / 2)), ta);
     for (int64_t k = 0; k <= n / 2; ++k) trt.push_back(root(k, n));
     parts = {&ta, &trt};
     slots = {&p->tw_a, &p->rt};

@@ -25,6 +25,14 @@ constexpr int col_lds_bytes(int n, int c, bool split = false) {
 constexpr int rows_per_wg(int n) {
   return threads_per_line(n) >= 256 ? 1 : 256 / threads_per_line(n);
 }
+// The C2C row kernel: 16 values per thread and a complex LDS exchange, except
+// for rows of 8192 and more, which take 32 values per thread (one stage fewer)
+// and the split exchange (half the LDS, so four workgroups fit a CU).
+constexpr int kRowsWideMin = 8192;
+constexpr int rows_values(int n) { return n >= kRowsWideMin ? 32 : sched_e(n); }
+constexpr bool rows_split(int n) { return n >= kRowsWideMin; }
+constexpr int rows_threads(int n) { return n / rows_values(n); }
+constexpr int rows_lines(int n) { return rows_threads(n) >= 256 ? 1 : 256 / rows_threads(n); }
 // Workgroups whose lines are read with a stride (column lanes) or stored
 // transposed (row lanes + transposing store) hold up to 16 adjacent lines, so
 // every strided access is a run of 16 x 8 B = 128 B.  When 16 values per
@@ -49,10 +57,10 @@ constexpr int tile_e(int n, bool rowlanes) { return tile_split(n, rowlanes) ? kS
 constexpr int tile_lines(int n, bool rowlanes) {
   return tile_c(n, tile_e(n, rowlanes), tile_split(n, rowlanes), rowlanes);
 }
-// Column-stage kernels (short columns, long runs): about 4096 elements per
+// Column-stage kernels (short columns, long runs): about 8192 elements per
 // workgroup, up to 64 adjacent lines (512 B runs), 16 values per thread.
 constexpr int colstage_lines(int n) {
-  int c = 4096 / n;
+  int c = 8192 / n;
   if (c > 64) c = 64;
   if (c < 1) c = 1;
   while (c > 1 && (c * threads_per_line(n) > kMaxThreads || col_lds_bytes(n, c) > kLdsBudgetBytes)) c /= 2;
@@ -60,7 +68,7 @@ constexpr int colstage_lines(int n) {
 }
 
 // values per thread of each kernel family (selects the radix schedule)
-constexpr int rows_values(int n) { return sched_e(n); }           // k_c2c_rows, k_r2c, k_c2r
+constexpr int real_values(int n) { return sched_e(n); }           // k_r2c, k_c2r
 constexpr int cols_values(int n) { return tile_e(n, false); }     // k_c2c_cols, k_fs_cols
 constexpr int tposed_values(int n) { return tile_e(n, true); }    // k_fs_rows
 constexpr int colstage_values(int n) { return sched_e(n); }       // k_col_stage
