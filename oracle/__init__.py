@@ -46,6 +46,9 @@ def _lib():
         lib.oracle_fftshift_index.argtypes = [_I64, _PTR]
         lib.oracle_fftshift_2d.argtypes = [_PTR, _PTR, _I64, _I64, _I64]
         lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_dft_bins.argtypes = [_PTR, _I64, _PTR, _I64, _PTR, ctypes.c_int, ctypes.c_int]
+        lib.oracle_dft2_bins.argtypes = [_PTR, _I64, _I64, _PTR, _PTR, _I64, _PTR, ctypes.c_int,
+                                         ctypes.c_int]
         _LIB = lib
     return _LIB
 
@@ -77,6 +80,27 @@ def dft_brute(x, sign: int = -1):
     x = _c128(x).reshape(-1)
     y = np.empty_like(x)
     _lib().oracle_dft_brute(_p(x), _p(y), x.size, sign)
+    return y
+
+
+def dft_bins(x, bins, sign: int = -1, nthreads: int = 0):
+    """Selected outputs of the DFT of one row by the definition (O(n) per bin)."""
+    x = _c128(x).reshape(-1)
+    b = np.ascontiguousarray(np.asarray(bins, dtype=np.int64).reshape(-1))
+    y = np.empty(b.size, np.complex128)
+    _check(_lib().oracle_dft_bins(_p(x), x.size, _p(b), b.size, _p(y), sign, nthreads), "dft_bins")
+    return y
+
+
+def dft2_bins(x, k1, k2, sign: int = -1, nthreads: int = 0):
+    """Selected outputs (k1[q], k2[q]) of the 2D DFT of one image by the definition."""
+    x = _c128(x)
+    ny, nx = x.shape
+    a = np.ascontiguousarray(np.asarray(k1, dtype=np.int64).reshape(-1))
+    b = np.ascontiguousarray(np.asarray(k2, dtype=np.int64).reshape(-1))
+    y = np.empty(a.size, np.complex128)
+    _check(_lib().oracle_dft2_bins(_p(x), ny, nx, _p(a), _p(b), a.size, _p(y), sign, nthreads),
+           "dft2_bins")
     return y
 
 

@@ -111,6 +111,113 @@ void oracle_dft_brute(const double* x, double* y, int64_t n, int sign) {
   }
 }
 
+/* Selected outputs of the same definition, one sum per requested bin:
+ * y[q] = sum_j x_j e^{sign 2 pi i j*bins[q]/n}, O(n) each, for checking
+ * transforms too long for a full oracle run.  Rows of `threads` threads split
+ * the sum; the partial sums are added in a fixed order. */
+typedef struct {
+  const double* x;
+  int64_t n, k;
+  int sign;
+  int parts;
+  double* acc; /* [parts][2] */
+} bin_ctx;
+
+static void bin_body(void* p, int64_t lo, int64_t hi) {
+  bin_ctx* c = (bin_ctx*)p;
+  for (int64_t part = lo; part < hi; ++part) {
+    int64_t j0 = c->n * part / c->parts, j1 = c->n * (part + 1) / c->parts;
+    double sr = 0.0, si = 0.0;
+    for (int64_t j = j0; j < j1; ++j) {
+      /* j*k mod n without overflow: n <= 2^31 keeps the product in int64 */
+      int64_t e = (int64_t)(((__int128)j * c->k) % c->n);
+      double a = TWO_PI * (double)e / (double)c->n;
+      double co = cos(a), sn = c->sign * sin(a);
+      double xr = c->x[2 * j], xi = c->x[2 * j + 1];
+      sr += xr * co - xi * sn;
+      si += xr * sn + xi * co;
+    }
+    c->acc[2 * part] = sr;
+    c->acc[2 * part + 1] = si;
+  }
+}
+
+int oracle_dft_bins(const double* x, int64_t n, const int64_t* bins, int64_t nbins, double* y,
+                    int sign, int threads) {
+  if (n < 1 || nbins < 0 || (sign != 1 && sign != -1)) return -1;
+  int parts = resolve_threads(threads) * 4;
+  double* acc = (double*)malloc(sizeof(double) * 2 * parts);
+  for (int64_t q = 0; q < nbins; ++q) {
+    if (bins[q] < 0 || bins[q] >= n) {
+      free(acc);
+      return -1;
+    }
+    bin_ctx c = {x, n, bins[q], sign, parts, acc};
+    parallel_for(threads, parts, bin_body, &c);
+    double sr = 0.0, si = 0.0;
+    for (int p = 0; p < parts; ++p) {
+      sr += acc[2 * p];
+      si += acc[2 * p + 1];
+    }
+    y[2 * q] = sr;
+    y[2 * q + 1] = si;
+  }
+  free(acc);
+  return 0;
+}
+
+/* Selected outputs of the 2D definition (Mota, section 2.7, Equation 19
+ * written as one double sum): y[q] = sum_{i,j} x[i][j] e^{sign 2 pi i (i*k1/ny
+ * + j*k2/nx)} for (k1, k2) = (k1s[q], k2s[q]); O(ny*nx) per output. */
+typedef struct {
+  const double* x;
+  int64_t ny, nx, k1, k2;
+  int sign;
+  double* acc; /* [ny][2] */
+} bin2_ctx;
+
+static void bin2_body(void* p, int64_t lo, int64_t hi) {
+  bin2_ctx* c = (bin2_ctx*)p;
+  for (int64_t i = lo; i < hi; ++i) {
+    double sr = 0.0, si = 0.0;
+    const double* row = c->x + 2 * i * c->nx;
+    for (int64_t j = 0; j < c->nx; ++j) {
+      /* exponent (i*k1*nx + j*k2*ny) / (ny*nx), reduced modulo ny*nx */
+      int64_t m = c->ny * c->nx;
+      int64_t e = (int64_t)((((__int128)i * c->k1 * c->nx) + ((__int128)j * c->k2 * c->ny)) % m);
+      double a = TWO_PI * (double)e / (double)m;
+      double co = cos(a), sn = c->sign * sin(a);
+      sr += row[2 * j] * co - row[2 * j + 1] * sn;
+      si += row[2 * j] * sn + row[2 * j + 1] * co;
+    }
+    c->acc[2 * i] = sr;
+    c->acc[2 * i + 1] = si;
+  }
+}
+
+int oracle_dft2_bins(const double* x, int64_t ny, int64_t nx, const int64_t* k1s,
+                     const int64_t* k2s, int64_t nbins, double* y, int sign, int threads) {
+  if (ny < 1 || nx < 1 || nbins < 0 || (sign != 1 && sign != -1)) return -1;
+  double* acc = (double*)malloc(sizeof(double) * 2 * ny);
+  for (int64_t q = 0; q < nbins; ++q) {
+    if (k1s[q] < 0 || k1s[q] >= ny || k2s[q] < 0 || k2s[q] >= nx) {
+      free(acc);
+      return -1;
+    }
+    bin2_ctx c = {x, ny, nx, k1s[q], k2s[q], sign, acc};
+    parallel_for(threads, ny, bin2_body, &c);
+    double sr = 0.0, si = 0.0;
+    for (int64_t i = 0; i < ny; ++i) {
+      sr += acc[2 * i];
+      si += acc[2 * i + 1];
+    }
+    y[2 * q] = sr;
+    y[2 * q + 1] = si;
+  }
+  free(acc);
+  return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* recursive radix-2 decimation in time                                       */
 /* ------------------------------------------------------------------------ */

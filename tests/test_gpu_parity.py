@@ -113,6 +113,57 @@ def test_fourstep_in_place():
     assert rel_l2(c2c(x, -1, inplace=True), oracle.c2c(x, -1)) <= TOL
 
 
+def _sampled_rel(got, want, rms):
+    """Relative L2 error estimated on sampled outputs: the sample's error norm
+    over what the full output's norm (rms * sqrt(count)) gives that many bins."""
+    got = np.asarray(got, np.complex128)
+    return float(np.linalg.norm(got - want) / (np.sqrt(got.size) * rms))
+
+
+def test_fourstep_max_length_sampled_bins():
+    """The longest supported length, 2^28 (2 GiB per buffer): sampled bins
+    against the definition, plus Parseval over the whole output."""
+    n = 1 << 28
+    say("four-step n=2^28 batch=1 forward (maximum length)")
+    x = np.random.default_rng(28).standard_normal(2 * n, dtype=np.float32).view(np.complex64)
+    y = c2c(x.reshape(1, n), -1)[0]
+    bins = np.array([0, 1, 12345, n // 2, n - 1, (1 << 27) + 3, 987654321 % n])
+    px = float(np.sum(np.abs(x.astype(np.complex128)) ** 2))
+    rms = np.sqrt(px)  # rms of the output bins: sqrt(n * px / n)
+    e = _sampled_rel(y[bins], oracle.dft_bins(x, bins, -1), rms)
+    say(f"2^28 sampled rel_l2 {e:.3e}")
+    assert e <= TOL
+    py = float(np.sum(np.abs(y.astype(np.complex128)) ** 2))
+    assert abs(py / (n * px) - 1) < 1e-5
+
+
+def test_2d_max_size_sampled_bins():
+    """The largest 2D image, 16384 x 16384 (tall path), with the shift fused:
+    sampled outputs against the 2D definition at the rotated indices."""
+    ny = nx = 16384
+    say("2d 16384x16384 shift (maximum size)")
+    x = np.random.default_rng(14).standard_normal(2 * ny * nx, dtype=np.float32).view(
+        np.complex64).reshape(ny, nx)
+    y = c2c_2d(x.reshape(1, ny, nx), -1, shift=1)[0]
+    i = np.array([0, 1, ny // 2, ny - 1, 777, 12000])
+    j = np.array([0, nx - 1, nx // 2, 3, 9001, 5])
+    want = oracle.dft2_bins(x, (i + ny // 2) % ny, (j + nx // 2) % nx, -1)
+    rms = np.sqrt(float(np.sum(np.abs(x.astype(np.complex128)) ** 2)))
+    e = _sampled_rel(y[i, j], want, rms)
+    say(f"16384^2 sampled rel_l2 {e:.3e}")
+    assert e <= TOL
+
+
+def test_deterministic_fourstep_and_tall_2d():
+    say("determinism four-step 2^20 and 2d 8192x64")
+    x = W.normal_c64((2, 1 << 20), np.random.default_rng(20))
+    a, b = c2c(x, -1), c2c(x, -1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    x2 = W.normal_c64((1, 8192, 64), np.random.default_rng(21))
+    a, b = c2c_2d(x2, -1, 1), c2c_2d(x2, -1, 1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_w3_full_size_sampled_rows():
     """Workload 3 at full size (32 x 2^22): every row is an independent
     transform; rows 0, 17 and 31 are compared with the oracle in full."""

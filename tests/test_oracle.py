@@ -54,6 +54,25 @@ def test_fft_matches_brute_force(n, sign):
         assert rel(y[r], dft_matrix(n, sign) @ x[r]) < 1e-12
 
 
+@pytest.mark.parametrize("n", [1, 7, 64, 1000])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_selected_bins_match_definition(n, sign):
+    x = crand(n, 30 + n)
+    bins = np.unique(np.array([0, 1, n // 2, n - 1, (5 * n) // 7]) % n)
+    assert rel(oracle.dft_bins(x, bins, sign), (dft_matrix(n, sign) @ x)[bins]) < 1e-12
+    assert rel(oracle.dft_bins(x, bins, sign, nthreads=1), oracle.dft_bins(x, bins, sign, nthreads=3)) < 1e-13
+
+
+@pytest.mark.parametrize("ny,nx", [(1, 1), (4, 8), (16, 2), (32, 32)])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_selected_2d_bins_match_double_sum(ny, nx, sign):
+    x = crand((ny, nx), ny + 5 * nx)
+    want = dft_matrix(ny, sign) @ x @ dft_matrix(nx, sign)
+    k1 = np.array([0, ny - 1, ny // 2, 1 % ny])
+    k2 = np.array([0, nx // 3, nx - 1, nx // 2])
+    assert rel(oracle.dft2_bins(x, k1, k2, sign), want[k1, k2]) < 1e-12
+
+
 def test_printed_n8_example():
     """Mota, section 2.2 EXAMPLE (after Equation 6): one cosine period, N = 8."""
     rows = np.loadtxt(os.path.join(HERE, "golden", "mota_dft_n8_example.txt"))
