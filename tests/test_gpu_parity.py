@@ -284,6 +284,58 @@ def test_w5_full_size():
             assert abs(y[i, j] - want_peak) / abs(want_peak) < 1e-4
 
 
+@pytest.mark.parametrize("n", [512, 1024])
+def test_2d_inverse_batched(n):
+    """2D inverse transforms of 4 images per batch (the ocean-demo shape of the
+    GLSL dissertation, Table 4, without the rendering)."""
+    say(f"2d inverse {n}x{n} batch=4")
+    x = W.normal_c64((4, n, n), np.random.default_rng(n + 4))
+    assert rel_l2(c2c_2d(x, +1), oracle.c2c_2d(x, +1)) <= TOL
+
+
+def test_graph_capture_replays():
+    """fft_exec launches kernels only, so it can be captured in a HIP graph;
+    every replay, with eager work in between, matches the eager result."""
+    import torch
+    say("graph capture: 1D n=4096, four-step 2^16, 2D 512x512")
+    cases = [(4096, 64, None), (1 << 16, 4, None), (512, 512, 2)]
+    for n, b, ny in cases:
+        if ny is None:
+            plan = F.fft_plan_create(n, b, F.FFT_C2C, F.FFT_FORWARD)
+            shape = (b, n)
+        else:
+            plan = F.fft_plan_create_2d(ny, n, b, F.FFT_C2C, F.FFT_FORWARD)
+            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)
+            shape = (b, ny, n)
+        try:
+            x = dev(W.normal_c64(shape, np.random.default_rng(n)))
+            y_eager = torch.empty_like(x)
+            y = torch.empty_like(x)
+            F.fft_exec(plan, x, y_eager)
+            torch.cuda.synchronize()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):       # warm-up on the capture stream
+                F.fft_exec(plan, x, y)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                F.fft_exec(plan, x, y)
+            want = y_eager.cpu().numpy()
+            for rep in range(3):
+                y.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(y.cpu().numpy().view(np.uint32), want.view(np.uint32)), rep
+                x.mul_(1.0)                   # eager work between replays
+                torch.cuda.synchronize()
+            del g
+        finally:
+            F.fft_plan_destroy(plan)
+
+
 # --------------------------------------------------------------------------
 # errors that need a live plan
 # --------------------------------------------------------------------------
