@@ -139,10 +139,10 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
   run_stages<H, E, -1, WL, L, false>(v, lds, a.tw, u, line);
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
-  __syncthreads();
+  lds_barrier();
 
   const int kout = a.mmax + 1;
   float2* out = static_cast<float2*>(a.out);
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
     else
       nyq[ln] = val;
   }
-  __syncthreads();
+  lds_barrier();
 
   float2 v[E];
   const float2 zero = make_float2(0.f, 0.f);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
     const float2 b = cmulc(csub(xk, cj), a.rt[k]);  // times e^{+2 pi i k/n}
     v[m] = make_float2(s.x - b.y, s.y + b.x);
   }
-  __syncthreads();
+  lds_barrier();
   run_stages<H, E, +1, WL, L, false>(v, lds, a.tw, u, line);
   if (valid) {
     float2* dst = static_cast<float2*>(a.out) + row * H;
@@ -332,22 +332,22 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   run_stages<N1, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
   // transposed read-back: slot p of thread tid is q = tid + NT*p, i.e. line
   // q % C, element q / C
-  __syncthreads();
+  lds_barrier();
   if constexpr (SPLIT) {
 #pragma unroll
     for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m].x;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int p = 0; p < E; ++p) {
       const int q = tid + NT * p;
       v[p].x = lds[L::at(q % C, q / C)];
     }
-    __syncthreads();
+    lds_barrier();
     int u2 = u, line2 = line, tid2 = tid;  // recompute addresses (see run_stage)
     asm volatile("" : "+v"(u2), "+v"(line2), "+v"(tid2));
 #pragma unroll
     for (int m = 0; m < E; ++m) lds[L::at(line2, u2 + T * m)] = v[m].y;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int p = 0; p < E; ++p) {
       const int q = tid2 + NT * p;
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int p = 0; p < E; ++p) {
       const int q = tid + NT * p;

@@ -298,16 +298,24 @@ struct ColLds {
   static constexpr int size(int lines) { return lds_pad<SPLIT, true>(N * C - 1) + 1; }
 };
 
-// Barrier between the LDS writes and reads of one exchange.  When every line
-// of the workgroup sits inside one wavefront, a wave-level barrier suffices.
+// Barrier between the LDS writes and reads of one exchange.  The fences are
+// restricted to LDS ("local" address space), so the barrier waits for LDS
+// traffic only and leaves global loads in flight (prefetching kernels rely on
+// this).  When every line of the workgroup sits inside one wavefront, a
+// wave-level barrier suffices.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 template <bool WAVE_LOCAL>
 __device__ __forceinline__ void lds_sync() {
   if constexpr (WAVE_LOCAL) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   } else {
-    __syncthreads();
+    lds_barrier();
   }
 }
 
