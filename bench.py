@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w4", "w5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--real-pairs", action="store_true",
+                    help="w4: two real rows per complex transform of length n")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -159,6 +161,8 @@ def main():
             p = F.fft_plan_create(n, batch, F.FFT_C2R if s > 0 else F.FFT_R2C, s)
             F.fft_plan_set(p, F.FFT_OPT_MMAX, spec["mmax"])
             F.fft_plan_set(p, F.FFT_OPT_SPEC_LAYOUT, 1)
+            if args.real_pairs:
+                F.fft_plan_set(p, F.FFT_OPT_REAL_PAIRS, 1)
         elif spec["kind"] == "2d":
             p = F.fft_plan_create_2d(spec["ny"], spec["nx"], batch, F.FFT_C2C, s)
             F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
@@ -239,7 +243,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": spec["label"], "n": n, "batch": batch,
+        "config": {"workload": spec["label"] + (", two rows per complex transform"
+                                                if args.real_pairs else ""), "n": n, "batch": batch,
                    "directions": len(spec["dirs"]),
                    "layout": "float32 rows / m-major complex64 spectrum" if spec["kind"] == "real"
                    else "interleaved complex64"},

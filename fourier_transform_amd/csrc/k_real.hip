@@ -26,7 +26,36 @@ struct C2ROp {
     return hipGetLastError();
   }
 };
+template <int N>
+struct R2CPairsOp {
+  static hipError_t run(const RealArgs& a, hipStream_t st) {
+    constexpr int C = real_rows_per_wg(N);
+    uint32_t grid;
+    hipError_t e = grid_of(a.rows / 2, C, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_r2c_pairs<N, C>), dim3(grid), dim3(threads_per_line(N) * C), 0, st, a);
+    return hipGetLastError();
+  }
+};
+template <int N>
+struct C2RPairsOp {
+  static hipError_t run(const RealArgs& a, hipStream_t st) {
+    constexpr int C = real_rows_per_wg(N);
+    uint32_t grid;
+    hipError_t e = grid_of(a.rows / 2, C, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_c2r_pairs<N, C>), dim3(grid), dim3(threads_per_line(N) * C), 0, st, a);
+    return hipGetLastError();
+  }
+};
 }  // namespace
+
+hipError_t launch_r2c_pairs(int n, const RealArgs& a, hipStream_t st) {
+  return dispatch_pow2<R2CPairsOp, 4, kMaxSinglePass>(n, a, st);
+}
+hipError_t launch_c2r_pairs(int n, const RealArgs& a, hipStream_t st) {
+  return dispatch_pow2<C2RPairsOp, 4, kMaxSinglePass>(n, a, st);
+}
 
 hipError_t launch_r2c(int h, const RealArgs& a, hipStream_t st) {
   return dispatch_pow2<R2COp, 2, kMaxSinglePass>(h, a, st);

@@ -242,6 +242,156 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Two real rows in one complex transform ("High Performance Fourier
+// Transforms on GPUs with GLSL", section 2.6, Equations 17-18): rows 2p and
+// 2p+1 become the real and imaginary parts of y, Y = FFT_N(y), and
+// X1(k) = (Y(k) + conj Y(N-k))/2, X2(k) = (Y(k) - conj Y(N-k))/(2i).
+// (Equation 18 is printed garbled; this is its reading, consistent with the
+// Xe/Xo split of the WGSL Fourier-stage source.)
+// ---------------------------------------------------------------------------
+template <int N, int C>
+__global__ __launch_bounds__(threads_per_line(N) * C) void k_r2c_pairs(RealArgs a) {
+  constexpr int E = real_values(N);
+  constexpr int T = N / E;
+  constexpr bool WL = T <= 64;
+  using L = RowLds<N>;
+  static_assert(row_lds_bytes(N, C) <= kLdsBudgetBytes, "LDS budget");
+  __shared__ float2 lds[L::size(C)];
+
+  const int tid = threadIdx.x;
+  const int line = tid / T, u = tid % T;
+  const int64_t pairs = a.rows / 2;
+  const int64_t pair = (int64_t)blockIdx.x * C + line;
+  float2 v[E];
+  if (pair < pairs) {
+    const float* x1 = static_cast<const float*>(a.in) + 2 * pair * N;
+    const float* x2 = x1 + N;
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = make_float2(x1[u + T * m], x2[u + T * m]);
+  } else {
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
+  }
+  run_stages<N, E, -1, WL, L, false>(v, lds, a.tw, u, line);
+  lds_barrier();
+#pragma unroll
+  for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
+  lds_barrier();
+
+  // outputs: (line, row of the pair, bin k); consecutive threads take
+  // consecutive bins (row-major) or consecutive rows (m-major)
+  const int kout = a.mmax + 1;
+  float2* out = static_cast<float2*>(a.out);
+  for (int q = tid; q < C * 2 * kout; q += C * T) {
+    int ln, which, k;
+    if (a.mmajor) {
+      const int r = q % (2 * C);
+      ln = r >> 1;
+      which = r & 1;
+      k = q / (2 * C);
+    } else {
+      const int r = q / kout;
+      ln = r >> 1;
+      which = r & 1;
+      k = q - r * kout;
+    }
+    const int64_t p = (int64_t)blockIdx.x * C + ln;
+    if (p >= pairs) continue;
+    const float2 yk = lds[L::at(ln, k)];
+    const float2 ym = lds[L::at(ln, (N - k) & (N - 1))];
+    float2 X;
+    if (which == 0) {
+      X = make_float2(0.5f * (yk.x + ym.x), 0.5f * (yk.y - ym.y));   // (Y(k) + conj Y(N-k)) / 2
+    } else {
+      const float dr = yk.x - ym.x, di = yk.y + ym.y;                 // Y(k) - conj Y(N-k)
+      X = make_float2(0.5f * di, -0.5f * dr);                         // divided by 2i
+    }
+    const int64_t row = 2 * p + which;
+    out[a.mmajor ? (int64_t)k * a.rows + row : row * kout + k] = X;
+  }
+}
+
+template <int N, int C>
+__global__ __launch_bounds__(threads_per_line(N) * C) void k_c2r_pairs(RealArgs a) {
+  constexpr int E = real_values(N);
+  constexpr int T = N / E;
+  constexpr int H = N / 2;
+  constexpr bool WL = T <= 64;
+  using L = RowLds<N>;
+  static_assert(row_lds_bytes(N, C) + 2 * C * 8 <= kLdsBudgetBytes, "LDS budget");
+  __shared__ float2 lds[L::size(C)];
+  __shared__ float2 nyq[2 * C];
+
+  const int tid = threadIdx.x;
+  const int line = tid / T, u = tid % T;
+  const int64_t pairs = a.rows / 2;
+  const int64_t pair = (int64_t)blockIdx.x * C + line;
+  const int mmax = a.mmax;
+  const int kin = mmax + 1;
+  const float2* F = static_cast<const float2*>(a.in);
+
+  // stage both spectra: row 2p at [0, H), row 2p+1 at [H, N); bin H apart
+  for (int q = tid; q < C * 2 * kin; q += C * T) {
+    int ln, which, k;
+    if (a.mmajor) {
+      const int r = q % (2 * C);
+      ln = r >> 1;
+      which = r & 1;
+      k = q / (2 * C);
+    } else {
+      const int r = q / kin;
+      ln = r >> 1;
+      which = r & 1;
+      k = q - r * kin;
+    }
+    const int64_t p = (int64_t)blockIdx.x * C + ln;
+    float2 val = make_float2(0.f, 0.f);
+    const int64_t row = 2 * p + which;
+    if (p < pairs) val = F[a.mmajor ? (int64_t)k * a.rows + row : row * kin + k];
+    if (k < H)
+      lds[L::at(ln, which * H + k)] = val;
+    else
+      nyq[2 * ln + which] = val;
+  }
+  lds_barrier();
+
+  // Y(k) = X1(k) + i X2(k) with each X Hermitian from its bins 0..mmax
+  float2 v[E];
+  const float2 zero = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    const int k = u + T * m;
+    float2 x[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float2 t;
+      if (k == 0) {
+        t = make_float2(lds[L::at(line, w * H)].x, 0.f);
+      } else if (k == H) {
+        t = mmax >= H ? make_float2(nyq[2 * line + w].x, 0.f) : zero;
+      } else if (k < H) {
+        t = k <= mmax ? lds[L::at(line, w * H + k)] : zero;
+      } else {
+        t = N - k <= mmax ? cconj(lds[L::at(line, w * H + N - k)]) : zero;
+      }
+      x[w] = t;
+    }
+    v[m] = make_float2(x[0].x - x[1].y, x[0].y + x[1].x);
+  }
+  lds_barrier();
+  run_stages<N, E, +1, WL, L, false>(v, lds, a.tw, u, line);
+  if (pair < pairs) {
+    float* y1 = static_cast<float*>(a.out) + 2 * pair * N;
+    float* y2 = y1 + N;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      y1[u + T * m] = v[m].x;
+      y2[u + T * m] = v[m].y;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Four-step pass 1: column transforms of length N2 over stride n1, each
 // output multiplied by W_n^{n1*k2}, stored in place of the column (to scratch)
 // ---------------------------------------------------------------------------

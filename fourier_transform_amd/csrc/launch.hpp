@@ -50,6 +50,10 @@ struct RealArgs {
 };
 hipError_t launch_r2c(int h, const RealArgs& a, hipStream_t stream);
 hipError_t launch_c2r(int h, const RealArgs& a, hipStream_t stream);
+// Two real rows per complex transform of the full length n (rows even;
+// tw: the stage table for n; rt unused).
+hipError_t launch_r2c_pairs(int n, const RealArgs& a, hipStream_t stream);
+hipError_t launch_c2r_pairs(int n, const RealArgs& a, hipStream_t stream);
 
 // Four-step transform of length n = n1*n2 (element n1 + N1*n2 -> bin
 // k2 + N2*k1).  Pass 1 (columns): in -> scratch, length-n2 transforms over

@@ -82,6 +82,7 @@ struct fft_plan {
   int shift = 0;
   int64_t mmax = 0;
   int spec_layout = 0;
+  int real_pairs = 0;
   bool executed = false;
   bool fourstep = false;
   int device = 0;
@@ -92,6 +93,7 @@ struct fft_plan {
   const float2* tw_a = nullptr;  // rows: n (1D), nx (2D), h (real), n1 (four-step rows)
   const float2* tw_b = nullptr;  // cols: ny (2D), n2 (four-step cols)
   const float2* rt = nullptr;    // real transforms: e^{-2 pi i k/n}, k = 0..n/2
+  const float2* tw_full = nullptr;  // real transforms, pair mode: stage table for n
   const float2* thi = nullptr;
   const float2* tlo = nullptr;
   // tall 2D images: column steps A (length ny/64) and B (length 64), W_ny table
@@ -206,6 +208,11 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     for (int64_t k = 0; k <= n / 2; ++k) trt.push_back(root(k, n));
     parts = {&ta, &trt};
     slots = {&p->tw_a, &p->rt};
+    if (n <= kMaxSinglePass) {  // for FFT_OPT_REAL_PAIRS
+      append_stage_table((int)n, real_values((int)n), tb);
+      parts.push_back(&tb);
+      slots.push_back(&p->tw_full);
+    }
   }
   if (finish_plan(p, parts, slots, scratch) != FFT_OK) {
     free_plan(p);
@@ -282,6 +289,13 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
       if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_SPEC_LAYOUT takes 0 or 1");
       p->spec_layout = (int)value;
       return ok();
+    case FFT_OPT_REAL_PAIRS:
+      if (p->kind == FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS applies to R2C/C2R plans only");
+      if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS takes 0 or 1");
+      if (value && (p->batch & 1)) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS needs an even batch");
+      if (value && !p->tw_full) return set_err(FFT_ENOTSUP, "FFT_OPT_REAL_PAIRS supports n <= 16384");
+      p->real_pairs = (int)value;
+      return ok();
     default:
       return set_err(FFT_EINVAL, "unknown option");
   }
@@ -350,8 +364,13 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       e = launch_col_stage((int)na, p->sign, false, cb, stream);
     }
   } else {
-    RealArgs a{in, out, p->tw_a, p->rt, p->batch, (int)p->mmax, p->spec_layout};
-    e = p->kind == FFT_R2C ? launch_r2c((int)(p->n / 2), a, stream) : launch_c2r((int)(p->n / 2), a, stream);
+    if (p->real_pairs) {
+      RealArgs a{in, out, p->tw_full, p->rt, p->batch, (int)p->mmax, p->spec_layout};
+      e = p->kind == FFT_R2C ? launch_r2c_pairs((int)p->n, a, stream) : launch_c2r_pairs((int)p->n, a, stream);
+    } else {
+      RealArgs a{in, out, p->tw_a, p->rt, p->batch, (int)p->mmax, p->spec_layout};
+      e = p->kind == FFT_R2C ? launch_r2c((int)(p->n / 2), a, stream) : launch_c2r((int)(p->n / 2), a, stream);
+    }
   }
   if (cur != p->device) (void)hipSetDevice(cur);
   if (e != hipSuccess) return hip_err(e, "kernel launch");
@@ -363,9 +382,15 @@ void fft_plan_destroy(fft_plan* p) {
     ok();
     return;
   }
-  // work enqueued with this plan may still read its tables and scratch
+  // work enqueued with this plan may still read its tables and scratch: wait
+  // for the plan's device, then free (restoring the caller's device)
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  const bool other = have_cur && cur != p->device;
+  if (other) (void)hipSetDevice(p->device);
   if (p->executed) (void)hipDeviceSynchronize();
   free_plan(p);
+  if (other) (void)hipSetDevice(cur);
   ok();
 }
 

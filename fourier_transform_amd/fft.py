@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libfft_amd.so")
 FFT_C2C, FFT_R2C, FFT_C2R = 0, 1, 2
 FFT_FORWARD, FFT_INVERSE = -1, 1
 FFT_OK, FFT_EINVAL, FFT_ENOTSUP, FFT_ENOMEM, FFT_EHIP, FFT_ESTATE = 0, -1, -2, -3, -4, -5
-FFT_OPT_SHIFT, FFT_OPT_MMAX, FFT_OPT_SPEC_LAYOUT = 1, 2, 3
+FFT_OPT_SHIFT, FFT_OPT_MMAX, FFT_OPT_SPEC_LAYOUT, FFT_OPT_REAL_PAIRS = 1, 2, 3, 4
 
 _NAMES = {0: "FFT_OK", -1: "FFT_EINVAL", -2: "FFT_ENOTSUP", -3: "FFT_ENOMEM",
           -4: "FFT_EHIP", -5: "FFT_ESTATE"}

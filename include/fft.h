@@ -80,7 +80,14 @@ enum fft_option {
   FFT_OPT_MMAX = 2,
   /* R2C/C2R spectrum layout: 0 = row-major [batch][mmax+1] (default),
    * 1 = m-major [mmax+1][batch]. */
-  FFT_OPT_SPEC_LAYOUT = 3
+  FFT_OPT_SPEC_LAYOUT = 3,
+  /* R2C/C2R: 1 = transform rows in pairs, rows 2p and 2p+1 as the real and
+   * imaginary parts of one complex transform of length n, separated by the
+   * even/odd symmetry of the result ("High Performance Fourier Transforms on
+   * GPUs with GLSL", section 2.6, Equations 17-18).  0 (default) = each row
+   * through a complex transform of length n/2.  Same results up to rounding.
+   * Needs an even batch (FFT_EINVAL) and n <= 16384 (FFT_ENOTSUP). */
+  FFT_OPT_REAL_PAIRS = 4
 };
 
 /*

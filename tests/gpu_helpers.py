@@ -67,7 +67,7 @@ def c2c_2d(x, sign, shift=0, inplace=False):
         F.fft_plan_destroy(plan)
 
 
-def r2c(x, mmax=None, mmajor=False):
+def r2c(x, mmax=None, mmajor=False, pairs=False):
     """x: float32 [batch][n]; returns complex64 [batch][mmax+1] or [mmax+1][batch]."""
     import torch
     n = x.shape[-1]
@@ -77,6 +77,7 @@ def r2c(x, mmax=None, mmajor=False):
     try:
         F.fft_plan_set(plan, F.FFT_OPT_MMAX, mmax)
         F.fft_plan_set(plan, F.FFT_OPT_SPEC_LAYOUT, int(mmajor))
+        F.fft_plan_set(plan, F.FFT_OPT_REAL_PAIRS, int(pairs))
         xd = dev(x)
         shape = (mmax + 1, batch) if mmajor else (batch, mmax + 1)
         yd = empty(shape, torch.complex64)
@@ -86,7 +87,7 @@ def r2c(x, mmax=None, mmajor=False):
         F.fft_plan_destroy(plan)
 
 
-def c2r(Fs, n, batch, mmax=None, mmajor=False):
+def c2r(Fs, n, batch, mmax=None, mmajor=False, pairs=False):
     """Fs: complex64 spectrum in the given layout; returns float32 [batch][n]."""
     import torch
     mmax = n // 2 if mmax is None else mmax
@@ -94,6 +95,7 @@ def c2r(Fs, n, batch, mmax=None, mmajor=False):
     try:
         F.fft_plan_set(plan, F.FFT_OPT_MMAX, mmax)
         F.fft_plan_set(plan, F.FFT_OPT_SPEC_LAYOUT, int(mmajor))
+        F.fft_plan_set(plan, F.FFT_OPT_REAL_PAIRS, int(pairs))
         xd = dev(Fs)
         yd = empty((batch, n), torch.float32)
         F.fft_exec(plan, xd, yd)

@@ -201,6 +201,41 @@ def test_real_sweep(logn):
         assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
 
 
+@pytest.mark.parametrize("logn", range(2, 15))
+def test_real_pairs_sweep(logn):
+    """Two real rows per complex transform (Mota, section 2.6, Eq. 17-18)."""
+    n = 1 << logn
+    g = np.random.default_rng(100 + logn)
+    for batch, mmax, mmajor in ((2, None, False), (6, n // 2 - 1, True), (20, max(0, n // 3), False),
+                                (4, 0, True)):
+        m = n // 2 if mmax is None else mmax
+        say(f"real pairs n={n} batch={batch} mmax={m} mmajor={mmajor}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = r2c(x, m, mmajor, pairs=True)
+        assert rel_l2(Fg.T if mmajor else Fg, oracle.r2c(x, m)) <= TOL, (n, batch, m)
+        S = (g.normal(size=(batch, m + 1)) + 1j * g.normal(size=(batch, m + 1))).astype(np.complex64)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        xg = c2r(Sin, n, batch, m, mmajor, pairs=True)
+        assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
+
+
+def test_real_pairs_options():
+    plan = F.fft_plan_create(64, 3, F.FFT_R2C, F.FFT_FORWARD)
+    try:
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_REAL_PAIRS, 1)      # odd batch
+        assert e.value.code == F.FFT_EINVAL
+    finally:
+        F.fft_plan_destroy(plan)
+    plan = F.fft_plan_create(32768, 2, F.FFT_C2R, F.FFT_INVERSE)
+    try:
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_REAL_PAIRS, 1)      # beyond one workgroup
+        assert e.value.code == F.FFT_ENOTSUP
+    finally:
+        F.fft_plan_destroy(plan)
+
+
 def test_w4_synthesis_then_analysis():
     """Workload 4: nlat=1024 rows, nphi=2048, mmax=682, m-major spectrum."""
     p = W.W4
