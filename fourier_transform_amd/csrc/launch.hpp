@@ -93,4 +93,19 @@ struct ColStageArgs {
 };
 hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
 
+// Band-limited direct transforms (any n, 2 <= n <= kMaxDirectLength):
+// analysis reads real rows [rows][n] (float) and writes bins 0..mmax;
+// synthesis reads bins 0..mmax and writes real rows.  The spectrum is complex
+// [rows][mmax+1], or [mmax+1][rows] when mmajor.  trig holds
+// (cos, sin)(2 pi t/n) for t = 0..n-1.  Requires 2 mmax < n.
+constexpr int kMaxDirectLength = 16384;
+struct DirectArgs {
+  const void* in;
+  void* out;
+  const float2* trig;
+  int64_t rows;
+  int n, mmax, mmajor;
+};
+hipError_t launch_direct(bool synthesis, const DirectArgs& a, hipStream_t stream);
+
 }  // namespace fftamd

@@ -101,20 +101,24 @@ struct fft_plan {
   const float2* tw_ca = nullptr;
   const float2* tw_cb = nullptr;
   const float2* wt = nullptr;
+  const float2* trig = nullptr;  // direct kinds: (cos, sin)(2 pi t/n)
   float2* scratch = nullptr;
 };
 
 namespace {
 
+bool is_direct(int kind) { return kind == FFT_R2C_DIRECT || kind == FFT_C2R_DIRECT; }
+bool is_analysis(int kind) { return kind == FFT_R2C || kind == FFT_R2C_DIRECT; }
+
 int check_kind_sign(int kind, int sign) {
-  if (kind != FFT_C2C && kind != FFT_R2C && kind != FFT_C2R)
-    return set_err(FFT_EINVAL, "kind must be FFT_C2C, FFT_R2C or FFT_C2R");
+  if (kind < FFT_C2C || kind > FFT_C2R_DIRECT)
+    return set_err(FFT_EINVAL, "kind must be FFT_C2C, FFT_R2C, FFT_C2R, FFT_R2C_DIRECT or FFT_C2R_DIRECT");
   if (sign != FFT_FORWARD && sign != FFT_INVERSE)
     return set_err(FFT_EINVAL, "sign must be FFT_FORWARD (-1) or FFT_INVERSE (+1)");
-  if (kind == FFT_R2C && sign != FFT_FORWARD)
-    return set_err(FFT_EINVAL, "FFT_R2C is a forward transform (sign must be -1)");
-  if (kind == FFT_C2R && sign != FFT_INVERSE)
-    return set_err(FFT_EINVAL, "FFT_C2R is an inverse transform (sign must be +1)");
+  if (is_analysis(kind) && sign != FFT_FORWARD)
+    return set_err(FFT_EINVAL, "R2C kinds are forward transforms (sign must be -1)");
+  if (kind != FFT_C2C && !is_analysis(kind) && sign != FFT_INVERSE)
+    return set_err(FFT_EINVAL, "C2R kinds are inverse transforms (sign must be +1)");
   return FFT_OK;
 }
 
@@ -156,6 +160,31 @@ int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
   return FFT_OK;
 }
 
+// direct kinds: the table trig[t] = (cos, sin)(2 pi t/n), t = 0..n-1
+fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
+  if (n < 2 || n > kMaxDirectLength)
+    return set_err(FFT_ENOTSUP, "direct kinds need 2 <= n <= 16384"), nullptr;
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = kind;
+  p->sign = sign;
+  p->mmax = (n - 1) / 2;
+  std::vector<float2> trig;
+  for (int64_t t = 0; t < n; ++t) {
+    const float2 w = root(t, n);  // (cos, -sin)
+    trig.push_back(make_float2(w.x, -w.y));
+  }
+  if (finish_plan(p, {&trig}, {&p->trig}, 0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,8 +193,9 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (n < 1) return set_err(FFT_EINVAL, "n must be >= 1"), nullptr;
   if (batch < 1) return set_err(FFT_EINVAL, "batch must be >= 1"), nullptr;
   if (check_kind_sign(kind, sign) != FFT_OK) return nullptr;
-  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n must be a power of two"), nullptr;
   if (check_total(n, batch, 1) != FFT_OK) return nullptr;
+  if (is_direct(kind)) return create_direct(n, batch, kind, sign);
+  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n must be a power of two"), nullptr;
   const int64_t max_len = kind == FFT_C2C ? (int64_t(1) << kFourStepMaxLog) : 2 * (int64_t)kMaxSinglePass;
   const int64_t min_len = kind == FFT_C2C ? 2 : 4;
   if (n < min_len || n > max_len)
@@ -280,6 +310,8 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
       return ok();
     case FFT_OPT_MMAX:
       if (p->kind == FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_MMAX applies to R2C/C2R plans only");
+      if (is_direct(p->kind) && (value < 0 || 2 * value >= p->n))
+        return set_err(FFT_EINVAL, "direct kinds need 0 <= mmax and 2 mmax < n");
       if (value < 0 || value > p->n / 2) return set_err(FFT_EINVAL, "mmax must satisfy 0 <= mmax <= n/2");
       p->mmax = value;
       return ok();
@@ -292,6 +324,7 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_REAL_PAIRS:
       if (p->kind == FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS applies to R2C/C2R plans only");
       if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS takes 0 or 1");
+      if (is_direct(p->kind)) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS applies to R2C/C2R plans only");
       if (value && (p->batch & 1)) return set_err(FFT_EINVAL, "FFT_OPT_REAL_PAIRS needs an even batch");
       if (value && !p->tw_full) return set_err(FFT_ENOTSUP, "FFT_OPT_REAL_PAIRS supports n <= 16384");
       p->real_pairs = (int)value;
@@ -307,8 +340,8 @@ int fft_plan_get_sizes(const fft_plan* p, int64_t* in_bytes, int64_t* out_bytes)
   const int64_t real = p->batch * p->n * 4;
   const int64_t spec = p->batch * (p->mmax + 1) * 8;
   int64_t i = cplx, o = cplx;
-  if (p->kind == FFT_R2C) i = real, o = spec;
-  if (p->kind == FFT_C2R) i = spec, o = real;
+  if (p->kind == FFT_R2C || p->kind == FFT_R2C_DIRECT) i = real, o = spec;
+  if (p->kind == FFT_C2R || p->kind == FFT_C2R_DIRECT) i = spec, o = real;
   if (in_bytes) *in_bytes = i;
   if (out_bytes) *out_bytes = o;
   return ok();
@@ -363,6 +396,9 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
                       nx, (uint32_t)ilog2c(nx), na * nx, nx, nx, nb * nx};
       e = launch_col_stage((int)na, p->sign, false, cb, stream);
     }
+  } else if (is_direct(p->kind)) {
+    DirectArgs a{in, out, p->trig, p->batch, (int)p->n, (int)p->mmax, p->spec_layout};
+    e = launch_direct(p->kind == FFT_C2R_DIRECT, a, stream);
   } else {
     if (p->real_pairs) {
       RealArgs a{in, out, p->tw_full, p->rt, p->batch, (int)p->mmax, p->spec_layout};

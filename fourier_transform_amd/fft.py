@@ -15,7 +15,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfft_amd.so")
 
-FFT_C2C, FFT_R2C, FFT_C2R = 0, 1, 2
+FFT_C2C, FFT_R2C, FFT_C2R, FFT_R2C_DIRECT, FFT_C2R_DIRECT = 0, 1, 2, 3, 4
 FFT_FORWARD, FFT_INVERSE = -1, 1
 FFT_OK, FFT_EINVAL, FFT_ENOTSUP, FFT_ENOMEM, FFT_EHIP, FFT_ESTATE = 0, -1, -2, -3, -4, -5
 FFT_OPT_SHIFT, FFT_OPT_MMAX, FFT_OPT_SPEC_LAYOUT, FFT_OPT_REAL_PAIRS = 1, 2, 3, 4

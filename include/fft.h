@@ -13,8 +13,9 @@
  *    n * x.
  *  - Data are fp32.  Complex values are interleaved (re, im) pairs: 8 bytes per
  *    element ("complex64").  Rows are contiguous; batches follow each other.
- *  - Sizes are powers of two.  Every other length is rejected with
- *    FFT_ENOTSUP (fourier.ts refuses non-power-of-two lengths at plan time).
+ *  - FFT sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
+ *    (fourier.ts refuses them for its FFT at plan time).  The direct kinds
+ *    below take any length from 2 to 16384.
  *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
  *    aligned.  The plan owns its twiddle tables and scratch (allocated at
  *    create, freed at destroy).
@@ -40,6 +41,17 @@
  *           Real transforms follow fourier.ts fftAnalysRealWGSL /
  *           fftSynthRealWGSL: one complex transform of length n/2 plus a
  *           Hermitian pack/unpack, so n >= 4 is required.
+ *  FFT_R2C_DIRECT, FFT_C2R_DIRECT
+ *           The band-limited direct sums of fourier.ts (dftAnalysWGSL,
+ *           dftSynthWGSL), for ANY length 2 <= n <= 16384:
+ *             analysis   F_m  = sum_j x_j exp(-2 pi i m j/n),   m = 0..mmax
+ *             synthesis  x_j  = Re F_0 + 2 sum_{m=1}^{mmax} Re(F_m exp(+2 pi i m j/n))
+ *           Same layouts (and FFT_OPT_SPEC_LAYOUT) as FFT_R2C / FFT_C2R, but
+ *           the band limit is strict, 2 mmax < n, as the source requires, and
+ *           mmax defaults to floor((n-1)/2).  Im F_0 is ignored.  Cost is
+ *           O(n mmax) per row (a real matrix product on the matrix cores);
+ *           the cos/sin factors come from a host-f64 table of n entries.
+ *           Only FFT_OPT_MMAX and FFT_OPT_SPEC_LAYOUT apply.
  */
 #ifndef FFT_AMD_FFT_H
 #define FFT_AMD_FFT_H
@@ -55,7 +67,7 @@ typedef struct fft_plan fft_plan; /* opaque */
 /* hipStream_t is `struct ihipStream_t*`; 0 / NULL is the null stream. */
 typedef struct ihipStream_t* fft_stream_t;
 
-enum fft_kind { FFT_C2C = 0, FFT_R2C = 1, FFT_C2R = 2 };
+enum fft_kind { FFT_C2C = 0, FFT_R2C = 1, FFT_C2R = 2, FFT_R2C_DIRECT = 3, FFT_C2R_DIRECT = 4 };
 enum fft_sign { FFT_FORWARD = -1, FFT_INVERSE = +1 };
 
 enum fft_status {
@@ -78,7 +90,7 @@ enum fft_option {
   /* R2C: keep bins 0..mmax; C2R: read bins 0..mmax.  0 <= mmax <= n/2
    * (fourier.ts: band limit |m| <= mmax < nphi/2).  Default n/2. */
   FFT_OPT_MMAX = 2,
-  /* R2C/C2R spectrum layout: 0 = row-major [batch][mmax+1] (default),
+  /* R2C/C2R (and the direct kinds) spectrum layout: 0 = row-major [batch][mmax+1] (default),
    * 1 = m-major [mmax+1][batch]. */
   FFT_OPT_SPEC_LAYOUT = 3,
   /* R2C/C2R: 1 = transform rows in pairs, rows 2p and 2p+1 as the real and
@@ -92,13 +104,16 @@ enum fft_option {
 
 /*
  * Create a plan for `batch` transforms of length n.
- * n: power of two, n >= 2 (C2C) or n >= 4 (R2C/C2R).  batch >= 1.
- * kind: FFT_C2C, FFT_R2C or FFT_C2R.  sign: FFT_FORWARD or FFT_INVERSE.
+ * n: power of two, n >= 2 (C2C) or n >= 4 (R2C/C2R); any 2 <= n <= 16384
+ * for the direct kinds.  batch >= 1.
+ * kind: enum fft_kind.  sign: FFT_FORWARD or FFT_INVERSE (FFT_FORWARD for the
+ * analysis kinds R2C and R2C_DIRECT, FFT_INVERSE for C2R and C2R_DIRECT).
  * Lengths up to 16384 run as one kernel (one workgroup per row, all stages in
  * LDS); longer C2C lengths, up to 2^28, run as two passes (four-step: strided
  * column transforms with the inter-pass twiddle fused into their store, then
  * row transforms with a transposing store) and own a scratch buffer of
  * batch*n*8 bytes.
+ * Direct plans own a table of n (cos, sin) pairs.
  * Uses the current HIP device.  Returns NULL on error (see fft_last_error).
  */
 fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);

@@ -111,3 +111,38 @@ def negate_odd(x, axes_parity):
     odd = (axes_parity & 1).astype(bool)
     u[odd] ^= np.uint32(0x80000000)
     return u.reshape(-1).view(np.complex64).reshape(x.shape)
+
+
+def direct_analysis(x, mmax=None, mmajor=False):
+    """FFT_R2C_DIRECT on x: float32 [batch][n] (any n); bins 0..mmax in the given layout."""
+    import torch
+    n = x.shape[-1]
+    batch = x.size // n
+    mmax = (n - 1) // 2 if mmax is None else mmax
+    plan = F.fft_plan_create(n, batch, F.FFT_R2C_DIRECT, F.FFT_FORWARD)
+    try:
+        F.fft_plan_set(plan, F.FFT_OPT_MMAX, mmax)
+        F.fft_plan_set(plan, F.FFT_OPT_SPEC_LAYOUT, int(mmajor))
+        xd = dev(x)
+        shape = (mmax + 1, batch) if mmajor else (batch, mmax + 1)
+        yd = empty(shape, torch.complex64)
+        F.fft_exec(plan, xd, yd)
+        return host(yd)
+    finally:
+        F.fft_plan_destroy(plan)
+
+
+def direct_synthesis(Fs, n, batch, mmax=None, mmajor=False):
+    """FFT_C2R_DIRECT: spectrum (bins 0..mmax, given layout) -> float32 [batch][n]."""
+    import torch
+    mmax = (n - 1) // 2 if mmax is None else mmax
+    plan = F.fft_plan_create(n, batch, F.FFT_C2R_DIRECT, F.FFT_INVERSE)
+    try:
+        F.fft_plan_set(plan, F.FFT_OPT_MMAX, mmax)
+        F.fft_plan_set(plan, F.FFT_OPT_SPEC_LAYOUT, int(mmajor))
+        xd = dev(Fs)
+        yd = empty((batch, n), torch.float32)
+        F.fft_exec(plan, xd, yd)
+        return host(yd)
+    finally:
+        F.fft_plan_destroy(plan)

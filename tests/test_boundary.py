@@ -57,6 +57,12 @@ def err_of(fn, *args):
     ((1 << 29, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # beyond the four-step range
     ((1 << 16, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),   # real transforms are single-pass
     ((1 << 40, 1 << 40, F.FFT_C2C, -1), F.FFT_EINVAL),  # size overflow
+    ((1000, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),      # the FFT kinds need powers of two
+    ((1, 1, F.FFT_R2C_DIRECT, -1), F.FFT_ENOTSUP),  # direct kinds: 2 <= n <= 16384
+    ((16385, 1, F.FFT_C2R_DIRECT, 1), F.FFT_ENOTSUP),
+    ((30, 1, F.FFT_R2C_DIRECT, 1), F.FFT_EINVAL),   # analysis is forward
+    ((30, 1, F.FFT_C2R_DIRECT, -1), F.FFT_EINVAL),  # synthesis is inverse
+    ((30, 1, 5, -1), F.FFT_EINVAL),                 # no kind 5
 ])
 def test_create_rejects(lib, args, code):
     assert err_of(F.fft_plan_create, *args) == code
@@ -73,6 +79,7 @@ def test_create_rejects(lib, args, code):
     ((1, 8, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((8, 8, 1, F.FFT_C2C, 3), F.FFT_EINVAL),
     ((8192, 2, 70000, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # tall images: at most 65535
+    ((8, 8, 1, F.FFT_R2C_DIRECT, -1), F.FFT_ENOTSUP),   # 2D plans are C2C only
 ])
 def test_create_2d_rejects(lib, args, code):
     assert err_of(F.fft_plan_create_2d, *args) == code
@@ -93,3 +100,14 @@ def test_valid_create_without_device_reports_hip_error(lib):
         pytest.skip("a device is present")
     code = err_of(F.fft_plan_create, 1024, 8, F.FFT_C2C, -1)
     assert code in (F.FFT_EHIP, F.FFT_ENOMEM)
+
+
+@pytest.mark.parametrize("n,kind,sign", [(2, F.FFT_R2C_DIRECT, -1), (1000, F.FFT_R2C_DIRECT, -1),
+                                         (999, F.FFT_C2R_DIRECT, 1), (16384, F.FFT_C2R_DIRECT, 1)])
+def test_direct_kinds_accept_any_length(lib, n, kind, sign):
+    """Any 2 <= n <= 16384 passes the checks of the direct kinds (with no GPU
+    the first HIP call then fails)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    assert err_of(F.fft_plan_create, n, 3, kind, sign) in (F.FFT_EHIP, F.FFT_ENOMEM)

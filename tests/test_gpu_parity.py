@@ -11,7 +11,8 @@ import oracle
 from fourier_transform_amd import fft as F
 from fourier_transform_amd import workloads as W
 
-from gpu_helpers import c2c, c2c_2d, c2r, dev, empty, host, negate_odd, r2c, rel_l2, say
+from gpu_helpers import (c2c, c2c_2d, c2r, dev, direct_analysis, direct_synthesis, empty, host,
+                         negate_odd, r2c, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -252,6 +253,96 @@ def test_w4_synthesis_then_analysis():
     e_closed = rel_l2(Fg / n, Fm)                    # R2C(C2R(F)) = n F
     say(f"w4 rel_l2 synthesis={e_syn:.3e} analysis={e_ana:.3e} closed_form={e_closed:.3e}")
     assert e_syn <= TOL and e_ana <= TOL and e_closed <= TOL
+
+
+# --------------------------------------------------------------------------
+# band-limited direct transforms (any length, matrix cores)
+# --------------------------------------------------------------------------
+def _spectrum(g, batch, m):
+    return (g.normal(size=(batch, m + 1)) + 1j * g.normal(size=(batch, m + 1))).astype(np.complex64)
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 30, 64, 100, 257, 1000, 2000, 4095])
+def test_direct_sweep(n):
+    """Direct analysis/synthesis against the oracle's direct sums (several
+    64 x 64 tiles, ragged rows and columns, both spectrum layouts)."""
+    g = np.random.default_rng(200 + n)
+    half = (n - 1) // 2
+    cases = [(1, half, False), (67, half, True), (130, n // 3 if 2 * (n // 3) < n else half, False),
+             (5, 0, True)]
+    for batch, m, mmajor in cases:
+        if n >= 2000 and batch > 8:
+            batch = 3                      # keep the O(batch n mmax) oracle fast
+        say(f"direct n={n} batch={batch} mmax={m} mmajor={mmajor}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = direct_analysis(x, m, mmajor)
+        assert rel_l2(Fg.T if mmajor else Fg, oracle.dft_analys_direct(x, m)) <= TOL, (n, batch, m)
+        S = _spectrum(g, batch, m)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        xg = direct_synthesis(Sin, n, batch, m, mmajor)
+        assert rel_l2(xg, oracle.dft_synth_direct(S, n, m)) <= TOL, (n, batch, m)
+
+
+@pytest.mark.parametrize("n", [4096, 16384])
+def test_direct_pow2_matches_fft_oracle(n):
+    """Power-of-two lengths against the oracle's FFT-based real transforms
+    (the same sums when 2 mmax < n), with more rows than one tile column."""
+    g = np.random.default_rng(300 + n)
+    batch, m = (130, n // 2 - 1) if n <= 4096 else (65, n // 2 - 1)
+    say(f"direct pow2 n={n} batch={batch} mmax={m}")
+    x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+    assert rel_l2(direct_analysis(x, m), oracle.r2c(x, m)) <= TOL
+    S = _spectrum(g, batch, m)
+    assert rel_l2(direct_synthesis(np.ascontiguousarray(S.T), n, batch, m, True),
+                  oracle.c2r(S, n, m)) <= TOL
+
+
+def test_direct_max_length_odd_sampled_rows():
+    """The longest odd length, 16383: every bin of sampled rows by the definition."""
+    n, batch, m = 16383, 70, 8191
+    g = np.random.default_rng(16383)
+    x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+    say(f"direct analysis n={n} batch={batch} mmax={m}")
+    Fg = direct_analysis(x, m)
+    for r in (0, 63, 69):
+        assert rel_l2(Fg[r], oracle.dft_bins(x[r], np.arange(m + 1))) <= TOL, r
+    S = _spectrum(g, batch, m)
+    say(f"direct synthesis n={n} batch={batch} mmax={m}")
+    xg = direct_synthesis(S, n, batch, m)
+    for r in (1, 64):
+        assert rel_l2(xg[r], oracle.dft_synth_direct(S[r:r + 1], n, m)[0]) <= TOL, r
+
+
+def test_direct_w4_shape():
+    """The w4 shape (nphi=2048, nlat=1024, mmax=682, m-major) through the
+    direct kinds, against the oracle's real transforms and the closed form
+    analysis(synthesis(F)) = n F."""
+    p = W.W4
+    n, nlat, mmax = p["nphi"], p["nlat"], p["mmax"]
+    Fm = W.workload4_spectrum()
+    say("w4 shape, direct synthesis")
+    xg = direct_synthesis(Fm, n, nlat, mmax, mmajor=True)
+    xo = oracle.c2r(Fm.T, n, mmax)
+    say("w4 shape, direct analysis")
+    x32 = xo.astype(np.float32)
+    Fg = direct_analysis(x32, mmax, mmajor=True)
+    e_syn, e_ana = rel_l2(xg, xo), rel_l2(Fg.T, oracle.r2c(x32, mmax))
+    e_closed = rel_l2(Fg / n, Fm)
+    say(f"direct w4 rel_l2 synthesis={e_syn:.3e} analysis={e_ana:.3e} closed_form={e_closed:.3e}")
+    assert e_syn <= TOL and e_ana <= TOL and e_closed <= TOL
+
+
+def test_direct_options():
+    plan = F.fft_plan_create(30, 2, F.FFT_R2C_DIRECT, F.FFT_FORWARD)
+    try:
+        assert F.fft_plan_get_sizes(plan) == (2 * 30 * 4, 2 * 15 * 8)   # default mmax 14
+        for opt, val in ((F.FFT_OPT_MMAX, 15), (F.FFT_OPT_MMAX, -1), (F.FFT_OPT_SHIFT, 1),
+                         (F.FFT_OPT_REAL_PAIRS, 1)):
+            with pytest.raises(F.FFTError) as e:
+                F.fft_plan_set(plan, opt, val)
+            assert e.value.code == F.FFT_EINVAL, (opt, val)
+    finally:
+        F.fft_plan_destroy(plan)
 
 
 # --------------------------------------------------------------------------
