@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "batched C2C fp32 FFT GFLOP/s (5N log2N) + achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix-core peak of the MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -79,7 +80,7 @@ def workload_spec(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def cpu_baseline(spec, x_host, reps=3):
+def cpu_baseline(spec, x_host, reps=3, direct=False):
     """Time the f64 oracle (as it stands, untuned) on the host cores.
 
     The sample is the whole workload when it is small enough, else its first
@@ -89,7 +90,15 @@ def cpu_baseline(spec, x_host, reps=3):
     import numpy as np
     import oracle
     n = spec["n"]
-    if spec["kind"] == "real":
+    if spec["kind"] == "real" and direct:
+        rows = min(spec["batch"], 64)           # the direct sums: O(n mmax) per row
+        xs = np.ascontiguousarray(x_host.T[:rows]).astype(np.complex128)
+
+        def run():
+            oracle.dft_analys_direct(oracle.dft_synth_direct(xs, n, spec["mmax"]), spec["mmax"])
+        flops = 2.5 * n * math.log2(n) * rows * 2
+        desc = f"{rows} of {spec['batch']} rows, direct synthesis then direct analysis"
+    elif spec["kind"] == "real":
         rows = spec["batch"]
         xs = np.ascontiguousarray(x_host.T).astype(np.complex128)   # [rows][mmax+1]
 
@@ -133,11 +142,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--real-pairs", action="store_true",
                     help="w4: two real rows per complex transform of length n")
+    ap.add_argument("--direct", action="store_true",
+                    help="w4: the band-limited direct sums on the matrix cores instead of the FFT")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the transforms are not sharded across devices", file=sys.stderr)
         sys.exit(2)
+    if (args.direct or args.real_pairs) and args.workload != "w4":
+        raise SystemExit("--direct and --real-pairs apply to the real-transform workload w4")
+    if args.direct and args.real_pairs:
+        raise SystemExit("--direct and --real-pairs exclude each other")
 
     import numpy as np
     import torch
@@ -158,7 +173,11 @@ def main():
     plans = []
     for s in spec["dirs"]:
         if spec["kind"] == "real":
-            p = F.fft_plan_create(n, batch, F.FFT_C2R if s > 0 else F.FFT_R2C, s)
+            if args.direct:
+                kind = F.FFT_C2R_DIRECT if s > 0 else F.FFT_R2C_DIRECT
+            else:
+                kind = F.FFT_C2R if s > 0 else F.FFT_R2C
+            p = F.fft_plan_create(n, batch, kind, s)
             F.fft_plan_set(p, F.FFT_OPT_MMAX, spec["mmax"])
             F.fft_plan_set(p, F.FFT_OPT_SPEC_LAYOUT, 1)
             if args.real_pairs:
@@ -226,10 +245,31 @@ def main():
         flops_step = 5.0 * n * math.log2(n) * batch * len(spec["dirs"])
         bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
     value = flops_step / (ms_per_step * 1e-3) / 1e9
-    achieved = bytes_per_exec / (avg_exec_ms * 1e-3) / 1e9
     key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
            "w4": "real_2048", "w5": "2d_8192x8192"}[args.workload]
-    traffic = stored_traffic(key)
+    if args.direct:
+        # a real matrix product of batch x n x 2(mmax+1) per launch, on the
+        # fp32 matrix cores
+        key = "direct_2048"
+        flops_exec = 2.0 * batch * n * 2 * (spec["mmax"] + 1)
+        achieved = flops_exec / (avg_exec_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+                "traffic": stored_traffic(key), "kernel": key, "avg_launch_ms": round(avg_exec_ms, 5),
+                "algorithmic_flops_per_launch": flops_exec,
+                "algorithmic_bytes_per_launch": bytes_per_exec}
+    else:
+        achieved = bytes_per_exec / (avg_exec_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": stored_traffic(key), "kernel": key,
+                "avg_launch_ms": round(avg_exec_ms, 5),
+                "algorithmic_bytes_per_launch": bytes_per_exec}
+    suffix = ""
+    if args.real_pairs:
+        suffix = ", two rows per complex transform"
+    if args.direct:
+        suffix = ", band-limited direct sums (matrix cores)"
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -243,16 +283,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": spec["label"] + (", two rows per complex transform"
-                                                if args.real_pairs else ""), "n": n, "batch": batch,
+        "config": {"workload": spec["label"] + suffix, "n": n, "batch": batch,
                    "directions": len(spec["dirs"]),
                    "layout": "float32 rows / m-major complex64 spectrum" if spec["kind"] == "real"
                    else "interleaved complex64"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": key,
-                     "avg_launch_ms": round(avg_exec_ms, 5),
-                     "algorithmic_bytes_per_launch": bytes_per_exec},
+        "roofline": roof,
         "copy_gbps": round(copy_gbps, 1),
     }
     if check is not None:
@@ -262,7 +297,7 @@ def main():
     del xd, bufs
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, x_host)
+        out["cpu_baseline"] = cpu_baseline(spec, x_host, direct=args.direct)
     print(json.dumps(out), flush=True)
 
 

@@ -97,7 +97,7 @@ hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs&
 // analysis reads real rows [rows][n] (float) and writes bins 0..mmax;
 // synthesis reads bins 0..mmax and writes real rows.  The spectrum is complex
 // [rows][mmax+1], or [mmax+1][rows] when mmajor.  trig holds
-// (cos, sin)(2 pi t/n) for t = 0..n-1.  Requires 2 mmax < n.
+// e^{-2 pi i u/n} = (cos, -sin)(2 pi u/n) for u = 0..n/2.  Requires 2 mmax < n.
 constexpr int kMaxDirectLength = 16384;
 struct DirectArgs {
   const void* in;

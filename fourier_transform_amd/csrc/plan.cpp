@@ -101,7 +101,7 @@ struct fft_plan {
   const float2* tw_ca = nullptr;
   const float2* tw_cb = nullptr;
   const float2* wt = nullptr;
-  const float2* trig = nullptr;  // direct kinds: (cos, sin)(2 pi t/n)
+  const float2* trig = nullptr;  // direct kinds: e^{-2 pi i u/n}, u = 0..n/2
   float2* scratch = nullptr;
 };
 
@@ -160,7 +160,7 @@ int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
   return FFT_OK;
 }
 
-// direct kinds: the table trig[t] = (cos, sin)(2 pi t/n), t = 0..n-1
+// direct kinds: the table e^{-2 pi i u/n} = (cos, -sin)(2 pi u/n), u = 0..n/2
 fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
   if (n < 2 || n > kMaxDirectLength)
     return set_err(FFT_ENOTSUP, "direct kinds need 2 <= n <= 16384"), nullptr;
@@ -173,10 +173,7 @@ fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
   p->sign = sign;
   p->mmax = (n - 1) / 2;
   std::vector<float2> trig;
-  for (int64_t t = 0; t < n; ++t) {
-    const float2 w = root(t, n);  // (cos, -sin)
-    trig.push_back(make_float2(w.x, -w.y));
-  }
+  for (int64_t u = 0; u <= n / 2; ++u) trig.push_back(root(u, n));
   if (finish_plan(p, {&trig}, {&p->trig}, 0) != FFT_OK) {
     free_plan(p);
     return nullptr;

@@ -332,6 +332,31 @@ def test_direct_w4_shape():
     assert e_syn <= TOL and e_ana <= TOL and e_closed <= TOL
 
 
+def test_direct_unaligned_buffers():
+    """Buffers only 8-byte aligned take the narrow-load variants; same results."""
+    import torch
+    n, batch, m = 64, 70, 31
+    g = np.random.default_rng(64)
+    x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+    S = _spectrum(g, batch, m + 1)[:, :m + 1]
+    say("direct analysis/synthesis from 8-byte aligned buffers")
+    for kind, sign, src, out_shape, want in (
+            (F.FFT_R2C_DIRECT, -1, x, (batch, m + 1), oracle.dft_analys_direct(x, m)),
+            (F.FFT_C2R_DIRECT, 1, S, (batch, n), oracle.dft_synth_direct(S, n, m))):
+        plan = F.fft_plan_create(n, batch, kind, sign)
+        try:
+            F.fft_plan_set(plan, F.FFT_OPT_MMAX, m)
+            flat = np.ascontiguousarray(src).view(np.float32).ravel()
+            buf = torch.zeros(flat.size + 2, dtype=torch.float32, device="cuda")
+            buf[2:] = torch.from_numpy(flat).cuda()
+            dt = torch.complex64 if kind == F.FFT_R2C_DIRECT else torch.float32
+            y = empty(out_shape, dt)
+            F.fft_exec(plan, buf.data_ptr() + 8, y)
+            assert rel_l2(host(y), want) <= TOL
+        finally:
+            F.fft_plan_destroy(plan)
+
+
 def test_direct_options():
     plan = F.fft_plan_create(30, 2, F.FFT_R2C_DIRECT, F.FFT_FORWARD)
     try:
