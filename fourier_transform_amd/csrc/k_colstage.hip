@@ -27,7 +27,7 @@ __global__ __launch_bounds__(colstage_lines(L) * (L / colstage_values(L))) void 
   float2 v[E];
   if (valid) {
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload(src, (uint32_t)(u + T * m) * a.s_in);
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, (uint32_t)(u + T * m) * a.s_in);
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);

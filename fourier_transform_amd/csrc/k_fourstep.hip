@@ -8,17 +8,26 @@ namespace fftamd {
 constexpr int kFourStepMin = 128;
 
 namespace {
+// The pass-1 kernel is specialised on the row count of the pass-2 workgroups
+// (and the reverse), which fixes the block layout of the scratch between
+// them.  The split makes n1 = n2 or n1 = n2/2, so two variants cover each.
 template <int S>
 struct FsColsOp {
   template <int N2>
   struct At {
-    static hipError_t run(const FourStepArgs& a, hipStream_t st) {
+    template <int BK>
+    static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N2, false);
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_cols<N2, S>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
+      hipLaunchKernelGGL((k_fs_cols<N2, S, BK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
       return hipGetLastError();
+    }
+    static hipError_t run(const FourStepArgs& a, hipStream_t st) {
+      if (a.n1 == N2) return go<tile_lines(N2, true)>(a, st);
+      if (2 * a.n1 == N2) return go<tile_lines(N2 / 2, true)>(a, st);
+      return hipErrorInvalidValue;
     }
   };
 };
@@ -26,13 +35,19 @@ template <int S>
 struct FsRowsOp {
   template <int N1>
   struct At {
-    static hipError_t run(const FourStepArgs& a, hipStream_t st) {
+    template <int BC>
+    static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N1, true);
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_rows<N1, S>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
+      hipLaunchKernelGGL((k_fs_rows<N1, S, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
       return hipGetLastError();
+    }
+    static hipError_t run(const FourStepArgs& a, hipStream_t st) {
+      if (a.n2 == N1) return go<tile_lines(N1, false)>(a, st);
+      if (a.n2 == 2 * N1) return go<tile_lines(2 * N1, false)>(a, st);
+      return hipErrorInvalidValue;
     }
   };
 };

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   if (valid) {
     const float2* src = a.in + row0 * N;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload(src, off + T * m);
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
     if (a.shift_mode) {
       const int par = a.shift_mode == 2 ? (int)(row & (a.rows_per_image - 1)) : 0;
 #pragma unroll
@@ -140,8 +140,10 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
   }
   run_stages<H, E, -1, WL, L, false>(v, lds, a.tw, u, line);
   lds_barrier();
-#pragma unroll
-  for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
+  static_for<0, E>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    lds[L::template at_k<T * m>(line, u)] = v[m];
+  });
   lds_barrier();
 
   const int kout = a.mmax + 1;
@@ -274,8 +276,10 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_r2c_pairs(RealArgs 
   }
   run_stages<N, E, -1, WL, L, false>(v, lds, a.tw, u, line);
   lds_barrier();
-#pragma unroll
-  for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
+  static_for<0, E>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    lds[L::template at_k<T * m>(line, u)] = v[m];
+  });
   lds_barrier();
 
   // outputs: (line, row of the pair, bin k); consecutive threads take
@@ -392,18 +396,39 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2r_pairs(RealArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass 1: column transforms of length N2 over stride n1, each
-// output multiplied by W_n^{n1*k2}, stored in place of the column (to scratch)
+// Intermediate layout of the four-step split (plan scratch, one transform
+// after the other).  Value (k2, c1) -- bin k2 of the column transform of
+// column c1 -- sits in a block of BK x BC values:
+//   ((k2 / BK) * (n1 / BC) + c1 / BC) * BK * BC + (k2 % BK) * BC + c1 % BC
+// BC is the number of columns a pass-1 workgroup transforms and BK the number
+// of rows a pass-2 workgroup transforms, so pass 1 stores whole blocks and
+// pass 2 reads whole blocks: both sides of the scratch are contiguous runs,
+// and only the caller's input (pass 1) and output (pass 2) are strided.
 // ---------------------------------------------------------------------------
-template <int N2, int S>
+template <int BK, int BC>
+__device__ __forceinline__ uint32_t fs_block_index(uint32_t k2, uint32_t c1, uint32_t n1) {
+  return ((k2 / BK) * (n1 / BC) + c1 / BC) * (BK * BC) + (k2 % BK) * BC + c1 % BC;
+}
+
+// ---------------------------------------------------------------------------
+// Four-step pass 1: column transforms of length N2 over stride n1, each
+// output multiplied by W_n^{n1*k2}, stored to scratch in the block layout
+// above (BK: rows per pass-2 workgroup)
+// ---------------------------------------------------------------------------
+template <int N2, int S, int BK>
 __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) void k_fs_cols(FourStepArgs a) {
   constexpr int E = tile_e(N2, false);
   constexpr bool SPLIT = tile_split(N2, false);
   constexpr int C = tile_lines(N2, false);
   constexpr int T = N2 / E;
   using L = ColLds<N2, C, SPLIT>;
-  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
+  constexpr int FP = E + 1;  // row pitch of the factor table (spreads the lines over the banks)
+  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) + C * FP * sizeof(float2) <= kLdsBudgetBytes,
+                "LDS budget");
+  // the stages' exchange barriers order the factor-table writes before the reads
+  static_assert(sched_stages(N2, E) >= 2, "pass 1 needs at least one LDS exchange");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  __shared__ float2 ftab[C * FP];
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -416,6 +441,19 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   const int64_t base = b * (int64_t)n1 * N2 + (c1 - line);
   const uint32_t off = (uint32_t)line + (uint32_t)u * n1;
   const uint32_t step = (uint32_t)T * n1;
+  // Inter-pass twiddle W_n^{c1*k2} with k2 = u + T*m, split as
+  // W_n^{c1*u} * W_n^{c1*T*m}: the first factor is one per thread, the
+  // second a table of C x E values per workgroup kept in LDS, so no value
+  // needs a scattered table lookup per element.  Each factor is read as
+  // thi[e >> bits] * tlo[e & mask] (both exponents stay below n).
+  const uint32_t mask = (1u << a.bits) - 1u;
+  const uint32_t c0 = c1 - line;
+  for (int q = tid; q < C * E; q += C * T) {
+    const uint32_t e = (c0 + (uint32_t)(q / E)) * (uint32_t)(T * (q % E));
+    ftab[(q / E) * FP + q % E] = cmul(gload(a.thi, e >> a.bits), gload(a.tlo, e & mask));
+  }
+  const uint32_t eu = c1 * (uint32_t)u;
+  const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
   float2 v[E];
   if (valid) {
     const float2* src = a.in + base;
@@ -431,13 +469,13 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   }
   run_stages<N2, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
   if (valid) {
-    const uint32_t mask = (1u << a.bits) - 1u;
-    float2* dst = a.out + base;
+    // the block layout, relative to the first block column of this group
+    float2* dst = a.out + b * (int64_t)n1 * N2 + c0 * BK;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      const uint32_t e = c1 * (uint32_t)(u + T * m);
-      const float2 w = cmul(gload(a.thi, e >> a.bits), gload(a.tlo, e & mask));
-      gstore_nt(dst, off + step * m, apply_tw<S>(v[m], w));
+      const uint32_t k2 = (uint32_t)(u + T * m);
+      const float2 w = cmul(wu, ftab[line * FP + m]);
+      gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line, n1), apply_tw<S>(v[m], w));
       if constexpr (E > 16) {
         if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
@@ -446,12 +484,13 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 }
 
 // ---------------------------------------------------------------------------
-// Four-step pass 2: row transforms of length N1 over contiguous rows k2,
-// element k1 stored at k2 + n2*k1.  The results go through LDS once more and
-// come back out with consecutive threads on consecutive rows, so each store
-// is a run of C elements.
+// Four-step pass 2: row transforms of length N1 over rows k2 of the block
+// layout (BC: columns per pass-1 workgroup), element k1 stored at
+// k2 + n2*k1.  The results go through LDS once more and come back out with
+// consecutive threads on consecutive rows, so each store is a run of C
+// elements.
 // ---------------------------------------------------------------------------
-template <int N1, int S>
+template <int N1, int S, int BC>
 __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) void k_fs_rows(FourStepArgs a) {
   constexpr int E = tile_e(N1, true);
   constexpr bool SPLIT = tile_split(N1, true);
@@ -471,47 +510,53 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   const int64_t g = g0 + line;
   float2 v[E];
   if (g < lines) {
-    const float2* src = a.in + g0 * N1;  // row k2 of transform b is at (b*n2 + k2)*N1
-    const uint32_t off = (uint32_t)(line * N1 + u);
+    // rows k2 = k20 .. k20 + C - 1 of transform b form one row of blocks
+    // starting at (b*n2 + k20)*N1 (k20 is a multiple of C)
+    const float2* src = a.in + g0 * N1;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
   run_stages<N1, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
   // transposed read-back: slot p of thread tid is q = tid + NT*p, i.e. line
-  // q % C, element q / C
+  // q % C = tid % C and element q / C = tid / C + (NT / C) * p (NT is a
+  // multiple of C)
   lds_barrier();
+  static_assert(NT % C == 0, "transposed read-back layout");
   if constexpr (SPLIT) {
-#pragma unroll
-    for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m].x;
+    static_for<0, E>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      lds[L::template at_k<T * m>(line, u)] = v[m].x;
+    });
     lds_barrier();
-#pragma unroll
-    for (int p = 0; p < E; ++p) {
-      const int q = tid + NT * p;
-      v[p].x = lds[L::at(q % C, q / C)];
-    }
+    static_for<0, E>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      v[p].x = lds[L::template at_k<(NT / C) * p>(tid % C, tid / C)];
+    });
     lds_barrier();
     int u2 = u, line2 = line, tid2 = tid;  // recompute addresses (see run_stage)
     asm volatile("" : "+v"(u2), "+v"(line2), "+v"(tid2));
-#pragma unroll
-    for (int m = 0; m < E; ++m) lds[L::at(line2, u2 + T * m)] = v[m].y;
+    static_for<0, E>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      lds[L::template at_k<T * m>(line2, u2)] = v[m].y;
+    });
     lds_barrier();
-#pragma unroll
-    for (int p = 0; p < E; ++p) {
-      const int q = tid2 + NT * p;
-      v[p].y = lds[L::at(q % C, q / C)];
-    }
+    static_for<0, E>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      v[p].y = lds[L::template at_k<(NT / C) * p>(tid2 % C, tid2 / C)];
+    });
   } else {
-#pragma unroll
-    for (int m = 0; m < E; ++m) lds[L::at(line, u + T * m)] = v[m];
+    static_for<0, E>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      lds[L::template at_k<T * m>(line, u)] = v[m];
+    });
     lds_barrier();
-#pragma unroll
-    for (int p = 0; p < E; ++p) {
-      const int q = tid + NT * p;
-      v[p] = lds[L::at(q % C, q / C)];
-    }
+    static_for<0, E>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      v[p] = lds[L::template at_k<(NT / C) * p>(tid % C, tid / C)];
+    });
   }
   const int ln = tid % C;  // the same line for every slot p (NT is a multiple of C)
   if (g0 + ln < lines) {

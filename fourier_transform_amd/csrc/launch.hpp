@@ -58,7 +58,9 @@ hipError_t launch_c2r_pairs(int n, const RealArgs& a, hipStream_t stream);
 // Four-step transform of length n = n1*n2 (element n1 + N1*n2 -> bin
 // k2 + N2*k1).  Pass 1 (columns): in -> scratch, length-n2 transforms over
 // stride n1, each output multiplied by W_n^{n1*k2}.  Pass 2 (rows): scratch ->
-// out, length-n1 transforms over contiguous rows, stored transposed.
+// out, length-n1 transforms over the rows k2, stored transposed.  The scratch
+// holds the values in blocks sized to both passes' workgroups (kernels.hpp,
+// fs_block_index); n1 must be n2 or n2/2.
 // W_n^e = thi[e >> bits] * tlo[e & (2^bits - 1)].
 struct FourStepArgs {
   const float2* in;

@@ -14,11 +14,10 @@ namespace fftamd {
 constexpr int threads_per_line(int n) { return n / sched_e(n); }
 // LDS bytes of c lines of length n (layouts: stockham.hpp RowLds / ColLds)
 constexpr int row_lds_bytes(int n, int c, bool split = false) {
-  return (split ? lds_pad<true, false>(c * (n + 1) - 1) : lds_pad<false, false>(c * (n + 1) - 1)) * (split ? 4 : 8) +
-         (split ? 4 : 8);
+  return row_lds_elems(n, c, split) * (split ? 4 : 8);
 }
 constexpr int col_lds_bytes(int n, int c, bool split = false) {
-  return (split ? lds_pad<true, true>(n * c - 1) : lds_pad<false, true>(n * c - 1)) * (split ? 4 : 8) + (split ? 4 : 8);
+  return col_lds_elems(n, c, split) * (split ? 4 : 8);
 }
 
 // Row lanes: at least 256 threads per workgroup (several short rows share one).

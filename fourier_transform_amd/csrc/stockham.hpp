@@ -112,9 +112,10 @@ __device__ __forceinline__ void gstore(float2* base, uint32_t i, float2 v) {
   *reinterpret_cast<float2*>(reinterpret_cast<char*>(base) + (i << 3)) = v;
 }
 // Streaming variants (non-temporal hint) for data touched once.  Used where
-// measurement shows they help: stores of whole rows, and both directions of
-// the four-step passes.  Not for the 2D column pass, whose 32 B runs rely on
-// neighbouring workgroups meeting in L2.
+// measurement shows they help: loads of whole rows and of column-stage
+// segments, stores of whole rows, and both directions of the four-step
+// passes.  Not for the 2D column pass, whose 32 B runs rely on neighbouring
+// workgroups meeting in L2.
 typedef float fftamd_v2f __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float2 gload_nt(const float2* __restrict__ base, uint32_t i) {
   const fftamd_v2f w = __builtin_nontemporal_load(
@@ -268,34 +269,92 @@ __device__ __forceinline__ void dft(float2* x) {
 
 // ---------------------------------------------------------------------------
 // LDS addressing.  Lines of one workgroup are stored either one after the
-// other (row lanes: consecutive threads walk along a line; lines are N + 1
-// elements apart so that reading across lines, as the transposing store does,
-// changes bank) or interleaved (column lanes: consecutive threads walk across
-// lines).  The linear index a is then padded so that the power-of-two strides
-// of the Stockham writes, the slot reads and the transposed reads spread over
-// the banks.  The paddings were chosen with a bank model of every exchange
+// other (row lanes: consecutive threads walk along a line) or interleaved
+// (column lanes: consecutive threads walk across lines).  Indices are padded
+// so that the power-of-two strides of the Stockham writes, the slot reads and
+// the transposed reads spread over the banks; row lines are an odd number of
+// elements apart, so reading across lines (the transposing store) changes
+// bank too.  The paddings were chosen with a bank model of every exchange
 // pattern used here (32 or 64 banks, 32- or 64-lane issue groups):
-//   row lanes:                a + a/32   (a/64 for 4-byte elements)
-//   column lanes, 8-byte:     a + a/32 + 8*(a/256)
-//   column lanes, 4-byte:     a + a/64
+//   row lanes:            line * P + p(i),  p(i) = i + i/G,  P = p(N) + 1,
+//                         G = 32 (8-byte elements) or 64 (4-byte)
+//   column lanes, 8-byte: p(a) = a + a/32 + 8*(a/256),  a = i*C + line
+//   column lanes, 4-byte: p(a) = a + a/64
 // SPLIT: the exchange moves 4-byte halves (real, then imaginary parts).
+//
+// at_k<K, A>(line, i0) addresses element i0 + K, where K is a compile-time
+// constant (the r*NS and T*m offsets of the unrolled loops) and the runtime
+// part i0 is a multiple of A.  Each padding is additive over multiples of its
+// period M (p(x + M q) = p(x) + p(M q)), so only K mod M enters the runtime
+// arithmetic -- and of that only the part above the alignment A -- and the
+// rest becomes the immediate offset of the LDS instruction.  The unrolled
+// loops then share a handful of runtime addresses instead of padding every
+// index separately.
 // ---------------------------------------------------------------------------
-template <bool SPLIT, bool COL>
-__host__ __device__ constexpr int lds_pad(int a) {
-  if (COL && SPLIT) return a + (a >> 6);
-  if (COL) return a + (a >> 5) + ((a >> 8) << 3);
-  if (SPLIT) return a + (a >> 6);
-  return a + (a >> 5);
+constexpr int row_pad_g(bool split) { return split ? 64 : 32; }
+constexpr int row_pitch(int n, bool split) { return n + n / row_pad_g(split) + 1; }
+constexpr int row_lds_elems(int n, int lines, bool split) {
+  return (lines - 1) * row_pitch(n, split) + (n - 1) + (n - 1) / row_pad_g(split) + 1;
 }
+template <bool SPLIT>
+__host__ __device__ constexpr uint32_t col_pad(uint32_t a) {
+  return SPLIT ? a + a / 64 : a + a / 32 + 8 * (a / 256);
+}
+constexpr int col_lds_elems(int n, int lines, bool split) {
+  return (int)(split ? col_pad<true>((uint32_t)(n * lines - 1)) : col_pad<false>((uint32_t)(n * lines - 1))) + 1;
+}
+
 template <int N, bool SPLIT = false>
 struct RowLds {
-  __device__ __forceinline__ static int at(int line, int i) { return lds_pad<SPLIT, false>(line * (N + 1) + i); }
-  static constexpr int size(int lines) { return lds_pad<SPLIT, false>(lines * (N + 1) - 1) + 1; }
+  static constexpr uint32_t G = row_pad_g(SPLIT);
+  static constexpr uint32_t P = row_pitch(N, SPLIT);
+  __host__ __device__ static constexpr uint32_t pad(uint32_t i) { return i + i / G; }
+  __device__ __forceinline__ static int at(int line, int i) {
+    return (int)((uint32_t)line * P + pad((uint32_t)i));
+  }
+  template <int K, int A = 1>
+  __device__ __forceinline__ static int at_k(int line, int i0) {
+    constexpr uint32_t r = (uint32_t)K % G;      // part of K below the period
+    constexpr uint32_t ra = r - r % (uint32_t)A;  // ... that can carry into i0's padding
+    constexpr uint32_t q = (uint32_t)K - r;
+    return (int)((uint32_t)line * P + pad((uint32_t)i0 + ra) + (r - ra) + pad(q));
+  }
+  static constexpr int size(int lines) { return row_lds_elems(N, lines, SPLIT); }
 };
 template <int N, int C, bool SPLIT = false>
 struct ColLds {
-  __device__ __forceinline__ static int at(int line, int i) { return lds_pad<SPLIT, true>(i * C + line); }
-  static constexpr int size(int lines) { return lds_pad<SPLIT, true>(N * C - 1) + 1; }
+  static constexpr uint32_t M = SPLIT ? 64 : 256;
+  __device__ __forceinline__ static int at(int line, int i) {
+    return (int)col_pad<SPLIT>((uint32_t)i * C + (uint32_t)line);
+  }
+  template <int K, int A = 1>
+  __device__ __forceinline__ static int at_k(int line, int i0) {
+    constexpr uint32_t kc = (uint32_t)K * C;
+    constexpr uint32_t r = kc % M;
+    return (int)(col_pad<SPLIT>((uint32_t)i0 * C + (uint32_t)line + r) + col_pad<SPLIT>(kc - r));
+  }
+  static constexpr int size(int lines) { return col_lds_elems(N, C, SPLIT); }
+};
+
+// Runtime part and compile-time offset of the Stockham write address of
+// butterfly k (element (b - j)*R + j + r*NS, b = u + T*k, j = b mod NS).
+// When NS divides T, b - j = (u - u mod NS) + T*k and the runtime part is the
+// same for every k; in the first stage (NS = 1) it is u*R, a multiple of R.
+template <int T, int R, int NS, int k>
+struct StageIdx {
+  static constexpr bool kShared = T % NS == 0;
+  static constexpr int K0 = kShared ? T * k * R : 0;
+  static constexpr int A = (kShared && NS == 1) ? R : 1;
+  __device__ __forceinline__ static int base(int u) {
+    if constexpr (kShared) {
+      const int jn = u & (NS - 1);
+      return (u - jn) * R + jn;
+    } else {
+      const int b = u + T * k;
+      const int j = b & (NS - 1);
+      return (b - j) * R + j;
+    }
+  }
 };
 
 // Barrier between the LDS writes and reads of one exchange.  The fences are
@@ -343,8 +402,8 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __
   static_assert(KB * R == E, "radix must divide the values per thread");
   constexpr bool last = (s == NST - 1);
   constexpr int OFF = sched_tw_off(N, E, s);
-#pragma unroll
-  for (int k = 0; k < KB; ++k) {
+  static_for<0, KB>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
     float2 x[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) x[r] = v[k + r * KB];
@@ -365,47 +424,53 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __
 #pragma unroll
       for (int r = 0; r < R; ++r) v[k + r * KB] = x[r];
     } else {
-      const int base = (b - j) * R + j;
-#pragma unroll
-      for (int r = 0; r < R; ++r) lds[Lds::at(line, base + r * NS)] = x[r];
+      using I = StageIdx<T, R, NS, k>;
+      const int base = I::base(u);
+      static_for<0, R>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        lds[Lds::template at_k<I::K0 + r * NS, I::A>(line, base)] = x[r];
+      });
     }
     // keep the scheduler from hoisting the next butterflies' twiddle loads
     // above this one: with many values per thread that would exhaust VGPRs
     if constexpr (KB > 1 && E > 16) __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   if constexpr (!last && !SPLIT) {
     lds_sync<WAVE_LOCAL>();
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = lds[Lds::at(line, u + T * m)];
+    static_for<0, E>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      v[m] = lds[Lds::template at_k<T * m>(line, u)];
+    });
     if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
   } else if constexpr (!last && SPLIT) {
-    // real parts
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int b = u + T * k;
-      const int base = (b - (b & (NS - 1))) * R + (b & (NS - 1));
-#pragma unroll
-      for (int r = 0; r < R; ++r) lds[Lds::at(line, base + r * NS)] = v[k + r * KB].x;
-    }
+    // real parts, then imaginary parts (v[.].y still hold the butterfly
+    // outputs meanwhile).  For the second half the empty asm hides that the
+    // indices are unchanged, so the LDS addresses are recomputed rather than
+    // kept live across the barriers.
+    auto exchange = [&](auto half, int uu, int ll) {
+      constexpr bool IM = decltype(half)::value;
+      static_for<0, KB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        using I = StageIdx<T, R, NS, k>;
+        const int base = I::base(uu);
+        static_for<0, R>([&](auto rc) {
+          constexpr int r = decltype(rc)::value;
+          const float2 y = v[k + r * KB];
+          lds[Lds::template at_k<I::K0 + r * NS, I::A>(ll, base)] = IM ? y.y : y.x;
+        });
+      });
+      lds_sync<WAVE_LOCAL>();
+      static_for<0, E>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const float w = lds[Lds::template at_k<T * m>(ll, uu)];
+        if constexpr (IM) v[m].y = w; else v[m].x = w;
+      });
+    };
+    exchange(std::integral_constant<bool, false>{}, u, line);
     lds_sync<WAVE_LOCAL>();
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m].x = lds[Lds::at(line, u + T * m)];
-    lds_sync<WAVE_LOCAL>();
-    // imaginary parts (v[.].y still hold the butterfly outputs).  The empty
-    // asm hides that the indices are unchanged, so the padded LDS addresses
-    // are recomputed rather than kept live across the barriers (2*E VGPRs).
     int u2 = u, line2 = line;
     asm volatile("" : "+v"(u2), "+v"(line2));
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int b = u2 + T * k;
-      const int base = (b - (b & (NS - 1))) * R + (b & (NS - 1));
-#pragma unroll
-      for (int r = 0; r < R; ++r) lds[Lds::at(line2, base + r * NS)] = v[k + r * KB].y;
-    }
-    lds_sync<WAVE_LOCAL>();
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m].y = lds[Lds::at(line2, u2 + T * m)];
+    exchange(std::integral_constant<bool, true>{}, u2, line2);
     if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
   }
 }
