@@ -46,6 +46,7 @@ def _lib():
         lib.oracle_fftshift_index.argtypes = [_I64, _PTR]
         lib.oracle_fftshift_2d.argtypes = [_PTR, _PTR, _I64, _I64, _I64]
         lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_dft.argtypes = [_PTR, _PTR, _I64, _I64, ctypes.c_int, ctypes.c_int]
         lib.oracle_dft_bins.argtypes = [_PTR, _I64, _PTR, _I64, _PTR, ctypes.c_int, ctypes.c_int]
         lib.oracle_dft2_bins.argtypes = [_PTR, _I64, _I64, _PTR, _PTR, _I64, _PTR, ctypes.c_int,
                                          ctypes.c_int]
@@ -80,6 +81,16 @@ def dft_brute(x, sign: int = -1):
     x = _c128(x).reshape(-1)
     y = np.empty_like(x)
     _lib().oracle_dft_brute(_p(x), _p(y), x.size, sign)
+    return y
+
+
+def dft(x, sign: int = -1, nthreads: int = 0):
+    """Batched DFT of any length over the last axis, by the definition
+    (Mota, section 2.2, Equation 5), O(n^2) per row."""
+    x = _c128(x)
+    n = x.shape[-1]
+    y = np.empty_like(x)
+    _check(_lib().oracle_dft(_p(x), _p(y), n, x.size // max(n, 1), sign, nthreads), "dft")
     return y
 
 
@@ -175,7 +186,8 @@ def dft_analys_direct(x, mmax: int):
 
 
 def fftshift_index(n: int):
-    """Integer index map of the shift: out[i] = Y[idx[i]], idx[i] = (i + n/2) mod n."""
+    """Integer index map of the shift: out[i] = Y[idx[i]], idx[i] = (i - n//2) mod n
+    (bin 0 moves to index n//2; for even n this is (i + n/2) mod n)."""
     idx = np.empty(n, np.int64)
     _check(_lib().oracle_fftshift_index(n, _p(idx)), "fftshift_index")
     return idx

@@ -30,8 +30,12 @@
  *  - Band-limited direct sums: fourier.ts dftSynthWGSL / dftAnalysWGSL
  *    (O(nphi * mmax) per row), used as an independent cross-check.
  *  - fftshift: "The 1D fftshift in CUDA by chessboard multiplication": the
- *    zero frequency moves to index N/2, i.e. out[i] = Y[(i + N/2) mod N] for
- *    even N; per axis in 2D.
+ *    zero frequency moves to index M = floor(N/2) (M = N/2 for even N, the
+ *    page's (N-1)/2 for odd N), i.e. out[i] = Y[(i - M) mod N]; per axis in
+ *    2D (even lengths there).
+ *  - Lengths that are not powers of two: the definition itself (oracle_dft),
+ *    with the factors e^{sign 2 pi i e/n} tabulated once per length for
+ *    e = 0..n-1 and indexed by e = (j*k) mod n.
  *
  * Threads: rows (and, in 2D, columns) are split statically over `threads`
  * POSIX threads; threads <= 0 means every online core.
@@ -109,6 +113,53 @@ void oracle_dft_brute(const double* x, double* y, int64_t n, int sign) {
     y[2 * k] = sr;
     y[2 * k + 1] = si;
   }
+}
+
+/* The same definition for a batch of rows of any length n >= 1, with the
+ * factors tabulated once: w[e] = e^{sign 2 pi i e/n}, e = 0..n-1, each from
+ * libm cos/sin of an exactly reduced angle, and y_k = sum_j x_j w[(j*k) mod n].
+ * O(n^2) per row; rows x bins are split over the threads. */
+typedef struct {
+  const double* x;
+  double* y;
+  const double* w;
+  int64_t n;
+} dft_ctx;
+
+static void dft_body(void* p, int64_t lo, int64_t hi) {
+  const dft_ctx* c = (const dft_ctx*)p;
+  const int64_t n = c->n;
+  for (int64_t t = lo; t < hi; ++t) {
+    const int64_t row = t / n, k = t % n;
+    const double* x = c->x + 2 * row * n;
+    double sr = 0.0, si = 0.0;
+    int64_t e = 0; /* (j*k) mod n, advanced by k per term */
+    for (int64_t j = 0; j < n; ++j) {
+      const double wr = c->w[2 * e], wi = c->w[2 * e + 1];
+      const double xr = x[2 * j], xi = x[2 * j + 1];
+      sr += xr * wr - xi * wi;
+      si += xr * wi + xi * wr;
+      e += k;
+      if (e >= n) e -= n;
+    }
+    c->y[2 * (row * n + k)] = sr;
+    c->y[2 * (row * n + k) + 1] = si;
+  }
+}
+
+int oracle_dft(const double* x, double* y, int64_t n, int64_t batch, int sign, int threads) {
+  if (n < 1 || batch < 1 || (sign != 1 && sign != -1) || x == y) return -1;
+  double* w = (double*)malloc(sizeof(double) * 2 * (size_t)n);
+  if (!w) return -2;
+  for (int64_t e = 0; e < n; ++e) {
+    const double a = TWO_PI * (double)e / (double)n;
+    w[2 * e] = cos(a);
+    w[2 * e + 1] = sign * sin(a);
+  }
+  dft_ctx c = {x, y, w, n};
+  parallel_for(threads, batch * n, dft_body, &c);
+  free(w);
+  return 0;
 }
 
 /* Selected outputs of the same definition, one sum per requested bin:
@@ -420,12 +471,14 @@ void oracle_dft_analys_direct(const double* x, double* F, int64_t n,
 }
 
 /* ------------------------------------------------------------------------ */
-/* fftshift as an index rotation (even lengths)                               */
+/* fftshift as an index rotation                                              */
 /* ------------------------------------------------------------------------ */
-/* idx[i] = (i + n/2) mod n: out[i] = Y[idx[i]] moves bin 0 to index n/2. */
+/* idx[i] = (i - M) mod n with M = floor(n/2): out[i] = Y[idx[i]] moves bin 0
+ * to index M (n/2 for even n, (n-1)/2 for odd n). */
 int oracle_fftshift_index(int64_t n, int64_t* idx) {
-  if (n < 2 || (n & 1)) return -1;
-  for (int64_t i = 0; i < n; ++i) idx[i] = (i + n / 2) % n;
+  if (n < 1) return -1;
+  const int64_t m = n / 2;
+  for (int64_t i = 0; i < n; ++i) idx[i] = ((i - m) % n + n) % n;
   return 0;
 }
 

@@ -158,6 +158,15 @@ def test_fftshift_index_matches_numpy_exactly(n):
     assert np.array_equal(oracle.fftshift_index(n), np.fft.ifftshift(a))
 
 
+@pytest.mark.parametrize("n", [1, 3, 5, 7, 9, 15, 1001])
+def test_fftshift_index_odd_matches_numpy_exactly(n):
+    """Odd lengths: bin 0 moves to index (n-1)/2, as numpy's fftshift does
+    (and unlike its ifftshift, which differs for odd n)."""
+    a = np.arange(n)
+    assert np.array_equal(oracle.fftshift_index(n), np.fft.fftshift(a))
+    assert oracle.fftshift_index(n)[(n - 1) // 2] == 0
+
+
 def test_fftshift_2d_matches_numpy_exactly():
     y = crand((2, 6, 8), 3)
     assert np.array_equal(oracle.fftshift_2d(y), np.fft.fftshift(y, axes=(-2, -1)))
@@ -253,7 +262,7 @@ def test_rejects_invalid_sizes():
     with pytest.raises(ValueError):
         oracle.c2c(np.zeros(6, np.complex128))
     with pytest.raises(ValueError):
-        oracle.fftshift_index(7)
+        oracle.fftshift_index(0)
     with pytest.raises(ValueError):
         oracle.r2c(np.zeros(8), mmax=5)
 
@@ -291,3 +300,65 @@ def test_workload_generators_are_deterministic():
     assert np.max(np.abs(a.real)) <= 1 and np.max(np.abs(a.imag)) <= 1
     F = workloads.workload4_spectrum()
     assert F.shape == (683, 1024) and np.all(F[0].imag == 0)
+
+
+# --------------------------------------------------------------------------
+# lengths that are not powers of two: the definition with tabulated factors
+# --------------------------------------------------------------------------
+GENERAL_N = [1, 2, 3, 5, 6, 7, 9, 12, 15, 30, 63, 100, 127, 1000, 1001]
+
+
+@pytest.mark.parametrize("n", [n for n in GENERAL_N if n <= 64])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_dft_any_length_matches_brute_force(n, sign):
+    """Against the double sum that evaluates every factor anew (oracle_dft_brute)."""
+    x = crand((3, n), 31 * n)
+    want = np.stack([oracle.dft_brute(r, sign) for r in x])
+    assert rel(oracle.dft(x, sign), want) < 1e-13
+
+
+@pytest.mark.parametrize("n", GENERAL_N)
+def test_dft_any_length_third_party(n):
+    """numpy's pocketfft (mixed radix / Bluestein inside) as a third-party check."""
+    x = crand((2, n), 5 * n + 1)
+    assert rel(oracle.dft(x, -1), np.fft.fft(x, axis=-1)) < 1e-12
+    assert rel(oracle.dft(x, +1), n * np.fft.ifft(x, axis=-1)) < 1e-12
+
+
+@pytest.mark.parametrize("n", [3, 7, 100, 1001])
+def test_dft_any_length_closed_forms(n):
+    """Impulse at j0 -> e^{sign 2 pi i k j0/n}; tone e^{2 pi i k0 j/n} -> n at bin k0
+    (forward); Parseval."""
+    j0, k0 = n // 3, (2 * n) // 5
+    imp = np.zeros(n, np.complex128)
+    imp[j0] = 1.0
+    k = np.arange(n)
+    for sign in (-1, 1):
+        assert rel(oracle.dft(imp, sign), np.exp(sign * 2j * np.pi * ((k * j0) % n) / n)) < 1e-13
+    tone = np.exp(2j * np.pi * ((k0 * k) % n) / n)
+    want = np.zeros(n, np.complex128)
+    want[k0] = n
+    assert np.max(np.abs(oracle.dft(tone, -1) - want)) < 1e-9 * n
+    x = crand(n, n)
+    assert abs(np.sum(np.abs(oracle.dft(x, -1)) ** 2) - n * np.sum(np.abs(x) ** 2)) < 1e-9 * n * n
+
+
+@pytest.mark.parametrize("n", [2, 8, 64, 1024])
+def test_dft_any_length_agrees_with_radix2(n):
+    """Two independent algorithms of the oracle agree at powers of two."""
+    x = crand((2, n), 17 * n)
+    for sign in (-1, 1):
+        assert rel(oracle.dft(x, sign), oracle.c2c(x, sign)) < 1e-12
+
+
+@pytest.mark.parametrize("n", [3, 5, 9, 101, 1001])
+def test_shift_theorem_odd(n):
+    """Chessboard page, odd case: multiplying x_j by e^{-sign 2 pi i M j/n},
+    M = (n-1)/2, moves bin 0 to index M -- the index map of the oracle."""
+    x = crand(n, 3 * n)
+    m = (n - 1) // 2
+    j = np.arange(n)
+    idx = oracle.fftshift_index(n)
+    for sign in (-1, 1):
+        ramp = np.exp(-sign * 2j * np.pi * ((m * j) % n) / n)
+        assert rel(oracle.dft(x * ramp, sign), oracle.dft(x, sign)[idx]) < 1e-12
