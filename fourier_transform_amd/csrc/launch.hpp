@@ -95,6 +95,25 @@ struct ColStageArgs {
 };
 hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
 
+// C2C rows of any length n (2 <= n <= kMaxBluesteinLength) by Bluestein's
+// chirp: with c_j = e^{sign pi i j^2/n}, y_k = c_k * (a conv b)_k, where
+// a_j = x_j pre_j (pre_j = c_j, times the shift ramp when requested) padded
+// with zeros to m >= 2n - 1 and b = conj(c) wrapped around; the convolution
+// is inverse_FFT_m(forward_FFT_m(a) * bhat) with bhat = forward_FFT_m(b)/m.
+// Rows of n complex64 values, contiguous; in place allowed.
+constexpr int kMaxBluesteinLength = 8192;
+struct BluesteinArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;    // stage table for m (forward)
+  const float2* pre;   // n factors applied on load
+  const float2* post;  // n factors applied on store (c_k)
+  const float2* bhat;  // m factors between the two transforms
+  int64_t rows;
+  int n;
+};
+hipError_t launch_bluestein(int m, const BluesteinArgs& a, hipStream_t stream);
+
 // Band-limited direct transforms (any n, 2 <= n <= kMaxDirectLength):
 // analysis reads real rows [rows][n] (float) and writes bins 0..mmax;
 // synthesis reads bins 0..mmax and writes real rows.  The spectrum is complex

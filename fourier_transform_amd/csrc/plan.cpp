@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <complex>
 #include <cstdint>
 #include <cstdio>
 #include <new>
@@ -70,6 +71,38 @@ void append_stage_table(int n, int e, std::vector<float2>& t) {
   if (t.empty()) t.push_back(make_float2(1.f, 0.f));  // keep offsets valid
 }
 
+// Bluestein chirp e^{sign pi i q/n} for the integer exponent q, reduced
+// modulo 2n first so that the angle is exact up to one rounding
+float2 chirp(int64_t q, int64_t n, int sign) {
+  const int64_t r = ((q % (2 * n)) + 2 * n) % (2 * n);
+  const double a = kTwoPi * 0.5 * (double)r / (double)n;
+  return make_float2((float)std::cos(a), (float)(sign * std::sin(a)));
+}
+
+// forward transform (e^{-2 pi i jk/m}) of a power-of-two length in f64 on the
+// host, for plan tables only: iterative radix 2, every twiddle from cos/sin
+// of its own angle
+void host_fft_f64(std::vector<std::complex<double>>& a) {
+  const size_t m = a.size();
+  for (size_t i = 1, j = 0; i < m; ++i) {
+    size_t bit = m >> 1;
+    for (; j & bit; bit >>= 1) j ^= bit;
+    j ^= bit;
+    if (i < j) std::swap(a[i], a[j]);
+  }
+  for (size_t len = 2; len <= m; len <<= 1) {
+    for (size_t k = 0; k < len / 2; ++k) {
+      const double ang = -kTwoPi * (double)k / (double)len;
+      const std::complex<double> w(std::cos(ang), std::sin(ang));
+      for (size_t i = 0; i < m; i += len) {
+        const std::complex<double> t = w * a[i + k + len / 2];
+        a[i + k + len / 2] = a[i + k] - t;
+        a[i + k] += t;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -102,6 +135,13 @@ struct fft_plan {
   const float2* tw_cb = nullptr;
   const float2* wt = nullptr;
   const float2* trig = nullptr;  // direct kinds: e^{-2 pi i u/n}, u = 0..n/2
+  // C2C lengths that are not powers of two (Bluestein): transform length bm,
+  // chirps c_j (and c_j times the shift ramp), forward transform of the chirp
+  bool bluestein = false;
+  int bm = 0;
+  const float2* chirp = nullptr;
+  const float2* chirp_shift = nullptr;
+  const float2* bhat = nullptr;
   float2* scratch = nullptr;
 };
 
@@ -182,6 +222,51 @@ fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
   return p;
 }
 
+// C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLength
+fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = FFT_C2C;
+  p->sign = sign;
+  p->bluestein = true;
+  int64_t m = 1;
+  while (m < 2 * n - 1) m <<= 1;
+  p->bm = (int)m;
+  std::vector<float2> ta, pre, pres, bh;
+  append_stage_table((int)m, rows_values((int)m), ta);
+  // c_j = e^{sign pi i j^2/n}; with the shift, times e^{-sign 2 pi i j h/n},
+  // h = floor(n/2), which moves bin 0 to index h ("The 1D fftshift in CUDA by
+  // chessboard multiplication": (-1)^j for even n, a complex ramp for odd n)
+  const int64_t h = n / 2;
+  for (int64_t j = 0; j < n; ++j) {
+    pre.push_back(chirp(j * j, n, sign));
+    pres.push_back(chirp(j * j - 2 * j * h, n, sign));
+  }
+  // b = conj(c) wrapped around to length m, transformed in f64, divided by m
+  std::vector<std::complex<double>> b((size_t)m, 0.0);
+  for (int64_t j = 0; j < n; ++j) {
+    const int64_t r = (j * j) % (2 * n);
+    const double a = kTwoPi * 0.5 * (double)r / (double)n;
+    const std::complex<double> cb(std::cos(a), -sign * std::sin(a));
+    b[(size_t)j] = cb;
+    if (j > 0) b[(size_t)(m - j)] = cb;
+  }
+  host_fft_f64(b);
+  for (int64_t k = 0; k < m; ++k) {
+    const std::complex<double> v = b[(size_t)k] / (double)m;
+    bh.push_back(make_float2((float)v.real(), (float)v.imag()));
+  }
+  if (finish_plan(p, {&ta, &pre, &pres, &bh}, {&p->tw_a, &p->chirp, &p->chirp_shift, &p->bhat}, 0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,7 +277,12 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (check_kind_sign(kind, sign) != FFT_OK) return nullptr;
   if (check_total(n, batch, 1) != FFT_OK) return nullptr;
   if (is_direct(kind)) return create_direct(n, batch, kind, sign);
-  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n must be a power of two"), nullptr;
+  if (kind == FFT_C2C && n > 1 && !is_pow2(n)) {
+    if (n > kMaxBluesteinLength)
+      return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 8192"), nullptr;
+    return create_bluestein(n, batch, sign);
+  }
+  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "R2C/C2R lengths must be powers of two"), nullptr;
   const int64_t max_len = kind == FFT_C2C ? (int64_t(1) << kFourStepMaxLog) : 2 * (int64_t)kMaxSinglePass;
   const int64_t min_len = kind == FFT_C2C ? 2 : 4;
   if (n < min_len || n > max_len)
@@ -301,7 +391,7 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_SHIFT:
       if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0 or 1");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
-      if (value && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
+      if (value && !p->bluestein && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
       p->shift = (int)value;
       return ok();
@@ -361,7 +451,11 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   p->executed = true;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
-  if (p->kind == FFT_C2C && p->dims == 1 && !p->fourstep) {
+  if (p->bluestein) {
+    BluesteinArgs a{src, dst, p->tw_a, p->shift ? p->chirp_shift : p->chirp, p->chirp, p->bhat, p->batch,
+                    (int)p->n};
+    e = launch_bluestein(p->bm, a, stream);
+  } else if (p->kind == FFT_C2C && p->dims == 1 && !p->fourstep) {
     RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1, 1};
     e = launch_c2c_rows((int)p->n, p->sign, a, stream);
   } else if (p->kind == FFT_C2C && p->dims == 1) {

@@ -13,7 +13,12 @@
  *    n * x.
  *  - Data are fp32.  Complex values are interleaved (re, im) pairs: 8 bytes per
  *    element ("complex64").  Rows are contiguous; batches follow each other.
- *  - FFT sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
+ *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
+ *    2^28), and any other length from 3 to 8192 by Bluestein's chirp
+ *    transform (two power-of-two transforms of length >= 2n - 1 inside one
+ *    kernel; the GLSL dissertation, section 2.3, names lengths beyond powers
+ *    of two as the extension of its radix-2 transforms).  R2C/C2R and 2D
+ *    sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
  *    (fourier.ts refuses them for its FFT at plan time).  The direct kinds
  *    below take any length from 2 to 16384.
  *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
@@ -73,7 +78,7 @@ enum fft_sign { FFT_FORWARD = -1, FFT_INVERSE = +1 };
 enum fft_status {
   FFT_OK = 0,
   FFT_EINVAL = -1,  /* bad argument: NULL, size < 1, bad kind/sign/option, misaligned */
-  FFT_ENOTSUP = -2, /* valid but unsupported: length not a power of two, too long */
+  FFT_ENOTSUP = -2, /* valid but unsupported: a length this kind does not take, too long */
   FFT_ENOMEM = -3,  /* device allocation failed */
   FFT_EHIP = -4,    /* a HIP runtime call or kernel launch failed (message has details) */
   FFT_ESTATE = -5   /* option set after the first fft_exec */
@@ -82,10 +87,14 @@ enum fft_status {
 enum fft_option {
   /* 1: multiply the input by (-1)^j in 1D, (-1)^(i+j) in 2D, while loading it,
    * which moves the zero frequency to the middle of the output (the chessboard
-   * fftshift: "The 1D fftshift in CUDA by chessboard multiplication").  The
-   * factor is applied by flipping the sign bits of both parts, before any
-   * arithmetic, so the result is bitwise the transform of the negated input.
-   * C2C only; every shifted axis must have even length.  Default 0. */
+   * fftshift: "The 1D fftshift in CUDA by chessboard multiplication").  For
+   * power-of-two lengths the factor is applied by flipping the sign bits of
+   * both parts, before any arithmetic, so the result is bitwise the transform
+   * of the negated input.  For the other 1D lengths (Bluestein path) the
+   * factor is e^{-sign 2 pi i j floor(n/2)/n}, folded into the chirp table
+   * (the page's odd case: a full complex exponential), and bin 0 lands at
+   * index floor(n/2) for odd n as well.  C2C only; 2D axes are even.
+   * Default 0. */
   FFT_OPT_SHIFT = 1,
   /* R2C: keep bins 0..mmax; C2R: read bins 0..mmax.  0 <= mmax <= n/2
    * (fourier.ts: band limit |m| <= mmax < nphi/2).  Default n/2. */
@@ -104,8 +113,9 @@ enum fft_option {
 
 /*
  * Create a plan for `batch` transforms of length n.
- * n: power of two, n >= 2 (C2C) or n >= 4 (R2C/C2R); any 2 <= n <= 16384
- * for the direct kinds.  batch >= 1.
+ * n: C2C: a power of two 2 <= n <= 2^28, or any 3 <= n <= 8192; R2C/C2R: a
+ * power of two 4 <= n <= 32768; the direct kinds: any 2 <= n <= 16384.
+ * batch >= 1.
  * kind: enum fft_kind.  sign: FFT_FORWARD or FFT_INVERSE (FFT_FORWARD for the
  * analysis kinds R2C and R2C_DIRECT, FFT_INVERSE for C2R and C2R_DIRECT).
  * Lengths up to 16384 run as one kernel (one workgroup per row, all stages in
@@ -113,7 +123,10 @@ enum fft_option {
  * column transforms with the inter-pass twiddle fused into their store, then
  * row transforms with a transposing store) and own a scratch buffer of
  * batch*n*8 bytes.
- * Direct plans own a table of n (cos, sin) pairs.
+ * Plans of C2C lengths that are not powers of two own a stage table of
+ * their internal length m (the power of two >= 2n - 1), two chirp tables of
+ * n entries and one of m entries, all built in f64 on the host.
+ * Direct plans own a table of n/2 + 1 (cos, -sin) pairs.
  * Uses the current HIP device.  Returns NULL on error (see fft_last_error).
  */
 fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);

@@ -1,0 +1,112 @@
+"""GPU parity for C2C lengths that are not powers of two (Bluestein's chirp
+transform inside one kernel), against the oracle's DFT by the definition.
+
+Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fourier_transform_amd import fft as F
+from fourier_transform_amd import workloads as W
+
+from gpu_helpers import c2c, dev, empty, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+SMALL = [3, 5, 6, 7, 9, 12, 15, 17, 31, 100, 127, 255, 257]
+LARGE = [1000, 1001, 2047, 3000, 4095, 4097, 5000, 6561, 8191]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    F.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", SMALL + LARGE)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_any_length_sweep(n, sign):
+    for batch in ((1, 3, 37) if n < 1000 else (1, 5)):
+        say(f"any-length c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 10 + batch))
+        y = c2c(x, sign)
+        assert rel_l2(y, oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n", [7, 1000, 4097])
+def test_any_length_in_place(n):
+    say(f"any-length c2c in place n={n}")
+    x = W.uniform_c64((4, n), np.random.default_rng(n + 1))
+    assert rel_l2(c2c(x, -1, inplace=True), oracle.dft(x, -1)) <= TOL
+
+
+@pytest.mark.parametrize("n", [3, 7, 12, 255, 1001, 4095, 6000])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_any_length_shift(n, sign):
+    """Fused shift (even and odd n): bin 0 lands at index floor(n/2), the
+    oracle's index map applied to its own transform."""
+    say(f"any-length shift n={n} sign={sign}")
+    x = W.uniform_c64((3, n), np.random.default_rng(n + 7))
+    want = oracle.dft(x, sign)[:, oracle.fftshift_index(n)]
+    assert rel_l2(c2c(x, sign, shift=1), want) <= TOL
+
+
+@pytest.mark.parametrize("n", [5, 1000, 8191])
+def test_any_length_round_trip(n):
+    say(f"any-length round trip n={n}")
+    x = W.uniform_c64((6, n), np.random.default_rng(n + 3))
+    z = c2c(c2c(x, -1), +1) / n
+    assert rel_l2(z, x) <= TOL
+
+
+def test_any_length_large_batch_sampled_rows():
+    """n = 1000, 16384 rows (the batched shape of the 4096-point workload):
+    every row against a property, sampled rows against the oracle."""
+    import torch
+    n, batch = 1000, 16384
+    say(f"any-length c2c n={n} batch={batch}")
+    x = W.uniform_c64((batch, n), np.random.default_rng(99))
+    pf = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    pi = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_INVERSE)
+    try:
+        xd = dev(x)
+        yd = torch.empty_like(xd)
+        zd = torch.empty_like(xd)
+        F.fft_exec(pf, xd, yd)
+        F.fft_exec(pi, yd, zd)
+        y, z = host(yd), host(zd)
+    finally:
+        F.fft_plan_destroy(pf)
+        F.fft_plan_destroy(pi)
+    rows = np.random.default_rng(5).choice(batch, 24, replace=False)
+    assert rel_l2(y[rows], oracle.dft(x[rows], -1)) <= TOL
+    assert rel_l2(y[-1:], oracle.dft(x[-1:], -1)) <= TOL     # the ragged last workgroup
+    assert rel_l2(z / n, x) <= TOL                            # round trip over every row
+    # Parseval over every row
+    e = np.abs(np.sum(np.abs(y.astype(np.complex128)) ** 2, axis=1) /
+               (n * np.sum(np.abs(x.astype(np.complex128)) ** 2, axis=1)) - 1)
+    assert e.max() <= 1e-5
+
+
+def test_any_length_deterministic():
+    say("any-length determinism n=3000 batch=64")
+    x = W.uniform_c64((64, 3000), np.random.default_rng(4))
+    a, b = c2c(x, -1), c2c(x, -1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_any_length_shift_option_and_sizes():
+    """Shift is accepted for odd lengths on this path; sizes are n, not the
+    internal transform length."""
+    plan = F.fft_plan_create(1001, 3, F.FFT_C2C, F.FFT_FORWARD)
+    try:
+        F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)
+        assert F.fft_plan_get_sizes(plan) == (3 * 1001 * 8, 3 * 1001 * 8)
+    finally:
+        F.fft_plan_destroy(plan)
