@@ -44,6 +44,7 @@ def _lib():
         lib.oracle_dft_analys_direct.argtypes = [_PTR, _PTR, _I64, _I64, _I64]
         lib.oracle_dft_analys_direct.restype = None
         lib.oracle_fftshift_index.argtypes = [_I64, _PTR]
+        lib.oracle_ifftshift_index.argtypes = [_I64, _PTR]
         lib.oracle_fftshift_2d.argtypes = [_PTR, _PTR, _I64, _I64, _I64]
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_dft.argtypes = [_PTR, _PTR, _I64, _I64, ctypes.c_int, ctypes.c_int]
@@ -190,6 +191,13 @@ def fftshift_index(n: int):
     (bin 0 moves to index n//2; for even n this is (i + n/2) mod n)."""
     idx = np.empty(n, np.int64)
     _check(_lib().oracle_fftshift_index(n, _p(idx)), "fftshift_index")
+    return idx
+
+
+def ifftshift_index(n: int):
+    """Index map of the inverse rotation: out[i] = Y[idx[i]], idx[i] = (i + n//2) mod n."""
+    idx = np.empty(n, np.int64)
+    _check(_lib().oracle_ifftshift_index(n, _p(idx)), "ifftshift_index")
     return idx
 
 

@@ -482,6 +482,16 @@ int oracle_fftshift_index(int64_t n, int64_t* idx) {
   return 0;
 }
 
+/* The inverse rotation (numpy's ifftshift): idx[i] = (i + M) mod n, M =
+ * floor(n/2), which moves index M back to 0.  Equal to the shift above for
+ * even n; for odd n the two differ by one place. */
+int oracle_ifftshift_index(int64_t n, int64_t* idx) {
+  if (n < 1) return -1;
+  const int64_t m = n / 2;
+  for (int64_t i = 0; i < n; ++i) idx[i] = (i + m) % n;
+  return 0;
+}
+
 /* out[b][i][j] = y[b][(i + ny/2) mod ny][(j + nx/2) mod nx]  (complex). */
 int oracle_fftshift_2d(const double* y, double* out, int64_t ny, int64_t nx,
                        int64_t batch) {

@@ -362,3 +362,24 @@ def test_shift_theorem_odd(n):
     for sign in (-1, 1):
         ramp = np.exp(-sign * 2j * np.pi * ((m * j) % n) / n)
         assert rel(oracle.dft(x * ramp, sign), oracle.dft(x, sign)[idx]) < 1e-12
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 6, 7, 9, 1001, 1024])
+def test_ifftshift_index_matches_numpy_exactly(n):
+    a = np.arange(n)
+    assert np.array_equal(oracle.ifftshift_index(n), np.fft.ifftshift(a))
+    # it undoes the shift
+    assert np.array_equal(np.arange(n)[oracle.fftshift_index(n)][oracle.ifftshift_index(n)], a)
+
+
+@pytest.mark.parametrize("n", [3, 5, 101, 1001])
+def test_ishift_theorem_odd(n):
+    """Multiplying x_j by e^{+sign 2 pi i M j/n}, M = floor(n/2), rotates the
+    spectrum the other way: the ifftshift index map."""
+    x = crand(n, 5 * n)
+    m = n // 2
+    j = np.arange(n)
+    idx = oracle.ifftshift_index(n)
+    for sign in (-1, 1):
+        ramp = np.exp(sign * 2j * np.pi * ((m * j) % n) / n)
+        assert rel(oracle.dft(x * ramp, sign), oracle.dft(x, sign)[idx]) < 1e-12
