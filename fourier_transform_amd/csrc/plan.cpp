@@ -141,6 +141,7 @@ struct fft_plan {
   int bm = 0;
   const float2* chirp = nullptr;
   const float2* chirp_shift = nullptr;
+  const float2* chirp_ishift = nullptr;
   const float2* bhat = nullptr;
   float2* scratch = nullptr;
 };
@@ -235,15 +236,18 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   int64_t m = 1;
   while (m < 2 * n - 1) m <<= 1;
   p->bm = (int)m;
-  std::vector<float2> ta, pre, pres, bh;
+  std::vector<float2> ta, pre, pres, prei, bh;
   append_stage_table((int)m, rows_values((int)m), ta);
   // c_j = e^{sign pi i j^2/n}; with the shift, times e^{-sign 2 pi i j h/n},
   // h = floor(n/2), which moves bin 0 to index h ("The 1D fftshift in CUDA by
-  // chessboard multiplication": (-1)^j for even n, a complex ramp for odd n)
+  // chessboard multiplication": (-1)^j for even n, a complex ramp for odd n);
+  // with the inverse shift, times e^{+sign 2 pi i j h/n}, which moves index h
+  // to 0 (the same for even n)
   const int64_t h = n / 2;
   for (int64_t j = 0; j < n; ++j) {
     pre.push_back(chirp(j * j, n, sign));
     pres.push_back(chirp(j * j - 2 * j * h, n, sign));
+    prei.push_back(chirp(j * j + 2 * j * h, n, sign));
   }
   // b = conj(c) wrapped around to length m, transformed in f64, divided by m
   std::vector<std::complex<double>> b((size_t)m, 0.0);
@@ -259,7 +263,8 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
     const std::complex<double> v = b[(size_t)k] / (double)m;
     bh.push_back(make_float2((float)v.real(), (float)v.imag()));
   }
-  if (finish_plan(p, {&ta, &pre, &pres, &bh}, {&p->tw_a, &p->chirp, &p->chirp_shift, &p->bhat}, 0) != FFT_OK) {
+  if (finish_plan(p, {&ta, &pre, &pres, &prei, &bh},
+                  {&p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift, &p->bhat}, 0) != FFT_OK) {
     free_plan(p);
     return nullptr;
   }
@@ -389,7 +394,7 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
   if (p->executed) return set_err(FFT_ESTATE, "options must be set before the first fft_exec");
   switch (option) {
     case FFT_OPT_SHIFT:
-      if (value != 0 && value != 1) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0 or 1");
+      if (value < 0 || value > 2) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0, 1 or 2");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
       if (value && !p->bluestein && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
@@ -452,8 +457,8 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
   if (p->bluestein) {
-    BluesteinArgs a{src, dst, p->tw_a, p->shift ? p->chirp_shift : p->chirp, p->chirp, p->bhat, p->batch,
-                    (int)p->n};
+    const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
+    BluesteinArgs a{src, dst, p->tw_a, pre, p->chirp, p->bhat, p->batch, (int)p->n};
     e = launch_bluestein(p->bm, a, stream);
   } else if (p->kind == FFT_C2C && p->dims == 1 && !p->fourstep) {
     RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1, 1};

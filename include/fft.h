@@ -93,8 +93,11 @@ enum fft_option {
    * of the negated input.  For the other 1D lengths (Bluestein path) the
    * factor is e^{-sign 2 pi i j floor(n/2)/n}, folded into the chirp table
    * (the page's odd case: a full complex exponential), and bin 0 lands at
-   * index floor(n/2) for odd n as well.  C2C only; 2D axes are even.
-   * Default 0. */
+   * index floor(n/2) for odd n as well.
+   * 2: the inverse rotation (numpy's ifftshift of the output: index floor(n/2)
+   * moves to 0), by the factor e^{+sign 2 pi i j floor(n/2)/n}; identical to 1
+   * for even lengths (every power-of-two and 2D axis).
+   * C2C only; 2D axes are even.  Default 0. */
   FFT_OPT_SHIFT = 1,
   /* R2C: keep bins 0..mmax; C2R: read bins 0..mmax.  0 <= mmax <= n/2
    * (fourier.ts: band limit |m| <= mmax < nphi/2).  Default n/2. */

@@ -42,7 +42,7 @@ def c2c(x, sign, shift=0, inplace=False):
     plan = F.fft_plan_create(n, batch, F.FFT_C2C, sign)
     try:
         if shift:
-            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)
+            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, shift)
         xd = dev(x)
         yd = xd if inplace else torch.empty_like(xd)
         F.fft_exec(plan, xd, yd)
@@ -58,7 +58,7 @@ def c2c_2d(x, sign, shift=0, inplace=False):
     plan = F.fft_plan_create_2d(ny, nx, batch, F.FFT_C2C, sign)
     try:
         if shift:
-            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)
+            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, shift)
         xd = dev(x)
         yd = xd if inplace else torch.empty_like(xd)
         F.fft_exec(plan, xd, yd)

@@ -57,6 +57,17 @@ def test_any_length_shift(n, sign):
     assert rel_l2(c2c(x, sign, shift=1), want) <= TOL
 
 
+@pytest.mark.parametrize("n", [3, 7, 12, 1001, 4095])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_any_length_inverse_shift(n, sign):
+    """Shift option 2: index floor(n/2) moves to 0 (numpy's ifftshift of the
+    output), for odd n one place away from option 1."""
+    say(f"any-length inverse shift n={n} sign={sign}")
+    x = W.uniform_c64((3, n), np.random.default_rng(n + 11))
+    want = oracle.dft(x, sign)[:, oracle.ifftshift_index(n)]
+    assert rel_l2(c2c(x, sign, shift=2), want) <= TOL
+
+
 @pytest.mark.parametrize("n", [5, 1000, 8191])
 def test_any_length_round_trip(n):
     say(f"any-length round trip n={n}")

@@ -401,6 +401,8 @@ def test_shift_bit_exact_1d():
         assert np.array_equal(ys.view(np.uint32), yr.view(np.uint32))
         # and the shift is the index rotation of the plain transform
         assert rel_l2(ys, oracle.c2c(x, -1)[:, oracle.fftshift_index(n)]) <= TOL
+        # the inverse rotation is the same map for even lengths, bit for bit
+        assert np.array_equal(c2c(x, -1, shift=2).view(np.uint32), ys.view(np.uint32))
 
 
 def test_shift_bit_exact_2d():
@@ -505,6 +507,13 @@ def test_exec_errors_and_state():
         assert e.value.code == F.FFT_EINVAL
         with pytest.raises(F.FFTError):
             F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)     # C2C only
+        pc = F.fft_plan_create(12, 2, F.FFT_C2C, F.FFT_FORWARD)
+        try:
+            with pytest.raises(F.FFTError) as e:
+                F.fft_plan_set(pc, F.FFT_OPT_SHIFT, 3)   # 0, 1 or 2
+            assert e.value.code == F.FFT_EINVAL
+        finally:
+            F.fft_plan_destroy(pc)
         y = empty((4, 33), torch.complex64)
         F.fft_exec(plan, x, y)
         with pytest.raises(F.FFTError) as e:
