@@ -77,6 +77,10 @@ def workload_spec(name):
         return dict(kind="2d", n=W.W5["ny"] * W.W5["nx"], ny=W.W5["ny"], nx=W.W5["nx"], batch=1,
                     dirs=(-1,), gen=W.workload5, passes=2,
                     label="2D C2C fp32 forward 8192x8192 with fused chessboard shift")
+    if name == "w6":
+        return dict(kind="c2c", n=W.W6["n"], batch=W.W6["batch"], dirs=(-1, 1), gen=W.workload6,
+                    passes=1, label="1D C2C fp32 forward+inverse N=1000 batch=65536 "
+                                    "(length not a power of two: chirp transform)")
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -115,12 +119,15 @@ def cpu_baseline(spec, x_host, reps=3, direct=False):
         flops = 5.0 * n * math.log2(n) * len(spec["dirs"])
         desc = f"whole {spec['ny']}x{spec['nx']} image, {len(spec['dirs'])} direction(s)"
     else:
-        rows = max(1, min(spec["batch"], (1 << 27) // n))
+        pow2 = n & (n - 1) == 0
+        # the radix-2 oracle for powers of two, else the definition (O(n^2)
+        # per row, so a smaller sample)
+        rows = max(1, min(spec["batch"], (1 << 27) // n if pow2 else (1 << 25) // (n * n) + 64))
         xs = x_host[:rows].astype(np.complex128)
 
         def run():
             for s in spec["dirs"]:
-                oracle.c2c(xs, s)
+                oracle.c2c(xs, s) if pow2 else oracle.dft(xs, s)
         flops = 5.0 * n * math.log2(n) * rows * len(spec["dirs"])
         desc = f"{rows} of {spec['batch']} rows, {len(spec['dirs'])} direction(s)"
     times = []
@@ -138,7 +145,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w4", "w5"])
+    ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w4", "w5", "w6"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--real-pairs", action="store_true",
                     help="w4: two real rows per complex transform of length n")
@@ -246,7 +253,7 @@ def main():
         bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
     value = flops_step / (ms_per_step * 1e-3) / 1e9
     key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
-           "w4": "real_2048", "w5": "2d_8192x8192"}[args.workload]
+           "w4": "real_2048", "w5": "2d_8192x8192", "w6": "bluestein_1000"}[args.workload]
     if args.direct:
         # a real matrix product of batch x n x 2(mmax+1) per launch, on the
         # fp32 matrix cores

@@ -17,6 +17,9 @@ rounded to float32):
      uniform in [0, 2 pi), plus complex noise with re and im i.i.d.
      N(0, 0.1^2)                                                (2D forward with
      the chessboard shift fused into the load)
+  6  [65536][1000] complex64, re and im i.i.d. U[-1, 1]         (forward + inverse
+     of a length that is not a power of two: the batched shape of workload 2,
+     about 512 MiB, at n = 1000)
 
 Random values are drawn with re and im interleaved (shape [..., 2]).
 """
@@ -30,6 +33,7 @@ W2 = dict(n=4096, batch=16384)
 W3 = dict(n=1 << 22, batch=32)
 W4 = dict(nphi=2048, nlat=1024, mmax=682)
 W5 = dict(ny=8192, nx=8192, tones=16, noise=0.1)
+W6 = dict(n=1000, batch=65536)
 
 
 def rng(workload: int, salt: int = 0):
@@ -61,6 +65,10 @@ def workload2(n=W2["n"], batch=W2["batch"], salt=0):
 
 def workload3(n=W3["n"], batch=W3["batch"], salt=0):
     return normal_c64((batch, n), rng(3, salt))
+
+
+def workload6(n=W6["n"], batch=W6["batch"], salt=0):
+    return uniform_c64((batch, n), rng(6, salt))
 
 
 def workload4_spectrum(nlat=W4["nlat"], mmax=W4["mmax"], salt=0):
