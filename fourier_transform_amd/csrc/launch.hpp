@@ -95,6 +95,34 @@ struct ColStageArgs {
 };
 hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
 
+// C2C rows whose length n <= kMaxMixedLength has no prime factor above 7:
+// mixed-radix Stockham stages of radix 2, 3, 4, 5, 7 or 8 (schedule chosen at
+// plan time), the line resident in LDS between stages.  Stage s has radix
+// radix[s], ns[s] = product of the radices before it, m[s] = n / radix[s]
+// butterflies, and its twiddles W_{ns*radix}^{r*j} at tw[twoff[s] + (r-1)*ns + j].
+// ns_magic[s] = ceil(2^32 / ns[s]), so that b / ns = umulhi(b, ns_magic) for
+// b < 2^16.  pre: n factors applied on load (the shift ramps), or null.
+// Threads: tpl per line, lines per workgroup; each thread takes butterflies
+// t, t + tpl, ..., at most kb = kMixedButterflies per stage, so
+// tpl * kb >= m[s] and every stage needs m[s] <= 1024 * kb.
+constexpr int kMaxMixedLength = 8192;
+constexpr int kMixedMaxStages = 16;
+constexpr int kMixedButterflies = 2;
+struct MixedArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;
+  const float2* pre;
+  int64_t rows;
+  int n, nstages, tpl, lines, kb;
+  int radix[kMixedMaxStages];
+  int ns[kMixedMaxStages];
+  int m[kMixedMaxStages];
+  int twoff[kMixedMaxStages];
+  uint32_t ns_magic[kMixedMaxStages];
+};
+hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
+
 // C2C rows of any length n (2 <= n <= kMaxBluesteinLength) by Bluestein's
 // chirp: with c_j = e^{sign pi i j^2/n}, y_k = c_k * (a conv b)_k, where
 // a_j = x_j pre_j (pre_j = c_j, times the shift ramp when requested) padded

@@ -5,6 +5,7 @@
 // error path can be exercised without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <complex>
 #include <cstdint>
@@ -143,6 +144,12 @@ struct fft_plan {
   const float2* chirp_shift = nullptr;
   const float2* chirp_ishift = nullptr;
   const float2* bhat = nullptr;
+  // C2C lengths with no prime factor above 7 (mixed radix): the schedule, and
+  // the load factors of the two shifts
+  bool mixed = false;
+  MixedArgs mx{};
+  const float2* mx_shift = nullptr;
+  const float2* mx_ishift = nullptr;
   float2* scratch = nullptr;
 };
 
@@ -223,6 +230,78 @@ fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
   return p;
 }
 
+// radices of the mixed-radix schedule for n = 2^a 3^b 5^c 7^d, or an empty
+// list when n has another prime factor: 8s (with 4 x 4 in place of 8 x 2),
+// the leftover 4 or 2, then 7s, 5s and 3s
+std::vector<int> mixed_radices(int64_t n) {
+  std::vector<int> r;
+  int a = 0;
+  while (n % 2 == 0) n /= 2, ++a;
+  if (a % 3 == 1 && a >= 4) {
+    for (int i = 0; i < a / 3 - 1; ++i) r.push_back(8);
+    r.push_back(4);
+    r.push_back(4);
+  } else {
+    for (int i = 0; i < a / 3; ++i) r.push_back(8);
+    if (a % 3 == 2) r.push_back(4);
+    if (a % 3 == 1) r.push_back(2);
+  }
+  for (int p : {7, 5, 3})
+    while (n % p == 0) n /= p, r.push_back(p);
+  if (n != 1) r.clear();
+  return r;
+}
+
+// C2C of a length with no prime factor above 7, not a power of two, <= kMaxMixedLength
+fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int>& rad) {
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = FFT_C2C;
+  p->sign = sign;
+  p->mixed = true;
+  MixedArgs& a = p->mx;
+  a.rows = batch;
+  a.n = (int)n;
+  a.nstages = (int)rad.size();
+  std::vector<float2> tw, sh, ish;
+  int64_t ns = 1, maxm = 0;
+  for (int st = 0; st < a.nstages; ++st) {
+    const int R = rad[st];
+    a.radix[st] = R;
+    a.ns[st] = (int)ns;
+    a.m[st] = (int)(n / R);
+    a.ns_magic[st] = ns == 1 ? 0u : (uint32_t)(((uint64_t(1) << 32) + (uint64_t)ns - 1) / (uint64_t)ns);
+    a.twoff[st] = (int)tw.size();
+    if (st > 0)
+      for (int r = 1; r < R; ++r)
+        for (int64_t j = 0; j < ns; ++j) tw.push_back(root((int64_t)r * j, ns * R));
+    maxm = std::max<int64_t>(maxm, n / R);
+    ns *= R;
+  }
+  if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
+  a.kb = kMixedButterflies;
+  a.tpl = (int)((maxm + a.kb - 1) / a.kb);
+  a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
+  // shift factors e^{-sign 2 pi i j h/n} and e^{+sign ...}, h = floor(n/2)
+  // ("The 1D fftshift in CUDA by chessboard multiplication", odd case)
+  const int64_t h = n / 2;
+  for (int64_t j = 0; j < n; ++j) {
+    const float2 w = root((j * h) % n, n);  // e^{-2 pi i jh/n}
+    const float2 wc = make_float2(w.x, -w.y);
+    sh.push_back(sign < 0 ? wc : w);
+    ish.push_back(sign < 0 ? w : wc);
+  }
+  if (finish_plan(p, {&tw, &sh, &ish}, {&a.tw, &p->mx_shift, &p->mx_ishift}, 0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
 // C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLength
 fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   fft_plan* p = new (std::nothrow) fft_plan();
@@ -285,6 +364,14 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (kind == FFT_C2C && n > 1 && !is_pow2(n)) {
     if (n > kMaxBluesteinLength)
       return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 8192"), nullptr;
+    // mixed radix when every prime factor is at most 7 and every stage has
+    // at most 1024 * kMixedButterflies butterflies (radix >= 2, 3, 4 for
+    // n up to 4096, 6144, 8192), else the chirp transform
+    const std::vector<int> rad = mixed_radices(n);
+    const int rmin = rad.empty() ? 0 : *std::min_element(rad.begin(), rad.end());
+    if (!rad.empty() && n <= kMaxMixedLength && (int)rad.size() <= kMixedMaxStages &&
+        n / rmin <= 1024 * kMixedButterflies)
+      return create_mixed(n, batch, sign, rad);
     return create_bluestein(n, batch, sign);
   }
   if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "R2C/C2R lengths must be powers of two"), nullptr;
@@ -396,7 +483,7 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_SHIFT:
       if (value < 0 || value > 2) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0, 1 or 2");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
-      if (value && !p->bluestein && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
+      if (value && !p->bluestein && !p->mixed && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
       p->shift = (int)value;
       return ok();
@@ -456,7 +543,13 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   p->executed = true;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
-  if (p->bluestein) {
+  if (p->mixed) {
+    MixedArgs a = p->mx;
+    a.in = src;
+    a.out = dst;
+    a.pre = p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
+    e = launch_mixed(p->sign, a, stream);
+  } else if (p->bluestein) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
     BluesteinArgs a{src, dst, p->tw_a, pre, p->chirp, p->bhat, p->batch, (int)p->n};
     e = launch_bluestein(p->bm, a, stream);

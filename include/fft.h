@@ -14,10 +14,12 @@
  *  - Data are fp32.  Complex values are interleaved (re, im) pairs: 8 bytes per
  *    element ("complex64").  Rows are contiguous; batches follow each other.
  *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
- *    2^28), and any other length from 3 to 8192 by Bluestein's chirp
- *    transform (two power-of-two transforms of length >= 2n - 1 inside one
- *    kernel; the GLSL dissertation, section 2.3, names lengths beyond powers
- *    of two as the extension of its radix-2 transforms).  R2C/C2R and 2D
+ *    2^28), and any other length from 3 to 8192 (the GLSL dissertation,
+ *    section 2.3, names mixed radices and other lengths as the extension of
+ *    its radix-2 transforms): lengths with no prime factor above 7 by
+ *    mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) when every stage
+ *    has at most 2048 butterflies, the others by Bluestein's chirp transform
+ *    (two power-of-two transforms of length >= 2n - 1 inside one kernel).  R2C/C2R and 2D
  *    sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
  *    (fourier.ts refuses them for its FFT at plan time).  The direct kinds
  *    below take any length from 2 to 16384.
@@ -90,10 +92,10 @@ enum fft_option {
    * fftshift: "The 1D fftshift in CUDA by chessboard multiplication").  For
    * power-of-two lengths the factor is applied by flipping the sign bits of
    * both parts, before any arithmetic, so the result is bitwise the transform
-   * of the negated input.  For the other 1D lengths (Bluestein path) the
-   * factor is e^{-sign 2 pi i j floor(n/2)/n}, folded into the chirp table
-   * (the page's odd case: a full complex exponential), and bin 0 lands at
-   * index floor(n/2) for odd n as well.
+   * of the negated input.  For the other 1D lengths the factor is
+   * e^{-sign 2 pi i j floor(n/2)/n}, a table applied on load (folded into the
+   * chirp on the chirp-transform path; the page's odd case: a full complex
+   * exponential), and bin 0 lands at index floor(n/2) for odd n as well.
    * 2: the inverse rotation (numpy's ifftshift of the output: index floor(n/2)
    * moves to 0), by the factor e^{+sign 2 pi i j floor(n/2)/n}; identical to 1
    * for even lengths (every power-of-two and 2D axis).
@@ -126,9 +128,11 @@ enum fft_option {
  * column transforms with the inter-pass twiddle fused into their store, then
  * row transforms with a transposing store) and own a scratch buffer of
  * batch*n*8 bytes.
- * Plans of C2C lengths that are not powers of two own a stage table of
- * their internal length m (the power of two >= 2n - 1), two chirp tables of
- * n entries and one of m entries, all built in f64 on the host.
+ * Plans of C2C lengths that are not powers of two own either the mixed-radix
+ * stage tables and two shift tables of n entries, or (chirp transform) a
+ * stage table of their internal length m (the power of two >= 2n - 1), three
+ * chirp tables of n entries and one of m entries, all built in f64 on the
+ * host.
  * Direct plans own a table of n/2 + 1 (cos, -sin) pairs.
  * Uses the current HIP device.  Returns NULL on error (see fft_last_error).
  */

@@ -1,5 +1,7 @@
-"""GPU parity for C2C lengths that are not powers of two (Bluestein's chirp
-transform inside one kernel), against the oracle's DFT by the definition.
+"""GPU parity for C2C lengths that are not powers of two, against the
+oracle's DFT by the definition: mixed-radix Stockham stages (radices 2, 3, 4,
+5, 7, 8) for lengths with no prime factor above 7, Bluestein's chirp
+transform inside one kernel for the others.
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -15,8 +17,9 @@ from gpu_helpers import c2c, dev, empty, host, rel_l2, say
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
-SMALL = [3, 5, 6, 7, 9, 12, 15, 17, 31, 100, 127, 255, 257]
-LARGE = [1000, 1001, 2047, 3000, 4095, 4097, 5000, 6561, 8191]
+SMALL = [3, 5, 6, 7, 9, 12, 14, 15, 17, 21, 31, 35, 48, 49, 96, 100, 127, 255, 257, 384]
+LARGE = [1000, 1001, 1029, 1536, 2047, 2401, 3000, 3072, 4095, 4097, 5000, 6144, 6250, 6561,
+         7168, 8000, 8191]
 
 
 @pytest.fixture(scope="module", autouse=True)
