@@ -11,7 +11,7 @@ namespace {
 // The pass-1 kernel is specialised on the row count of the pass-2 workgroups
 // (and the reverse), which fixes the block layout of the scratch between
 // them.  The split makes n1 = n2 or n1 = n2/2, so two variants cover each.
-template <int S>
+template <int S, bool HOOK>
 struct FsColsOp {
   template <int N2>
   struct At {
@@ -21,7 +21,7 @@ struct FsColsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_cols<N2, S, BK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
+      hipLaunchKernelGGL((k_fs_cols<N2, S, BK, HOOK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
@@ -31,7 +31,7 @@ struct FsColsOp {
     }
   };
 };
-template <int S>
+template <int S, bool HOOK>
 struct FsRowsOp {
   template <int N1>
   struct At {
@@ -41,7 +41,7 @@ struct FsRowsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_rows<N1, S, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
+      hipLaunchKernelGGL((k_fs_rows<N1, S, BC, HOOK>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
@@ -53,12 +53,20 @@ struct FsRowsOp {
 };
 }  // namespace
 
-hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t st) {
-  if (sign < 0) return dispatch_pow2<FsColsOp<-1>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
-  return dispatch_pow2<FsColsOp<1>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
+hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t st, bool hook) {
+  if (hook) {
+    if (sign < 0) return dispatch_pow2<FsColsOp<-1, true>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
+    return dispatch_pow2<FsColsOp<1, true>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
+  }
+  if (sign < 0) return dispatch_pow2<FsColsOp<-1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
+  return dispatch_pow2<FsColsOp<1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
 }
-hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t st) {
-  if (sign < 0) return dispatch_pow2<FsRowsOp<-1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
-  return dispatch_pow2<FsRowsOp<1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t st, bool hook) {
+  if (hook) {
+    if (sign < 0) return dispatch_pow2<FsRowsOp<-1, true>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+    return dispatch_pow2<FsRowsOp<1, true>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+  }
+  if (sign < 0) return dispatch_pow2<FsRowsOp<-1, false>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+  return dispatch_pow2<FsRowsOp<1, false>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
 }
 }  // namespace fftamd

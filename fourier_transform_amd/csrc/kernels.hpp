@@ -415,7 +415,7 @@ __device__ __forceinline__ uint32_t fs_block_index(uint32_t k2, uint32_t c1, uin
 // output multiplied by W_n^{n1*k2}, stored to scratch in the block layout
 // above (BK: rows per pass-2 workgroup)
 // ---------------------------------------------------------------------------
-template <int N2, int S, int BK>
+template <int N2, int S, int BK, bool HOOK>
 __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) void k_fs_cols(FourStepArgs a) {
   constexpr int E = tile_e(N2, false);
   constexpr bool SPLIT = tile_split(N2, false);
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   const bool valid = g0 + line < a.batch * (int64_t)n1;
   const int64_t b = g0 / n1;
   const uint32_t c1 = (uint32_t)(g0 - b * n1) + line;
-  const int64_t base = b * (int64_t)n1 * N2 + (c1 - line);
+  const int64_t base = (HOOK ? b * a.in_stride : b * (int64_t)n1 * N2) + (c1 - line);
   const uint32_t off = (uint32_t)line + (uint32_t)u * n1;
   const uint32_t step = (uint32_t)T * n1;
   // Inter-pass twiddle W_n^{c1*k2} with k2 = u + T*m, split as
@@ -455,7 +455,19 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   const uint32_t eu = c1 * (uint32_t)u;
   const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
   float2 v[E];
-  if (valid) {
+  if (valid && HOOK) {
+    // element j = c1 + n1*k2 of a row of in_len values (zero beyond), times pre[j]
+    const float2* src = a.in + base;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const uint32_t j = c0 + off + step * m;
+      v[m] = make_float2(0.f, 0.f);
+      if (j < (uint32_t)a.in_len) {
+        v[m] = gload_nt(src, off + step * m);
+        if (a.pre) v[m] = cmul(v[m], gload(a.pre, j));
+      }
+    }
+  } else if (valid) {
     const float2* src = a.in + base;
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + step * m);
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 // consecutive threads on consecutive rows, so each store is a run of C
 // elements.
 // ---------------------------------------------------------------------------
-template <int N1, int S, int BC>
+template <int N1, int S, int BC, bool HOOK>
 __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) void k_fs_rows(FourStepArgs a) {
   constexpr int E = tile_e(N1, true);
   constexpr bool SPLIT = tile_split(N1, true);
@@ -563,12 +575,18 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
     // n2 >= 128 > C: the group's rows belong to one transform b
     const int64_t b = g0 / n2;
     const int64_t k20 = g0 - b * n2;
-    float2* dst = a.out + b * n2 * N1 + k20;
+    float2* dst = a.out + (HOOK ? b * a.out_stride : b * n2 * N1) + k20;
     const uint32_t off = (uint32_t)ln + (uint32_t)(tid / C) * (uint32_t)n2;
     const uint32_t step = (uint32_t)(NT / C) * (uint32_t)n2;
 #pragma unroll
     for (int p = 0; p < E; ++p) {
-      gstore_nt(dst, off + step * p, v[p]);
+      if constexpr (HOOK) {
+        // output k = k20 + off + step*p of a row of out_len values, times post[k]
+        const uint32_t k = (uint32_t)k20 + off + step * p;
+        if (k < (uint32_t)a.out_len) gstore_nt(dst, off + step * p, a.post ? cmul(v[p], gload(a.post, k)) : v[p]);
+      } else {
+        gstore_nt(dst, off + step * p, v[p]);
+      }
       if constexpr (E > 16) {
         if ((p & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }

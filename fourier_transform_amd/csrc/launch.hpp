@@ -71,9 +71,18 @@ struct FourStepArgs {
   int64_t batch;
   int n1, n2, bits;
   int shift;  // pass 1 only: multiply element j by (-1)^j (1D chessboard)
+  // Hooked variants (hook = true in the launchers), for transforms embedded
+  // in a longer computation: pass 1 reads rows of in_len values in_stride
+  // apart (zero beyond in_len) and multiplies element j by pre[j] (if set);
+  // pass 2 writes rows out_stride apart, only outputs k < out_len, multiplied
+  // by post[k] (if set).  The unhooked variants ignore these fields.
+  const float2* pre;
+  const float2* post;
+  int64_t in_stride, out_stride;
+  int in_len, out_len;
 };
-hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream);
-hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream);
+hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream, bool hook = false);
+hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream, bool hook = false);
 
 // One step of a column transform split in two (2D column pass of tall images,
 // ny = na * nb; column row index i = ia + na*ib, output k = kb + nb*ka).
@@ -130,6 +139,9 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
 // is inverse_FFT_m(forward_FFT_m(a) * bhat) with bhat = forward_FFT_m(b)/m.
 // Rows of n complex64 values, contiguous; in place allowed.
 constexpr int kMaxBluesteinLength = 8192;
+// longer lengths run the same computation as two four-step transforms
+// (launch_fourstep_* with hooks), up to this length
+constexpr int64_t kMaxBluesteinLengthLarge = int64_t(1) << 22;
 struct BluesteinArgs {
   const float2* in;
   float2* out;

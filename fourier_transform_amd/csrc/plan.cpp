@@ -302,7 +302,12 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   return p;
 }
 
-// C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLength
+// C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLengthLarge.
+// The transforms of length m >= 2n - 1 run inside one kernel per row batch
+// while m <= kMaxSinglePass; above, as two four-step transforms whose
+// hooked passes apply the chirp on load, the chirp transform between them
+// and the chirp again on store (four passes over batch x m values, through
+// two plan-owned scratch buffers).
 fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
@@ -315,8 +320,22 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   int64_t m = 1;
   while (m < 2 * n - 1) m <<= 1;
   p->bm = (int)m;
-  std::vector<float2> ta, pre, pres, prei, bh;
-  append_stage_table((int)m, rows_values((int)m), ta);
+  std::vector<float2> ta, tb, thi, tlo, pre, pres, prei, bh;
+  size_t scratch = 0;
+  if (m <= kMaxSinglePass) {
+    append_stage_table((int)m, rows_values((int)m), ta);
+  } else {
+    const int L = ilog2c(m);
+    p->fourstep = true;
+    p->n1 = 1 << (L / 2);
+    p->n2 = 1 << (L - L / 2);
+    p->bits = L - L / 2;
+    append_stage_table(p->n1, tposed_values(p->n1), ta);
+    append_stage_table(p->n2, cols_values(p->n2), tb);
+    for (int64_t hh = 0; hh < (m >> p->bits); ++hh) thi.push_back(root(hh << p->bits, m));
+    for (int64_t l = 0; l < (int64_t(1) << p->bits); ++l) tlo.push_back(root(l, m));
+    scratch = 2 * (size_t)(m * batch) * sizeof(float2);
+  }
   // c_j = e^{sign pi i j^2/n}; with the shift, times e^{-sign 2 pi i j h/n},
   // h = floor(n/2), which moves bin 0 to index h ("The 1D fftshift in CUDA by
   // chessboard multiplication": (-1)^j for even n, a complex ramp for odd n);
@@ -342,8 +361,13 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
     const std::complex<double> v = b[(size_t)k] / (double)m;
     bh.push_back(make_float2((float)v.real(), (float)v.imag()));
   }
-  if (finish_plan(p, {&ta, &pre, &pres, &prei, &bh},
-                  {&p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift, &p->bhat}, 0) != FFT_OK) {
+  std::vector<std::vector<float2>*> parts = {&ta, &pre, &pres, &prei, &bh};
+  std::vector<const float2**> slots = {&p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift, &p->bhat};
+  if (p->fourstep) {
+    parts.insert(parts.end(), {&tb, &thi, &tlo});
+    slots.insert(slots.end(), {&p->tw_b, &p->thi, &p->tlo});
+  }
+  if (finish_plan(p, parts, slots, scratch) != FFT_OK) {
     free_plan(p);
     return nullptr;
   }
@@ -362,8 +386,8 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (check_total(n, batch, 1) != FFT_OK) return nullptr;
   if (is_direct(kind)) return create_direct(n, batch, kind, sign);
   if (kind == FFT_C2C && n > 1 && !is_pow2(n)) {
-    if (n > kMaxBluesteinLength)
-      return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 8192"), nullptr;
+    if (n > kMaxBluesteinLengthLarge)
+      return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 2^22"), nullptr;
     // mixed radix when every prime factor is at most 7 and every stage has
     // at most 1024 * kMixedButterflies butterflies (radix >= 2, 3, 4 for
     // n up to 4096, 6144, 8192), else the chirp transform
@@ -549,6 +573,30 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     a.out = dst;
     a.pre = p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
     e = launch_mixed(p->sign, a, stream);
+  } else if (p->bluestein && p->fourstep) {
+    const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
+    const int64_t m = p->bm;
+    float2* s1 = p->scratch;
+    float2* s2 = p->scratch + m * p->batch;
+    // forward transform of the chirped row (zero beyond n) into s2
+    FourStepArgs f1{src, s1, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
+                    pre, nullptr, p->n, 0, (int)p->n, 0};
+    e = launch_fourstep_cols(p->n2, -1, f1, stream, true);
+    if (e == hipSuccess) {
+      FourStepArgs f2{s1, s2, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
+      e = launch_fourstep_rows(p->n1, -1, f2, stream);
+    }
+    // inverse transform of (that times bhat), the first n outputs times c_k, into out
+    if (e == hipSuccess) {
+      FourStepArgs i1{s2, s1, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
+                      p->bhat, nullptr, m, 0, (int)m, 0};
+      e = launch_fourstep_cols(p->n2, +1, i1, stream, true);
+    }
+    if (e == hipSuccess) {
+      FourStepArgs i2{s1, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
+                      nullptr, p->chirp, 0, p->n, 0, (int)p->n};
+      e = launch_fourstep_rows(p->n1, +1, i2, stream, true);
+    }
   } else if (p->bluestein) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
     BluesteinArgs a{src, dst, p->tw_a, pre, p->chirp, p->bhat, p->batch, (int)p->n};

@@ -14,12 +14,14 @@
  *  - Data are fp32.  Complex values are interleaved (re, im) pairs: 8 bytes per
  *    element ("complex64").  Rows are contiguous; batches follow each other.
  *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
- *    2^28), and any other length from 3 to 8192 (the GLSL dissertation,
+ *    2^28), and any other length from 3 to 2^22 (the GLSL dissertation,
  *    section 2.3, names mixed radices and other lengths as the extension of
  *    its radix-2 transforms): lengths with no prime factor above 7 by
  *    mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) when every stage
- *    has at most 2048 butterflies, the others by Bluestein's chirp transform
- *    (two power-of-two transforms of length >= 2n - 1 inside one kernel).  R2C/C2R and 2D
+ *    has at most 2048 butterflies (n <= 8192), the others by Bluestein's
+ *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
+ *    inside one kernel while m <= 16384, else as two four-step transforms
+ *    (four passes) through a scratch buffer of 2 * batch * m * 8 bytes.  R2C/C2R and 2D
  *    sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
  *    (fourier.ts refuses them for its FFT at plan time).  The direct kinds
  *    below take any length from 2 to 16384.
@@ -118,7 +120,7 @@ enum fft_option {
 
 /*
  * Create a plan for `batch` transforms of length n.
- * n: C2C: a power of two 2 <= n <= 2^28, or any 3 <= n <= 8192; R2C/C2R: a
+ * n: C2C: a power of two 2 <= n <= 2^28, or any 3 <= n <= 2^22; R2C/C2R: a
  * power of two 4 <= n <= 32768; the direct kinds: any 2 <= n <= 16384.
  * batch >= 1.
  * kind: enum fft_kind.  sign: FFT_FORWARD or FFT_INVERSE (FFT_FORWARD for the

@@ -50,8 +50,8 @@ def err_of(fn, *args):
     ((8, 1, F.FFT_C2C, 0), F.FFT_EINVAL),           # bad sign
     ((8, 1, F.FFT_R2C, +1), F.FFT_EINVAL),          # R2C is forward
     ((8, 1, F.FFT_C2R, -1), F.FFT_EINVAL),          # C2R is inverse
-    ((8193, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),      # not a power of two and above 8192
-    ((12289, 4, F.FFT_C2C, 1), F.FFT_ENOTSUP),
+    (((1 << 22) + 1, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),  # not a power of two and above 2^22
+    ((5000000, 4, F.FFT_C2C, 1), F.FFT_ENOTSUP),
     ((1, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),         # too short
     ((2, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),         # real transforms need n >= 4
     ((1 << 29, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # beyond the four-step range
@@ -113,10 +113,10 @@ def test_direct_kinds_accept_any_length(lib, n, kind, sign):
     assert err_of(F.fft_plan_create, n, 3, kind, sign) in (F.FFT_EHIP, F.FFT_ENOMEM)
 
 
-@pytest.mark.parametrize("n", [3, 12, 1000, 1001, 8191])
-def test_c2c_any_length_up_to_8192_passes_the_checks(lib, n):
-    """C2C lengths that are not powers of two (Bluestein path) are accepted up
-    to 8192 (with no GPU the first HIP call then fails)."""
+@pytest.mark.parametrize("n", [3, 12, 1000, 1001, 8191, 8193, 100000, (1 << 22) - 1])
+def test_c2c_any_length_up_to_2p22_passes_the_checks(lib, n):
+    """C2C lengths that are not powers of two (mixed-radix or chirp paths) are
+    accepted up to 2^22 (with no GPU the first HIP call then fails)."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("a device is present")

@@ -124,3 +124,43 @@ def test_any_length_shift_option_and_sizes():
         assert F.fft_plan_get_sizes(plan) == (3 * 1001 * 8, 3 * 1001 * 8)
     finally:
         F.fft_plan_destroy(plan)
+
+
+# --------------------------------------------------------------------------
+# lengths above 8192: the chirp transform through two hooked four-step
+# transforms of length m >= 2n - 1
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [8193, 10000, 12289, 20000])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_any_length_large_full(n, sign):
+    say(f"any-length (four-step chirp) n={n} sign={sign}")
+    x = W.uniform_c64((3, n), np.random.default_rng(n + 21))
+    assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL
+
+
+@pytest.mark.parametrize("n", [65537, 100000, 1000003, (1 << 22) - 1])
+def test_any_length_large_sampled_bins(n):
+    """Longer rows: 64 sampled bins of every row by the definition, the round
+    trip and Parseval over every value."""
+    batch = 2
+    say(f"any-length (four-step chirp) n={n} batch={batch}")
+    x = W.uniform_c64((batch, n), np.random.default_rng(n % 1000 + 5))
+    y = c2c(x, -1)
+    bins = np.unique(np.concatenate([[0, 1, n // 2, n - 1],
+                                     np.random.default_rng(7).integers(0, n, 60)]))
+    for r in range(batch):
+        assert rel_l2(y[r, bins], oracle.dft_bins(x[r], bins, -1)) <= TOL
+    z = c2c(y, +1) / n
+    assert rel_l2(z, x) <= TOL
+    e = np.abs(np.sum(np.abs(y.astype(np.complex128)) ** 2) /
+               (n * np.sum(np.abs(x.astype(np.complex128)) ** 2)) - 1)
+    assert e <= 1e-5
+
+
+@pytest.mark.parametrize("n,shift", [(10001, 1), (10001, 2), (16000, 1)])
+def test_any_length_large_shift_and_in_place(n, shift):
+    say(f"any-length (four-step chirp) shift={shift} n={n}, in place")
+    x = W.uniform_c64((2, n), np.random.default_rng(n + shift))
+    idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
+    want = oracle.dft(x, -1)[:, idx]
+    assert rel_l2(c2c(x, -1, shift=shift, inplace=True), want) <= TOL
