@@ -80,8 +80,17 @@ def workload_spec(name):
     if name == "w6":
         return dict(kind="c2c", n=W.W6["n"], batch=W.W6["batch"], dirs=(-1, 1), gen=W.workload6,
                     passes=1, label="1D C2C fp32 forward+inverse N=1000 batch=65536 "
-                                    "(length not a power of two: chirp transform)")
+                                    "(length not a power of two)")
     raise SystemExit(f"unknown workload {name}")
+
+
+def any_length_spec(n):
+    """Workload 6 at another length: about the same 512 MiB, rows of n values."""
+    from fourier_transform_amd import workloads as W
+    batch = max(1, (1000 * 65536) // n)
+    return dict(kind="c2c", n=n, batch=batch, dirs=(-1, 1),
+                gen=lambda: W.workload6(n=n, batch=batch), passes=1,
+                label=f"1D C2C fp32 forward+inverse N={n} batch={batch} (length not a power of two)")
 
 
 def cpu_baseline(spec, x_host, reps=3, direct=False):
@@ -149,6 +158,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--real-pairs", action="store_true",
                     help="w4: two real rows per complex transform of length n")
+    ap.add_argument("--n", type=int, default=None,
+                    help="w6 only: the row length (default 1000; rows scaled to keep ~512 MiB)")
     ap.add_argument("--direct", action="store_true",
                     help="w4: the band-limited direct sums on the matrix cores instead of the FFT")
     args = ap.parse_args()
@@ -160,6 +171,10 @@ def main():
         raise SystemExit("--direct and --real-pairs apply to the real-transform workload w4")
     if args.direct and args.real_pairs:
         raise SystemExit("--direct and --real-pairs exclude each other")
+    if args.n is not None and args.workload != "w6":
+        raise SystemExit("--n applies to the any-length workload w6")
+    if args.n is not None and (args.n < 3 or args.n & (args.n - 1) == 0):
+        raise SystemExit("--n takes a length >= 3 that is not a power of two")
 
     import numpy as np
     import torch
@@ -168,7 +183,7 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no HIP device")
     F.lib()  # fail loudly if the library is missing
-    spec = workload_spec(args.workload)
+    spec = any_length_spec(args.n) if args.n is not None else workload_spec(args.workload)
     n, batch = spec["n"], spec["batch"]
     x_host = spec["gen"]()
     xd = torch.from_numpy(x_host).cuda()
@@ -253,7 +268,7 @@ def main():
         bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
     value = flops_step / (ms_per_step * 1e-3) / 1e9
     key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
-           "w4": "real_2048", "w5": "2d_8192x8192", "w6": "bluestein_1000"}[args.workload]
+           "w4": "real_2048", "w5": "2d_8192x8192", "w6": f"any_{n}"}[args.workload]
     if args.direct:
         # a real matrix product of batch x n x 2(mmax+1) per launch, on the
         # fp32 matrix cores
