@@ -386,11 +386,14 @@ int oracle_fft_2d(const double* x, double* y, int64_t ny, int64_t nx,
  * x is [batch][n] real, F is [batch][mmax+1] complex (row-major). */
 int oracle_r2c(const double* x, double* F, int64_t n, int64_t batch,
                int64_t mmax, int threads) {
-  if (!is_pow2(n) || mmax < 0 || mmax > n / 2 || batch < 0) return -1;
+  if (n < 1 || mmax < 0 || mmax > n / 2 || batch < 0) return -1;
   double* xc = (double*)calloc((size_t)(2 * n * batch), sizeof(double));
   double* Y = (double*)malloc(sizeof(double) * 2 * n * batch);
   for (int64_t i = 0; i < n * batch; ++i) xc[2 * i] = x[i];
-  int rc = oracle_fft(xc, Y, n, batch, -1, threads);
+  /* the radix-2 transform for powers of two, the definition otherwise */
+  int rc = batch == 0 ? 0
+                      : (is_pow2(n) ? oracle_fft(xc, Y, n, batch, -1, threads)
+                                    : oracle_dft(xc, Y, n, batch, -1, threads));
   if (rc == 0)
     for (int64_t b = 0; b < batch; ++b)
       memcpy(F + 2 * b * (mmax + 1), Y + 2 * b * n,
@@ -406,7 +409,7 @@ int oracle_r2c(const double* x, double* F, int64_t n, int64_t batch,
  * F is [batch][mmax+1] complex (row-major), x is [batch][n] real. */
 int oracle_c2r(const double* F, double* x, int64_t n, int64_t batch,
                int64_t mmax, int threads) {
-  if (!is_pow2(n) || n < 2 || mmax < 0 || mmax > n / 2 || batch < 0) return -1;
+  if (n < 2 || mmax < 0 || mmax > n / 2 || batch < 0) return -1;
   double* X = (double*)calloc((size_t)(2 * n * batch), sizeof(double));
   double* y = (double*)malloc(sizeof(double) * 2 * n * batch);
   for (int64_t b = 0; b < batch; ++b) {
@@ -426,7 +429,9 @@ int oracle_c2r(const double* F, double* x, int64_t n, int64_t batch,
       row[2 * (n - m) + 1] = -f[2 * m + 1];
     }
   }
-  int rc = oracle_fft(X, y, n, batch, +1, threads);
+  int rc = batch == 0 ? 0
+                      : (is_pow2(n) ? oracle_fft(X, y, n, batch, +1, threads)
+                                    : oracle_dft(X, y, n, batch, +1, threads));
   if (rc == 0)
     for (int64_t i = 0; i < n * batch; ++i) x[i] = y[2 * i];
   free(X);

@@ -383,3 +383,37 @@ def test_ishift_theorem_odd(n):
     for sign in (-1, 1):
         ramp = np.exp(sign * 2j * np.pi * ((m * j) % n) / n)
         assert rel(oracle.dft(x * ramp, sign), oracle.dft(x, sign)[idx]) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# real transforms at lengths that are not powers of two (the definition)
+# --------------------------------------------------------------------------
+REAL_ANY_N = [3, 6, 7, 10, 15, 100, 999, 1000]
+
+
+@pytest.mark.parametrize("n", REAL_ANY_N)
+def test_r2c_any_length(n):
+    """Against numpy's rfft (third party) and the band-limited direct analysis
+    (the oracle's separate fourier.ts sums)."""
+    x = np.random.default_rng(n).normal(size=(3, n))
+    assert rel(oracle.r2c(x), np.fft.rfft(x, axis=-1)) < 1e-12
+    m = (n - 1) // 2
+    assert rel(oracle.r2c(x, m), oracle.dft_analys_direct(x, m)) < 1e-12
+
+
+@pytest.mark.parametrize("n", REAL_ANY_N)
+def test_c2r_any_length(n):
+    """Against the direct synthesis sums, numpy's irfft for the full half
+    spectrum, and the band-limited round trip R2C(C2R(F)) = n F."""
+    g = np.random.default_rng(n + 1)
+    m = (n - 1) // 2
+    F = g.normal(size=(3, m + 1)) + 1j * g.normal(size=(3, m + 1))
+    F[:, 0] = F[:, 0].real
+    x = oracle.c2r(F, n, m)
+    assert rel(x, oracle.dft_synth_direct(F, n, m)) < 1e-12
+    assert rel(oracle.r2c(x, m), n * F) < 1e-12
+    H = g.normal(size=(2, n // 2 + 1)) + 1j * g.normal(size=(2, n // 2 + 1))
+    H[:, 0] = H[:, 0].real
+    if n % 2 == 0:
+        H[:, -1] = H[:, -1].real
+    assert rel(oracle.c2r(H, n), n * np.fft.irfft(H, n, axis=-1)) < 1e-12
