@@ -154,6 +154,29 @@ struct BluesteinArgs {
 };
 hipError_t launch_bluestein(int m, const BluesteinArgs& a, hipStream_t stream);
 
+// Real transforms of lengths that are not powers of two: the complex
+// transform runs on an any-length C2C plan (mixed radix or chirp); these
+// element-wise kernels do the packing around it ("fourier.ts" header and
+// fftAnalysRealWGSL / fftSynthRealWGSL for even n = 2h; the definition of the
+// real transform for odd n).  Spectrum: bins 0..mmax, [rows][mmax+1] or
+// [mmax+1][rows] when mmajor.  rt: e^{-2 pi i k/n}, k = 0..n/2.
+struct RealAnyArgs {
+  const void* in;
+  void* out;
+  const float2* rt;
+  int64_t rows;
+  int n, len, mmax, mmajor;  // len: complex row length of the scratch (n/2 or n)
+};
+// even n: Z = FFT_h(x viewed as h complex) -> bins (Xe + W^k Xo)
+hipError_t launch_real_unpack(const RealAnyArgs& a, hipStream_t stream);
+// even n: bins -> Z (Hermitian assembly), then inverse FFT_h gives x as h complex
+hipError_t launch_real_pack(const RealAnyArgs& a, hipStream_t stream);
+// odd n: x -> (x, 0); FFT_n -> bins 0..mmax; bins -> full Hermitian row; Re of a row
+hipError_t launch_real_complexify(const RealAnyArgs& a, hipStream_t stream);
+hipError_t launch_real_extract(const RealAnyArgs& a, hipStream_t stream);
+hipError_t launch_real_hermitian(const RealAnyArgs& a, hipStream_t stream);
+hipError_t launch_real_part(const RealAnyArgs& a, hipStream_t stream);
+
 // Band-limited direct transforms (any n, 2 <= n <= kMaxDirectLength):
 // analysis reads real rows [rows][n] (float) and writes bins 0..mmax;
 // synthesis reads bins 0..mmax and writes real rows.  The spectrum is complex

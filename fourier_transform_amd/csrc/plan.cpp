@@ -150,6 +150,10 @@ struct fft_plan {
   MixedArgs mx{};
   const float2* mx_shift = nullptr;
   const float2* mx_ishift = nullptr;
+  // R2C/C2R of lengths that are not powers of two: an any-length C2C plan of
+  // length n/2 (even n) or n (odd n) plus the packing kernels
+  bool real_any = false;
+  fft_plan* inner = nullptr;
   float2* scratch = nullptr;
 };
 
@@ -179,6 +183,7 @@ int check_total(int64_t a, int64_t b, int64_t c) {
 
 void free_plan(fft_plan* p) {
   if (!p) return;
+  if (p->inner) free_plan(p->inner);
   if (p->tables) (void)hipFree(p->tables);
   if (p->scratch) (void)hipFree(p->scratch);
   delete p;
@@ -375,6 +380,46 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   return p;
 }
 
+// any-length C2C plan (mixed radix when possible, else the chirp transform)
+fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
+  const std::vector<int> rad = mixed_radices(n);
+  const int rmin = rad.empty() ? 0 : *std::min_element(rad.begin(), rad.end());
+  if (!rad.empty() && n <= kMaxMixedLength && (int)rad.size() <= kMixedMaxStages &&
+      n / rmin <= 1024 * kMixedButterflies)
+    return create_mixed(n, batch, sign, rad);
+  return create_bluestein(n, batch, sign);
+}
+
+// R2C/C2R of a length that is not a power of two (3 <= n <= kMaxBluesteinLengthLarge)
+fft_plan* create_real_any(int64_t n, int64_t batch, int kind, int sign) {
+  const bool even = n % 2 == 0;
+  const int64_t len = even ? n / 2 : n;
+  fft_plan* inner = create_c2c_any(len, batch, sign);
+  if (!inner) return nullptr;
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) {
+    free_plan(inner);
+    return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  }
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = kind;
+  p->sign = sign;
+  p->mmax = n / 2;
+  p->real_any = true;
+  p->inner = inner;
+  std::vector<float2> trt;
+  for (int64_t k = 0; k <= n / 2; ++k) trt.push_back(root(k, n));
+  const size_t scratch = (size_t)(batch * len) * sizeof(float2) * (even ? 1 : 2);
+  if (finish_plan(p, {&trt}, {&p->rt}, scratch) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,14 +436,14 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     // mixed radix when every prime factor is at most 7 and every stage has
     // at most 1024 * kMixedButterflies butterflies (radix >= 2, 3, 4 for
     // n up to 4096, 6144, 8192), else the chirp transform
-    const std::vector<int> rad = mixed_radices(n);
-    const int rmin = rad.empty() ? 0 : *std::min_element(rad.begin(), rad.end());
-    if (!rad.empty() && n <= kMaxMixedLength && (int)rad.size() <= kMixedMaxStages &&
-        n / rmin <= 1024 * kMixedButterflies)
-      return create_mixed(n, batch, sign, rad);
-    return create_bluestein(n, batch, sign);
+    return create_c2c_any(n, batch, sign);
   }
-  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "R2C/C2R lengths must be powers of two"), nullptr;
+  if (kind != FFT_C2C && n > 2 && !is_pow2(n)) {
+    if (n > kMaxBluesteinLengthLarge)
+      return set_err(FFT_ENOTSUP, "R2C/C2R lengths that are not powers of two must be <= 2^22"), nullptr;
+    return create_real_any(n, batch, kind, sign);
+  }
+  if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n out of range"), nullptr;
   const int64_t max_len = kind == FFT_C2C ? (int64_t(1) << kFourStepMaxLog) : 2 * (int64_t)kMaxSinglePass;
   const int64_t min_len = kind == FFT_C2C ? 2 : 4;
   if (n < min_len || n > max_len)
@@ -567,6 +612,33 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   p->executed = true;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
+  if (p->real_any) {
+    const bool even = p->n % 2 == 0;
+    const int64_t len = even ? p->n / 2 : p->n;
+    float2* s1 = p->scratch;
+    float2* s2 = p->scratch + p->batch * len;
+    RealAnyArgs ra{nullptr, nullptr, p->rt, p->batch, (int)p->n, (int)len, (int)p->mmax, p->spec_layout};
+    int rc = FFT_OK;
+    if (p->kind == FFT_R2C && even) {
+      rc = fft_exec(p->inner, in, s1, stream_);  // x read as len complex values per row
+      if (rc == FFT_OK) ra.in = s1, ra.out = out, e = launch_real_unpack(ra, stream);
+    } else if (p->kind == FFT_R2C) {
+      ra.in = in, ra.out = s1, e = launch_real_complexify(ra, stream);
+      if (e == hipSuccess) rc = fft_exec(p->inner, s1, s2, stream_);
+      if (e == hipSuccess && rc == FFT_OK) ra.in = s2, ra.out = out, e = launch_real_extract(ra, stream);
+    } else if (even) {
+      ra.in = in, ra.out = s1, e = launch_real_pack(ra, stream);
+      if (e == hipSuccess) rc = fft_exec(p->inner, s1, out, stream_);  // x written as len complex values
+    } else {
+      ra.in = in, ra.out = s1, e = launch_real_hermitian(ra, stream);
+      if (e == hipSuccess) rc = fft_exec(p->inner, s1, s2, stream_);
+      if (e == hipSuccess && rc == FFT_OK) ra.in = s2, ra.out = out, e = launch_real_part(ra, stream);
+    }
+    if (cur != p->device) (void)hipSetDevice(cur);
+    if (rc != FFT_OK) return rc;
+    if (e != hipSuccess) return hip_err(e, "kernel launch");
+    return ok();
+  }
   if (p->mixed) {
     MixedArgs a = p->mx;
     a.in = src;

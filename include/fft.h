@@ -21,10 +21,15 @@
  *    has at most 2048 butterflies (n <= 8192), the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
  *    inside one kernel while m <= 16384, else as two four-step transforms
- *    (four passes) through a scratch buffer of 2 * batch * m * 8 bytes.  R2C/C2R and 2D
- *    sizes are powers of two; other lengths are rejected with FFT_ENOTSUP
- *    (fourier.ts refuses them for its FFT at plan time).  The direct kinds
- *    below take any length from 2 to 16384.
+ *    (four passes) through a scratch buffer of 2 * batch * m * 8 bytes.
+ *  - R2C/C2R lengths: powers of two from 4 to 32768 (one kernel), and any
+ *    other length from 3 to 2^22 (fourier.ts refuses these for its FFT; here
+ *    an any-length complex transform of n/2 values for even n, with the same
+ *    Hermitian pack/unpack as the power-of-two path in separate kernels, or
+ *    of n values for odd n, through a plan-owned scratch buffer of
+ *    batch * n * 4 bytes (even n) or 2 * batch * n * 8 bytes (odd n)).
+ *  - 2D sizes are powers of two; other sizes are rejected with FFT_ENOTSUP.
+ *    The direct kinds below take any length from 2 to 16384.
  *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
  *    aligned.  The plan owns its twiddle tables and scratch (allocated at
  *    create, freed at destroy).
@@ -49,7 +54,8 @@
  *           Only sign = FFT_INVERSE.  in == out is rejected.
  *           Real transforms follow fourier.ts fftAnalysRealWGSL /
  *           fftSynthRealWGSL: one complex transform of length n/2 plus a
- *           Hermitian pack/unpack, so n >= 4 is required.
+ *           Hermitian pack/unpack (power-of-two n >= 4, and any even n); odd
+ *           lengths transform (x, 0) / the full Hermitian row of length n.
  *  FFT_R2C_DIRECT, FFT_C2R_DIRECT
  *           The band-limited direct sums of fourier.ts (dftAnalysWGSL,
  *           dftSynthWGSL), for ANY length 2 <= n <= 16384:
@@ -121,7 +127,8 @@ enum fft_option {
 /*
  * Create a plan for `batch` transforms of length n.
  * n: C2C: a power of two 2 <= n <= 2^28, or any 3 <= n <= 2^22; R2C/C2R: a
- * power of two 4 <= n <= 32768; the direct kinds: any 2 <= n <= 16384.
+ * power of two 4 <= n <= 32768, or any 3 <= n <= 2^22; the direct kinds: any
+ * 2 <= n <= 16384.
  * batch >= 1.
  * kind: enum fft_kind.  sign: FFT_FORWARD or FFT_INVERSE (FFT_FORWARD for the
  * analysis kinds R2C and R2C_DIRECT, FFT_INVERSE for C2R and C2R_DIRECT).

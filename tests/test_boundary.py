@@ -57,7 +57,7 @@ def err_of(fn, *args):
     ((1 << 29, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # beyond the four-step range
     ((1 << 16, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),   # real transforms are single-pass
     ((1 << 40, 1 << 40, F.FFT_C2C, -1), F.FFT_EINVAL),  # size overflow
-    ((1000, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),      # the FFT kinds need powers of two
+    (((1 << 22) + 2, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),  # R2C beyond 2^22 that is not a power of two
     ((1, 1, F.FFT_R2C_DIRECT, -1), F.FFT_ENOTSUP),  # direct kinds: 2 <= n <= 16384
     ((16385, 1, F.FFT_C2R_DIRECT, 1), F.FFT_ENOTSUP),
     ((30, 1, F.FFT_R2C_DIRECT, 1), F.FFT_EINVAL),   # analysis is forward

@@ -12,7 +12,7 @@ import oracle
 from fourier_transform_amd import fft as F
 from fourier_transform_amd import workloads as W
 
-from gpu_helpers import c2c, dev, empty, host, rel_l2, say
+from gpu_helpers import c2c, c2r, dev, empty, host, r2c, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -164,3 +164,40 @@ def test_any_length_large_shift_and_in_place(n, shift):
     idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
     want = oracle.dft(x, -1)[:, idx]
     assert rel_l2(c2c(x, -1, shift=shift, inplace=True), want) <= TOL
+
+
+# --------------------------------------------------------------------------
+# R2C / C2R at lengths that are not powers of two: an any-length complex
+# transform of n/2 (even n) or n (odd n) with the packing kernels around it
+# --------------------------------------------------------------------------
+REAL_N = [3, 5, 6, 7, 10, 12, 15, 100, 101, 360, 999, 1000, 1440, 2001, 4002, 10000, 20002]
+
+
+@pytest.mark.parametrize("n", REAL_N)
+def test_real_any_length_sweep(n):
+    g = np.random.default_rng(n + 33)
+    for batch, mmax, mmajor in ((1, None, False), (5, n // 3, True), (19, n // 2, False), (6, 0, True)):
+        if n > 4096 and batch > 5:
+            batch = 3
+        m = n // 2 if mmax is None else mmax
+        say(f"any-length r2c/c2r n={n} batch={batch} mmax={m} mmajor={mmajor}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = r2c(x, m, mmajor)
+        assert rel_l2(Fg.T if mmajor else Fg, oracle.r2c(x, m)) <= TOL, (n, batch, m)
+        S = (g.normal(size=(batch, m + 1)) + 1j * g.normal(size=(batch, m + 1))).astype(np.complex64)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        xg = c2r(Sin, n, batch, m, mmajor)
+        assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
+
+
+def test_real_any_length_options():
+    """Two-for-one packing needs a power-of-two length; sizes follow n."""
+    plan = F.fft_plan_create(1000, 4, F.FFT_R2C, F.FFT_FORWARD)
+    try:
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_REAL_PAIRS, 1)
+        assert e.value.code == F.FFT_ENOTSUP
+        F.fft_plan_set(plan, F.FFT_OPT_MMAX, 100)
+        assert F.fft_plan_get_sizes(plan) == (4 * 1000 * 4, 4 * 101 * 8)
+    finally:
+        F.fft_plan_destroy(plan)
