@@ -126,7 +126,8 @@ def c2c(x, sign: int = -1, nthreads: int = 0):
 
 
 def c2c_2d(x, sign: int = -1, nthreads: int = 0):
-    """2D transform over the last two axes: rows, then columns (Equation 19)."""
+    """2D transform over the last two axes: rows, then columns (Equation 19);
+    any sizes (the definition per axis when it is not a power of two)."""
     x = _c128(x)
     ny, nx = x.shape[-2], x.shape[-1]
     y = np.empty_like(x)
@@ -202,7 +203,7 @@ def ifftshift_index(n: int):
 
 
 def fftshift_2d(y):
-    """Rotate both of the last two axes by half their length (even sizes)."""
+    """Shift both of the last two axes: bin 0 to index floor(n/2) (numpy's fftshift)."""
     y = _c128(y)
     ny, nx = y.shape[-2], y.shape[-1]
     out = np.empty_like(y)

@@ -365,17 +365,60 @@ static void cols_body(void* p, int64_t lo, int64_t hi) {
   free(res);
 }
 
+/* columns of a length that is not a power of two: the definition, with the
+ * factors e^{sign 2 pi i e/ny} tabulated once (w[e], e = 0..ny-1) */
+static void cols_dft_body(void* p, int64_t lo, int64_t hi) {
+  cols_ctx* c = (cols_ctx*)p;
+  const int64_t ny = c->ny;
+  double* col = (double*)malloc(sizeof(double) * 2 * ny);
+  for (int64_t q = lo; q < hi; ++q) {
+    int64_t b = q / c->nx, j = q % c->nx;
+    double* base = c->y + 2 * (b * ny * c->nx + j);
+    for (int64_t i = 0; i < ny; ++i) {
+      col[2 * i] = base[2 * i * c->nx];
+      col[2 * i + 1] = base[2 * i * c->nx + 1];
+    }
+    for (int64_t k = 0; k < ny; ++k) {
+      double sr = 0.0, si = 0.0;
+      int64_t e = 0;
+      for (int64_t i = 0; i < ny; ++i) {
+        const double wr = c->w[2 * e], wi = c->w[2 * e + 1];
+        sr += col[2 * i] * wr - col[2 * i + 1] * wi;
+        si += col[2 * i] * wi + col[2 * i + 1] * wr;
+        e += k;
+        if (e >= ny) e -= ny;
+      }
+      base[2 * k * c->nx] = sr;
+      base[2 * k * c->nx + 1] = si;
+    }
+  }
+  free(col);
+}
+
 int oracle_fft_2d(const double* x, double* y, int64_t ny, int64_t nx,
                   int64_t batch, int sign, int threads) {
-  if (!is_pow2(ny) || !is_pow2(nx) || batch < 0 || (sign != 1 && sign != -1) ||
-      x == y)
-    return -1;
-  int rc = oracle_fft(x, y, nx, batch * ny, sign, threads);
+  if (ny < 1 || nx < 1 || batch < 0 || (sign != 1 && sign != -1) || x == y) return -1;
+  if (batch == 0) return 0;
+  /* rows: the radix-2 transform for powers of two, the definition otherwise */
+  int rc = is_pow2(nx) ? oracle_fft(x, y, nx, batch * ny, sign, threads)
+                       : oracle_dft(x, y, nx, batch * ny, sign, threads);
   if (rc) return rc;
-  double* w = make_twiddles(ny, sign);
-  cols_ctx c = {y, ny, nx, w};
-  parallel_for(threads, batch * nx, cols_body, &c);
-  free(w);
+  if (is_pow2(ny)) {
+    double* w = make_twiddles(ny, sign);
+    cols_ctx c = {y, ny, nx, w};
+    parallel_for(threads, batch * nx, cols_body, &c);
+    free(w);
+  } else {
+    double* w = (double*)malloc(sizeof(double) * 2 * (size_t)ny);
+    for (int64_t e = 0; e < ny; ++e) {
+      const double a = TWO_PI * (double)e / (double)ny;
+      w[2 * e] = cos(a);
+      w[2 * e + 1] = sign * sin(a);
+    }
+    cols_ctx c = {y, ny, nx, w};
+    parallel_for(threads, batch * nx, cols_dft_body, &c);
+    free(w);
+  }
   return 0;
 }
 
@@ -497,15 +540,16 @@ int oracle_ifftshift_index(int64_t n, int64_t* idx) {
   return 0;
 }
 
-/* out[b][i][j] = y[b][(i + ny/2) mod ny][(j + nx/2) mod nx]  (complex). */
+/* out[b][i][j] = y[b][(i - floor(ny/2)) mod ny][(j - floor(nx/2)) mod nx]
+ * (complex): the shift of each axis. */
 int oracle_fftshift_2d(const double* y, double* out, int64_t ny, int64_t nx,
                        int64_t batch) {
-  if (ny < 2 || nx < 2 || (ny & 1) || (nx & 1) || y == out) return -1;
+  if (ny < 1 || nx < 1 || y == out) return -1;
   for (int64_t b = 0; b < batch; ++b)
     for (int64_t i = 0; i < ny; ++i) {
-      int64_t si = (i + ny / 2) % ny;
+      int64_t si = ((i - ny / 2) % ny + ny) % ny;
       for (int64_t j = 0; j < nx; ++j) {
-        int64_t sj = (j + nx / 2) % nx;
+        int64_t sj = ((j - nx / 2) % nx + nx) % nx;
         const double* src = y + 2 * ((b * ny + si) * nx + sj);
         double* dst = out + 2 * ((b * ny + i) * nx + j);
         dst[0] = src[0];

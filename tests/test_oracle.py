@@ -417,3 +417,23 @@ def test_c2r_any_length(n):
     if n % 2 == 0:
         H[:, -1] = H[:, -1].real
     assert rel(oracle.c2r(H, n), n * np.fft.irfft(H, n, axis=-1)) < 1e-12
+
+
+
+@pytest.mark.parametrize("ny,nx", [(3, 5), (6, 8), (8, 6), (15, 12), (100, 64), (7, 1)])
+def test_2d_any_size(ny, nx):
+    """2D at sizes that are not powers of two: numpy's fft2 (third party), the
+    written-out double sum on a few bins, and separability."""
+    x = crand((2, ny, nx), ny * 100 + nx)
+    y = oracle.c2c_2d(x, -1)
+    assert rel(y, np.fft.fft2(x, axes=(-2, -1))) < 1e-12
+    k1, k2 = np.array([0, ny - 1, ny // 2]), np.array([0, nx // 3, nx - 1])
+    assert rel(y[0][k1, k2], oracle.dft2_bins(x[0], k1, k2, -1)) < 1e-12
+    u, v = crand(ny, 1), crand(nx, 2)
+    assert rel(oracle.c2c_2d(np.outer(u, v), +1), np.outer(oracle.dft(u, +1), oracle.dft(v, +1))) < 1e-12
+
+
+@pytest.mark.parametrize("ny,nx", [(3, 5), (7, 7), (6, 9)])
+def test_fftshift_2d_odd_matches_numpy(ny, nx):
+    y = crand((2, ny, nx), 4)
+    assert np.array_equal(oracle.fftshift_2d(y), np.fft.fftshift(y, axes=(-2, -1)))
