@@ -177,6 +177,12 @@ hipError_t launch_real_extract(const RealAnyArgs& a, hipStream_t stream);
 hipError_t launch_real_hermitian(const RealAnyArgs& a, hipStream_t stream);
 hipError_t launch_real_part(const RealAnyArgs& a, hipStream_t stream);
 
+// Transpose of `images` complex64 matrices [rows][cols] -> [cols][rows]
+// (out must not overlap in), through 32 x 32 LDS tiles so both sides are
+// coalesced.  Used by 2D plans with an axis that is not a power of two.
+hipError_t launch_transpose(const float2* in, float2* out, int64_t rows, int64_t cols, int64_t images,
+                            hipStream_t stream);
+
 // Band-limited direct transforms (any n, 2 <= n <= kMaxDirectLength):
 // analysis reads real rows [rows][n] (float) and writes bins 0..mmax;
 // synthesis reads bins 0..mmax and writes real rows.  The spectrum is complex

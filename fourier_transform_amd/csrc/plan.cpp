@@ -154,6 +154,10 @@ struct fft_plan {
   // length n/2 (even n) or n (odd n) plus the packing kernels
   bool real_any = false;
   fft_plan* inner = nullptr;
+  // 2D plans with an axis that is not a power of two: row plans of nx (inner)
+  // and of ny (inner2, run on the transposed image)
+  bool any2d = false;
+  fft_plan* inner2 = nullptr;
   float2* scratch = nullptr;
 };
 
@@ -184,6 +188,7 @@ int check_total(int64_t a, int64_t b, int64_t c) {
 void free_plan(fft_plan* p) {
   if (!p) return;
   if (p->inner) free_plan(p->inner);
+  if (p->inner2) free_plan(p->inner2);
   if (p->tables) (void)hipFree(p->tables);
   if (p->scratch) (void)hipFree(p->scratch);
   delete p;
@@ -505,8 +510,45 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   if (batch < 1) return set_err(FFT_EINVAL, "batch must be >= 1"), nullptr;
   if (check_kind_sign(kind, sign) != FFT_OK) return nullptr;
   if (kind != FFT_C2C) return set_err(FFT_ENOTSUP, "2D plans support FFT_C2C only"), nullptr;
-  if (!is_pow2(ny) || !is_pow2(nx))
-    return set_err(FFT_ENOTSUP, "ny and nx must be powers of two"), nullptr;
+  if (!is_pow2(ny) || !is_pow2(nx)) {
+    // rows, transpose, rows of the transposed image, transpose back
+    if (ny < 2 || nx < 2 || ny > kMaxBluesteinLengthLarge || nx > kMaxBluesteinLengthLarge)
+      return set_err(FFT_ENOTSUP, "2D sizes that are not powers of two must lie in [2, 2^22]"), nullptr;
+    if (check_total(ny, nx, batch) != FFT_OK) return nullptr;
+    if (batch > 65535)
+      return set_err(FFT_ENOTSUP, "2D plans with a size that is not a power of two take at most 65535 images"),
+             nullptr;
+    fft_plan* rows = fft_plan_create(nx, batch * ny, FFT_C2C, sign);
+    if (!rows) return nullptr;
+    fft_plan* cols = fft_plan_create(ny, batch * nx, FFT_C2C, sign);
+    if (!cols) {
+      free_plan(rows);
+      return nullptr;
+    }
+    fft_plan* p = new (std::nothrow) fft_plan();
+    if (!p) {
+      free_plan(rows);
+      free_plan(cols);
+      return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+    }
+    p->dims = 2;
+    p->ny = ny;
+    p->nx = nx;
+    p->n = ny * nx;
+    p->batch = batch;
+    p->kind = kind;
+    p->sign = sign;
+    p->any2d = true;
+    p->inner = rows;
+    p->inner2 = cols;
+    std::vector<float2> none(1, make_float2(0.f, 0.f));
+    if (finish_plan(p, {&none}, {&p->tw_a}, (size_t)(ny * nx * batch) * sizeof(float2)) != FFT_OK) {
+      free_plan(p);
+      return nullptr;
+    }
+    ok();
+    return p;
+  }
   if (ny < 2 || nx < 2 || ny > kMaxSinglePass || nx > kMaxSinglePass)
     return set_err(FFT_ENOTSUP, "2D sizes must lie in [2, 16384]"), nullptr;
   if (check_total(ny, nx, batch) != FFT_OK) return nullptr;
@@ -552,8 +594,12 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_SHIFT:
       if (value < 0 || value > 2) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0, 1 or 2");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
-      if (value && !p->bluestein && !p->mixed && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
+      if (value && !p->bluestein && !p->mixed && !p->any2d && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
+      if (p->any2d) {  // the shift of each axis, in its row plan
+        if (fft_plan_set(p->inner, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
+        if (fft_plan_set(p->inner2, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
+      }
       p->shift = (int)value;
       return ok();
     case FFT_OPT_MMAX:
@@ -612,6 +658,16 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   p->executed = true;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
+  if (p->any2d) {
+    int rc = fft_exec(p->inner, in, out, stream_);
+    if (rc == FFT_OK) e = launch_transpose(dst, p->scratch, p->ny, p->nx, p->batch, stream);
+    if (rc == FFT_OK && e == hipSuccess) rc = fft_exec(p->inner2, p->scratch, p->scratch, stream_);
+    if (rc == FFT_OK && e == hipSuccess) e = launch_transpose(p->scratch, dst, p->nx, p->ny, p->batch, stream);
+    if (cur != p->device) (void)hipSetDevice(cur);
+    if (rc != FFT_OK) return rc;
+    if (e != hipSuccess) return hip_err(e, "kernel launch");
+    return ok();
+  }
   if (p->real_any) {
     const bool even = p->n % 2 == 0;
     const int64_t len = even ? p->n / 2 : p->n;

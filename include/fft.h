@@ -28,7 +28,10 @@
  *    Hermitian pack/unpack as the power-of-two path in separate kernels, or
  *    of n values for odd n, through a plan-owned scratch buffer of
  *    batch * n * 4 bytes (even n) or 2 * batch * n * 8 bytes (odd n)).
- *  - 2D sizes are powers of two; other sizes are rejected with FFT_ENOTSUP.
+ *  - 2D sizes: powers of two from 2 to 16384 (row pass, then column pass),
+ *    or any sizes from 2 to 2^22 (row transforms, a tiled transpose, row
+ *    transforms of the transposed image, a transpose back; at most 65535
+ *    images; plan-owned scratch of batch * ny * nx * 8 bytes).
  *    The direct kinds below take any length from 2 to 16384.
  *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
  *    aligned.  The plan owns its twiddle tables and scratch (allocated at
@@ -149,7 +152,9 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);
 
 /*
  * 2D C2C plan over [batch][ny][nx] complex64: every row, then every column
- * (Mota, section 2.7, Equation 19).  ny, nx: powers of two in [2, 16384].
+ * (Mota, section 2.7, Equation 19).  ny, nx: powers of two in [2, 16384], or
+ * any sizes in [2, 2^22] (then at most 65535 images; the shift options act
+ * on each axis).
  * Only kind = FFT_C2C.  Images with ny >= 8192 rows run the column transform
  * as two steps of 64 x ny/64 points (three passes in all, each with long
  * contiguous runs), own a scratch buffer of batch*ny*nx*8 bytes and take at

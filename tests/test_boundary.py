@@ -74,7 +74,8 @@ def test_create_rejects(lib, args, code):
     ((0, 8, 1, F.FFT_C2C, -1), F.FFT_EINVAL),
     ((8, 8, 0, F.FFT_C2C, -1), F.FFT_EINVAL),
     ((8, 8, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),
-    ((6, 8, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
+    ((6, 8, 70000, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # any sizes: at most 65535 images
+    ((6, (1 << 22) + 1, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((8, 32768, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((1, 8, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),
     ((8, 8, 1, F.FFT_C2C, 3), F.FFT_EINVAL),

@@ -12,7 +12,7 @@ import oracle
 from fourier_transform_amd import fft as F
 from fourier_transform_amd import workloads as W
 
-from gpu_helpers import c2c, c2r, dev, empty, host, r2c, rel_l2, say
+from gpu_helpers import c2c, c2c_2d, c2r, dev, empty, host, r2c, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -201,3 +201,30 @@ def test_real_any_length_options():
         assert F.fft_plan_get_sizes(plan) == (4 * 1000 * 4, 4 * 101 * 8)
     finally:
         F.fft_plan_destroy(plan)
+
+
+# --------------------------------------------------------------------------
+# 2D plans with an axis that is not a power of two (rows, transpose, rows,
+# transpose back); the shift is the shift of each axis
+# --------------------------------------------------------------------------
+SIZES_2D = [(3, 5, 2), (6, 10, 3), (100, 64, 2), (64, 100, 2), (360, 180, 1), (1000, 999, 1), (17, 1024, 2),
+            (10001, 6, 1)]
+
+
+@pytest.mark.parametrize("ny,nx,batch", SIZES_2D)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_2d_any_size(ny, nx, batch, sign):
+    say(f"2D any size {ny}x{nx} batch={batch} sign={sign}")
+    x = W.uniform_c64((batch, ny, nx), np.random.default_rng(ny * 7 + nx))
+    assert rel_l2(c2c_2d(x, sign), oracle.c2c_2d(x, sign)) <= TOL
+
+
+@pytest.mark.parametrize("ny,nx", [(3, 5), (7, 8), (100, 99)])
+@pytest.mark.parametrize("shift", [1, 2])
+def test_2d_any_size_shift_and_in_place(ny, nx, shift):
+    say(f"2D any size {ny}x{nx} shift={shift}, in place")
+    x = W.uniform_c64((2, ny, nx), np.random.default_rng(ny + nx + shift))
+    iy = oracle.fftshift_index(ny) if shift == 1 else oracle.ifftshift_index(ny)
+    ix = oracle.fftshift_index(nx) if shift == 1 else oracle.ifftshift_index(nx)
+    want = oracle.c2c_2d(x, -1)[:, iy][:, :, ix]
+    assert rel_l2(c2c_2d(x, -1, shift=shift, inplace=True), want) <= TOL
