@@ -228,3 +228,28 @@ def test_2d_any_size_shift_and_in_place(ny, nx, shift):
     ix = oracle.fftshift_index(nx) if shift == 1 else oracle.ifftshift_index(nx)
     want = oracle.c2c_2d(x, -1)[:, iy][:, :, ix]
     assert rel_l2(c2c_2d(x, -1, shift=shift, inplace=True), want) <= TOL
+
+
+# --------------------------------------------------------------------------
+# buffers beyond 2^31 elements (64-bit row offsets): the seeded block tiled
+# on the device, sampled rows at the start, the middle and the ragged end
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,batch", [(4096, (1 << 19) + 3), (1000, (1 << 21) + 5), (1001, (1 << 21) + 7)])
+def test_beyond_2p31_elements(n, batch):
+    import torch
+    say(f"c2c n={n} batch={batch} ({batch * n * 8 / 2**30:.1f} GiB per buffer)")
+    block = W.uniform_c64((64, n), np.random.default_rng(n + 77))
+    xd = dev(block).repeat((batch + 63) // 64, 1)[:batch].contiguous()
+    plan = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    try:
+        yd = torch.empty_like(xd)
+        F.fft_exec(plan, xd, yd)
+        torch.cuda.synchronize()
+        rows = np.array([0, 1, 63, batch // 2, batch - 65, batch - 2, batch - 1])
+        y = yd[torch.from_numpy(rows).cuda()].cpu().numpy()
+    finally:
+        F.fft_plan_destroy(plan)
+        del xd
+        torch.cuda.empty_cache()
+    want = oracle.dft(block[rows % 64], -1) if n & (n - 1) else oracle.c2c(block[rows % 64], -1)
+    assert rel_l2(y, want) <= TOL
