@@ -104,6 +104,23 @@ struct ColStageArgs {
 };
 hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
 
+// C2C rows of length n = p * q, p in {3, 5, 7, 9, 15, 25}, q a power of two
+// >= kMinPqPow2, n <= kMaxPqLength: p power-of-two transforms of length q in
+// registers (interleaved sub-rows), the twiddle W_n^{p k} (wn: e^{-2 pi i e/n},
+// e < n), and p-point DFTs through LDS.  shift: multiply element j by (-1)^j
+// (n is even).  In place allowed.
+constexpr int kMaxPqLength = 16384;
+constexpr int kMinPqPow2 = 16;
+struct PqArgs {
+  const float2* in;
+  float2* out;
+  const float2* tw;  // stage table of q (row-kernel schedule)
+  const float2* wn;
+  int64_t rows;
+  int shift;
+};
+hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream);
+
 // C2C rows whose length n <= kMaxMixedLength has no prime factor above 7:
 // mixed-radix Stockham stages of radix 2, 3, 4, 5, 7 or 8 (schedule chosen at
 // plan time), the line resident in LDS between stages.  Stage s has radix

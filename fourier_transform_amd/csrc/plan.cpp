@@ -146,6 +146,10 @@ struct fft_plan {
   const float2* bhat = nullptr;
   // C2C lengths with no prime factor above 7 (mixed radix): the schedule, and
   // the load factors of the two shifts
+  // C2C lengths p * q (p in {3, 5, 7, 9, 15, 25}, q a power of two >= 16)
+  bool pq = false;
+  int pq_p = 0, pq_q = 0;
+  const float2* wn = nullptr;
   bool mixed = false;
   MixedArgs mx{};
   const float2* mx_shift = nullptr;
@@ -385,8 +389,41 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   return p;
 }
 
-// any-length C2C plan (mixed radix when possible, else the chirp transform)
+// n = p * q with p in {3, 5, 7, 9, 15, 25} and q a power of two >= kMinPqPow2,
+// n <= kMaxPqLength: the odd factor p (largest of the list first), else 0
+int pq_factor(int64_t n) {
+  if (n > kMaxPqLength) return 0;
+  for (int p : {25, 15, 9, 7, 5, 3})
+    if (n % p == 0 && is_pow2(n / p) && n / p >= kMinPqPow2) return p;
+  return 0;
+}
+
+fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = FFT_C2C;
+  p->sign = sign;
+  p->pq = true;
+  p->pq_p = pf;
+  p->pq_q = (int)(n / pf);
+  std::vector<float2> ta, wn;
+  append_stage_table(p->pq_q, rows_values(p->pq_q), ta);
+  for (int64_t e = 0; e < n; ++e) wn.push_back(root(e, n));
+  if (finish_plan(p, {&ta, &wn}, {&p->tw_a, &p->wn}, 0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
+// any-length C2C plan: p * 2^k in registers when possible, then mixed radix,
+// else the chirp transform
 fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
+  if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
   const std::vector<int> rad = mixed_radices(n);
   const int rmin = rad.empty() ? 0 : *std::min_element(rad.begin(), rad.end());
   if (!rad.empty() && n <= kMaxMixedLength && (int)rad.size() <= kMixedMaxStages &&
@@ -695,7 +732,10 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     if (e != hipSuccess) return hip_err(e, "kernel launch");
     return ok();
   }
-  if (p->mixed) {
+  if (p->pq) {
+    PqArgs a{src, dst, p->tw_a, p->wn, p->batch, p->shift ? 1 : 0};
+    e = launch_pq(p->pq_q, p->pq_p, p->sign, a, stream);
+  } else if (p->mixed) {
     MixedArgs a = p->mx;
     a.in = src;
     a.out = dst;

@@ -16,9 +16,11 @@
  *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
  *    2^28), and any other length from 3 to 2^22 (the GLSL dissertation,
  *    section 2.3, names mixed radices and other lengths as the extension of
- *    its radix-2 transforms): lengths with no prime factor above 7 by
+ *    its radix-2 transforms): n = p * 2^k (p in 3, 5, 7, 9, 15, 25, 2^k >= 16,
+ *    n <= 16384) in one register-resident kernel (p power-of-two transforms,
+ *    twiddles, p-point DFTs); other lengths with no prime factor above 7 by
  *    mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) when every stage
- *    has at most 2048 butterflies (n <= 8192), the others by Bluestein's
+ *    has at most 2048 butterflies (n <= 8192); the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
  *    inside one kernel while m <= 16384, else as two four-step transforms
  *    (four passes) through a scratch buffer of 2 * batch * m * 8 bytes.

@@ -1,7 +1,8 @@
 """GPU parity for C2C lengths that are not powers of two, against the
-oracle's DFT by the definition: mixed-radix Stockham stages (radices 2, 3, 4,
-5, 7, 8) for lengths with no prime factor above 7, Bluestein's chirp
-transform inside one kernel for the others.
+oracle's DFT by the definition: p x 2^k (p in 3, 5, 7, 9, 15, 25) in
+registers, mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) for the
+other lengths with no prime factor above 7, Bluestein's chirp transform for
+the rest.
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -253,3 +254,32 @@ def test_beyond_2p31_elements(n, batch):
         torch.cuda.empty_cache()
     want = oracle.dft(block[rows % 64], -1) if n & (n - 1) else oracle.c2c(block[rows % 64], -1)
     assert rel_l2(y, want) <= TOL
+
+
+# --------------------------------------------------------------------------
+# p x 2^k in one register-resident kernel (p in 3, 5, 7, 9, 15, 25)
+# --------------------------------------------------------------------------
+PQ_N = [48, 80, 240, 400, 576, 960, 1792, 2304, 2560, 3840, 4608, 6400, 9216, 10240, 12288, 12800,
+        14336, 15360]
+
+
+@pytest.mark.parametrize("n", PQ_N)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_pq_sweep(n, sign):
+    for batch in (1, 7):
+        say(f"p x 2^k c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 3 + batch))
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n", [48, 1536, 15360])
+def test_pq_shift_bit_exact_and_in_place(n):
+    """The shift is the exact sign flip of (-1)^j (n even): bitwise the
+    transform of the negated input; and the rotation of the oracle's."""
+    from gpu_helpers import negate_odd
+    x = W.uniform_c64((3, n), np.random.default_rng(n + 9))
+    ys = c2c(x, -1, shift=1)
+    xn = negate_odd(x, np.broadcast_to(np.arange(n), x.shape))
+    assert np.array_equal(ys.view(np.uint32), c2c(xn, -1).view(np.uint32))
+    assert rel_l2(ys, oracle.dft(x, -1)[:, oracle.fftshift_index(n)]) <= TOL
+    assert rel_l2(c2c(x, +1, inplace=True), oracle.dft(x, +1)) <= TOL
