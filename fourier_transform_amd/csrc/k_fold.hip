@@ -1,0 +1,203 @@
+// Tall 2D images in two passes over HBM.
+//
+// The column transform of length ny = NA * NB is split as in the four-step
+// method ("High Performance Fourier Transforms on GPUs with GLSL", section
+// 2.4): with row index y = yb + NB*ya and bin k = ka + NA*kb,
+//   X[ka + NA*kb] = sum_yb W_NB^{yb*kb} W_ny^{yb*ka} sum_ya x[yb + NB*ya] W_NA^{ya*ka}
+// (W_L = e^{sign 2 pi i/L}).  Row transforms along x commute with all of it.
+//
+// Pass 1 (k_rows_fold): one workgroup per (image, yb) holds the NA rows
+// yb + NB*ya in registers, transforms each along x (Stockham stages, split
+// LDS exchange), then exchanges once more so that every thread holds all NA
+// rows at a few columns, runs the NA-point DFT across the rows, multiplies
+// output ka by W_ny^{yb*ka} and stores it as row ka + NA*yb of the scratch
+// image: the NA rows a workgroup writes are adjacent.
+//
+// Pass 2 (k_fold_cols): for each ka, NB-point transforms of 16-column tiles
+// over rows ka + NA*j of the scratch (j = 0 .. NB-1), stored to the same rows
+// of the output, where row ka + NA*kb is bin ka + NA*kb: the natural order.
+// Both sides are runs of 16 x 8 B = 128 B.
+//
+// Against rows + two column steps this moves each element through HBM twice
+// instead of three times.
+#include "kernels.hpp"
+
+namespace fftamd {
+
+// ---------------------------------------------------------------------------
+// pass 1: N = nx, NA rows per workgroup, EF values per thread
+// ---------------------------------------------------------------------------
+template <int N, int NA, int EF, int S>
+__global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
+  constexpr int E = EF;
+  constexpr int T = N / E;   // threads per row
+  constexpr int MP = E / NA;  // columns per thread in the step across rows
+  constexpr bool WL = T <= 64;
+  using L = RowLds<N, true>;
+  static_assert(L::size(NA) * sizeof(float) <= kLdsBudgetBytes, "LDS budget");
+  static_assert(T % 2 == 0 && MP >= 1, "fold shape");
+  __shared__ float lds[L::size(NA)];
+
+  const int tid = threadIdx.x;
+  const int line = tid / T, u = tid % T;
+  const uint32_t nb = (uint32_t)(a.ny / NA);
+  const int64_t img = (int64_t)(blockIdx.x / nb);
+  const uint32_t yb = blockIdx.x - (uint32_t)img * nb;
+  // rows yb + nb*line of the image; 32-bit offsets from a uniform base
+  const float2* src = a.in + (img * a.ny + yb) * N;
+  const uint32_t off = (uint32_t)line * nb * N + (uint32_t)u;
+  float2 v[E];
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
+  if (a.shift && ((yb + (uint32_t)u) & 1)) {  // (-1)^(y + x): nb and T are even
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
+  }
+  run_stages<N, E, S, WL, L, true>(v, lds, a.tw, u, line);
+
+  // Across rows: thread (line, u) takes columns u + T*(line*MP + i), i < MP,
+  // of every row; v[ya*MP + i] receives row ya.  Real parts, then imaginary.
+  lds_barrier();
+  const int i0 = u + T * MP * line;
+  static_for<0, E>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    lds[L::template at_k<T * m>(line, u)] = v[m].x;
+  });
+  lds_barrier();
+  static_for<0, NA>([&](auto yc) {
+    constexpr int ya = decltype(yc)::value;
+    static_for<0, MP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      v[ya * MP + i].x = lds[L::template at_k<T * i>(ya, i0)];
+    });
+  });
+  lds_barrier();
+  int u2 = u, line2 = line, i02 = i0;  // recompute addresses (see run_stage)
+  asm volatile("" : "+v"(u2), "+v"(line2), "+v"(i02));
+  static_for<0, E>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    lds[L::template at_k<T * m>(line2, u2)] = v[m].y;
+  });
+  lds_barrier();
+  static_for<0, NA>([&](auto yc) {
+    constexpr int ya = decltype(yc)::value;
+    static_for<0, MP>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      v[ya * MP + i].y = lds[L::template at_k<T * i>(ya, i02)];
+    });
+  });
+
+  // W_ny^{yb*ka}, one factor per output row (yb*ka < ny)
+  float2 w[NA];
+#pragma unroll
+  for (int ka = 1; ka < NA; ++ka) w[ka] = gload(a.wy, yb * (uint32_t)ka);
+  float2* dst = a.out + (img * a.ny + (int64_t)NA * yb) * N;
+#pragma unroll
+  for (int i = 0; i < MP; ++i) {
+    float2 x[NA];
+#pragma unroll
+    for (int ya = 0; ya < NA; ++ya) x[ya] = v[ya * MP + i];
+    dft<NA, S>(x);
+#pragma unroll
+    for (int ka = 0; ka < NA; ++ka) {
+      const float2 y = ka == 0 ? x[0] : apply_tw<S>(x[ka], w[ka]);
+      gstore_nt(dst, (uint32_t)(ka * N + i0 + T * i), y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pass 2: NB-point column transforms over rows ka + NA*j, C adjacent columns
+// per workgroup, E values per thread, split LDS exchange
+// ---------------------------------------------------------------------------
+template <int N, int C, int E, int S>
+__global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
+  constexpr int T = N / E;
+  using L = ColLds<N, C, true>;
+  static_assert(L::size(C) * sizeof(float) <= kLdsBudgetBytes, "LDS budget");
+  __shared__ float lds[L::size(C)];
+
+  const int tid = threadIdx.x;
+  const int line = tid % C, u = tid / C;
+  // column groups numbered (image, ka, x / C); nx is a multiple of C
+  // Plain block order: the workgroups in flight together take adjacent
+  // tiles across the whole chip, so each row's runs are read close together
+  // in time (faster here than grouping adjacent tiles per XCD, which only
+  // pays when runs are shorter than an L2 line).
+  const int64_t g0 = (int64_t)blockIdx.x * C;
+  const uint32_t nx = (uint32_t)a.nx;
+  const int64_t vi = g0 / nx;
+  const uint32_t x0 = (uint32_t)(g0 - vi * nx);
+  const int na = (int)(a.ny / N);
+  const int64_t img = vi / na;
+  const int ka = (int)(vi - img * na);
+  const int64_t base = (img * a.ny + ka) * (int64_t)nx + x0;
+  const uint32_t pitch = (uint32_t)na * nx;
+  const uint32_t off = (uint32_t)line + (uint32_t)u * pitch;
+  const uint32_t step = (uint32_t)T * pitch;
+  float2 v[E];
+  const float2* src = a.in + base;
+#pragma unroll
+  for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + step * m);
+  run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
+  float2* dst = a.out + base;
+#pragma unroll
+  for (int m = 0; m < E; ++m) {
+    gstore_nt(dst, off + step * m, v[m]);
+    if constexpr (E > 16) {
+      if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+namespace {
+template <int NY, int NX, int S>
+hipError_t run_fold(const FoldArgs& a, hipStream_t st) {
+  constexpr int NA = fold_na(NY, NX);
+  constexpr int NB = NY / NA;
+  constexpr int E1 = fold_row_values(NX, NA);
+  constexpr int C = fold_c(NB);
+  constexpr int E2 = fold_col_values(NB, C);
+  if (a.ny != NY || a.nx != NX || a.images < 1) return hipErrorInvalidValue;
+  const int64_t g1 = a.images * NB;
+  const int64_t g2 = a.images * NA * (NX / C);
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  FoldArgs p1 = a;
+  p1.out = a.scratch;
+  hipLaunchKernelGGL((k_rows_fold<NX, NA, E1, S>), dim3((uint32_t)g1), dim3(NA * NX / E1), 0, st, p1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FoldArgs p2 = a;
+  p2.in = a.scratch;
+  hipLaunchKernelGGL((k_fold_cols<NB, C, E2, S>), dim3((uint32_t)g2), dim3(C * NB / E2), 0, st, p2);
+  return hipGetLastError();
+}
+
+template <int S>
+hipError_t fold_sign(const FoldArgs& a, hipStream_t st) {
+  if (a.ny == 8192) {
+    if (a.nx == 8192) return run_fold<8192, 8192, S>(a, st);
+    if (a.nx == 2048) return run_fold<8192, 2048, S>(a, st);
+  } else if (a.ny == 16384) {
+    if (a.nx == 4096) return run_fold<16384, 4096, S>(a, st);
+    if (a.nx == 1024) return run_fold<16384, 1024, S>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+// The shapes where the two passes beat rows + two column steps on MI355X
+// (8192 x 8192: 593 against 650 us; 16384 x 4096: 576 against 606 us;
+// 8192 x 2048 and 16384 x 1024: 120-125 against 150 us).  For 8192 x 4096 and
+// 16384 x 2048 the three-pass form is faster (its row pass on 4096 or 2048
+// points runs near the copy rate, while a 16K-point pass-1 tile holds one
+// workgroup per CU): 291 against 324 us, 298 against 314 us.
+bool fold_supported(int64_t ny, int64_t nx) {
+  return (ny == 8192 && (nx == 8192 || nx == 2048)) || (ny == 16384 && (nx == 4096 || nx == 1024));
+}
+
+hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t st) {
+  return sign < 0 ? fold_sign<-1>(a, st) : fold_sign<1>(a, st);
+}
+
+}  // namespace fftamd

@@ -104,6 +104,26 @@ struct ColStageArgs {
 };
 hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs& a, hipStream_t stream);
 
+// Tall 2D images [images][ny][nx] in two passes (k_fold.hip), for the shapes
+// fold_supported() accepts; na = fold_na(ny, nx), nb = ny / na.  Pass 1: rows
+// yb + nb*ya (ya < na) transformed along x, the na-point DFT across them,
+// output ka times W_ny^{yb*ka}, stored as row ka + na*yb of scratch.  Pass 2:
+// nb-point transforms over rows ka + na*j of scratch, stored to the same rows
+// of out (natural order).  in may equal out; scratch must not overlap either.
+struct FoldArgs {
+  const float2* in;
+  float2* out;
+  float2* scratch;    // images * ny * nx elements
+  const float2* tw;   // stage table of nx, fold_row_values(nx, na) values per thread
+  const float2* tw2;  // stage table of nb, fold_col_values(nb, fold_c(nb)) values per thread
+  const float2* wy;   // e^{-2 pi i e/ny}, e < ny
+  int64_t images;
+  int64_t ny, nx;
+  int shift;          // 1: (-1)^(y + x) on the load (fftshift of both axes)
+};
+bool fold_supported(int64_t ny, int64_t nx);
+hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t stream);
+
 // C2C rows of length n = p * q, p in {3, 5, 7, 9, 15, 25}, q a power of two
 // >= kMinPqPow2, n <= kMaxPqLength: p power-of-two transforms of length q in
 // registers (interleaved sub-rows), the twiddle W_n^{p k} (wn: e^{-2 pi i e/n},

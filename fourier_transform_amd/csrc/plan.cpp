@@ -130,8 +130,11 @@ struct fft_plan {
   const float2* tw_full = nullptr;  // real transforms, pair mode: stage table for n
   const float2* thi = nullptr;
   const float2* tlo = nullptr;
-  // tall 2D images: column steps A (length ny/64) and B (length 64), W_ny table
+  // tall 2D images: column steps A (length ny/64) and B (length 64), W_ny table;
+  // fold: the two-pass form instead (tw_ca: rows of nx for the fold kernel,
+  // tw_cb: columns of kFoldColLength)
   bool tall = false;
+  bool fold = false;
   const float2* tw_ca = nullptr;
   const float2* tw_cb = nullptr;
   const float2* wt = nullptr;
@@ -606,9 +609,16 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   int rc;
   if (ny >= kTallRows) {
     p->tall = true;
-    const int nb = (int)(ny / kTallSplit);
-    append_stage_table(nb, colstage_values(nb), tca);
-    append_stage_table(kTallSplit, colstage_values(kTallSplit), tcb);
+    p->fold = fold_supported(ny, nx);
+    if (p->fold) {
+      const int na = fold_na(ny, nx), nb = (int)(ny / na);
+      append_stage_table((int)nx, fold_row_values((int)nx, na), tca);
+      append_stage_table(nb, fold_col_values(nb, fold_c(nb)), tcb);
+    } else {
+      const int nb = (int)(ny / kTallSplit);
+      append_stage_table(nb, colstage_values(nb), tca);
+      append_stage_table(kTallSplit, colstage_values(kTallSplit), tcb);
+    }
     for (int64_t e = 0; e < ny; ++e) wt.push_back(root(e, ny));
     rc = finish_plan(p, {&ta, &tca, &tcb, &wt}, {&p->tw_a, &p->tw_ca, &p->tw_cb, &p->wt},
                      (size_t)(ny * nx * batch) * sizeof(float2));
@@ -786,6 +796,10 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       ColsArgs c{dst, dst, p->tw_b, p->ny, p->nx, p->batch};
       e = launch_c2c_cols((int)p->ny, p->sign, c, stream);
     }
+  } else if (p->kind == FFT_C2C && p->fold) {
+    // rows and the first column factor: in -> scratch; columns: scratch -> out
+    FoldArgs a{src, dst, p->scratch, p->tw_ca, p->tw_cb, p->wt, p->batch, p->ny, p->nx, p->shift ? 1 : 0};
+    e = launch_fold_2d(p->sign, a, stream);
   } else if (p->kind == FFT_C2C) {
     // rows: in -> scratch; column step A in place on scratch; step B scratch -> out
     const uint32_t nx = (uint32_t)p->nx, na = kTallSplit, nb = (uint32_t)(p->ny / kTallSplit);

@@ -72,4 +72,13 @@ constexpr int cols_values(int n) { return tile_e(n, false); }     // k_c2c_cols,
 constexpr int tposed_values(int n) { return tile_e(n, true); }    // k_fs_rows
 constexpr int colstage_values(int n) { return sched_e(n); }       // k_col_stage
 
+// Two-pass tall 2D images (k_fold.hip): na rows per pass-1 workgroup (na * nx
+// <= 32768 points), column length nb = ny / na = 2048 in pass 2 with 16
+// adjacent columns per workgroup (128 B runs), and the values per thread of
+// each pass (64 for 32K-point tiles: 512 threads of up to 256 VGPRs).
+constexpr int fold_na(int64_t ny, int64_t nx) { return (void)nx, (int)(ny / 2048); }
+constexpr int fold_c(int nb) { return (void)nb, 16; }
+constexpr int fold_row_values(int nx, int na) { return nx * na >= 32768 ? 64 : 32; }
+constexpr int fold_col_values(int nb, int c) { return (void)nb, (void)c, 64; }
+
 }  // namespace fftamd

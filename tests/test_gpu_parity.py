@@ -391,6 +391,27 @@ def test_2d_sweep(ny, nx, shift):
     assert rel_l2(yi, want_i) <= TOL
 
 
+@pytest.mark.parametrize("ny,nx,batch", [(8192, 8192, 1), (8192, 2048, 2), (16384, 1024, 2), (16384, 4096, 1),
+                                         (8192, 4096, 1), (16384, 2048, 1)])
+def test_2d_tall(ny, nx, batch):
+    """Tall images: the two-pass form (rows with the first column factor,
+    then columns of ny/na) for the first four shapes, rows + two column steps
+    for the last two.  Forward with the shift out of place, inverse in place,
+    against the oracle; the shift bit for bit against the chessboard-negated
+    input."""
+    say(f"2d two-pass {ny}x{nx} batch={batch}")
+    x = W.normal_c64((batch, ny, nx), np.random.default_rng(ny + nx))
+    y = c2c_2d(x, -1, shift=1)
+    assert rel_l2(y, oracle.fftshift_2d(oracle.c2c_2d(x, -1))) <= TOL
+    ii, jj = np.meshgrid(np.arange(ny), np.arange(nx), indexing="ij")
+    xn = negate_odd(x, np.broadcast_to(ii + jj, x.shape))
+    del ii, jj
+    assert np.array_equal(c2c_2d(xn, -1).view(np.uint32), y.view(np.uint32))
+    del xn, y
+    yi = c2c_2d(x, +1, inplace=True)
+    assert rel_l2(yi, oracle.c2c_2d(x, +1)) <= TOL
+
+
 def test_shift_bit_exact_1d():
     for n, batch in ((1024, 8), (4096, 3), (1 << 16, 2)):
         say(f"shift bit-exact 1d n={n}")
