@@ -103,6 +103,7 @@ def cpu_baseline(spec, x_host, reps=3, direct=False):
     import numpy as np
     import oracle
     n = spec["n"]
+    one_thread = None
     if spec["kind"] == "real" and direct:
         rows = min(spec["batch"], 64)           # the direct sums: O(n mmax) per row
         xs = np.ascontiguousarray(x_host.T[:rows]).astype(np.complex128)
@@ -139,14 +140,27 @@ def cpu_baseline(spec, x_host, reps=3, direct=False):
                 oracle.c2c(xs, s) if pow2 else oracle.dft(xs, s)
         flops = 5.0 * n * math.log2(n) * rows * len(spec["dirs"])
         desc = f"{rows} of {spec['batch']} rows, {len(spec['dirs'])} direction(s)"
+        if pow2:
+            # the same transform on one thread, on 1/16 of the sample: a per-core figure
+            rows1 = max(1, rows // 16)
+            x1 = xs[:rows1]
+            t0 = time.perf_counter()
+            for s in spec["dirs"]:
+                oracle.c2c(x1, s, nthreads=1)
+            dt1 = time.perf_counter() - t0
+            one_thread = {"value": round(5.0 * n * math.log2(n) * rows1 * len(spec["dirs"]) / dt1 / 1e9, 3),
+                          "sample": f"{rows1} rows, {len(spec['dirs'])} direction(s), one run"}
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
         run()
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
-    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(0),
-            "kind": "oracle", "sample": desc + f", median of {reps} runs, {dt:.3f} s each"}
+    out = {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(0),
+           "kind": "oracle", "sample": desc + f", median of {reps} runs, {dt:.3f} s each"}
+    if one_thread is not None:
+        out["one_thread"] = one_thread
+    return out
 
 
 def main():
@@ -237,6 +251,22 @@ def main():
     wall = time.perf_counter() - t0
     avg_exec_ms = ev0.elapsed_time(ev1) / (args.steps * len(plans))
 
+    # each direction on its own (same buffers), outside the timed region
+    per_dir = None
+    if len(plans) == 2:
+        per_dir = {}
+        src = xd
+        for name, p, dst in zip(("forward", "inverse") if spec["dirs"][0] < 0 else ("inverse", "forward"),
+                                plans, bufs):
+            d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            d0.record(stream)
+            for _ in range(args.steps):
+                F.fft_exec(p, src, dst, stream.cuda_stream)
+            d1.record(stream)
+            torch.cuda.synchronize()
+            per_dir[name] = round(d0.elapsed_time(d1) / args.steps, 5)
+            src = dst
+
     # correctness guard for the numbers: the round trip must return N x
     check = None
     if len(spec["dirs"]) == 2:
@@ -314,6 +344,8 @@ def main():
     }
     if check is not None:
         out["round_trip_rel_l2"] = check
+    if per_dir is not None:
+        out["ms_per_direction"] = per_dir
     for p in plans:
         F.fft_plan_destroy(p)
     del xd, bufs
