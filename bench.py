@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -32,14 +33,24 @@ FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix-core peak of the MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_only(text):
+    """Source text without comments and blank lines (string literals kept)."""
+    text = _TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash():
-    """Hash of the kernel sources; stored HBM-traffic counters are used only
-    while it matches."""
+    """Hash of the kernel sources, comments left out; stored HBM-traffic
+    counters are used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fourier_transform_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hpp", ".hip")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0")
+            h.update(code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

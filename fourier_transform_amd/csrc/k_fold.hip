@@ -1,8 +1,10 @@
 // Tall 2D images in two passes over HBM.
 //
-// The column transform of length ny = NA * NB is split as in the four-step
-// method ("High Performance Fourier Transforms on GPUs with GLSL", section
-// 2.4): with row index y = yb + NB*ya and bin k = ka + NA*kb,
+// A 2D transform is the row transforms followed by the column transforms
+// (Mota, section 2.7, Equation 19).  Here the column transform of length
+// ny = NA * NB is split as in the four-step method (named in "Fast Fourier
+// Transform on CPU and GPU", Working Progress, for transforms that do not fit
+// on chip): with row index y = yb + NB*ya and bin k = ka + NA*kb,
 //   X[ka + NA*kb] = sum_yb W_NB^{yb*kb} W_ny^{yb*ka} sum_ya x[yb + NB*ya] W_NA^{ya*ka}
 // (W_L = e^{sign 2 pi i/L}).  Row transforms along x commute with all of it.
 //
