@@ -18,7 +18,10 @@
 // Pass 2 (k_fold_cols): for each ka, NB-point transforms of 16-column tiles
 // over rows ka + NA*j of the scratch (j = 0 .. NB-1), stored to the same rows
 // of the output, where row ka + NA*kb is bin ka + NA*kb: the natural order.
-// Both sides are runs of 16 x 8 B = 128 B.
+// Both sides are runs of 16 x 8 B = 128 B.  The scratch rows come in groups
+// of NA with a little padding after each group, so pass 2 reads with a stride
+// that is not a power of two; its writes keep the output's power-of-two row
+// pitch.
 //
 // Against rows + two column steps this moves each element through HBM twice
 // instead of three times.
@@ -93,7 +96,9 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   float2 w[NA];
 #pragma unroll
   for (int ka = 1; ka < NA; ++ka) w[ka] = gload(a.wy, yb * (uint32_t)ka);
-  float2* dst = a.out + (img * a.ny + (int64_t)NA * yb) * N;
+  // scratch: group yb of image img, its NA rows adjacent
+  constexpr int64_t GP = fold_group_pitch(N, NA);
+  float2* dst = a.out + (img * nb + yb) * GP;
 #pragma unroll
   for (int i = 0; i < MP; ++i) {
     float2 x[NA];
@@ -133,16 +138,21 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
   const int na = (int)(a.ny / N);
   const int64_t img = vi / na;
   const int ka = (int)(vi - img * na);
-  const int64_t base = (img * a.ny + ka) * (int64_t)nx + x0;
+  // input: the scratch, groups of na rows fold_group_pitch apart; output:
+  // rows ka + na*j of the image
+  const uint32_t gp = (uint32_t)fold_group_pitch(nx, na);
   const uint32_t pitch = (uint32_t)na * nx;
+  float2 v[E];
+  {
+    const float2* src = a.in + img * (a.ny / na) * gp + (int64_t)ka * nx + x0;
+    const uint32_t off = (uint32_t)line + (uint32_t)u * gp;
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + (uint32_t)T * gp * m);
+  }
+  run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
   const uint32_t off = (uint32_t)line + (uint32_t)u * pitch;
   const uint32_t step = (uint32_t)T * pitch;
-  float2 v[E];
-  const float2* src = a.in + base;
-#pragma unroll
-  for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + step * m);
-  run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
-  float2* dst = a.out + base;
+  float2* dst = a.out + (img * a.ny + ka) * (int64_t)nx + x0;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
     gstore_nt(dst, off + step * m, v[m]);

@@ -107,13 +107,15 @@ hipError_t launch_col_stage(int len, int sign, bool twiddle, const ColStageArgs&
 // Tall 2D images [images][ny][nx] in two passes (k_fold.hip), for the shapes
 // fold_supported() accepts; na = fold_na(ny, nx), nb = ny / na.  Pass 1: rows
 // yb + nb*ya (ya < na) transformed along x, the na-point DFT across them,
-// output ka times W_ny^{yb*ka}, stored as row ka + na*yb of scratch.  Pass 2:
-// nb-point transforms over rows ka + na*j of scratch, stored to the same rows
-// of out (natural order).  in may equal out; scratch must not overlap either.
+// output ka times W_ny^{yb*ka}, stored as row ka of group yb of scratch
+// (groups of na adjacent rows, fold_group_pitch(nx, na) elements apart).
+// Pass 2: nb-point transforms over row ka of every group, stored to rows
+// ka + na*j of out (natural order).  in may equal out; scratch must not
+// overlap either.
 struct FoldArgs {
   const float2* in;
   float2* out;
-  float2* scratch;    // images * ny * nx elements
+  float2* scratch;    // fold_scratch_elems(ny, nx, images) elements
   const float2* tw;   // stage table of nx, fold_row_values(nx, na) values per thread
   const float2* tw2;  // stage table of nb, fold_col_values(nb, fold_c(nb)) values per thread
   const float2* wy;   // e^{-2 pi i e/ny}, e < ny

@@ -620,8 +620,9 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
       append_stage_table(kTallSplit, colstage_values(kTallSplit), tcb);
     }
     for (int64_t e = 0; e < ny; ++e) wt.push_back(root(e, ny));
+    const size_t scratch = (size_t)(p->fold ? fold_scratch_elems(ny, nx, batch) : ny * nx * batch);
     rc = finish_plan(p, {&ta, &tca, &tcb, &wt}, {&p->tw_a, &p->tw_ca, &p->tw_cb, &p->wt},
-                     (size_t)(ny * nx * batch) * sizeof(float2));
+                     scratch * sizeof(float2));
   } else {
     append_stage_table((int)ny, cols_values((int)ny), tb);
     rc = finish_plan(p, {&ta, &tb}, {&p->tw_a, &p->tw_b}, 0);

@@ -80,5 +80,15 @@ constexpr int fold_na(int64_t ny, int64_t nx) { return (void)nx, (int)(ny / 2048
 constexpr int fold_c(int nb) { return (void)nb, 16; }
 constexpr int fold_row_values(int nx, int na) { return nx * na >= 32768 ? 64 : 32; }
 constexpr int fold_col_values(int nb, int c) { return (void)nb, (void)c, 64; }
+// Scratch of the two-pass form: per image nb groups of na adjacent rows, each
+// group followed by kFoldPad unused elements, so pass 2's column reads step
+// by na*nx + kFoldPad elements instead of a power of two (a power-of-two
+// stride keeps each tile's runs on few HBM channels: measured 302 against
+// 211 us for the same tile copy).
+constexpr int kFoldPad = 16;
+constexpr int64_t fold_group_pitch(int64_t nx, int na) { return na * nx + kFoldPad; }
+constexpr int64_t fold_scratch_elems(int64_t ny, int64_t nx, int64_t images) {
+  return images * (ny / fold_na(ny, nx)) * fold_group_pitch(nx, fold_na(ny, nx));
+}
 
 }  // namespace fftamd
