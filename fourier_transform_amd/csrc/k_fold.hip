@@ -189,23 +189,25 @@ template <int S>
 hipError_t fold_sign(const FoldArgs& a, hipStream_t st) {
   if (a.ny == 8192) {
     if (a.nx == 8192) return run_fold<8192, 8192, S>(a, st);
+    if (a.nx == 4096) return run_fold<8192, 4096, S>(a, st);
     if (a.nx == 2048) return run_fold<8192, 2048, S>(a, st);
   } else if (a.ny == 16384) {
     if (a.nx == 4096) return run_fold<16384, 4096, S>(a, st);
+    if (a.nx == 2048) return run_fold<16384, 2048, S>(a, st);
     if (a.nx == 1024) return run_fold<16384, 1024, S>(a, st);
   }
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-// The shapes where the two passes beat rows + two column steps on MI355X
-// (8192 x 8192: 593 against 650 us; 16384 x 4096: 576 against 606 us;
-// 8192 x 2048 and 16384 x 1024: 120-125 against 150 us).  For 8192 x 4096 and
-// 16384 x 2048 the three-pass form is faster (its row pass on 4096 or 2048
-// points runs near the copy rate, while a 16K-point pass-1 tile holds one
-// workgroup per CU): 291 against 324 us, 298 against 314 us.
+// The shapes with a pass-1 tile of at most 32768 points and pass-2 columns
+// of 2048.  On MI355X the two passes beat rows + two column steps on each of
+// them (8192 x 8192: 566 against 650 us; 16384 x 4096: 551 against 606 us;
+// 8192 x 4096: 295 against 303 us; 16384 x 2048: 285 against 297 us; 8192 x
+// 2048 and 16384 x 1024: 115-120 against 150 us).
 bool fold_supported(int64_t ny, int64_t nx) {
-  return (ny == 8192 && (nx == 8192 || nx == 2048)) || (ny == 16384 && (nx == 4096 || nx == 1024));
+  return (ny == 8192 && (nx == 8192 || nx == 4096 || nx == 2048)) ||
+         (ny == 16384 && (nx == 4096 || nx == 2048 || nx == 1024));
 }
 
 hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t st) {

@@ -394,11 +394,10 @@ def test_2d_sweep(ny, nx, shift):
 @pytest.mark.parametrize("ny,nx,batch", [(8192, 8192, 1), (8192, 2048, 2), (16384, 1024, 2), (16384, 4096, 1),
                                          (8192, 4096, 1), (16384, 2048, 1)])
 def test_2d_tall(ny, nx, batch):
-    """Tall images: the two-pass form (rows with the first column factor,
-    then columns of ny/na) for the first four shapes, rows + two column steps
-    for the last two.  Forward with the shift out of place, inverse in place,
-    against the oracle; the shift bit for bit against the chessboard-negated
-    input."""
+    """Tall images on the two-pass form (rows with the first column factor,
+    then columns of 2048).  Forward with the shift out of place, inverse in
+    place, against the oracle; the shift bit for bit against the
+    chessboard-negated input."""
     say(f"2d two-pass {ny}x{nx} batch={batch}")
     x = W.normal_c64((batch, ny, nx), np.random.default_rng(ny + nx))
     y = c2c_2d(x, -1, shift=1)
