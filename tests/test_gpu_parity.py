@@ -98,7 +98,7 @@ def test_deterministic_repeat():
 # --------------------------------------------------------------------------
 # four-step (lengths beyond one workgroup)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("logn", [15, 16, 17, 20])
+@pytest.mark.parametrize("logn", [15, 16, 17, 20, 21, 22])
 @pytest.mark.parametrize("sign", [-1, 1])
 def test_fourstep_sweep(logn, sign):
     n = 1 << logn
