@@ -469,8 +469,10 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
     }
   } else if (valid) {
     const float2* src = a.in + base;
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + step * m);
+    static_for<0, E>([&](auto ic) {
+      constexpr int m = load_slot<N2, E>(decltype(ic)::value);
+      v[m] = gload_nt(src, off + step * m);
+    });
     if (a.shift && (c1 & 1)) {  // element index c1 + n1*k has the parity of c1 (n1 even)
 #pragma unroll
       for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
@@ -525,8 +527,10 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
     // rows k2 = k20 .. k20 + C - 1 of transform b form one row of blocks
     // starting at (b*n2 + k20)*N1 (k20 is a multiple of C)
     const float2* src = a.in + g0 * N1;
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
+    static_for<0, E>([&](auto ic) {
+      constexpr int m = load_slot<N1, E>(decltype(ic)::value);
+      v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
+    });
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);

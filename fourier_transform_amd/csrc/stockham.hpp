@@ -378,6 +378,26 @@ __device__ __forceinline__ void lds_sync() {
   }
 }
 
+// Order in which a thread loads its E values of a line from HBM: the order
+// in which the first stage consumes them.  Butterfly k of that stage reads
+// slots k + r*KB; dft() takes R = 32 and 64 as R = A*B and transforms the
+// inputs a + A*b for one a at a time, and R = 8 and 16 as the even half, then
+// the odd half.  Loads return in issue order, so the first sub-transform can
+// start while the later loads are still in flight.
+constexpr int dft_use_order(int R, int i) {
+  if (R == 32 || R == 64) {
+    const int A = R == 32 ? 4 : 8, B = R / A;
+    return i / B + A * (i % B);
+  }
+  if (R == 8 || R == 16) return 2 * (i % (R / 2)) + i / (R / 2);
+  return i;
+}
+template <int N, int E>
+constexpr int load_slot(int i) {
+  constexpr int R = sched_r0(N, E), KB = E / R;
+  return i / R + KB * dft_use_order(R, i % R);
+}
+
 // ---------------------------------------------------------------------------
 // the stages.  E values per thread (E a multiple of every radix, T = N/E
 // threads per line).  On entry and exit v[m] holds element u + T*m of `line`.
