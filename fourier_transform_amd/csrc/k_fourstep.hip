@@ -18,6 +18,7 @@ struct FsColsOp {
     template <int BK>
     static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N2, false);
+      if ((a.batch * a.n1) % C != 0) return hipErrorInvalidValue;  // the kernel loads whole groups
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
@@ -38,6 +39,7 @@ struct FsRowsOp {
     template <int BC>
     static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N1, true);
+      if ((a.batch * a.n2) % C != 0) return hipErrorInvalidValue;  // the kernel loads whole groups
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;

@@ -410,6 +410,32 @@ __device__ __forceinline__ uint32_t fs_block_index(uint32_t k2, uint32_t c1, uin
   return ((k2 / BK) * (n1 / BC) + c1 / BC) * (BK * BC) + (k2 % BK) * BC + c1 % BC;
 }
 
+// Stage 1 of the four-step passes reads its twiddles from an LDS copy of its
+// part of the table when that fits beside the exchange buffers: R - 1 factors
+// per butterfly from a 2-level L2 path otherwise, with two workgroups' worth
+// of latency to hide at one workgroup per CU.
+template <int N, int E>
+constexpr int fs_tw1_elems() {
+  return sched_stages(N, E) >= 2 ? sched_tw_off(N, E, 2) - sched_tw_off(N, E, 1) : 0;
+}
+template <int N, int E, int NT, int TQ>
+__device__ __forceinline__ void fs_fetch_tw1(float2* tq, const float2* __restrict__ tw, int tid) {
+  constexpr int O1 = sched_tw_off(N, E, 1);
+#pragma unroll
+  for (int i = 0; i < TQ; ++i) {  // clamped rather than skipped: every wave issues the same loads
+    const int q = tid + NT * i;
+    tq[i] = gload(tw, (uint32_t)(O1 + (q < fs_tw1_elems<N, E>() ? q : fs_tw1_elems<N, E>() - 1)));
+  }
+}
+template <int N, int E, int NT, int TQ>
+__device__ __forceinline__ void fs_store_tw1(float2* twl, const float2* tq, int tid) {
+#pragma unroll
+  for (int i = 0; i < TQ; ++i) {
+    const int q = tid + NT * i;
+    if (q < fs_tw1_elems<N, E>()) twl[q] = tq[i];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Four-step pass 1: column transforms of length N2 over stride n1, each
 // output multiplied by W_n^{n1*k2}, stored to scratch in the block layout
@@ -427,8 +453,11 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
                 "LDS budget");
   // the stages' exchange barriers order the factor-table writes before the reads
   static_assert(sched_stages(N2, E) >= 2, "pass 1 needs at least one LDS exchange");
+  constexpr int TW1 = fs_tw1_elems<N2, E>();
+  constexpr bool LTW = L::size(C) * sizeof(lds_elem_t<SPLIT>) + (C * FP + TW1) * sizeof(float2) <= kLdsBudgetBytes;
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
   __shared__ float2 ftab[C * FP];
+  __shared__ float2 twl[LTW ? TW1 : 1];
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -448,12 +477,26 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   // thi[e >> bits] * tlo[e & mask] (both exponents stay below n).
   const uint32_t mask = (1u << a.bits) - 1u;
   const uint32_t c0 = c1 - line;
-  for (int q = tid; q < C * E; q += C * T) {
-    const uint32_t e = (c0 + (uint32_t)(q / E)) * (uint32_t)(T * (q % E));
-    ftab[(q / E) * FP + q % E] = cmul(gload(a.thi, e >> a.bits), gload(a.tlo, e & mask));
+  // The small loads (factor table, this thread's factor, the stage-1
+  // twiddles) are issued first and consumed only after the line's loads have
+  // been issued: loads complete in issue order, so waiting for them then does
+  // not wait for the line.
+  constexpr int NT = C * T;
+  constexpr int FQ = (C * E + NT - 1) / NT;
+  float2 fh[FQ], fl[FQ];
+#pragma unroll
+  for (int i = 0; i < FQ; ++i) {
+    const int q = tid + NT * i;
+    if (q < C * E) {
+      const uint32_t e = (c0 + (uint32_t)(q / E)) * (uint32_t)(T * (q % E));
+      fh[i] = gload(a.thi, e >> a.bits);
+      fl[i] = gload(a.tlo, e & mask);
+    }
   }
-  const uint32_t eu = c1 * (uint32_t)u;
-  const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
+  float2 tq[TQ];
+  if constexpr (LTW) fs_fetch_tw1<N2, E, NT, TQ>(tq, a.tw, tid);
+  __builtin_amdgcn_sched_barrier(0);
   float2 v[E];
   if (valid && HOOK) {
     // element j = c1 + n1*k2 of a row of in_len values (zero beyond), times pre[j]
@@ -467,22 +510,40 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
         if (a.pre) v[m] = cmul(v[m], gload(a.pre, j));
       }
     }
-  } else if (valid) {
+  } else if (!HOOK) {
+    // unconditional (every launched group is whole: batch*n1 is a multiple
+    // of C), so the waits for the small loads above stay partial
     const float2* src = a.in + base;
     static_for<0, E>([&](auto ic) {
       constexpr int m = load_slot<N2, E>(decltype(ic)::value);
       v[m] = gload_nt(src, off + step * m);
     });
-    if (a.shift && (c1 & 1)) {  // element index c1 + n1*k has the parity of c1 (n1 even)
-#pragma unroll
-      for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
-    }
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N2, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
+  __builtin_amdgcn_sched_barrier(0);
+  // LDS writes of the small tables; stage 0's exchange barriers order them
+  // before their reads (stage 1's twiddles, the factor table in the store)
+#pragma unroll
+  for (int i = 0; i < FQ; ++i) {
+    const int q = tid + NT * i;
+    if (q < C * E) ftab[(q / E) * FP + q % E] = cmul(fh[i], fl[i]);
+  }
+  if constexpr (LTW) fs_store_tw1<N2, E, NT, TQ>(twl, tq, tid);
+  if (valid && !HOOK && a.shift && (c1 & 1)) {  // element index c1 + n1*k has the parity of c1 (n1 even)
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
+  }
+  if constexpr (LTW) {
+    const TwLdsStage<1> tws{a.tw, twl, (uint32_t)sched_tw_off(N2, E, 1)};
+    run_stages<N2, E, S, false, L, SPLIT>(v, lds, tws, u, line);
+  } else {
+    run_stages<N2, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
+  }
   if (valid) {
+    const uint32_t eu = c1 * (uint32_t)u;
+    const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
     // the block layout, relative to the first block column of this group
     float2* dst = a.out + b * (int64_t)n1 * N2 + c0 * BK;
 #pragma unroll
@@ -514,28 +575,44 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr bool WL = T <= 64;
   using L = RowLds<N1, SPLIT>;
   static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
+  constexpr int TW1 = fs_tw1_elems<N1, E>();
+  constexpr bool LTW = sched_stages(N1, E) >= 2 &&
+                       L::size(C) * sizeof(lds_elem_t<SPLIT>) + TW1 * sizeof(float2) <= kLdsBudgetBytes;
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  __shared__ float2 twl[LTW ? TW1 : 1];
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
+  // stage-1 twiddles: fetched before the line's loads, stored to LDS after
+  // them (see k_fs_cols)
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
+  float2 tq[TQ];
+  if constexpr (LTW) fs_fetch_tw1<N1, E, NT, TQ>(tq, a.tw, tid);
+  __builtin_amdgcn_sched_barrier(0);
   const int64_t n2 = a.n2;
   const int64_t lines = a.batch * n2;
   const int64_t g0 = (int64_t)xcd_grouped_block(blockIdx.x, gridDim.x) * C;
   const int64_t g = g0 + line;
   float2 v[E];
-  if (g < lines) {
+  {
     // rows k2 = k20 .. k20 + C - 1 of transform b form one row of blocks
-    // starting at (b*n2 + k20)*N1 (k20 is a multiple of C)
+    // starting at (b*n2 + k20)*N1 (k20 is a multiple of C).  Unconditional:
+    // every launched group is whole (batch*n2 is a multiple of C).
     const float2* src = a.in + g0 * N1;
     static_for<0, E>([&](auto ic) {
       constexpr int m = load_slot<N1, E>(decltype(ic)::value);
       v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
     });
-  } else {
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
-  run_stages<N1, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
+  if constexpr (LTW) {
+    __builtin_amdgcn_sched_barrier(0);
+    fs_store_tw1<N1, E, NT, TQ>(twl, tq, tid);
+    lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
+    const TwLdsStage<1> tws{a.tw, twl, (uint32_t)sched_tw_off(N1, E, 1)};
+    run_stages<N1, E, S, WL, L, SPLIT>(v, lds, tws, u, line);
+  } else {
+    run_stages<N1, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
+  }
   // transposed read-back: slot p of thread tid is q = tid + NT*p, i.e. line
   // q % C = tid % C and element q / C = tid / C + (NT / C) * p (NT is a
   // multiple of C)

@@ -410,9 +410,31 @@ constexpr int load_slot(int i) {
 // On return other threads may still be reading LDS: synchronise before
 // writing it again.
 // ---------------------------------------------------------------------------
-template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, int s, class LdsT>
-__device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __restrict__ tw, int u,
-                                          int line) {
+// Twiddle sources of the stages: the table in global memory (a plain
+// pointer), or TwLdsStage<LS>, which reads stage LS from a copy of that
+// stage's part of the table in LDS (the copy starts at table offset `off`)
+// and the other stages from global memory.
+template <int LS>
+struct TwLdsStage {
+  const float2* __restrict__ g;
+  const float2* l;
+  uint32_t off;
+};
+template <int s>
+__device__ __forceinline__ float2 tw_at(const float2* __restrict__ t, uint32_t i) {
+  return gload(t, i);
+}
+template <int s, int LS>
+__device__ __forceinline__ float2 tw_at(const TwLdsStage<LS>& t, uint32_t i) {
+  if constexpr (s == LS) {
+    return t.l[i - t.off];
+  } else {
+    return gload(t.g, i);
+  }
+}
+
+template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, int s, class LdsT, class TW>
+__device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, int u, int line) {
   static_assert(SPLIT == std::is_same<LdsT, float>::value, "LDS element type");
   constexpr int T = N / E;
   constexpr int NST = sched_stages(N, E);
@@ -432,7 +454,7 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __
     if constexpr (s > 0) {
 #pragma unroll
       for (int r = 1; r < R; ++r) {
-        x[r] = apply_tw<S>(x[r], gload(tw, (uint32_t)(OFF + (r - 1) * NS + j)));
+        x[r] = apply_tw<S>(x[r], tw_at<s>(tw, (uint32_t)(OFF + (r - 1) * NS + j)));
         // bound the twiddle loads in flight for large radices (VGPR budget)
         if constexpr (R > 16) {
           if ((r & 15) == 15) __builtin_amdgcn_sched_barrier(0);
@@ -495,9 +517,8 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const float2* __
   }
 }
 
-template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, class LdsT>
-__device__ __forceinline__ void run_stages(float2* v, LdsT* lds, const float2* __restrict__ tw,
-                                           int u, int line) {
+template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, class LdsT, class TW>
+__device__ __forceinline__ void run_stages(float2* v, LdsT* lds, const TW& tw, int u, int line) {
   static_for<0, sched_stages(N, E)>([&](auto sc) {
     run_stage<N, E, S, WAVE_LOCAL, Lds, SPLIT, decltype(sc)::value>(v, lds, tw, u, line);
   });

@@ -411,6 +411,15 @@ def test_2d_tall(ny, nx, batch):
     assert rel_l2(yi, oracle.c2c_2d(x, +1)) <= TOL
 
 
+def test_2d_tall_inverse_shift_is_the_same_map():
+    """Even sizes: ifftshift is the same index map as fftshift, so SHIFT = 2
+    gives the SHIFT = 1 output bit for bit on the two-pass tall path."""
+    say("2d two-pass 8192x2048 shift=2 vs shift=1")
+    x = W.normal_c64((1, 8192, 2048), np.random.default_rng(82))
+    a, b = c2c_2d(x, +1, shift=1), c2c_2d(x, +1, shift=2)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 def test_shift_bit_exact_1d():
     for n, batch in ((1024, 8), (4096, 3), (1 << 16, 2)):
         say(f"shift bit-exact 1d n={n}")
