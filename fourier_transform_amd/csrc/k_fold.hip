@@ -41,24 +41,50 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   using L = RowLds<N, true>;
   static_assert(L::size(NA) * sizeof(float) <= kLdsBudgetBytes, "LDS budget");
   static_assert(T % 2 == 0 && MP >= 1, "fold shape");
+  constexpr int NT = NA * T;
+  // stage 1 reads its twiddles from an LDS copy (as in the four-step passes)
+  constexpr int TW1 = fs_tw1_elems<N, E>();
+  constexpr bool LTW = sched_stages(N, E) >= 2 && L::size(NA) * sizeof(float) + TW1 * sizeof(float2) <= kLdsBudgetBytes;
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   __shared__ float lds[L::size(NA)];
+  __shared__ float2 twl[LTW ? TW1 : 1];
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
   const uint32_t nb = (uint32_t)(a.ny / NA);
   const int64_t img = (int64_t)(blockIdx.x / nb);
   const uint32_t yb = blockIdx.x - (uint32_t)img * nb;
+  // the small loads first (see k_fs_cols): W_ny^{yb*ka}, one factor per
+  // output row (yb*ka < ny), and the stage-1 twiddles
+  float2 w[NA];
+#pragma unroll
+  for (int ka = 1; ka < NA; ++ka) w[ka] = gload(a.wy, yb * (uint32_t)ka);
+  float2 tq[TQ];
+  if constexpr (LTW) fs_fetch_tw1<N, E, NT, TQ>(tq, a.tw, tid);
+  __builtin_amdgcn_sched_barrier(0);
   // rows yb + nb*line of the image; 32-bit offsets from a uniform base
   const float2* src = a.in + (img * a.ny + yb) * N;
   const uint32_t off = (uint32_t)line * nb * N + (uint32_t)u;
   float2 v[E];
-#pragma unroll
-  for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
+  static_for<0, E>([&](auto ic) {
+    constexpr int m = load_slot<N, E>(decltype(ic)::value);
+    v[m] = gload_nt(src, off + T * m);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LTW) {
+    fs_store_tw1<N, E, NT, TQ>(twl, tq, tid);
+    lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
+  }
   if (a.shift && ((yb + (uint32_t)u) & 1)) {  // (-1)^(y + x): nb and T are even
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
   }
-  run_stages<N, E, S, WL, L, true>(v, lds, a.tw, u, line);
+  if constexpr (LTW) {
+    const TwLdsStage<1> tws{a.tw, twl, (uint32_t)sched_tw_off(N, E, 1)};
+    run_stages<N, E, S, WL, L, true>(v, lds, tws, u, line);
+  } else {
+    run_stages<N, E, S, WL, L, true>(v, lds, a.tw, u, line);
+  }
 
   // Across rows: thread (line, u) takes columns u + T*(line*MP + i), i < MP,
   // of every row; v[ya*MP + i] receives row ya.  Real parts, then imaginary.
@@ -92,10 +118,6 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
     });
   });
 
-  // W_ny^{yb*ka}, one factor per output row (yb*ka < ny)
-  float2 w[NA];
-#pragma unroll
-  for (int ka = 1; ka < NA; ++ka) w[ka] = gload(a.wy, yb * (uint32_t)ka);
   // scratch: group yb of image img, its NA rows adjacent
   constexpr int64_t GP = fold_group_pitch(N, NA);
   float2* dst = a.out + (img * nb + yb) * GP;
@@ -122,7 +144,12 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
   constexpr int T = N / E;
   using L = ColLds<N, C, true>;
   static_assert(L::size(C) * sizeof(float) <= kLdsBudgetBytes, "LDS budget");
+  constexpr int NT = C * T;
+  constexpr int TW1 = fs_tw1_elems<N, E>();
+  constexpr bool LTW = sched_stages(N, E) >= 2 && L::size(C) * sizeof(float) + TW1 * sizeof(float2) <= kLdsBudgetBytes;
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   __shared__ float lds[L::size(C)];
+  __shared__ float2 twl[LTW ? TW1 : 1];
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -142,14 +169,28 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
   // rows ka + na*j of the image
   const uint32_t gp = (uint32_t)fold_group_pitch(nx, na);
   const uint32_t pitch = (uint32_t)na * nx;
+  float2 tq[TQ];
+  if constexpr (LTW) fs_fetch_tw1<N, E, NT, TQ>(tq, a.tw2, tid);
+  __builtin_amdgcn_sched_barrier(0);
   float2 v[E];
   {
     const float2* src = a.in + img * (a.ny / na) * gp + (int64_t)ka * nx + x0;
     const uint32_t off = (uint32_t)line + (uint32_t)u * gp;
-#pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + (uint32_t)T * gp * m);
+    static_for<0, E>([&](auto ic) {
+      constexpr int m = load_slot<N, E>(decltype(ic)::value);
+      v[m] = gload_nt(src, off + (uint32_t)T * gp * m);
+    });
   }
-  run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LTW) {
+    // stage 0's exchange barriers (workgroup-wide here) order these writes
+    // before stage 1 reads them
+    fs_store_tw1<N, E, NT, TQ>(twl, tq, tid);
+    const TwLdsStage<1> tws{a.tw2, twl, (uint32_t)sched_tw_off(N, E, 1)};
+    run_stages<N, E, S, false, L, true>(v, lds, tws, u, line);
+  } else {
+    run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
+  }
   const uint32_t off = (uint32_t)line + (uint32_t)u * pitch;
   const uint32_t step = (uint32_t)T * pitch;
   float2* dst = a.out + (img * a.ny + ka) * (int64_t)nx + x0;
