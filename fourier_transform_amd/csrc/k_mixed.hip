@@ -76,24 +76,106 @@ __device__ __forceinline__ void dft_prime(float2* x) {
   for (int k = 0; k < R; ++k) x[k] = out[k];
 }
 
-template <int S>
+constexpr int inv_mod(int a, int m) {
+  for (int i = 1; i < m; ++i)
+    if ((a * i) % m == 1) return i;
+  return 1;
+}
+
+template <int R, int S>
+__device__ __forceinline__ void dft_small(float2* x);
+
+// R = A*B with A, B coprime, by the prime-factor index maps (no twiddles):
+// input n = (B n1 + A n2) mod R, output k = (B (B^-1 mod A) k1 + A (A^-1 mod B) k2)
+// mod R, so that W_R^{nk} = W_A^{n1 k1} W_B^{n2 k2} (Good's mapping; the
+// two-factor split of [Mota] section 2.3.1 without its twiddle factors).
+template <int A, int B, int S>
+__device__ __forceinline__ void dft_pfa(float2* x) {
+  constexpr int R = A * B;
+  constexpr int BI = inv_mod(B % A, A), AI = inv_mod(A % B, B);
+  float2 y[A][B];
+  static_for<0, B>([&](auto n2c) {
+    constexpr int n2 = decltype(n2c)::value;
+    float2 t[A];
+    static_for<0, A>([&](auto n1c) {
+      constexpr int n1 = decltype(n1c)::value;
+      t[n1] = x[(B * n1 + A * n2) % R];
+    });
+    dft_small<A, S>(t);
+#pragma unroll
+    for (int k1 = 0; k1 < A; ++k1) y[k1][n2] = t[k1];
+  });
+  static_for<0, A>([&](auto k1c) {
+    constexpr int k1 = decltype(k1c)::value;
+    float2 t[B];
+#pragma unroll
+    for (int n2 = 0; n2 < B; ++n2) t[n2] = y[k1][n2];
+    dft_small<B, S>(t);
+    static_for<0, B>([&](auto k2c) {
+      constexpr int k2 = decltype(k2c)::value;
+      x[(B * BI * k1 + A * AI * k2) % R] = t[k2];
+    });
+  });
+}
+
+template <int R, int S>
+__device__ __forceinline__ void dft_small(float2* x) {
+  if constexpr (R == 2 || R == 4 || R == 8 || R == 16) {
+    dft<R, S>(x);
+  } else if constexpr (R == 3 || R == 5 || R == 7) {
+    dft_prime<R, S>(x);
+  } else if constexpr (R == 6) {
+    dft_pfa<2, 3, S>(x);
+  } else if constexpr (R == 10) {
+    dft_pfa<2, 5, S>(x);
+  } else if constexpr (R == 12) {
+    dft_pfa<4, 3, S>(x);
+  } else if constexpr (R == 14) {
+    dft_pfa<2, 7, S>(x);
+  } else {
+    static_assert(R == 15, "radix");
+    dft_pfa<3, 5, S>(x);
+  }
+}
+
+// radices of the schedules (mixed_radices on the host): up to 8 with two
+// butterflies per thread, up to 16 with one
+template <int S, int RMAX>
 __device__ __forceinline__ void dft_any(int R, float2* x) {
-  switch (R) {
-    case 2: dft<2, S>(x); break;
-    case 3: dft_prime<3, S>(x); break;
-    case 4: dft<4, S>(x); break;
-    case 5: dft_prime<5, S>(x); break;
-    case 7: dft_prime<7, S>(x); break;
-    default: dft<8, S>(x); break;
+  if constexpr (RMAX <= 8) {
+    switch (R) {
+      case 2: dft_small<2, S>(x); break;
+      case 3: dft_small<3, S>(x); break;
+      case 4: dft_small<4, S>(x); break;
+      case 5: dft_small<5, S>(x); break;
+      case 6: dft_small<6, S>(x); break;
+      case 7: dft_small<7, S>(x); break;
+      default: dft_small<8, S>(x); break;
+    }
+  } else {
+    switch (R) {
+      case 2: dft_small<2, S>(x); break;
+      case 3: dft_small<3, S>(x); break;
+      case 4: dft_small<4, S>(x); break;
+      case 5: dft_small<5, S>(x); break;
+      case 6: dft_small<6, S>(x); break;
+      case 7: dft_small<7, S>(x); break;
+      case 8: dft_small<8, S>(x); break;
+      case 10: dft_small<10, S>(x); break;
+      case 12: dft_small<12, S>(x); break;
+      case 14: dft_small<14, S>(x); break;
+      case 15: dft_small<15, S>(x); break;
+      default: dft_small<16, S>(x); break;
+    }
   }
 }
 
 __host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + (i >> 5); }
 }  // namespace
 
-// KB = 2 butterflies of at most 8 values per thread and stage, up to 1024
-// threads (so at most 128 VGPRs)
-template <int S, int KB>
+// KB butterflies of at most RMAX values per thread and stage (2 x 8 or
+// 1 x 16), up to 1024 threads (so at most 128 VGPRs)
+template <int S, int KB, int RMAX>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -107,7 +189,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   const float2* src = a.in + row * n;
   float2* dst = a.out + row * n;
 
-  float2 x[KB][8];
+  float2 x[KB][RMAX];
   for (int s = 0; s < a.nstages; ++s) {
     const int R = a.radix[s];
     const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
@@ -118,7 +200,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
         const uint32_t b = (uint32_t)(t + tpl * i);
         if (valid && b < m) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
+          for (int r = 0; r < RMAX; ++r) {
             if (r < R) {
               float2 v = gload_nt(src, b + r * m);
               if (a.pre) v = cmul(v, gload(a.pre, b + r * m));
@@ -133,7 +215,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
         const uint32_t b = (uint32_t)(t + tpl * i);
         if (b < m) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
+          for (int r = 0; r < RMAX; ++r)
             if (r < R) x[i][r] = L[mixed_pad(b + r * m)];
         }
       }
@@ -148,10 +230,10 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
           const uint32_t j = b - __umulhi(b, a.ns_magic[s]) * ns;
           const float2* tw = a.tw + a.twoff[s] + j;
 #pragma unroll
-          for (int r = 1; r < 8; ++r)
+          for (int r = 1; r < RMAX; ++r)
             if (r < R) x[i][r] = apply_tw<S>(x[i][r], tw[(r - 1) * ns]);
         }
-        dft_any<S>(R, x[i]);
+        dft_any<S, RMAX>(R, x[i]);
       }
     }
     // scatter the outputs: (b - j) R + j + q ns
@@ -163,7 +245,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
           const uint32_t j = ns == 1 ? 0u : b - __umulhi(b, a.ns_magic[s]) * ns;
           const uint32_t base = (b - j) * (uint32_t)R + j;
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
+          for (int r = 0; r < RMAX; ++r)
             if (r < R) L[mixed_pad(base + r * ns)] = x[i][r];
         }
       }
@@ -175,7 +257,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
         const uint32_t b = (uint32_t)(t + tpl * i);
         if (b < m) {
 #pragma unroll
-          for (int r = 0; r < 8; ++r)
+          for (int r = 0; r < RMAX; ++r)
             if (r < R) gstore_nt(dst, b + r * ns, x[i][r]);
         }
       }
@@ -185,20 +267,31 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
 
 hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   if (a.n < 2 || a.n > kMaxMixedLength || a.nstages < 1 || a.nstages > kMixedMaxStages || a.tpl < 1 ||
-      a.lines < 1 || a.tpl * a.lines > 1024 || a.rows < 1 || a.kb != kMixedButterflies)
+      a.lines < 1 || a.tpl * a.lines > 1024 || a.rows < 1 || (a.kb != 1 && a.kb != 2))
     return hipErrorInvalidValue;
-  for (int s = 0; s < a.nstages; ++s)  // every butterfly of every stage has a thread
-    if ((int64_t)a.tpl * a.kb < a.m[s]) return hipErrorInvalidValue;
+  int rmax = 0;
+  for (int s = 0; s < a.nstages; ++s) {
+    const int R = a.radix[s];
+    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9 || R == 11 || R == 13) return hipErrorInvalidValue;
+    if ((int64_t)a.tpl * a.kb < a.m[s]) return hipErrorInvalidValue;  // every butterfly has a thread
+    rmax = R > rmax ? R : rmax;
+  }
   uint32_t grid;
   hipError_t e = grid_of(a.rows, a.lines, &grid);
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)a.lines * (mixed_pad((uint32_t)a.n) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  if (sign < 0)
-    hipLaunchKernelGGL((k_mixed<-1, kMixedButterflies>), dim3(grid), block, lds, st, a);
-  else
-    hipLaunchKernelGGL((k_mixed<1, kMixedButterflies>), dim3(grid), block, lds, st, a);
+  if (rmax > 8) {
+    if (sign < 0)
+      hipLaunchKernelGGL((k_mixed<-1, 1, 16>), dim3(grid), block, lds, st, a);
+    else
+      hipLaunchKernelGGL((k_mixed<1, 1, 16>), dim3(grid), block, lds, st, a);
+  } else if (sign < 0) {
+    hipLaunchKernelGGL((k_mixed<-1, 2, 8>), dim3(grid), block, lds, st, a);
+  } else {
+    hipLaunchKernelGGL((k_mixed<1, 2, 8>), dim3(grid), block, lds, st, a);
+  }
   return hipGetLastError();
 }
 

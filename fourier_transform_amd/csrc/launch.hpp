@@ -151,8 +151,9 @@ hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream
 // ns_magic[s] = ceil(2^32 / ns[s]), so that b / ns = umulhi(b, ns_magic) for
 // b < 2^16.  pre: n factors applied on load (the shift ramps), or null.
 // Threads: tpl per line, lines per workgroup; each thread takes butterflies
-// t, t + tpl, ..., at most kb = kMixedButterflies per stage, so
-// tpl * kb >= m[s] and every stage needs m[s] <= 1024 * kb.
+// t, t + tpl, ..., at most kb per stage (2 when every radix is at most 8,
+// kMixedButterflies; 1 when radices go up to 16: 2..8, 10, 12, 14, 15, 16),
+// so tpl * kb >= m[s] and every stage needs m[s] <= 1024 * kb.
 constexpr int kMaxMixedLength = 8192;
 constexpr int kMixedMaxStages = 16;
 constexpr int kMixedButterflies = 2;

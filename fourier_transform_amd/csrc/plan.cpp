@@ -10,6 +10,7 @@
 #include <complex>
 #include <cstdint>
 #include <cstdio>
+#include <functional>
 #include <new>
 #include <string>
 #include <vector>
@@ -247,10 +248,18 @@ fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
   return p;
 }
 
-// radices of the mixed-radix schedule for n = 2^a 3^b 5^c 7^d, or an empty
-// list when n has another prime factor: 8s (with 4 x 4 in place of 8 x 2),
-// the leftover 4 or 2, then 7s, 5s and 3s
-std::vector<int> mixed_radices(int64_t n) {
+// Radices of the mixed-radix schedule: the fewest factors of n from `set`
+// (descending) that are all >= rlo (so that no stage has more than n/rlo
+// butterflies); among those the most even ones (smallest ratio of the
+// largest to the smallest radix: with one butterfly per thread, a stage of
+// large radix leaves most threads idle), then the larger smallest radix.
+// Empty when there is none (n has a prime factor above 7, or needs smaller
+// radices).  With the composite radices 10, 12, 14, 15 and 16, 1000 is
+// 10 x 10 x 10: three stages and two LDS round trips instead of 8 x 5 x 5 x 5.
+// The fixed-order schedule with radices up to 8: 8s (with 4 x 4 in place of
+// 8 x 2), the leftover 4 or 2, then 7s, 5s and 3s; empty when n has another
+// prime factor.
+std::vector<int> mixed_radices_fixed(int64_t n) {
   std::vector<int> r;
   int a = 0;
   while (n % 2 == 0) n /= 2, ++a;
@@ -269,8 +278,34 @@ std::vector<int> mixed_radices(int64_t n) {
   return r;
 }
 
+std::vector<int> mixed_radices(int64_t n, const std::vector<int>& set, int rlo) {
+  std::vector<int> best, cur;
+  std::function<void(int64_t, size_t)> dfs = [&](int64_t m, size_t from) {
+    if (m == 1) {
+      // cur and best are descending: front() is the largest radix, back() the smallest
+      const bool better =
+          best.empty() || cur.size() < best.size() ||
+          (cur.size() == best.size() &&
+           (cur.front() * best.back() < best.front() * cur.back() ||
+            (cur.front() * best.back() == best.front() * cur.back() && cur.back() > best.back())));
+      if (better) best = cur;
+      return;
+    }
+    if (!best.empty() && cur.size() >= best.size()) return;
+    for (size_t i = from; i < set.size(); ++i) {
+      if (set[i] < rlo) break;
+      if (m % set[i] != 0) continue;
+      cur.push_back(set[i]);
+      dfs(m / set[i], i);
+      cur.pop_back();
+    }
+  };
+  dfs(n, 0);
+  return best;
+}
+
 // C2C of a length with no prime factor above 7, not a power of two, <= kMaxMixedLength
-fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int>& rad) {
+fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int>& rad, int kb) {
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
   p->n = n;
@@ -299,7 +334,7 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
     ns *= R;
   }
   if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
-  a.kb = kMixedButterflies;
+  a.kb = kb;
   a.tpl = (int)((maxm + a.kb - 1) / a.kb);
   a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
   // shift factors e^{-sign 2 pi i j h/n} and e^{+sign ...}, h = floor(n/2)
@@ -427,11 +462,28 @@ fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
 // else the chirp transform
 fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
   if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
-  const std::vector<int> rad = mixed_radices(n);
-  const int rmin = rad.empty() ? 0 : *std::min_element(rad.begin(), rad.end());
-  if (!rad.empty() && n <= kMaxMixedLength && (int)rad.size() <= kMixedMaxStages &&
-      n / rmin <= 1024 * kMixedButterflies)
-    return create_mixed(n, batch, sign, rad);
+  // Schedules, in order (measured on MI355X against each other):
+  //  1. radices up to 16, one butterfly per thread, when the smallest radix
+  //     is at least 6 or a line takes at most 256 threads (1000: 10 10 10,
+  //     345 against 431 us per 512 MiB; with a radix-5 stage and a long line,
+  //     e.g. 2000 as 10 8 5 5, the small-radix stages of 2 x 8 per thread
+  //     were faster: 554 against 406 us);
+  //  2. radices up to 8 in the fixed order below, two butterflies per thread;
+  //  3. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
+  //  4. the chirp transform.
+  if (n <= kMaxMixedLength) {
+    static const std::vector<int> wide = {16, 15, 14, 12, 10, 8, 7, 6, 5, 4, 3, 2};
+    static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
+    const std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
+    if (!w.empty() && (int)w.size() <= kMixedMaxStages && (w.back() >= 6 || n / w.back() <= 256))
+      return create_mixed(n, batch, sign, w, 1);
+    const int rlo2 = (int)((n + 2 * 1024 - 1) / (2 * 1024));
+    for (const std::vector<int>& r : {mixed_radices_fixed(n), mixed_radices(n, narrow, rlo2)}) {
+      if (r.empty() || (int)r.size() > kMixedMaxStages) continue;
+      if (n / *std::min_element(r.begin(), r.end()) <= 1024 * kMixedButterflies)
+        return create_mixed(n, batch, sign, r, kMixedButterflies);
+    }
+  }
   return create_bluestein(n, batch, sign);
 }
 
@@ -478,9 +530,9 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (kind == FFT_C2C && n > 1 && !is_pow2(n)) {
     if (n > kMaxBluesteinLengthLarge)
       return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 2^22"), nullptr;
-    // mixed radix when every prime factor is at most 7 and every stage has
-    // at most 1024 * kMixedButterflies butterflies (radix >= 2, 3, 4 for
-    // n up to 4096, 6144, 8192), else the chirp transform
+    // p * 2^k in registers, else mixed radix when every prime factor is at
+    // most 7 and every stage has at most 1024 butterflies per thread slot,
+    // else the chirp transform
     return create_c2c_any(n, batch, sign);
   }
   if (kind != FFT_C2C && n > 2 && !is_pow2(n)) {

@@ -1,8 +1,8 @@
 """GPU parity for C2C lengths that are not powers of two, against the
 oracle's DFT by the definition: p x 2^k (p in 3, 5, 7, 9, 15, 25) in
-registers, mixed-radix Stockham stages (radices 2, 3, 4, 5, 7, 8) for the
-other lengths with no prime factor above 7, Bluestein's chirp transform for
-the rest.
+registers, mixed-radix Stockham stages (radices 2..8, 10, 12, 14, 15, 16) for
+the other lengths with no prime factor above 7, Bluestein's chirp transform
+for the rest.
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -18,9 +18,15 @@ from gpu_helpers import c2c, c2c_2d, c2r, dev, empty, host, r2c, rel_l2, say
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
-SMALL = [3, 5, 6, 7, 9, 12, 14, 15, 17, 21, 31, 35, 48, 49, 96, 100, 127, 255, 257, 384]
-LARGE = [1000, 1001, 1029, 1536, 2047, 2401, 3000, 3072, 4095, 4097, 5000, 6144, 6250, 6561,
-         7168, 8000, 8191]
+# radix schedules of some mixed lengths: radices up to 16, one butterfly per
+# thread: 18: 6 3; 42: 7 6; 150: 15 10; 360: 10 6 6; 720: 12 10 6;
+# 840: 12 10 7; 1000: 10 10 10; 1296: 6 6 6 6; 6000: 10 10 10 6.  Radices up
+# to 8, two per thread: 2000: 4 4 5 5 5; 3000: 8 5 5 5 3; 4000: 8 4 5 5 5;
+# 7776: 6 6 6 6 6.
+SMALL = [3, 5, 6, 7, 9, 12, 14, 15, 17, 18, 21, 31, 35, 42, 48, 49, 96, 100, 127, 150, 255, 257, 360,
+         384, 720, 840]
+LARGE = [1000, 1001, 1029, 1296, 1536, 2000, 2047, 2401, 3000, 3072, 4000, 4095, 4097, 5000, 6000,
+         6144, 6250, 6561, 7168, 7776, 8000, 8191]
 
 
 @pytest.fixture(scope="module", autouse=True)
