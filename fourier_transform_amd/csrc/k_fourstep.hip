@@ -32,7 +32,7 @@ struct FsColsOp {
     }
   };
 };
-template <int S, bool HOOK>
+template <int S>
 struct FsRowsOp {
   template <int N1>
   struct At {
@@ -43,7 +43,7 @@ struct FsRowsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_rows<N1, S, BC, HOOK>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
+      hipLaunchKernelGGL((k_fs_rows<N1, S, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
@@ -63,12 +63,8 @@ hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStre
   if (sign < 0) return dispatch_pow2<FsColsOp<-1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
   return dispatch_pow2<FsColsOp<1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
 }
-hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t st, bool hook) {
-  if (hook) {
-    if (sign < 0) return dispatch_pow2<FsRowsOp<-1, true>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
-    return dispatch_pow2<FsRowsOp<1, true>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
-  }
-  if (sign < 0) return dispatch_pow2<FsRowsOp<-1, false>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
-  return dispatch_pow2<FsRowsOp<1, false>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t st) {
+  if (sign < 0) return dispatch_pow2<FsRowsOp<-1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
+  return dispatch_pow2<FsRowsOp<1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
 }
 }  // namespace fftamd

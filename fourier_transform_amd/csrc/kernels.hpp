@@ -565,7 +565,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 // consecutive threads on consecutive rows, so each store is a run of C
 // elements.
 // ---------------------------------------------------------------------------
-template <int N1, int S, int BC, bool HOOK>
+template <int N1, int S, int BC>
 __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) void k_fs_rows(FourStepArgs a) {
   constexpr int E = tile_e(N1, true);
   constexpr bool SPLIT = tile_split(N1, true);
@@ -656,18 +656,12 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
     // n2 >= 128 > C: the group's rows belong to one transform b
     const int64_t b = g0 / n2;
     const int64_t k20 = g0 - b * n2;
-    float2* dst = a.out + (HOOK ? b * a.out_stride : b * n2 * N1) + k20;
+    float2* dst = a.out + b * n2 * N1 + k20;
     const uint32_t off = (uint32_t)ln + (uint32_t)(tid / C) * (uint32_t)n2;
     const uint32_t step = (uint32_t)(NT / C) * (uint32_t)n2;
 #pragma unroll
     for (int p = 0; p < E; ++p) {
-      if constexpr (HOOK) {
-        // output k = k20 + off + step*p of a row of out_len values, times post[k]
-        const uint32_t k = (uint32_t)k20 + off + step * p;
-        if (k < (uint32_t)a.out_len) gstore_nt(dst, off + step * p, a.post ? cmul(v[p], gload(a.post, k)) : v[p]);
-      } else {
-        gstore_nt(dst, off + step * p, v[p]);
-      }
+      gstore_nt(dst, off + step * p, v[p]);
       if constexpr (E > 16) {
         if ((p & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }

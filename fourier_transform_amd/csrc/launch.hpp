@@ -71,18 +71,32 @@ struct FourStepArgs {
   int64_t batch;
   int n1, n2, bits;
   int shift;  // pass 1 only: multiply element j by (-1)^j (1D chessboard)
-  // Hooked variants (hook = true in the launchers), for transforms embedded
-  // in a longer computation: pass 1 reads rows of in_len values in_stride
-  // apart (zero beyond in_len) and multiplies element j by pre[j] (if set);
-  // pass 2 writes rows out_stride apart, only outputs k < out_len, multiplied
-  // by post[k] (if set).  The unhooked variants ignore these fields.
+  // The hooked pass 1 (hook = true in launch_fourstep_cols), for the chirp
+  // transform: it reads rows of in_len values in_stride apart (zero beyond
+  // in_len) and multiplies element j by pre[j] (if set).  The chirp passes
+  // after it (launch_chirp_mid/out) use pre, post, out_stride, out_len and
+  // sink as described there.  Other passes ignore these fields.
   const float2* pre;
   const float2* post;
   int64_t in_stride, out_stride;
   int in_len, out_len;
+  float2* sink;  // launch_chirp_out: >= 1024 elements nothing else reads (dropped outputs land there)
 };
 hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream, bool hook = false);
-hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream, bool hook = false);
+hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream);
+// The chirp transform above m = 16384 after its first four-step pass
+// (k_chirp.hip), on FourStepArgs of the length m = n1*n2:
+// launch_chirp_mid: rows k2 of pass 1's block layout (in) through the
+//   forward n1-point transform, times pre[k2*n1 + k1] (the chirp's transform
+//   at bin k2 + n2*k1), the inverse n1-point transform and W_m^{-j1*k2};
+//   rows stored contiguously to out as [batch][n2][n1].  tw: stage table of
+//   n1 (tposed_values); thi/tlo/bits: the two-level table of m.
+// launch_chirp_out: columns j1 of in ([batch][n2][n1]) through the inverse
+//   n2-point transform over k2; output j = j1 + n1*j2 kept for j < out_len,
+//   times post[j], written to row b of out (out_stride apart); outputs past
+//   out_len are written to sink instead.  tw: stage table of n2 (cols_values).
+hipError_t launch_chirp_mid(int n1, const FourStepArgs& a, hipStream_t stream);
+hipError_t launch_chirp_out(int n2, const FourStepArgs& a, hipStream_t stream);
 
 // One step of a column transform split in two (2D column pass of tall images,
 // ny = na * nb; column row index i = ia + na*ib, output k = kb + nb*ka).
@@ -179,8 +193,8 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
 // is inverse_FFT_m(forward_FFT_m(a) * bhat) with bhat = forward_FFT_m(b)/m.
 // Rows of n complex64 values, contiguous; in place allowed.
 constexpr int kMaxBluesteinLength = 8192;
-// longer lengths run the same computation as two four-step transforms
-// (launch_fourstep_* with hooks), up to this length
+// longer lengths run the same computation in three passes (the hooked
+// launch_fourstep_cols, launch_chirp_mid, launch_chirp_out), up to this length
 constexpr int64_t kMaxBluesteinLengthLarge = int64_t(1) << 22;
 struct BluesteinArgs {
   const float2* in;

@@ -148,6 +148,7 @@ struct fft_plan {
   const float2* chirp_shift = nullptr;
   const float2* chirp_ishift = nullptr;
   const float2* bhat = nullptr;
+  const float2* bhat_t = nullptr;  // above m = 16384: bhat[k2 + n2*k1] at k2*n1 + k1
   // C2C lengths with no prime factor above 7 (mixed radix): the schedule, and
   // the load factors of the two shifts
   // C2C lengths p * q (p in {3, 5, 7, 9, 15, 25}, q a power of two >= 16)
@@ -356,10 +357,11 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
 
 // C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLengthLarge.
 // The transforms of length m >= 2n - 1 run inside one kernel per row batch
-// while m <= kMaxSinglePass; above, as two four-step transforms whose
-// hooked passes apply the chirp on load, the chirp transform between them
-// and the chirp again on store (four passes over batch x m values, through
-// two plan-owned scratch buffers).
+// while m <= kMaxSinglePass; above, in three passes over batch x m values
+// through two plan-owned scratch buffers: the forward transform's column
+// pass with the chirp applied on load, one row pass for the forward row
+// factor, the product with bhat and the inverse row factor, and the inverse
+// column pass with the chirp applied on store.
 fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
@@ -372,7 +374,7 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   int64_t m = 1;
   while (m < 2 * n - 1) m <<= 1;
   p->bm = (int)m;
-  std::vector<float2> ta, tb, thi, tlo, pre, pres, prei, bh;
+  std::vector<float2> ta, tb, thi, tlo, pre, pres, prei, bh, bht;
   size_t scratch = 0;
   if (m <= kMaxSinglePass) {
     append_stage_table((int)m, rows_values((int)m), ta);
@@ -416,8 +418,11 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   std::vector<std::vector<float2>*> parts = {&ta, &pre, &pres, &prei, &bh};
   std::vector<const float2**> slots = {&p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift, &p->bhat};
   if (p->fourstep) {
-    parts.insert(parts.end(), {&tb, &thi, &tlo});
-    slots.insert(slots.end(), {&p->tw_b, &p->thi, &p->tlo});
+    // the row pass between the transforms reads bhat row by row: k2*n1 + k1
+    for (int64_t k2 = 0; k2 < p->n2; ++k2)
+      for (int64_t k1 = 0; k1 < p->n1; ++k1) bht.push_back(bh[(size_t)(k2 + p->n2 * k1)]);
+    parts.insert(parts.end(), {&tb, &thi, &tlo, &bht});
+    slots.insert(slots.end(), {&p->tw_b, &p->thi, &p->tlo, &p->bhat_t});
   }
   if (finish_plan(p, parts, slots, scratch) != FFT_OK) {
     free_plan(p);
@@ -809,24 +814,22 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     const int64_t m = p->bm;
     float2* s1 = p->scratch;
     float2* s2 = p->scratch + m * p->batch;
-    // forward transform of the chirped row (zero beyond n) into s2
+    // pass 1: the chirped row (zero beyond n), forward n2-point column
+    // transforms with the four-step factor, into s1
     FourStepArgs f1{src, s1, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
                     pre, nullptr, p->n, 0, (int)p->n, 0};
     e = launch_fourstep_cols(p->n2, -1, f1, stream, true);
+    // pass 2: rows through the forward n1-point transform, times bhat, the
+    // inverse n1-point transform and its factor, into s2
     if (e == hipSuccess) {
-      FourStepArgs f2{s1, s2, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
-      e = launch_fourstep_rows(p->n1, -1, f2, stream);
+      FourStepArgs f2{s1, s2, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0, p->bhat_t};
+      e = launch_chirp_mid(p->n1, f2, stream);
     }
-    // inverse transform of (that times bhat), the first n outputs times c_k, into out
+    // pass 3: inverse n2-point column transforms, the first n outputs times c_k, into out
     if (e == hipSuccess) {
-      FourStepArgs i1{s2, s1, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
-                      p->bhat, nullptr, m, 0, (int)m, 0};
-      e = launch_fourstep_cols(p->n2, +1, i1, stream, true);
-    }
-    if (e == hipSuccess) {
-      FourStepArgs i2{s1, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
-                      nullptr, p->chirp, 0, p->n, 0, (int)p->n};
-      e = launch_fourstep_rows(p->n1, +1, i2, stream, true);
+      FourStepArgs f3{s2, dst, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
+                      nullptr, p->chirp, 0, p->n, 0, (int)p->n, s1};  // s1 is free after pass 2
+      e = launch_chirp_out(p->n2, f3, stream);
     }
   } else if (p->bluestein) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;

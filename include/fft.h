@@ -22,8 +22,9 @@
  *    mixed-radix Stockham stages (radices 2 to 8, 10, 12, 14, 15, 16) when
  *    every stage has at most 2048 butterflies (n <= 8192); the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
- *    inside one kernel while m <= 16384, else as two four-step transforms
- *    (four passes) through a scratch buffer of 2 * batch * m * 8 bytes.
+ *    inside one kernel while m <= 16384, else in three passes (the second
+ *    holds the inner factors of both transforms) through a scratch buffer of
+ *    2 * batch * m * 8 bytes.
  *  - R2C/C2R lengths: powers of two from 4 to 32768 (one kernel), and any
  *    other length from 3 to 2^22 (fourier.ts refuses these for its FFT; here
  *    an any-length complex transform of n/2 values for even n, with the same
