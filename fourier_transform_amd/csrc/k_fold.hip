@@ -12,16 +12,15 @@
 // yb + NB*ya in registers, transforms each along x (Stockham stages, split
 // LDS exchange), then exchanges once more so that every thread holds all NA
 // rows at a few columns, runs the NA-point DFT across the rows, multiplies
-// output ka by W_ny^{yb*ka} and stores it as row ka + NA*yb of the scratch
-// image: the NA rows a workgroup writes are adjacent.
+// output ka by W_ny^{yb*ka} and stores it as row ka of group yb of the
+// scratch: the NA rows a workgroup writes are adjacent.
 //
 // Pass 2 (k_fold_cols): for each ka, NB-point transforms of 16-column tiles
-// over rows ka + NA*j of the scratch (j = 0 .. NB-1), stored to the same rows
-// of the output, where row ka + NA*kb is bin ka + NA*kb: the natural order.
-// Both sides are runs of 16 x 8 B = 128 B.  The scratch rows come in groups
-// of NA with a little padding after each group, so pass 2 reads with a stride
-// that is not a power of two; its writes keep the output's power-of-two row
-// pitch.
+// over row ka of every scratch group (yb = 0 .. NB-1), stored to rows
+// ka + NA*kb of the output, which hold bin ka + NA*kb: the natural order.
+// Both sides are runs of 16 x 8 B = 128 B.  Each scratch group of NA rows is
+// followed by a little padding, so pass 2 reads with a stride that is not a
+// power of two; its writes keep the output's power-of-two row pitch.
 //
 // Against rows + two column steps this moves each element through HBM twice
 // instead of three times.
