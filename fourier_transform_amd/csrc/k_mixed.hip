@@ -138,130 +138,125 @@ __device__ __forceinline__ void dft_small(float2* x) {
   }
 }
 
-// radices of the schedules (mixed_radices on the host): up to 8 with two
-// butterflies per thread, up to 16 with one
-template <int S, int RMAX>
-__device__ __forceinline__ void dft_any(int R, float2* x) {
-  if constexpr (RMAX <= 8) {
-    switch (R) {
-      case 2: dft_small<2, S>(x); break;
-      case 3: dft_small<3, S>(x); break;
-      case 4: dft_small<4, S>(x); break;
-      case 5: dft_small<5, S>(x); break;
-      case 6: dft_small<6, S>(x); break;
-      case 7: dft_small<7, S>(x); break;
-      default: dft_small<8, S>(x); break;
+__host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + (i >> 5); }
+}  // namespace
+
+// One stage of radix R (compile-time, so the butterfly loops are straight
+// code): KB butterflies per thread, b = t + tpl*i.  The first stage gathers
+// its inputs from HBM (times pre), the others from the line in LDS; the last
+// stage stores to HBM, the others back to LDS.
+template <int S, int KB, int R>
+__device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last, uint32_t t, uint32_t tpl,
+                                            bool valid, const float2* src, float2* dst, float2* L) {
+  const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
+  float2 x[KB][R];
+  // gather the inputs of this thread's butterflies: b + r*m
+  if (s == 0) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const uint32_t b = t + tpl * i;
+      if (valid && b < m) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float2 v = gload_nt(src, b + r * m);
+          if (a.pre) v = cmul(v, gload(a.pre, b + r * m));
+          x[i][r] = v;
+        }
+      }
     }
   } else {
-    switch (R) {
-      case 2: dft_small<2, S>(x); break;
-      case 3: dft_small<3, S>(x); break;
-      case 4: dft_small<4, S>(x); break;
-      case 5: dft_small<5, S>(x); break;
-      case 6: dft_small<6, S>(x); break;
-      case 7: dft_small<7, S>(x); break;
-      case 8: dft_small<8, S>(x); break;
-      case 10: dft_small<10, S>(x); break;
-      case 12: dft_small<12, S>(x); break;
-      case 14: dft_small<14, S>(x); break;
-      case 15: dft_small<15, S>(x); break;
-      default: dft_small<16, S>(x); break;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const uint32_t b = t + tpl * i;
+      if (b < m) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[i][r] = L[mixed_pad(b + r * m)];
+      }
+    }
+    lds_barrier();  // every read of this stage precedes its writes
+  }
+  // twiddles and the R-point DFTs
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    const uint32_t b = t + tpl * i;
+    if (b < m) {
+      if (s > 0) {
+        const uint32_t j = b - __umulhi(b, a.ns_magic[s]) * ns;
+        const float2* tw = a.tw + a.twoff[s] + j;
+#pragma unroll
+        for (int r = 1; r < R; ++r) x[i][r] = apply_tw<S>(x[i][r], tw[(r - 1) * ns]);
+      }
+      dft_small<R, S>(x[i]);
+    }
+  }
+  // scatter the outputs: (b - j) R + j + q ns
+  if (!last) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const uint32_t b = t + tpl * i;
+      if (b < m) {
+        const uint32_t j = ns == 1 ? 0u : b - __umulhi(b, a.ns_magic[s]) * ns;
+        const uint32_t base = (b - j) * (uint32_t)R + j;
+#pragma unroll
+        for (int r = 0; r < R; ++r) L[mixed_pad(base + r * ns)] = x[i][r];
+      }
+    }
+    lds_barrier();
+  } else if (valid) {
+    // last stage: ns = m and j = b, so output q of butterfly b is b + q m
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const uint32_t b = t + tpl * i;
+      if (b < m) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) gstore_nt(dst, b + r * ns, x[i][r]);
+      }
     }
   }
 }
 
-__host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + (i >> 5); }
-}  // namespace
-
 // KB butterflies of at most RMAX values per thread and stage (2 x 8 or
-// 1 x 16), up to 1024 threads (so at most 128 VGPRs)
+// 1 x 16), up to 1024 threads (so at most 128 VGPRs).  The radix of each
+// stage selects a compiled stage (radices of the schedules: 2..8, and with
+// RMAX = 16 also 10, 12, 14, 15, 16).
 template <int S, int KB, int RMAX>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
-  const int tpl = a.tpl;
+  const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
-  const int line = tid / tpl, t = tid - line * tpl;
+  const int line = tid / (int)tpl;
+  const uint32_t t = (uint32_t)(tid - line * (int)tpl);
   const int64_t row = (int64_t)blockIdx.x * a.lines + line;
   const bool valid = row < a.rows;
   const uint32_t n = (uint32_t)a.n;
   float2* L = smem + (size_t)line * (mixed_pad(n) + 1);
   const float2* src = a.in + row * n;
   float2* dst = a.out + row * n;
-
-  float2 x[KB][RMAX];
   for (int s = 0; s < a.nstages; ++s) {
-    const int R = a.radix[s];
-    const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
-    // gather the inputs of this thread's butterflies: b + r*m
-    if (s == 0) {
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const uint32_t b = (uint32_t)(t + tpl * i);
-        if (valid && b < m) {
-#pragma unroll
-          for (int r = 0; r < RMAX; ++r) {
-            if (r < R) {
-              float2 v = gload_nt(src, b + r * m);
-              if (a.pre) v = cmul(v, gload(a.pre, b + r * m));
-              x[i][r] = v;
-            }
+    const bool last = s + 1 == a.nstages;
+#define FFTAMD_STAGE(R) mixed_stage<S, KB, R>(a, s, last, t, tpl, valid, src, dst, L)
+    switch (a.radix[s]) {
+      case 2: FFTAMD_STAGE(2); break;
+      case 3: FFTAMD_STAGE(3); break;
+      case 4: FFTAMD_STAGE(4); break;
+      case 5: FFTAMD_STAGE(5); break;
+      case 6: FFTAMD_STAGE(6); break;
+      case 7: FFTAMD_STAGE(7); break;
+      case 8: FFTAMD_STAGE(8); break;
+      default:
+        if constexpr (RMAX > 8) {
+          switch (a.radix[s]) {
+            case 10: FFTAMD_STAGE(10); break;
+            case 12: FFTAMD_STAGE(12); break;
+            case 14: FFTAMD_STAGE(14); break;
+            case 15: FFTAMD_STAGE(15); break;
+            default: FFTAMD_STAGE(16); break;
           }
         }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const uint32_t b = (uint32_t)(t + tpl * i);
-        if (b < m) {
-#pragma unroll
-          for (int r = 0; r < RMAX; ++r)
-            if (r < R) x[i][r] = L[mixed_pad(b + r * m)];
-        }
-      }
-      lds_barrier();  // every read of this stage precedes its writes
+        break;
     }
-    // twiddles and the R-point DFTs
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      const uint32_t b = (uint32_t)(t + tpl * i);
-      if (b < m) {
-        if (s > 0) {
-          const uint32_t j = b - __umulhi(b, a.ns_magic[s]) * ns;
-          const float2* tw = a.tw + a.twoff[s] + j;
-#pragma unroll
-          for (int r = 1; r < RMAX; ++r)
-            if (r < R) x[i][r] = apply_tw<S>(x[i][r], tw[(r - 1) * ns]);
-        }
-        dft_any<S, RMAX>(R, x[i]);
-      }
-    }
-    // scatter the outputs: (b - j) R + j + q ns
-    if (s + 1 < a.nstages) {
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const uint32_t b = (uint32_t)(t + tpl * i);
-        if (b < m) {
-          const uint32_t j = ns == 1 ? 0u : b - __umulhi(b, a.ns_magic[s]) * ns;
-          const uint32_t base = (b - j) * (uint32_t)R + j;
-#pragma unroll
-          for (int r = 0; r < RMAX; ++r)
-            if (r < R) L[mixed_pad(base + r * ns)] = x[i][r];
-        }
-      }
-      lds_barrier();
-    } else if (valid) {
-      // last stage: ns = m and j = b, so output q of butterfly b is b + q m
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const uint32_t b = (uint32_t)(t + tpl * i);
-        if (b < m) {
-#pragma unroll
-          for (int r = 0; r < RMAX; ++r)
-            if (r < R) gstore_nt(dst, b + r * ns, x[i][r]);
-        }
-      }
-    }
+#undef FFTAMD_STAGE
   }
 }
 
