@@ -467,21 +467,20 @@ fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
 // else the chirp transform
 fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
   if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
-  // Schedules, in order (measured on MI355X against each other):
-  //  1. radices up to 16, one butterfly per thread, when the smallest radix
-  //     is at least 6 or a line takes at most 256 threads (1000: 10 10 10,
-  //     345 against 431 us per 512 MiB; with a radix-5 stage and a long line,
-  //     e.g. 2000 as 10 8 5 5, the small-radix stages of 2 x 8 per thread
-  //     were faster: 554 against 406 us);
-  //  2. radices up to 8 in the fixed order below, two butterflies per thread;
+  // Schedules, in order:
+  //  1. radices up to 16, one butterfly per thread (1000: 10 10 10, three
+  //     stages).  Measured against the fixed order of step 2 on MI355X with
+  //     each stage compiled for its radix: better or equal for 1000, 2000,
+  //     2500 (253 against 330 us per 512 MiB), 3000, 3500, 4500, 6000, 8000,
+  //     worse for 4000 and 5000 (325 against 291, 289 against 280 us);
+  //  2. radices up to 8 in a fixed order, two butterflies per thread;
   //  3. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
   //  4. the chirp transform.
   if (n <= kMaxMixedLength) {
     static const std::vector<int> wide = {16, 15, 14, 12, 10, 8, 7, 6, 5, 4, 3, 2};
     static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
     const std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
-    if (!w.empty() && (int)w.size() <= kMixedMaxStages && (w.back() >= 6 || n / w.back() <= 256))
-      return create_mixed(n, batch, sign, w, 1);
+    if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_mixed(n, batch, sign, w, 1);
     const int rlo2 = (int)((n + 2 * 1024 - 1) / (2 * 1024));
     for (const std::vector<int>& r : {mixed_radices_fixed(n), mixed_radices(n, narrow, rlo2)}) {
       if (r.empty() || (int)r.size() > kMixedMaxStages) continue;

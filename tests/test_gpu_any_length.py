@@ -20,9 +20,9 @@ TOL = 1e-5
 
 # radix schedules of some mixed lengths: radices up to 16, one butterfly per
 # thread: 18: 6 3; 42: 7 6; 150: 15 10; 360: 10 6 6; 720: 12 10 6;
-# 840: 12 10 7; 1000: 10 10 10; 1296: 6 6 6 6; 6000: 10 10 10 6.  Radices up
-# to 8, two per thread: 2000: 4 4 5 5 5; 3000: 8 5 5 5 3; 4000: 8 4 5 5 5;
-# 7776: 6 6 6 6 6.
+# 840: 12 10 7; 1000: 10 10 10; 1296: 6 6 6 6; 2000: 10 8 5 5;
+# 3000: 10 10 6 5; 4000: 10 10 8 5; 6000: 10 10 10 6.  Radices up to 8, two
+# per thread: 7776: 6 6 6 6 6.
 SMALL = [3, 5, 6, 7, 9, 12, 14, 15, 17, 18, 21, 31, 35, 42, 48, 49, 96, 100, 127, 150, 255, 257, 360,
          384, 720, 840]
 LARGE = [1000, 1001, 1029, 1296, 1536, 2000, 2047, 2401, 3000, 3072, 4000, 4095, 4097, 5000, 6000,
