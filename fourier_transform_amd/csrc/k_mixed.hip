@@ -1,5 +1,5 @@
 // Mixed-radix Stockham transform for C2C rows whose length has no prime
-// factor above 7 (radices 2, 3, 4, 5, 7, 8).  The GLSL dissertation ("High
+// factor above 13 (radices 2..8, 10..16).  The GLSL dissertation ("High
 // Performance Fourier Transforms on GPUs with GLSL", section 2.3) names
 // mixed radices as the way beyond powers of two; the stage itself is the
 // natural-order Stockham step of the WGSL Fourier-stage source (turing-sphere
@@ -28,9 +28,27 @@ __device__ __forceinline__ float cosq(int k) {
     return -0.5f;
   } else if constexpr (R == 5) {
     return k == 1 ? 0.3090169943749474241022934f : -0.8090169943749474241022934f;
-  } else {
+  } else if constexpr (R == 7) {
     return k == 1 ? 0.6234898018587335305250049f
                   : (k == 2 ? -0.2225209339563144042889026f : -0.9009688679024191262361023f);
+  } else if constexpr (R == 11) {
+    switch (k) {
+      case 1: return 0.8412535328311811688618116f;
+      case 2: return 0.4154150130018864255292741f;
+      case 3: return -0.1423148382732851404437927f;
+      case 4: return -0.6548607339452850640569251f;
+      default: return -0.9594929736144973898903681f;
+    }
+  } else {
+    static_assert(R == 13, "radix");
+    switch (k) {
+      case 1: return 0.8854560256532098959003755f;
+      case 2: return 0.5680647467311558025118076f;
+      case 3: return 0.1205366802553230533490677f;
+      case 4: return -0.3546048870425356259696379f;
+      case 5: return -0.7485107481711010986346306f;
+      default: return -0.9709418174260520271569823f;
+    }
   }
 }
 template <int R>
@@ -39,9 +57,27 @@ __device__ __forceinline__ float sinq(int k) {
     return 0.8660254037844386467637232f;
   } else if constexpr (R == 5) {
     return k == 1 ? 0.9510565162951535721164393f : 0.5877852522924731291687060f;
-  } else {
+  } else if constexpr (R == 7) {
     return k == 1 ? 0.7818314824680298087084445f
                   : (k == 2 ? 0.9749279121818236070181317f : 0.4338837391175581204757683f);
+  } else if constexpr (R == 11) {
+    switch (k) {
+      case 1: return 0.5406408174555975821076360f;
+      case 2: return 0.9096319953545183714117154f;
+      case 3: return 0.9898214418809327323760920f;
+      case 4: return 0.7557495743542582837740358f;
+      default: return 0.2817325568414296977114179f;
+    }
+  } else {
+    static_assert(R == 13, "radix");
+    switch (k) {
+      case 1: return 0.4647231720437685456560153f;
+      case 2: return 0.8229838658936563945796174f;
+      case 3: return 0.9927088740980539928007516f;
+      case 4: return 0.9350162426854148234397846f;
+      case 5: return 0.6631226582407952023767855f;
+      default: return 0.2393156642875577671487537f;
+    }
   }
 }
 template <int R, int S>
@@ -122,7 +158,7 @@ template <int R, int S>
 __device__ __forceinline__ void dft_small(float2* x) {
   if constexpr (R == 2 || R == 4 || R == 8 || R == 16) {
     dft<R, S>(x);
-  } else if constexpr (R == 3 || R == 5 || R == 7) {
+  } else if constexpr (R == 3 || R == 5 || R == 7 || R == 11 || R == 13) {
     dft_prime<R, S>(x);
   } else if constexpr (R == 6) {
     dft_pfa<2, 3, S>(x);
@@ -218,7 +254,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
 // KB butterflies of at most RMAX values per thread and stage (2 x 8 or
 // 1 x 16), up to 1024 threads (so at most 128 VGPRs).  The radix of each
 // stage selects a compiled stage (radices of the schedules: 2..8, and with
-// RMAX = 16 also 10, 12, 14, 15, 16).
+// RMAX = 16 also 10 .. 16).
 template <int S, int KB, int RMAX>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
@@ -248,7 +284,9 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
         if constexpr (RMAX > 8) {
           switch (a.radix[s]) {
             case 10: FFTAMD_STAGE(10); break;
+            case 11: FFTAMD_STAGE(11); break;
             case 12: FFTAMD_STAGE(12); break;
+            case 13: FFTAMD_STAGE(13); break;
             case 14: FFTAMD_STAGE(14); break;
             case 15: FFTAMD_STAGE(15); break;
             default: FFTAMD_STAGE(16); break;
@@ -267,7 +305,7 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   int rmax = 0;
   for (int s = 0; s < a.nstages; ++s) {
     const int R = a.radix[s];
-    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9 || R == 11 || R == 13) return hipErrorInvalidValue;
+    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9) return hipErrorInvalidValue;
     if ((int64_t)a.tpl * a.kb < a.m[s]) return hipErrorInvalidValue;  // every butterfly has a thread
     rmax = R > rmax ? R : rmax;
   }

@@ -157,7 +157,7 @@ struct PqArgs {
 };
 hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream);
 
-// C2C rows whose length n <= kMaxMixedLength has no prime factor above 7:
+// C2C rows whose length n <= kMaxMixedLength has no prime factor above 13:
 // mixed-radix Stockham stages of radix 2, 3, 4, 5, 7 or 8 (schedule chosen at
 // plan time), the line resident in LDS between stages.  Stage s has radix
 // radix[s], ns[s] = product of the radices before it, m[s] = n / radix[s]
@@ -166,7 +166,7 @@ hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream
 // b < 2^16.  pre: n factors applied on load (the shift ramps), or null.
 // Threads: tpl per line, lines per workgroup; each thread takes butterflies
 // t, t + tpl, ..., at most kb per stage (2 when every radix is at most 8,
-// kMixedButterflies; 1 when radices go up to 16: 2..8, 10, 12, 14, 15, 16),
+// kMixedButterflies; 1 when radices go up to 16: 2..8, 10..16),
 // so tpl * kb >= m[s] and every stage needs m[s] <= 1024 * kb.
 constexpr int kMaxMixedLength = 8192;
 constexpr int kMixedMaxStages = 16;

@@ -149,7 +149,7 @@ struct fft_plan {
   const float2* chirp_ishift = nullptr;
   const float2* bhat = nullptr;
   const float2* bhat_t = nullptr;  // above m = 16384: bhat[k2 + n2*k1] at k2*n1 + k1
-  // C2C lengths with no prime factor above 7 (mixed radix): the schedule, and
+  // C2C lengths with no prime factor above 13 (mixed radix): the schedule, and
   // the load factors of the two shifts
   // C2C lengths p * q (p in {3, 5, 7, 9, 15, 25}, q a power of two >= 16)
   bool pq = false;
@@ -254,8 +254,8 @@ fft_plan* create_direct(int64_t n, int64_t batch, int kind, int sign) {
 // butterflies); among those the most even ones (smallest ratio of the
 // largest to the smallest radix: with one butterfly per thread, a stage of
 // large radix leaves most threads idle), then the larger smallest radix.
-// Empty when there is none (n has a prime factor above 7, or needs smaller
-// radices).  With the composite radices 10, 12, 14, 15 and 16, 1000 is
+// Empty when there is none (n has a prime factor the set lacks, or needs
+// smaller radices).  With the composite radices 10, 12, 14, 15 and 16, 1000 is
 // 10 x 10 x 10: three stages and two LDS round trips instead of 8 x 5 x 5 x 5.
 // The fixed-order schedule with radices up to 8: 8s (with 4 x 4 in place of
 // 8 x 2), the leftover 4 or 2, then 7s, 5s and 3s; empty when n has another
@@ -305,7 +305,7 @@ std::vector<int> mixed_radices(int64_t n, const std::vector<int>& set, int rlo) 
   return best;
 }
 
-// C2C of a length with no prime factor above 7, not a power of two, <= kMaxMixedLength
+// C2C of a length with no prime factor above 13, not a power of two, <= kMaxMixedLength
 fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int>& rad, int kb) {
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
@@ -477,7 +477,7 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
   //  3. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
   //  4. the chirp transform.
   if (n <= kMaxMixedLength) {
-    static const std::vector<int> wide = {16, 15, 14, 12, 10, 8, 7, 6, 5, 4, 3, 2};
+    static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
     const std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
     if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_mixed(n, batch, sign, w, 1);
@@ -535,7 +535,7 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     if (n > kMaxBluesteinLengthLarge)
       return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 2^22"), nullptr;
     // p * 2^k in registers, else mixed radix when every prime factor is at
-    // most 7 and every stage has at most 1024 butterflies per thread slot,
+    // most 13 and every stage has at most 1024 butterflies per thread slot,
     // else the chirp transform
     return create_c2c_any(n, batch, sign);
   }

@@ -18,8 +18,8 @@
  *    section 2.3, names mixed radices and other lengths as the extension of
  *    its radix-2 transforms): n = p * 2^k (p in 3, 5, 7, 9, 15, 25, 2^k >= 16,
  *    n <= 16384) in one register-resident kernel (p power-of-two transforms,
- *    twiddles, p-point DFTs); other lengths with no prime factor above 7 by
- *    mixed-radix Stockham stages (radices 2 to 8, 10, 12, 14, 15, 16) when
+ *    twiddles, p-point DFTs); other lengths with no prime factor above 13 by
+ *    mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when
  *    every stage has at most 2048 butterflies (n <= 8192); the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
  *    inside one kernel while m <= 16384, else in three passes (the second

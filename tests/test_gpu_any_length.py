@@ -1,8 +1,8 @@
 """GPU parity for C2C lengths that are not powers of two, against the
 oracle's DFT by the definition: p x 2^k (p in 3, 5, 7, 9, 15, 25) in
-registers, mixed-radix Stockham stages (radices 2..8, 10, 12, 14, 15, 16) for
-the other lengths with no prime factor above 7, Bluestein's chirp transform
-for the rest.
+registers, mixed-radix Stockham stages (radices 2..8, 10..16) for the other
+lengths with no prime factor above 13, Bluestein's chirp transform for the
+rest.
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -21,12 +21,13 @@ TOL = 1e-5
 # radix schedules of some mixed lengths: radices up to 16, one butterfly per
 # thread: 18: 6 3; 42: 7 6; 150: 15 10; 360: 10 6 6; 720: 12 10 6;
 # 840: 12 10 7; 1000: 10 10 10; 1296: 6 6 6 6; 2000: 10 8 5 5;
-# 3000: 10 10 6 5; 4000: 10 10 8 5; 6000: 10 10 10 6.  Radices up to 8, two
-# per thread: 7776: 6 6 6 6 6.
-SMALL = [3, 5, 6, 7, 9, 12, 14, 15, 17, 18, 21, 31, 35, 42, 48, 49, 96, 100, 127, 150, 255, 257, 360,
-         384, 720, 840]
-LARGE = [1000, 1001, 1029, 1296, 1536, 2000, 2047, 2401, 3000, 3072, 4000, 4095, 4097, 5000, 6000,
-         6144, 6250, 6561, 7168, 7776, 8000, 8191]
+# 3000: 10 10 6 5; 4000: 10 10 8 5; 6000: 10 10 10 6; 1001: 13 11 7;
+# 1331: 11 11 11; 2197: 13 13 13; 2002: 14 13 11; 5005: 13 11 7 5.  Radices
+# up to 8, two per thread: 7776: 6 6 6 6 6.
+SMALL = [3, 5, 6, 7, 9, 11, 12, 13, 14, 15, 17, 18, 21, 31, 35, 42, 48, 49, 96, 100, 121, 127, 143, 150,
+         169, 255, 257, 360, 384, 720, 840]
+LARGE = [1000, 1001, 1029, 1296, 1331, 1536, 2000, 2002, 2047, 2197, 2401, 3000, 3072, 4000, 4095,
+         4097, 5000, 5005, 6000, 6144, 6250, 6561, 7168, 7776, 8000, 8191]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -134,8 +135,9 @@ def test_any_length_shift_option_and_sizes():
 
 
 # --------------------------------------------------------------------------
-# lengths above 8192: the chirp transform through two hooked four-step
-# transforms of length m >= 2n - 1
+# lengths above 8192: the chirp transform in three passes over m >= 2n - 1
+# points (the hooked four-step column pass, the fused row pass, the inverse
+# column pass)
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("n", [8193, 10000, 12289, 20000])
 @pytest.mark.parametrize("sign", [-1, 1])
@@ -241,7 +243,7 @@ def test_2d_any_size_shift_and_in_place(ny, nx, shift):
 # buffers beyond 2^31 elements (64-bit row offsets): the seeded block tiled
 # on the device, sampled rows at the start, the middle and the ragged end
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("n,batch", [(4096, (1 << 19) + 3), (1000, (1 << 21) + 5), (1001, (1 << 21) + 7)])
+@pytest.mark.parametrize("n,batch", [(4096, (1 << 19) + 3), (1000, (1 << 21) + 5), (1009, (1 << 21) + 7)])
 def test_beyond_2p31_elements(n, batch):
     import torch
     say(f"c2c n={n} batch={batch} ({batch * n * 8 / 2**30:.1f} GiB per buffer)")
