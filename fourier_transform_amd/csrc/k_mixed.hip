@@ -179,7 +179,8 @@ __host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + 
 
 // One stage of radix R (compile-time, so the butterfly loops are straight
 // code): KB butterflies per thread, b = t + tpl*i.  The first stage gathers
-// its inputs from HBM (times pre), the others from the line in LDS; the last
+// its inputs from HBM (times pre, or sign-flipped at odd indices when flip
+// is set), the others from the line in LDS; the last
 // stage stores to HBM, the others back to LDS.
 template <int S, int KB, int R>
 __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last, uint32_t t, uint32_t tpl,
@@ -196,6 +197,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
         for (int r = 0; r < R; ++r) {
           float2 v = gload_nt(src, b + r * m);
           if (a.pre) v = cmul(v, gload(a.pre, b + r * m));
+          if (a.flip && ((b + r * m) & 1)) v = negate_bits(v);
           x[i][r] = v;
         }
       }

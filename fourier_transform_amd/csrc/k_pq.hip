@@ -1,5 +1,6 @@
 // C2C rows of length n = P * Q with P in {3, 5, 7, 9, 15, 25} and Q a power of
-// two (16 <= Q, n <= 16384), in one kernel with the data in registers.  This
+// two, 8192 < n <= 16384 (one Q per P), in one kernel with the data in
+// registers.  This
 // is the four-step split inside a workgroup ("High Performance Fourier
 // Transforms on GPUs with GLSL", section 2.3 names mixed radices as the way
 // beyond powers of two): element j = p + P q of a row,
@@ -270,7 +271,7 @@ struct PqOp {
   template <int Q>
   struct At {
     static hipError_t run(const PqArgs& a, hipStream_t st) {
-      if constexpr (P * Q > kMaxPqLength || Q < kMinPqPow2) {
+      if constexpr (P * Q > kMaxPqLength || P * Q < kMinPqLength) {
         return hipErrorInvalidValue;
       } else {
         constexpr int C = pq_rows(Q, P);
@@ -286,12 +287,12 @@ struct PqOp {
 template <int S>
 hipError_t launch_pq_sign(int q, int p, const PqArgs& a, hipStream_t st) {
   switch (p) {
-    case 3: return dispatch_pow2<PqOp<3, S>::template At, kMinPqPow2, 4096>(q, a, st);
-    case 5: return dispatch_pow2<PqOp<5, S>::template At, kMinPqPow2, 2048>(q, a, st);
-    case 7: return dispatch_pow2<PqOp<7, S>::template At, kMinPqPow2, 2048>(q, a, st);
-    case 9: return dispatch_pow2<PqOp<9, S>::template At, kMinPqPow2, 1024>(q, a, st);
-    case 15: return dispatch_pow2<PqOp<15, S>::template At, kMinPqPow2, 1024>(q, a, st);
-    case 25: return dispatch_pow2<PqOp<25, S>::template At, kMinPqPow2, 512>(q, a, st);
+    case 3: return dispatch_pow2<PqOp<3, S>::template At, 4096, 4096>(q, a, st);
+    case 5: return dispatch_pow2<PqOp<5, S>::template At, 2048, 2048>(q, a, st);
+    case 7: return dispatch_pow2<PqOp<7, S>::template At, 2048, 2048>(q, a, st);
+    case 9: return dispatch_pow2<PqOp<9, S>::template At, 1024, 1024>(q, a, st);
+    case 15: return dispatch_pow2<PqOp<15, S>::template At, 1024, 1024>(q, a, st);
+    case 25: return dispatch_pow2<PqOp<25, S>::template At, 512, 512>(q, a, st);
     default: return hipErrorInvalidValue;
   }
 }

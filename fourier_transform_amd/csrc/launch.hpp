@@ -140,13 +140,14 @@ struct FoldArgs {
 bool fold_supported(int64_t ny, int64_t nx);
 hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t stream);
 
-// C2C rows of length n = p * q, p in {3, 5, 7, 9, 15, 25}, q a power of two
-// >= kMinPqPow2, n <= kMaxPqLength: p power-of-two transforms of length q in
-// registers (interleaved sub-rows), the twiddle W_n^{p k} (wn: e^{-2 pi i e/n},
-// e < n), and p-point DFTs through LDS.  shift: multiply element j by (-1)^j
-// (n is even).  In place allowed.
+// C2C rows of length n = p * q, p in {3, 5, 7, 9, 15, 25}, q a power of two,
+// kMinPqLength <= n <= kMaxPqLength (shorter lengths of this form take the
+// mixed-radix kernel): p power-of-two transforms of length q in registers
+// (interleaved sub-rows), the twiddle W_n^{p k} (wn: e^{-2 pi i e/n}, e < n),
+// and p-point DFTs through LDS.  shift: multiply element j by (-1)^j (n is
+// even).  In place allowed.
+constexpr int kMinPqLength = 8193;
 constexpr int kMaxPqLength = 16384;
-constexpr int kMinPqPow2 = 16;
 struct PqArgs {
   const float2* in;
   float2* out;
@@ -178,6 +179,7 @@ struct MixedArgs {
   const float2* pre;
   int64_t rows;
   int n, nstages, tpl, lines, kb;
+  int flip;  // 1: negate the elements of odd index on load (exact sign flip; the shift of even n)
   int radix[kMixedMaxStages];
   int ns[kMixedMaxStages];
   int m[kMixedMaxStages];

@@ -338,10 +338,12 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   a.kb = kb;
   a.tpl = (int)((maxm + a.kb - 1) / a.kb);
   a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
-  // shift factors e^{-sign 2 pi i j h/n} and e^{+sign ...}, h = floor(n/2)
-  // ("The 1D fftshift in CUDA by chessboard multiplication", odd case)
+  // shift factors of odd n, e^{-sign 2 pi i j h/n} and e^{+sign ...}, h =
+  // floor(n/2) ("The 1D fftshift in CUDA by chessboard multiplication", odd
+  // case); for even n the kernel flips the signs of odd j exactly instead
   const int64_t h = n / 2;
-  for (int64_t j = 0; j < n; ++j) {
+  if (n % 2 == 0) sh.push_back(make_float2(1.f, 0.f)), ish.push_back(make_float2(1.f, 0.f));
+  for (int64_t j = 0; n % 2 == 1 && j < n; ++j) {
     const float2 w = root((j * h) % n, n);  // e^{-2 pi i jh/n}
     const float2 wc = make_float2(w.x, -w.y);
     sh.push_back(sign < 0 ? wc : w);
@@ -432,12 +434,12 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   return p;
 }
 
-// n = p * q with p in {3, 5, 7, 9, 15, 25} and q a power of two >= kMinPqPow2,
-// n <= kMaxPqLength: the odd factor p (largest of the list first), else 0
+// n = p * q with p in {3, 5, 7, 9, 15, 25} and q a power of two, kMinPqLength
+// <= n <= kMaxPqLength: the odd factor p, else 0
 int pq_factor(int64_t n) {
-  if (n > kMaxPqLength) return 0;
+  if (n < kMinPqLength || n > kMaxPqLength) return 0;
   for (int p : {25, 15, 9, 7, 5, 3})
-    if (n % p == 0 && is_pow2(n / p) && n / p >= kMinPqPow2) return p;
+    if (n % p == 0 && is_pow2(n / p)) return p;
   return 0;
 }
 
@@ -463,11 +465,14 @@ fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
   return p;
 }
 
-// any-length C2C plan: p * 2^k in registers when possible, then mixed radix,
+// any-length C2C plan: mixed radix when possible, then p * 2^k in registers,
 // else the chirp transform
 fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
-  if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
-  // Schedules, in order:
+  // Up to 8192 points the mixed-radix kernel, above that p * 2^k in
+  // registers (with each mixed-radix stage compiled for its radix it beat
+  // the p * 2^k kernel on most lengths it shares, e.g. 3072: 216 against
+  // 310 us, 6144: 266 against 312 us; 384 and 768 were 5 % slower), else the
+  // chirp transform.  Mixed-radix schedules, in order:
   //  1. radices up to 16, one butterfly per thread (1000: 10 10 10, three
   //     stages).  Measured against the fixed order of step 2 on MI355X with
   //     each stage compiled for its radix: better or equal for 1000, 2000,
@@ -488,6 +493,7 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
         return create_mixed(n, batch, sign, r, kMixedButterflies);
     }
   }
+  if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
   return create_bluestein(n, batch, sign);
 }
 
@@ -806,7 +812,10 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     MixedArgs a = p->mx;
     a.in = src;
     a.out = dst;
-    a.pre = p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
+    // even n: both shifts are the exact sign flip (-1)^j; odd n: the ramps
+    const bool even = p->n % 2 == 0;
+    a.flip = even && p->shift ? 1 : 0;
+    a.pre = even ? nullptr : p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
     e = launch_mixed(p->sign, a, stream);
   } else if (p->bluestein && p->fourstep) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;

@@ -16,11 +16,11 @@
  *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
  *    2^28), and any other length from 3 to 2^22 (the GLSL dissertation,
  *    section 2.3, names mixed radices and other lengths as the extension of
- *    its radix-2 transforms): n = p * 2^k (p in 3, 5, 7, 9, 15, 25, 2^k >= 16,
- *    n <= 16384) in one register-resident kernel (p power-of-two transforms,
- *    twiddles, p-point DFTs); other lengths with no prime factor above 13 by
- *    mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when
- *    every stage has at most 2048 butterflies (n <= 8192); the others by Bluestein's
+ *    its radix-2 transforms): lengths with no prime factor above 13 by
+ *    mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every stage
+ *    has at most 2048 butterflies (n <= 8192); n = p * 2^k (p in 3, 5, 7, 9,
+ *    15, 25, 8192 < n <= 16384) in one register-resident kernel (p
+ *    power-of-two transforms, twiddles, p-point DFTs); the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,
  *    inside one kernel while m <= 16384, else in three passes (the second
  *    holds the inner factors of both transforms) through a scratch buffer of
@@ -104,9 +104,10 @@ enum fft_option {
   /* 1: multiply the input by (-1)^j in 1D, (-1)^(i+j) in 2D, while loading it,
    * which moves the zero frequency to the middle of the output (the chessboard
    * fftshift: "The 1D fftshift in CUDA by chessboard multiplication").  For
-   * power-of-two lengths the factor is applied by flipping the sign bits of
-   * both parts, before any arithmetic, so the result is bitwise the transform
-   * of the negated input.  For the other 1D lengths the factor is
+   * power-of-two lengths, and even lengths of the mixed-radix and p * 2^k
+   * kernels, the factor is applied by flipping the sign bits of both parts,
+   * before any arithmetic, so the result is bitwise the transform of the
+   * negated input.  For the other 1D lengths the factor is
    * e^{-sign 2 pi i j floor(n/2)/n}, a table applied on load (folded into the
    * chirp on the chirp-transform path; the page's odd case: a full complex
    * exponential), and bin 0 lands at index floor(n/2) for odd n as well.

@@ -265,7 +265,8 @@ def test_beyond_2p31_elements(n, batch):
 
 
 # --------------------------------------------------------------------------
-# p x 2^k in one register-resident kernel (p in 3, 5, 7, 9, 15, 25)
+# p x 2^k (p in 3, 5, 7, 9, 15, 25): above 8192 points in one
+# register-resident kernel, up to 8192 in the mixed-radix kernel
 # --------------------------------------------------------------------------
 PQ_N = [48, 80, 240, 400, 576, 960, 1792, 2304, 2560, 3840, 4608, 6400, 9216, 10240, 12288, 12800,
         14336, 15360]
@@ -280,10 +281,11 @@ def test_pq_sweep(n, sign):
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
 
 
-@pytest.mark.parametrize("n", [48, 1536, 15360])
-def test_pq_shift_bit_exact_and_in_place(n):
+@pytest.mark.parametrize("n", [6, 48, 1000, 1536, 2002, 15360])
+def test_even_shift_bit_exact_and_in_place(n):
     """The shift is the exact sign flip of (-1)^j (n even): bitwise the
-    transform of the negated input; and the rotation of the oracle's."""
+    transform of the negated input; and the rotation of the oracle's.  Up to
+    2002 the mixed-radix kernel, 15360 the p x 2^k kernel."""
     from gpu_helpers import negate_odd
     x = W.uniform_c64((3, n), np.random.default_rng(n + 9))
     ys = c2c(x, -1, shift=1)
