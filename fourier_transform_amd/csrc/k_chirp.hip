@@ -34,10 +34,16 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr bool WL = T <= 64;
   constexpr int FP = E + 1;
   using L = RowLds<N1, SPLIT>;
-  static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) + C * FP * sizeof(float2) <= kLdsBudgetBytes,
-                "LDS budget");
+  constexpr int LB = L::size(C) * sizeof(lds_elem_t<SPLIT>) + C * FP * sizeof(float2);
+  static_assert(LB <= kLdsBudgetBytes, "LDS budget");
+  // stage-1 twiddles from an LDS copy when it fits (as in k_fs_rows), for the
+  // forward and the inverse stages
+  constexpr int TW1 = fs_tw1_elems<N1, E>();
+  constexpr bool LTW = sched_stages(N1, E) >= 2 && LB + TW1 * sizeof(float2) <= kLdsBudgetBytes;
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
   __shared__ float2 ftab[C * FP];
+  __shared__ float2 twl[LTW ? TW1 : 1];
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -52,6 +58,8 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   const uint32_t mask = (1u << a.bits) - 1u;
   constexpr int FQ = (C * E + NT - 1) / NT;
   float2 fh[FQ], fl[FQ];
+  float2 tq[TQ];
+  if constexpr (LTW) fs_fetch_tw1<N1, E, NT, TQ>(tq, a.tw, tid);
 #pragma unroll
   for (int i = 0; i < FQ; ++i) {
     const int q = tid + NT * i;
@@ -68,29 +76,59 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
   }
+  // bins k = k2 + n2*k1, k1 = u + T*m are multiplied by the chirp's transform
+  // after the forward stages.  With 16 values per thread its loads and those
+  // of W_m^{k2*u} are issued here, behind the row's loads, so the workgroup
+  // waits for memory once; with 64 values per thread the VGPR budget keeps
+  // them after the stages (in groups of 8).
+  constexpr bool EARLY = E <= 16;
+  const float2* bt = a.pre + (int64_t)k20 * N1;  // uniform base, 32-bit offsets
+  const uint32_t bo = (uint32_t)line * N1 + (uint32_t)u;
+  const uint32_t eu = k2 * (uint32_t)u;
+  float2 bv[EARLY ? E : 1];
+  float2 uh, ul;
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int m = 0; m < E; ++m) bv[m] = gload(bt, bo + (uint32_t)(T * m));
+    uh = gload(a.thi, eu >> a.bits);
+    ul = gload(a.tlo, eu & mask);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < FQ; ++i) {
     const int q = tid + NT * i;
     if (q < C * E) ftab[(q / E) * FP + q % E] = cmul(fh[i], fl[i]);
   }
-  run_stages<N1, E, -1, WL, L, SPLIT>(v, lds, a.tw, u, line);
-  // bins k = k2 + n2*k1, k1 = u + T*m: times the chirp's transform (loads in
-  // groups of 8, not hoisted above the stages: VGPR budget)
+  const TwLdsStage<1> tws{a.tw, twl, (uint32_t)sched_tw_off(N1, E, 1)};
+  const auto tw = [&]() {
+    if constexpr (LTW) {
+      return tws;
+    } else {
+      return a.tw;
+    }
+  }();
+  if constexpr (LTW) {
+    fs_store_tw1<N1, E, NT, TQ>(twl, tq, tid);
+    lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
+  }
+  run_stages<N1, E, -1, WL, L, SPLIT>(v, lds, tw, u, line);
   __builtin_amdgcn_sched_barrier(0);
-  const float2* bt = a.pre + (int64_t)k20 * N1;  // uniform base, 32-bit offsets
-  const uint32_t bo = (uint32_t)line * N1 + (uint32_t)u;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
-    v[m] = cmul(v[m], gload(bt, bo + (uint32_t)(T * m)));
-    if constexpr (E > 16) {
+    if constexpr (EARLY) {
+      v[m] = cmul(v[m], bv[m]);
+    } else {
+      v[m] = cmul(v[m], gload(bt, bo + (uint32_t)(T * m)));
       if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
   }
   lds_barrier();  // the forward stages' last reads precede the inverse stages' writes; publishes ftab
-  run_stages<N1, E, 1, WL, L, SPLIT>(v, lds, a.tw, u, line);
-  const uint32_t eu = k2 * (uint32_t)u;  // fetched here: live across the stages it would spill
-  const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
+  run_stages<N1, E, 1, WL, L, SPLIT>(v, lds, tw, u, line);
+  if constexpr (!EARLY) {  // fetched here: live across the stages it would spill
+    uh = gload(a.thi, eu >> a.bits);
+    ul = gload(a.tlo, eu & mask);
+  }
+  const float2 wu = cmul(uh, ul);
   float2* dst = a.out + (g0 + line) * N1;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
