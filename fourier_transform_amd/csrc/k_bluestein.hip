@@ -23,8 +23,8 @@ __global__ __launch_bounds__(rows_threads(M) * C) void k_bluestein(BluesteinArgs
   constexpr bool SPLIT = rows_split(M);
   constexpr int T = M / E;
   constexpr bool WL = T <= 64;  // every line inside one wavefront
-  using L = RowLds<M, SPLIT>;
-  static_assert(row_lds_bytes(M, C, SPLIT) <= kLdsBudgetBytes, "LDS budget");
+  using L = RowLds<M, SPLIT, E>;
+  static_assert(row_lds_bytes(M, C, SPLIT, E) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;

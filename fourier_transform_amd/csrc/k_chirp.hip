@@ -33,7 +33,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr int NT = C * T;
   constexpr bool WL = T <= 64;
   constexpr int FP = E + 1;
-  using L = RowLds<N1, SPLIT>;
+  using L = RowLds<N1, SPLIT, E>;
   constexpr int LB = L::size(C) * sizeof(lds_elem_t<SPLIT>) + C * FP * sizeof(float2);
   static_assert(LB <= kLdsBudgetBytes, "LDS budget");
   // stage-1 twiddles from an LDS copy when it fits (as in k_fs_rows), for the

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   constexpr int T = N / E;   // threads per row
   constexpr int MP = E / NA;  // columns per thread in the step across rows
   constexpr bool WL = T <= 64;
-  using L = RowLds<N, true>;
+  using L = RowLds<N, true, E>;
   static_assert(L::size(NA) * sizeof(float) <= kLdsBudgetBytes, "LDS budget");
   static_assert(T % 2 == 0 && MP >= 1, "fold shape");
   constexpr int NT = NA * T;

@@ -28,8 +28,8 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   constexpr bool SPLIT = rows_split(N);
   constexpr int T = N / E;
   constexpr bool WL = T <= 64;  // every line inside one wavefront
-  using L = RowLds<N, SPLIT>;
-  static_assert(row_lds_bytes(N, C, SPLIT) <= kLdsBudgetBytes, "LDS budget");
+  using L = RowLds<N, SPLIT, E>;
+  static_assert(row_lds_bytes(N, C, SPLIT, E) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
 
   const int tid = threadIdx.x;
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr int T = N1 / E;
   constexpr int NT = C * T;
   constexpr bool WL = T <= 64;
-  using L = RowLds<N1, SPLIT>;
+  using L = RowLds<N1, SPLIT, E>;
   static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   constexpr int TW1 = fs_tw1_elems<N1, E>();
   constexpr bool LTW = sched_stages(N1, E) >= 2 &&

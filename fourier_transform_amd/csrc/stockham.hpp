@@ -272,12 +272,19 @@ __device__ __forceinline__ void dft(float2* x) {
 // other (row lanes: consecutive threads walk along a line) or interleaved
 // (column lanes: consecutive threads walk across lines).  Indices are padded
 // so that the power-of-two strides of the Stockham writes, the slot reads and
-// the transposed reads spread over the banks; row lines are an odd number of
-// elements apart, so reading across lines (the transposing store) changes
-// bank too.  The paddings were chosen with a bank model of every exchange
-// pattern used here (32 or 64 banks, 32- or 64-lane issue groups):
-//   row lanes:            line * P + p(i),  p(i) = i + i/G,  P = p(N) + 1,
-//                         G = 32 (8-byte elements) or 64 (4-byte)
+// the transposed reads spread over the banks.  The bank model: 32 banks of 4
+// bytes serving 128 bytes per clock, so a 4-byte access serves 32 lanes per
+// clock and an 8-byte access 16; a clock's cost is the largest number of
+// distinct dwords on one bank.  It reproduces the bank-conflict and
+// LDS-active cycles that the SQ counters report for these kernels on gfx950.
+//   row lanes:            line * P + p(i),  p(i) = i + i/G.
+//                         8-byte: G = 16, the stride (radix 16) between the
+//                         lanes of a first-stage write; P = p(N) + 1 is odd,
+//                         so 16 lines read at one index (the transposing
+//                         store) fall on distinct bank pairs.
+//                         4-byte: G = E (32 or 64), again the first-stage
+//                         radix; P = 2 mod 32, so 16 lines read at two
+//                         neighbouring indices fill the 32 banks once.
 //   column lanes, 8-byte: p(a) = a + a/32 + 8*(a/256),  a = i*C + line
 //   column lanes, 4-byte: p(a) = a + a/64
 // SPLIT: the exchange moves 4-byte halves (real, then imaginary parts).
@@ -291,10 +298,13 @@ __device__ __forceinline__ void dft(float2* x) {
 // loops then share a handful of runtime addresses instead of padding every
 // index separately.
 // ---------------------------------------------------------------------------
-constexpr int row_pad_g(bool split) { return split ? 64 : 32; }
-constexpr int row_pitch(int n, bool split) { return n + n / row_pad_g(split) + 1; }
-constexpr int row_lds_elems(int n, int lines, bool split) {
-  return (lines - 1) * row_pitch(n, split) + (n - 1) + (n - 1) / row_pad_g(split) + 1;
+constexpr int row_pad_g(bool split, int e) { return split ? (e >= 64 ? 64 : 32) : 16; }
+constexpr int row_pitch(int n, bool split, int e) {
+  const int p = n + n / row_pad_g(split, e) + 1;
+  return split ? p + (34 - p % 32) % 32 : p;
+}
+constexpr int row_lds_elems(int n, int lines, bool split, int e) {
+  return (lines - 1) * row_pitch(n, split, e) + (n - 1) + (n - 1) / row_pad_g(split, e) + 1;
 }
 template <bool SPLIT>
 __host__ __device__ constexpr uint32_t col_pad(uint32_t a) {
@@ -304,10 +314,10 @@ constexpr int col_lds_elems(int n, int lines, bool split) {
   return (int)(split ? col_pad<true>((uint32_t)(n * lines - 1)) : col_pad<false>((uint32_t)(n * lines - 1))) + 1;
 }
 
-template <int N, bool SPLIT = false>
+template <int N, bool SPLIT = false, int E = 16>
 struct RowLds {
-  static constexpr uint32_t G = row_pad_g(SPLIT);
-  static constexpr uint32_t P = row_pitch(N, SPLIT);
+  static constexpr uint32_t G = row_pad_g(SPLIT, E);
+  static constexpr uint32_t P = row_pitch(N, SPLIT, E);
   __host__ __device__ static constexpr uint32_t pad(uint32_t i) { return i + i / G; }
   __device__ __forceinline__ static int at(int line, int i) {
     return (int)((uint32_t)line * P + pad((uint32_t)i));
@@ -319,7 +329,7 @@ struct RowLds {
     constexpr uint32_t q = (uint32_t)K - r;
     return (int)((uint32_t)line * P + pad((uint32_t)i0 + ra) + (r - ra) + pad(q));
   }
-  static constexpr int size(int lines) { return row_lds_elems(N, lines, SPLIT); }
+  static constexpr int size(int lines) { return row_lds_elems(N, lines, SPLIT, E); }
 };
 template <int N, int C, bool SPLIT = false>
 struct ColLds {
