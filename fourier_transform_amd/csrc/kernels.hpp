@@ -573,7 +573,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   constexpr int T = N1 / E;
   constexpr int NT = C * T;
   constexpr bool WL = T <= 64;
-  using L = RowLds<N1, SPLIT, E>;
+  using L = RowLds<N1, SPLIT, E, true>;  // transposed read-back
   static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   constexpr int TW1 = fs_tw1_elems<N1, E>();
   constexpr bool LTW = sched_stages(N1, E) >= 2 &&

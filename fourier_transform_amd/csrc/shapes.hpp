@@ -13,8 +13,8 @@ namespace fftamd {
 // ---------------------------------------------------------------------------
 constexpr int threads_per_line(int n) { return n / sched_e(n); }
 // LDS bytes of c lines of length n (layouts: stockham.hpp RowLds / ColLds)
-constexpr int row_lds_bytes(int n, int c, bool split = false, int e = 16) {
-  return row_lds_elems(n, c, split, e) * (split ? 4 : 8);
+constexpr int row_lds_bytes(int n, int c, bool split = false, int e = 16, bool xread = false) {
+  return row_lds_elems(n, c, split, e, xread) * (split ? 4 : 8);
 }
 constexpr int col_lds_bytes(int n, int c, bool split = false) {
   return col_lds_elems(n, c, split) * (split ? 4 : 8);
@@ -41,7 +41,7 @@ constexpr int rows_lines(int n) { return rows_threads(n) >= 256 ? 1 : 256 / rows
 constexpr int kSplitValues = 64;
 constexpr bool tile_fits(int n, int e, int c, bool split, bool rowlanes) {
   return e <= n && c * (n / e) <= kMaxThreads &&
-         (rowlanes ? row_lds_bytes(n, c, split, e) : col_lds_bytes(n, c, split)) <= kLdsBudgetBytes;
+         (rowlanes ? row_lds_bytes(n, c, split, e, true) : col_lds_bytes(n, c, split)) <= kLdsBudgetBytes;
 }
 constexpr int tile_c(int n, int e, bool split, bool rowlanes) {
   int c = 16;

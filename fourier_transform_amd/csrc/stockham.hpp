@@ -272,19 +272,25 @@ __device__ __forceinline__ void dft(float2* x) {
 // other (row lanes: consecutive threads walk along a line) or interleaved
 // (column lanes: consecutive threads walk across lines).  Indices are padded
 // so that the power-of-two strides of the Stockham writes, the slot reads and
-// the transposed reads spread over the banks.  The bank model: 32 banks of 4
-// bytes serving 128 bytes per clock, so a 4-byte access serves 32 lanes per
-// clock and an 8-byte access 16; a clock's cost is the largest number of
-// distinct dwords on one bank.  It reproduces the bank-conflict and
-// LDS-active cycles that the SQ counters report for these kernels on gfx950.
+// the transposed reads spread over the banks.  The bank model for reads and
+// 4-byte accesses, fitted to the SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE
+// counters of these kernels and of probes with fixed access patterns on
+// gfx950: a clock's cost is the largest number of distinct dwords on one
+// bank; 8-byte reads serve 32 lanes per clock over 64 banks, 4-byte accesses
+// 32 lanes per clock over 32 banks.  (The 8-byte writes of the first stage,
+// lanes 16 elements apart, still cost one extra clock in four whichever
+// padding period of 16, 32 or 64 is used; that was measured, not modelled.)
 //   row lanes:            line * P + p(i),  p(i) = i + i/G.
-//                         8-byte: G = 16, the stride (radix 16) between the
-//                         lanes of a first-stage write; P = p(N) + 1 is odd,
-//                         so 16 lines read at one index (the transposing
-//                         store) fall on distinct bank pairs.
-//                         4-byte: G = E (32 or 64), again the first-stage
-//                         radix; P = 2 mod 32, so 16 lines read at two
-//                         neighbouring indices fill the 32 banks once.
+//                         8-byte: G = 32, so 32 consecutive elements stay in
+//                         one block of the 64 banks.  P = T mod 32 for lines
+//                         of T < 32 threads, so the lines that share a clock
+//                         tile the banks.  Lines that are also read across
+//                         (the transposed read-back of the four-step row
+//                         pass: 16 lines at two neighbouring indices per
+//                         clock) take P = 6 mod 32, best for every T there.
+//                         4-byte: G = E (32 or 64), the stride between the
+//                         lanes of a first-stage write; P = 2 mod 32, so the
+//                         16 lines of a read-back clock fill the 32 banks.
 //   column lanes, 8-byte: p(a) = a + a/32 + 8*(a/256),  a = i*C + line
 //   column lanes, 4-byte: p(a) = a + a/64
 // SPLIT: the exchange moves 4-byte halves (real, then imaginary parts).
@@ -298,13 +304,17 @@ __device__ __forceinline__ void dft(float2* x) {
 // loops then share a handful of runtime addresses instead of padding every
 // index separately.
 // ---------------------------------------------------------------------------
-constexpr int row_pad_g(bool split, int e) { return split ? (e >= 64 ? 64 : 32) : 16; }
-constexpr int row_pitch(int n, bool split, int e) {
-  const int p = n + n / row_pad_g(split, e) + 1;
-  return split ? p + (34 - p % 32) % 32 : p;
+constexpr int row_pad_g(bool split, int e) { return split && e >= 64 ? 64 : 32; }
+constexpr int row_pad(int i, bool split, int e) { return i + i / row_pad_g(split, e); }
+// xread: lines are also read across (16 lines at two neighbouring indices)
+constexpr int row_pitch(int n, bool split, int e, bool xread) {
+  const int p = row_pad(n, split, e) + 1;
+  const int t = n / e;
+  const int target = split ? 2 : xread ? 6 : t < 32 ? t : 1;
+  return p + ((target - p % 32) % 32 + 32) % 32;
 }
-constexpr int row_lds_elems(int n, int lines, bool split, int e) {
-  return (lines - 1) * row_pitch(n, split, e) + (n - 1) + (n - 1) / row_pad_g(split, e) + 1;
+constexpr int row_lds_elems(int n, int lines, bool split, int e, bool xread = false) {
+  return (lines - 1) * row_pitch(n, split, e, xread) + row_pad(n - 1, split, e) + 1;
 }
 template <bool SPLIT>
 __host__ __device__ constexpr uint32_t col_pad(uint32_t a) {
@@ -314,10 +324,10 @@ constexpr int col_lds_elems(int n, int lines, bool split) {
   return (int)(split ? col_pad<true>((uint32_t)(n * lines - 1)) : col_pad<false>((uint32_t)(n * lines - 1))) + 1;
 }
 
-template <int N, bool SPLIT = false, int E = 16>
+template <int N, bool SPLIT = false, int E = 16, bool XREAD = false>
 struct RowLds {
   static constexpr uint32_t G = row_pad_g(SPLIT, E);
-  static constexpr uint32_t P = row_pitch(N, SPLIT, E);
+  static constexpr uint32_t P = row_pitch(N, SPLIT, E, XREAD);
   __host__ __device__ static constexpr uint32_t pad(uint32_t i) { return i + i / G; }
   __device__ __forceinline__ static int at(int line, int i) {
     return (int)((uint32_t)line * P + pad((uint32_t)i));
@@ -329,7 +339,7 @@ struct RowLds {
     constexpr uint32_t q = (uint32_t)K - r;
     return (int)((uint32_t)line * P + pad((uint32_t)i0 + ra) + (r - ra) + pad(q));
   }
-  static constexpr int size(int lines) { return row_lds_elems(N, lines, SPLIT, E); }
+  static constexpr int size(int lines) { return row_lds_elems(N, lines, SPLIT, E, XREAD); }
 };
 template <int N, int C, bool SPLIT = false>
 struct ColLds {
