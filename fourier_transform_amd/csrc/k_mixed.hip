@@ -174,7 +174,14 @@ __device__ __forceinline__ void dft_small(float2* x) {
   }
 }
 
-__host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + (i >> 5); }
+// LDS index of element i of a line: with PAD one pad element after every 32
+// elements.  The stage reads are runs of consecutive elements starting at
+// offsets r*m that are rarely multiples of 32, which a pad splits; the
+// first-stage writes are R elements apart, which a pad spreads over the banks
+// when R = 16.  The plan chooses; the choice is compiled in (as a runtime
+// shift it cost 4-9 %: no immediate LDS offsets).
+template <bool PAD>
+__host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return PAD ? i + (i >> 5) : i; }
 }  // namespace
 
 // One stage of radix R (compile-time, so the butterfly loops are straight
@@ -182,7 +189,7 @@ __host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return i + 
 // its inputs from HBM (times pre, or sign-flipped at odd indices when flip
 // is set), the others from the line in LDS; the last
 // stage stores to HBM, the others back to LDS.
-template <int S, int KB, int R>
+template <int S, int KB, int R, bool PAD>
 __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last, uint32_t t, uint32_t tpl,
                                             bool valid, const float2* src, float2* dst, float2* L) {
   const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
@@ -208,7 +215,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
       const uint32_t b = t + tpl * i;
       if (b < m) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[i][r] = L[mixed_pad(b + r * m)];
+        for (int r = 0; r < R; ++r) x[i][r] = L[mixed_pad<PAD>(b + r * m)];
       }
     }
     lds_barrier();  // every read of this stage precedes its writes
@@ -236,7 +243,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
         const uint32_t j = ns == 1 ? 0u : b - __umulhi(b, a.ns_magic[s]) * ns;
         const uint32_t base = (b - j) * (uint32_t)R + j;
 #pragma unroll
-        for (int r = 0; r < R; ++r) L[mixed_pad(base + r * ns)] = x[i][r];
+        for (int r = 0; r < R; ++r) L[mixed_pad<PAD>(base + r * ns)] = x[i][r];
       }
     }
     lds_barrier();
@@ -257,7 +264,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
 // 1 x 16), up to 1024 threads (so at most 128 VGPRs).  The radix of each
 // stage selects a compiled stage (radices of the schedules: 2..8, and with
 // RMAX = 16 also 10 .. 16).
-template <int S, int KB, int RMAX>
+template <int S, int KB, int RMAX, bool PAD>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -268,12 +275,12 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   const int64_t row = (int64_t)blockIdx.x * a.lines + line;
   const bool valid = row < a.rows;
   const uint32_t n = (uint32_t)a.n;
-  float2* L = smem + (size_t)line * (mixed_pad(n) + 1);
+  float2* L = smem + (size_t)line * (mixed_pad<PAD>(n) + 1);
   const float2* src = a.in + row * n;
   float2* dst = a.out + row * n;
   for (int s = 0; s < a.nstages; ++s) {
     const bool last = s + 1 == a.nstages;
-#define FFTAMD_STAGE(R) mixed_stage<S, KB, R>(a, s, last, t, tpl, valid, src, dst, L)
+#define FFTAMD_STAGE(R) mixed_stage<S, KB, R, PAD>(a, s, last, t, tpl, valid, src, dst, L)
     switch (a.radix[s]) {
       case 2: FFTAMD_STAGE(2); break;
       case 3: FFTAMD_STAGE(3); break;
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
 
 hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   if (a.n < 2 || a.n > kMaxMixedLength || a.nstages < 1 || a.nstages > kMixedMaxStages || a.tpl < 1 ||
-      a.lines < 1 || a.tpl * a.lines > 1024 || a.rows < 1 || (a.kb != 1 && a.kb != 2))
+      a.lines < 1 || a.tpl * a.lines > 1024 || a.rows < 1 || (a.kb != 1 && a.kb != 2) || (a.pad != 0 && a.pad != 1))
     return hipErrorInvalidValue;
   int rmax = 0;
   for (int s = 0; s < a.nstages; ++s) {
@@ -314,18 +321,27 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   uint32_t grid;
   hipError_t e = grid_of(a.rows, a.lines, &grid);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)a.lines * (mixed_pad((uint32_t)a.n) + 1) * sizeof(float2);
+  const size_t lds =
+      (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
   if (rmax > 8) {
-    if (sign < 0)
-      hipLaunchKernelGGL((k_mixed<-1, 1, 16>), dim3(grid), block, lds, st, a);
-    else
-      hipLaunchKernelGGL((k_mixed<1, 1, 16>), dim3(grid), block, lds, st, a);
+    if (a.pad) {
+      if (sign < 0)
+        hipLaunchKernelGGL((k_mixed<-1, 1, 16, true>), dim3(grid), block, lds, st, a);
+      else
+        hipLaunchKernelGGL((k_mixed<1, 1, 16, true>), dim3(grid), block, lds, st, a);
+    } else if (sign < 0) {
+      hipLaunchKernelGGL((k_mixed<-1, 1, 16, false>), dim3(grid), block, lds, st, a);
+    } else {
+      hipLaunchKernelGGL((k_mixed<1, 1, 16, false>), dim3(grid), block, lds, st, a);
+    }
+  } else if (a.pad) {
+    return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    hipLaunchKernelGGL((k_mixed<-1, 2, 8>), dim3(grid), block, lds, st, a);
+    hipLaunchKernelGGL((k_mixed<-1, 2, 8, false>), dim3(grid), block, lds, st, a);
   } else {
-    hipLaunchKernelGGL((k_mixed<1, 2, 8>), dim3(grid), block, lds, st, a);
+    hipLaunchKernelGGL((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
   }
   return hipGetLastError();
 }

@@ -180,6 +180,7 @@ struct MixedArgs {
   int64_t rows;
   int n, nstages, tpl, lines, kb;
   int flip;  // 1: negate the elements of odd index on load (exact sign flip; the shift of even n)
+  int pad;  // LDS line: 1 = one pad element after every 32 elements, 0 = none
   int radix[kMixedMaxStages];
   int ns[kMixedMaxStages];
   int m[kMixedMaxStages];

@@ -336,6 +336,13 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   }
   if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
   a.kb = kb;
+  // LDS padding: one element every 32 when the first stage is radix 16 (its
+  // writes are 16 elements apart), none otherwise (the stage reads are runs
+  // that a pad splits).  Measured on MI355X against padding every schedule:
+  // first radix 16 (1280, 1536, 1792, 2560, 3072, 3584) 3-8 % faster with the
+  // pad; first radix 8, 10, 12, 14 (48 ... 7168) equal or up to 7.6 % faster
+  // without it (6400 383.7 -> 357.7 us, 7168 379.9 -> 351.2 us per 512 MiB).
+  a.pad = rad[0] == 16 ? 1 : 0;
   a.tpl = (int)((maxm + a.kb - 1) / a.kb);
   // 256 threads per workgroup where a line has fewer.  Filling the last
   // wavefront with more lines per workgroup (n = 1000: 7 lines, 700 of 704
