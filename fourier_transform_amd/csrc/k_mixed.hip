@@ -182,20 +182,26 @@ __device__ __forceinline__ void dft_small(float2* x) {
 // shift it cost 4-9 %: no immediate LDS offsets).
 template <bool PAD>
 __host__ __device__ __forceinline__ uint32_t mixed_pad(uint32_t i) { return PAD ? i + (i >> 5) : i; }
+// LDS elements of one Rader line of N values: the padded line, x_0 and A_0
+__host__ __device__ __forceinline__ uint32_t rader_line(uint32_t N, bool pad) {
+  return (pad ? mixed_pad<true>(N) : mixed_pad<false>(N)) + 2;
+}
 }  // namespace
 
 // One stage of radix R (compile-time, so the butterfly loops are straight
 // code): KB butterflies per thread, b = t + tpl*i.  The first stage gathers
 // its inputs from HBM (times pre, or sign-flipped at odd indices when flip
-// is set), the others from the line in LDS; the last
-// stage stores to HBM, the others back to LDS.
-template <int S, int KB, int R, bool PAD>
+// is set), the others from the line in LDS; the last stage stores to HBM,
+// the others back to LDS.  IO bit 1: the first stage reads the line in LDS
+// too; IO bit 2: the last stage writes the line in LDS in natural order
+// (transforms whose input and output stay on chip).
+template <int S, int KB, int R, bool PAD, int IO = 0>
 __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last, uint32_t t, uint32_t tpl,
                                             bool valid, const float2* src, float2* dst, float2* L) {
   const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
   float2 x[KB][R];
   // gather the inputs of this thread's butterflies: b + r*m
-  if (s == 0) {
+  if (s == 0 && !(IO & 1)) {
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       const uint32_t b = t + tpl * i;
@@ -247,6 +253,16 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
       }
     }
     lds_barrier();
+  } else if constexpr ((IO & 2) != 0) {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      const uint32_t b = t + tpl * i;
+      if (b < m) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) L[mixed_pad<PAD>(b + r * ns)] = x[i][r];
+      }
+    }
+    lds_barrier();
   } else if (valid) {
     // last stage: ns = m and j = b, so output q of butterfly b is b + q m
 #pragma unroll
@@ -264,23 +280,14 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
 // 1 x 16), up to 1024 threads (so at most 128 VGPRs).  The radix of each
 // stage selects a compiled stage (radices of the schedules: 2..8, and with
 // RMAX = 16 also 10 .. 16).
-template <int S, int KB, int RMAX, bool PAD>
-__global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
-  extern __shared__ float4 smem4[];
-  float2* smem = reinterpret_cast<float2*>(smem4);
-  const uint32_t tpl = (uint32_t)a.tpl;
-  const int tid = threadIdx.x;
-  const int line = tid / (int)tpl;
-  const uint32_t t = (uint32_t)(tid - line * (int)tpl);
-  const int64_t row = (int64_t)blockIdx.x * a.lines + line;
-  const bool valid = row < a.rows;
-  const uint32_t n = (uint32_t)a.n;
-  float2* L = smem + (size_t)line * (mixed_pad<PAD>(n) + 1);
-  const float2* src = a.in + row * n;
-  float2* dst = a.out + row * n;
+// every stage of the schedule, each compiled for its radix (a switch on the
+// schedule's radix selects it; radices 2..8, and with RMAX = 16 also 10..16)
+template <int S, int KB, int RMAX, bool PAD, int IO>
+__device__ __forceinline__ void mixed_stages(const MixedArgs& a, uint32_t t, uint32_t tpl, bool valid,
+                                             const float2* src, float2* dst, float2* L) {
   for (int s = 0; s < a.nstages; ++s) {
     const bool last = s + 1 == a.nstages;
-#define FFTAMD_STAGE(R) mixed_stage<S, KB, R, PAD>(a, s, last, t, tpl, valid, src, dst, L)
+#define FFTAMD_STAGE(R) mixed_stage<S, KB, R, PAD, IO>(a, s, last, t, tpl, valid, src, dst, L)
     switch (a.radix[s]) {
       case 2: FFTAMD_STAGE(2); break;
       case 3: FFTAMD_STAGE(3); break;
@@ -307,17 +314,95 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   }
 }
 
-hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
+// KB butterflies of at most RMAX values per thread and stage (2 x 8 or
+// 1 x 16), up to 1024 threads (so at most 128 VGPRs).
+template <int S, int KB, int RMAX, bool PAD>
+__global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
+  extern __shared__ float4 smem4[];
+  float2* smem = reinterpret_cast<float2*>(smem4);
+  const uint32_t tpl = (uint32_t)a.tpl;
+  const int tid = threadIdx.x;
+  const int line = tid / (int)tpl;
+  const uint32_t t = (uint32_t)(tid - line * (int)tpl);
+  const int64_t row = (int64_t)blockIdx.x * a.lines + line;
+  const bool valid = row < a.rows;
+  const uint32_t n = (uint32_t)a.n;
+  float2* L = smem + (size_t)line * (mixed_pad<PAD>(n) + 1);
+  mixed_stages<S, KB, RMAX, PAD, 0>(a, t, tpl, valid, a.in + row * n, a.out + row * n, L);
+}
+
+// Rader's transform of a prime length p (see launch.hpp), one line of
+// N = p - 1 values in LDS per row: load the row coalesced and place x_j
+// (j >= 1) at position (-ind j) mod N, the forward N-point transform, the
+// product with conv (A_0 = sum of x_j, j >= 1, kept aside), the inverse
+// N-point transform, then X_0 = x_0 + A_0 and X_j = x_0 + c_(ind j), stored
+// coalesced.  The pre factors (the shift of odd lengths) apply on load.
+template <bool PAD>
+__global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
+  extern __shared__ float4 smem4[];
+  float2* smem = reinterpret_cast<float2*>(smem4);
+  const uint32_t tpl = (uint32_t)a.tpl;
+  const int tid = threadIdx.x;
+  const int line = tid / (int)tpl;
+  const uint32_t t = (uint32_t)(tid - line * (int)tpl);
+  const int64_t row = (int64_t)blockIdx.x * a.lines + line;
+  const bool valid = row < a.rows;
+  const uint32_t N = (uint32_t)a.n, p = (uint32_t)rd.p;
+  const uint32_t lp = rader_line(N, PAD);
+  float2* L = smem + (size_t)line * lp;
+  float2* x0s = L + (lp - 2);  // x_0, then A_0
+  const float2* src = a.in + row * (int64_t)p;
+  float2* dst = a.out + row * (int64_t)p;
+  if (valid) {
+    for (uint32_t j = t; j < p; j += tpl) {
+      float2 v = gload_nt(src, j);
+      if (a.pre) v = cmul(v, gload(a.pre, j));
+      if (j == 0) {
+        x0s[0] = v;
+      } else {
+        L[mixed_pad<PAD>((uint32_t)rd.perm[j].x)] = v;
+      }
+    }
+  }
+  lds_barrier();
+  mixed_stages<-1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  for (uint32_t k = t; k < N; k += tpl) {
+    const float2 A = L[mixed_pad<PAD>(k)];
+    if (k == 0) x0s[1] = A;
+    L[mixed_pad<PAD>(k)] = cmul(A, gload(rd.conv, k));
+  }
+  lds_barrier();
+  mixed_stages<1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  if (valid) {
+    const float2 x0 = x0s[0];
+    for (uint32_t j = t; j < p; j += tpl) {
+      const float2 c = j == 0 ? x0s[1] : L[mixed_pad<PAD>((uint32_t)rd.perm[j].y)];
+      gstore_nt(dst, j, make_float2(x0.x + c.x, x0.y + c.y));
+    }
+  }
+}
+
+namespace {
+// the checks every launch of a schedule needs (host side, before any HIP call)
+bool mixed_schedule_ok(const MixedArgs& a, int* rmax_out) {
   if (a.n < 2 || a.n > kMaxMixedLength || a.nstages < 1 || a.nstages > kMixedMaxStages || a.tpl < 1 ||
       a.lines < 1 || a.tpl * a.lines > 1024 || a.rows < 1 || (a.kb != 1 && a.kb != 2) || (a.pad != 0 && a.pad != 1))
-    return hipErrorInvalidValue;
+    return false;
   int rmax = 0;
   for (int s = 0; s < a.nstages; ++s) {
     const int R = a.radix[s];
-    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9) return hipErrorInvalidValue;
-    if ((int64_t)a.tpl * a.kb < a.m[s]) return hipErrorInvalidValue;  // every butterfly has a thread
+    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9) return false;
+    if ((int64_t)a.tpl * a.kb < a.m[s]) return false;  // every butterfly has a thread
     rmax = R > rmax ? R : rmax;
   }
+  *rmax_out = rmax;
+  return true;
+}
+}  // namespace
+
+hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
+  int rmax = 0;
+  if (!mixed_schedule_ok(a, &rmax)) return hipErrorInvalidValue;
   uint32_t grid;
   hipError_t e = grid_of(a.rows, a.lines, &grid);
   if (e != hipSuccess) return e;
@@ -343,6 +428,23 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   } else {
     hipLaunchKernelGGL((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st) {
+  int rmax = 0;
+  if (!mixed_schedule_ok(a, &rmax) || a.kb != 1 || rd.p != a.n + 1 || !rd.conv || !rd.perm)
+    return hipErrorInvalidValue;
+  uint32_t grid;
+  hipError_t e = grid_of(a.rows, a.lines, &grid);
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)a.lines * rader_line((uint32_t)a.n, a.pad != 0) * sizeof(float2);
+  if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
+  const dim3 block((uint32_t)(a.tpl * a.lines));
+  if (a.pad)
+    hipLaunchKernelGGL((k_rader<true>), dim3(grid), block, lds, st, a, rd);
+  else
+    hipLaunchKernelGGL((k_rader<false>), dim3(grid), block, lds, st, a, rd);
   return hipGetLastError();
 }
 

@@ -189,6 +189,26 @@ struct MixedArgs {
 };
 hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
 
+// C2C rows of a prime length p by Rader's algorithm ("High Performance
+// Fourier Transforms on GPUs with GLSL", section 2.3, names it beside
+// Bluestein's for prime lengths; the steps below are the textbook form):
+// with g a generator of the nonzero residues mod p and N = p - 1,
+//   X_(g^q) = x_0 + sum_r x_(g^-r) w^(g^(q - r)),  X_0 = x_0 + sum_(j>0) x_j,
+// a cyclic convolution of length N done with the mixed-radix stages of `a`
+// (a schedule of N, kb = 1; a.in / a.out hold rows of p values).
+//   conv: the forward N-point transform of b_m = w^(g^m) divided by N (w =
+//         e^{sign 2 pi i/p}; the sign of the transform lives here);
+//   perm: for j = 1 .. p-1, .x = position of x_j in the convolution input
+//         ((N - ind j) mod N), .y = index of the convolution output that
+//         X_j takes (ind j), with g^(ind j) = j.
+// a.pre (the shift of odd lengths) multiplies the input on load.
+struct RaderArgs {
+  const float2* conv;
+  const int2* perm;
+  int p;
+};
+hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t stream);
+
 // C2C rows of any length n (2 <= n <= kMaxBluesteinLength) by Bluestein's
 // chirp: with c_j = e^{sign pi i j^2/n}, y_k = c_k * (a conv b)_k, where
 // a_j = x_j pre_j (pre_j = c_j, times the shift ramp when requested) padded

@@ -10,6 +10,7 @@
 #include <complex>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
 #include <functional>
 #include <new>
 #include <string>
@@ -105,6 +106,74 @@ void host_fft_f64(std::vector<std::complex<double>>& a) {
   }
 }
 
+// forward transform (e^{-2 pi i jk/m}) of any length in f64 on the host, for
+// plan tables only: split by the smallest prime factor q of m (inputs q
+// apart), recursively; a prime length is summed directly, every factor from
+// cos/sin of its own angle (the product jk reduced mod m in integers)
+void host_dft_f64(std::vector<std::complex<double>>& a) {
+  const size_t m = a.size();
+  if (m <= 1) return;
+  size_t q = 2;
+  while (m % q) ++q;
+  std::vector<std::complex<double>> out(m);
+  auto w = [m](size_t e) {
+    const double ang = -kTwoPi * (double)(e % m) / (double)m;
+    return std::complex<double>(std::cos(ang), std::sin(ang));
+  };
+  if (q == m) {
+    for (size_t k = 0; k < m; ++k) {
+      std::complex<double> s = 0.0;
+      for (size_t j = 0; j < m; ++j) s += a[j] * w(j * k);
+      out[k] = s;
+    }
+  } else {
+    const size_t r = m / q;
+    std::vector<std::vector<std::complex<double>>> sub(q, std::vector<std::complex<double>>(r));
+    for (size_t i = 0; i < q; ++i)
+      for (size_t j = 0; j < r; ++j) sub[i][j] = a[i + q * j];
+    for (auto& v : sub) host_dft_f64(v);
+    for (size_t k = 0; k < m; ++k) {
+      std::complex<double> s = 0.0;
+      for (size_t i = 0; i < q; ++i) s += w(i * k) * sub[i][k % r];
+      out[k] = s;
+    }
+  }
+  a.swap(out);
+}
+
+bool is_prime(int64_t n) {
+  if (n < 2) return false;
+  for (int64_t d = 2; d * d <= n; ++d)
+    if (n % d == 0) return false;
+  return true;
+}
+
+int64_t pow_mod(int64_t b, int64_t e, int64_t m) {
+  int64_t r = 1 % m;
+  b %= m;
+  for (; e; e >>= 1, b = b * b % m)
+    if (e & 1) r = r * b % m;
+  return r;
+}
+
+// smallest generator of the nonzero residues mod a prime p
+int64_t primitive_root(int64_t p) {
+  std::vector<int64_t> qs;
+  int64_t m = p - 1;
+  for (int64_t d = 2; d * d <= m; ++d)
+    if (m % d == 0) {
+      qs.push_back(d);
+      while (m % d == 0) m /= d;
+    }
+  if (m > 1) qs.push_back(m);
+  for (int64_t g = 2; g < p; ++g) {
+    bool gen = true;
+    for (int64_t q : qs) gen = gen && pow_mod(g, (p - 1) / q, p) != 1;
+    if (gen) return g;
+  }
+  return 1;  // p = 2
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -156,7 +225,10 @@ struct fft_plan {
   int pq_p = 0, pq_q = 0;
   const float2* wn = nullptr;
   bool mixed = false;
+  bool rader = false;  // mx holds the schedule of n - 1
   MixedArgs mx{};
+  const float2* rd_conv = nullptr;
+  const float2* rd_perm = nullptr;  // int2 pairs (RaderArgs.perm) in float2 slots
   const float2* mx_shift = nullptr;
   const float2* mx_ishift = nullptr;
   // R2C/C2R of lengths that are not powers of two: an any-length C2C plan of
@@ -368,6 +440,82 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   return p;
 }
 
+// C2C of a prime length p by Rader's algorithm: a cyclic convolution of
+// length N = p - 1 on the mixed-radix schedule rad of N (one butterfly per
+// thread, radices up to 16).  Tables: the stage twiddles of N, conv (the f64
+// transform of b_m = e^{sign 2 pi i g^m/p}, divided by N), the index pairs
+// of each j, and the shift ramps.
+fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector<int>& rad) {
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  const int64_t n = p_len, N = n - 1;
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = FFT_C2C;
+  p->sign = sign;
+  p->rader = true;
+  MixedArgs& a = p->mx;
+  a.rows = batch;
+  a.n = (int)N;
+  a.nstages = (int)rad.size();
+  std::vector<float2> tw, conv, perm, sh, ish;
+  int64_t ns = 1, maxm = 0;
+  for (int st = 0; st < a.nstages; ++st) {
+    const int R = rad[st];
+    a.radix[st] = R;
+    a.ns[st] = (int)ns;
+    a.m[st] = (int)(N / R);
+    a.ns_magic[st] = ns == 1 ? 0u : (uint32_t)(((uint64_t(1) << 32) + (uint64_t)ns - 1) / (uint64_t)ns);
+    a.twoff[st] = (int)tw.size();
+    if (st > 0)
+      for (int r = 1; r < R; ++r)
+        for (int64_t j = 0; j < ns; ++j) tw.push_back(root((int64_t)r * j, ns * R));
+    maxm = std::max<int64_t>(maxm, N / R);
+    ns *= R;
+  }
+  if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
+  a.kb = 1;
+  a.pad = rad[0] == 16 ? 1 : 0;  // as for the mixed-radix plans
+  a.tpl = (int)maxm;
+  a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
+  // generator powers and discrete logarithms
+  const int64_t g = primitive_root(n);
+  std::vector<int64_t> ind(n, 0);
+  for (int64_t q = 0, gq = 1; q < N; ++q, gq = gq * g % n) ind[gq] = q;
+  std::vector<std::complex<double>> b(N);
+  for (int64_t m = 0, gm = 1; m < N; ++m, gm = gm * g % n) {
+    const double ang = (double)sign * kTwoPi * (double)gm / (double)n;
+    b[m] = std::complex<double>(std::cos(ang), std::sin(ang));
+  }
+  host_dft_f64(b);
+  for (int64_t k = 0; k < N; ++k)
+    conv.push_back(make_float2((float)(b[k].real() / (double)N), (float)(b[k].imag() / (double)N)));
+  for (int64_t j = 0; j < n; ++j) {
+    const int32_t in_pos = j == 0 ? 0 : (int32_t)((N - ind[j]) % N);
+    const int32_t out_pos = j == 0 ? 0 : (int32_t)ind[j];
+    float2 v;
+    std::memcpy(&v.x, &in_pos, sizeof(float));
+    std::memcpy(&v.y, &out_pos, sizeof(float));
+    perm.push_back(v);
+  }
+  // shift factors of an odd length (as for the mixed-radix plans)
+  const int64_t h = n / 2;
+  for (int64_t j = 0; j < n; ++j) {
+    const float2 w = root((j * h) % n, n);
+    const float2 wc = make_float2(w.x, -w.y);
+    sh.push_back(sign < 0 ? wc : w);
+    ish.push_back(sign < 0 ? w : wc);
+  }
+  if (finish_plan(p, {&tw, &conv, &perm, &sh, &ish}, {&a.tw, &p->rd_conv, &p->rd_perm, &p->mx_shift, &p->mx_ishift},
+                  0) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
 // C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLengthLarge.
 // The transforms of length m >= 2n - 1 run inside one kernel per row batch
 // while m <= kMaxSinglePass; above, in three passes over batch x m values
@@ -503,6 +651,14 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
       if (n / *std::min_element(r.begin(), r.end()) <= 1024 * kMixedButterflies)
         return create_mixed(n, batch, sign, r, kMixedButterflies);
     }
+  }
+  // primes up to 8193 whose p - 1 has a schedule: Rader's convolution of
+  // length p - 1 in one kernel (1009: two 1008-point transforms instead of
+  // the chirp transform's two of 2048)
+  if (n <= kMaxMixedLength + 1 && is_prime(n)) {
+    static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
+    const std::vector<int> w = mixed_radices(n - 1, wide, (int)((n - 1 + 1023) / 1024));
+    if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_rader(n, batch, sign, w);
   }
   if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
   return create_bluestein(n, batch, sign);
@@ -715,7 +871,8 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_SHIFT:
       if (value < 0 || value > 2) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0, 1 or 2");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
-      if (value && !p->bluestein && !p->mixed && !p->any2d && ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
+      if (value && !p->bluestein && !p->mixed && !p->rader && !p->any2d &&
+          ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
       if (p->any2d) {  // the shift of each axis, in its row plan
         if (fft_plan_set(p->inner, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
@@ -828,6 +985,14 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     a.flip = even && p->shift ? 1 : 0;
     a.pre = even ? nullptr : p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
     e = launch_mixed(p->sign, a, stream);
+  } else if (p->rader) {  // odd n: the shifts are the ramps
+    MixedArgs a = p->mx;
+    a.in = src;
+    a.out = dst;
+    a.flip = 0;
+    a.pre = p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
+    const RaderArgs rd{p->rd_conv, reinterpret_cast<const int2*>(p->rd_perm), (int)p->n};
+    e = launch_rader(a, rd, stream);
   } else if (p->bluestein && p->fourstep) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
     const int64_t m = p->bm;

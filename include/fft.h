@@ -18,7 +18,9 @@
  *    section 2.3, names mixed radices and other lengths as the extension of
  *    its radix-2 transforms): lengths with no prime factor above 13 by
  *    mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every stage
- *    has at most 2048 butterflies (n <= 8192); n = p * 2^k (p in 3, 5, 7, 9,
+ *    has at most 2048 butterflies (n <= 8192); primes p <= 8193 whose p - 1
+ *    has such a schedule by Rader's algorithm (a cyclic convolution of length
+ *    p - 1 on those stages, in one kernel); n = p * 2^k (p in 3, 5, 7, 9,
  *    15, 25, 8192 < n <= 16384) in one register-resident kernel (p
  *    power-of-two transforms, twiddles, p-point DFTs); the others by Bluestein's
  *    chirp transform: two power-of-two transforms of length m >= 2n - 1,

@@ -1,8 +1,9 @@
 """GPU parity for C2C lengths that are not powers of two, against the
-oracle's DFT by the definition: p x 2^k (p in 3, 5, 7, 9, 15, 25) in
-registers, mixed-radix Stockham stages (radices 2..8, 10..16) for the other
-lengths with no prime factor above 13, Bluestein's chirp transform for the
-rest.
+oracle's DFT by the definition: mixed-radix Stockham stages (radices 2..8,
+10..16) for the lengths with no prime factor above 13, Rader's convolution of
+length p - 1 on those stages for primes p whose p - 1 has a schedule, p x 2^k
+(p in 3, 5, 7, 9, 15, 25) in registers above 8192, Bluestein's chirp
+transform for the rest.
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -30,6 +31,13 @@ LARGE = [1000, 1001, 1029, 1296, 1331, 1536, 2000, 2002, 2047, 2197, 2401, 3000,
          4097, 5000, 5005, 6000, 6144, 6250, 6561, 7168, 7776, 8000, 8191]
 
 
+# primes by Rader's algorithm (the schedule of p - 1): 17: 16; 19: 6 3;
+# 23: 11 2; 97: 12 8; 127: 7 6 3; 257: 16 16; 331: 11 6 5; 1009: 12 12 7;
+# 2003: 14 13 11; 4001: 10 10 8 5; 7001: 10 10 10 7.  Primes whose p - 1
+# has no schedule take the chirp transform: 509, 1019, 8191.
+RADER = [17, 19, 23, 29, 37, 41, 97, 101, 127, 193, 257, 331, 641, 1009, 1201, 2003, 2017, 3001, 4001, 7001]
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _device():
     import torch
@@ -50,14 +58,25 @@ def test_any_length_sweep(n, sign):
         assert rel_l2(y, oracle.dft(x, sign)) <= TOL, (n, batch)
 
 
-@pytest.mark.parametrize("n", [7, 1000, 4097])
+@pytest.mark.parametrize("n", RADER + [509, 1019])
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_primes(n, sign):
+    """Primes: Rader's convolution where p - 1 has a schedule, else the chirp
+    transform; batches that leave the last workgroup's lines partly empty."""
+    for batch in (1, 7, 65):
+        say(f"prime c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 13 + batch))
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n", [7, 1000, 1009, 4097])
 def test_any_length_in_place(n):
     say(f"any-length c2c in place n={n}")
     x = W.uniform_c64((4, n), np.random.default_rng(n + 1))
     assert rel_l2(c2c(x, -1, inplace=True), oracle.dft(x, -1)) <= TOL
 
 
-@pytest.mark.parametrize("n", [3, 7, 12, 255, 1001, 4095, 6000])
+@pytest.mark.parametrize("n", [3, 7, 12, 101, 255, 1001, 1009, 4095, 6000])
 @pytest.mark.parametrize("sign", [-1, 1])
 def test_any_length_shift(n, sign):
     """Fused shift (even and odd n): bin 0 lands at index floor(n/2), the
@@ -68,7 +87,7 @@ def test_any_length_shift(n, sign):
     assert rel_l2(c2c(x, sign, shift=1), want) <= TOL
 
 
-@pytest.mark.parametrize("n", [3, 7, 12, 1001, 4095])
+@pytest.mark.parametrize("n", [3, 7, 12, 257, 1001, 4095])
 @pytest.mark.parametrize("sign", [-1, 1])
 def test_any_length_inverse_shift(n, sign):
     """Shift option 2: index floor(n/2) moves to 0 (numpy's ifftshift of the
@@ -79,7 +98,7 @@ def test_any_length_inverse_shift(n, sign):
     assert rel_l2(c2c(x, sign, shift=2), want) <= TOL
 
 
-@pytest.mark.parametrize("n", [5, 1000, 8191])
+@pytest.mark.parametrize("n", [5, 1000, 2017, 8191])
 def test_any_length_round_trip(n):
     say(f"any-length round trip n={n}")
     x = W.uniform_c64((6, n), np.random.default_rng(n + 3))
@@ -179,7 +198,7 @@ def test_any_length_large_shift_and_in_place(n, shift):
 # R2C / C2R at lengths that are not powers of two: an any-length complex
 # transform of n/2 (even n) or n (odd n) with the packing kernels around it
 # --------------------------------------------------------------------------
-REAL_N = [3, 5, 6, 7, 10, 12, 15, 100, 101, 360, 999, 1000, 1440, 2001, 4002, 10000, 20002]
+REAL_N = [3, 5, 6, 7, 10, 12, 15, 100, 101, 360, 999, 1000, 1440, 2001, 2018, 4002, 10000, 20002]
 
 
 @pytest.mark.parametrize("n", REAL_N)
@@ -217,7 +236,7 @@ def test_real_any_length_options():
 # transpose back); the shift is the shift of each axis
 # --------------------------------------------------------------------------
 SIZES_2D = [(3, 5, 2), (6, 10, 3), (100, 64, 2), (64, 100, 2), (360, 180, 1), (1000, 999, 1), (17, 1024, 2),
-            (10001, 6, 1)]
+            (97, 331, 1), (10001, 6, 1)]
 
 
 @pytest.mark.parametrize("ny,nx,batch", SIZES_2D)
@@ -243,7 +262,8 @@ def test_2d_any_size_shift_and_in_place(ny, nx, shift):
 # buffers beyond 2^31 elements (64-bit row offsets): the seeded block tiled
 # on the device, sampled rows at the start, the middle and the ragged end
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("n,batch", [(4096, (1 << 19) + 3), (1000, (1 << 21) + 5), (1009, (1 << 21) + 7)])
+@pytest.mark.parametrize("n,batch", [(4096, (1 << 19) + 3), (1000, (1 << 21) + 5), (1009, (1 << 21) + 7),
+                                     (1019, (1 << 21) + 9)])
 def test_beyond_2p31_elements(n, batch):
     import torch
     say(f"c2c n={n} batch={batch} ({batch * n * 8 / 2**30:.1f} GiB per buffer)")

@@ -479,8 +479,8 @@ def test_graph_capture_replays():
     """fft_exec launches kernels only, so it can be captured in a HIP graph;
     every replay, with eager work in between, matches the eager result."""
     import torch
-    say("graph capture: 1D n=4096, four-step 2^16, 2D 512x512, mixed radix 1000, chirp 1009 and 10001")
-    cases = [(4096, 64, None), (1 << 16, 4, None), (512, 512, 2), (1000, 16, None), (1009, 8, None),
+    say("graph capture: 1D n=4096, four-step 2^16, 2D 512x512, mixed radix 1000, Rader 1009, chirp 1019 and 10001")
+    cases = [(4096, 64, None), (1 << 16, 4, None), (512, 512, 2), (1000, 16, None), (1009, 8, None), (1019, 8, None),
              (10001, 2, None)]
     for n, b, ny in cases:
         if ny is None:
