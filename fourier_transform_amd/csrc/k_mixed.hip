@@ -382,6 +382,38 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   }
 }
 
+// Bluestein's chirp transform on a convolution length m with a mixed-radix
+// schedule: the row times pre, zero beyond n, as a line of m values in LDS;
+// the forward m-point stages; the product with bhat; the inverse stages; the
+// outputs j < n times post.
+template <bool PAD>
+__global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixedArgs c) {
+  extern __shared__ float4 smem4[];
+  float2* smem = reinterpret_cast<float2*>(smem4);
+  const uint32_t tpl = (uint32_t)a.tpl;
+  const int tid = threadIdx.x;
+  const int line = tid / (int)tpl;
+  const uint32_t t = (uint32_t)(tid - line * (int)tpl);
+  const int64_t row = (int64_t)blockIdx.x * a.lines + line;
+  const bool valid = row < a.rows;
+  const uint32_t m = (uint32_t)a.n, n = (uint32_t)c.n;
+  float2* L = smem + (size_t)line * (mixed_pad<PAD>(m) + 1);
+  const float2* src = a.in + row * (int64_t)n;
+  float2* dst = a.out + row * (int64_t)n;
+  for (uint32_t j = t; j < m; j += tpl) {
+    float2 v = make_float2(0.f, 0.f);
+    if (valid && j < n) v = cmul(gload_nt(src, j), gload(a.pre, j));
+    L[mixed_pad<PAD>(j)] = v;
+  }
+  lds_barrier();
+  mixed_stages<-1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  for (uint32_t k = t; k < m; k += tpl) L[mixed_pad<PAD>(k)] = cmul(L[mixed_pad<PAD>(k)], gload(c.bhat, k));
+  lds_barrier();
+  mixed_stages<1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  if (valid)
+    for (uint32_t j = t; j < n; j += tpl) gstore_nt(dst, j, cmul(L[mixed_pad<PAD>(j)], gload(c.post, j)));
+}
+
 namespace {
 // the checks every launch of a schedule needs (host side, before any HIP call)
 bool mixed_schedule_ok(const MixedArgs& a, int* rmax_out) {
@@ -445,6 +477,24 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
     hipLaunchKernelGGL((k_rader<true>), dim3(grid), block, lds, st, a, rd);
   else
     hipLaunchKernelGGL((k_rader<false>), dim3(grid), block, lds, st, a, rd);
+  return hipGetLastError();
+}
+
+hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, hipStream_t st) {
+  int rmax = 0;
+  if (!mixed_schedule_ok(a, &rmax) || a.kb != 1 || c.n < 2 || 2 * c.n - 1 > a.n || !a.pre || !c.bhat || !c.post)
+    return hipErrorInvalidValue;
+  uint32_t grid;
+  hipError_t e = grid_of(a.rows, a.lines, &grid);
+  if (e != hipSuccess) return e;
+  const size_t lds =
+      (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
+  if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
+  const dim3 block((uint32_t)(a.tpl * a.lines));
+  if (a.pad)
+    hipLaunchKernelGGL((k_bluestein_mixed<true>), dim3(grid), block, lds, st, a, c);
+  else
+    hipLaunchKernelGGL((k_bluestein_mixed<false>), dim3(grid), block, lds, st, a, c);
   return hipGetLastError();
 }
 

@@ -209,6 +209,18 @@ struct RaderArgs {
 };
 hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t stream);
 
+// Bluestein's chirp transform (below) with a convolution length m that is
+// not a power of two: the mixed-radix stages of `a` (a schedule of m, kb = 1;
+// a.in / a.out hold rows of n values, a.pre the n chirp factors applied on
+// load) run on a line of m values in LDS; bhat: the m factors between the
+// two transforms; post: the n factors applied on store.
+struct ChirpMixedArgs {
+  const float2* bhat;
+  const float2* post;
+  int n;
+};
+hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, hipStream_t stream);
+
 // C2C rows of any length n (2 <= n <= kMaxBluesteinLength) by Bluestein's
 // chirp: with c_j = e^{sign pi i j^2/n}, y_k = c_k * (a conv b)_k, where
 // a_j = x_j pre_j (pre_j = c_j, times the shift ramp when requested) padded

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <complex>
 #include <cstdint>
@@ -212,6 +213,7 @@ struct fft_plan {
   // C2C lengths that are not powers of two (Bluestein): transform length bm,
   // chirps c_j (and c_j times the shift ramp), forward transform of the chirp
   bool bluestein = false;
+  bool bmixed = false;  // convolution length bm with a mixed-radix schedule (mx)
   int bm = 0;
   const float2* chirp = nullptr;
   const float2* chirp_shift = nullptr;
@@ -440,6 +442,34 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   return p;
 }
 
+// A schedule of N with one butterfly per thread (radices up to 16) into a,
+// its stage twiddles appended to tw; lines per workgroup and padding as for
+// the mixed-radix plans.  Used by the transforms whose N-point stages run on
+// a line in LDS (Rader, Bluestein on a mixed-radix length).
+void fill_schedule(MixedArgs& a, int64_t N, const std::vector<int>& rad, std::vector<float2>& tw) {
+  a.n = (int)N;
+  a.nstages = (int)rad.size();
+  int64_t ns = 1, maxm = 0;
+  for (int st = 0; st < a.nstages; ++st) {
+    const int R = rad[st];
+    a.radix[st] = R;
+    a.ns[st] = (int)ns;
+    a.m[st] = (int)(N / R);
+    a.ns_magic[st] = ns == 1 ? 0u : (uint32_t)(((uint64_t(1) << 32) + (uint64_t)ns - 1) / (uint64_t)ns);
+    a.twoff[st] = (int)tw.size();
+    if (st > 0)
+      for (int r = 1; r < R; ++r)
+        for (int64_t j = 0; j < ns; ++j) tw.push_back(root((int64_t)r * j, ns * R));
+    maxm = std::max<int64_t>(maxm, N / R);
+    ns *= R;
+  }
+  if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
+  a.kb = 1;
+  a.pad = rad[0] == 16 ? 1 : 0;
+  a.tpl = (int)maxm;
+  a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
+}
+
 // C2C of a prime length p by Rader's algorithm: a cyclic convolution of
 // length N = p - 1 on the mixed-radix schedule rad of N (one butterfly per
 // thread, radices up to 16).  Tables: the stage twiddles of N, conv (the f64
@@ -457,28 +487,8 @@ fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector
   p->rader = true;
   MixedArgs& a = p->mx;
   a.rows = batch;
-  a.n = (int)N;
-  a.nstages = (int)rad.size();
   std::vector<float2> tw, conv, perm, sh, ish;
-  int64_t ns = 1, maxm = 0;
-  for (int st = 0; st < a.nstages; ++st) {
-    const int R = rad[st];
-    a.radix[st] = R;
-    a.ns[st] = (int)ns;
-    a.m[st] = (int)(N / R);
-    a.ns_magic[st] = ns == 1 ? 0u : (uint32_t)(((uint64_t(1) << 32) + (uint64_t)ns - 1) / (uint64_t)ns);
-    a.twoff[st] = (int)tw.size();
-    if (st > 0)
-      for (int r = 1; r < R; ++r)
-        for (int64_t j = 0; j < ns; ++j) tw.push_back(root((int64_t)r * j, ns * R));
-    maxm = std::max<int64_t>(maxm, N / R);
-    ns *= R;
-  }
-  if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
-  a.kb = 1;
-  a.pad = rad[0] == 16 ? 1 : 0;  // as for the mixed-radix plans
-  a.tpl = (int)maxm;
-  a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
+  fill_schedule(a, N, rad, tw);
   // generator powers and discrete logarithms
   const int64_t g = primitive_root(n);
   std::vector<int64_t> ind(n, 0);
@@ -534,10 +544,31 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   p->bluestein = true;
   int64_t m = 1;
   while (m < 2 * n - 1) m <<= 1;
+  // A convolution length with a mixed-radix schedule where it is much
+  // shorter than the power of two (n just above a power of two: 1034 can use
+  // 2080 = 16 x 13 x 10 instead of 4096).  Among the lengths c >= 2n - 1 with
+  // 1.3 c < m, the one with the smallest c x stages, when m >= 4096.
+  // Measured on MI355X per 512 MiB: 1034 973 -> 908 us, 1049 966 -> 863 us,
+  // 2053 1325 -> 1139 us, 2111 1298 -> 1044 us; with m <= 2048 the
+  // power-of-two kernel is as fast or faster (263: 885 against 914 us).
+  std::vector<int> msched;
+  if (m >= 4096) {
+    static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
+    int64_t best_cost = INT64_MAX, best_c = 0;
+    for (int64_t c = 2 * n - 1; c <= kMaxMixedLength && 13 * c < 10 * m && 2 * c < best_cost; ++c) {
+      const std::vector<int> w = mixed_radices(c, wide, (int)((c + 1023) / 1024));
+      if (w.empty() || (int)w.size() > kMixedMaxStages) continue;
+      if (c * (int64_t)w.size() < best_cost) best_cost = c * (int64_t)w.size(), best_c = c, msched = w;
+    }
+    if (best_c) m = best_c, p->bmixed = true;
+  }
   p->bm = (int)m;
   std::vector<float2> ta, tb, thi, tlo, pre, pres, prei, bh, bht;
   size_t scratch = 0;
-  if (m <= kMaxSinglePass) {
+  if (p->bmixed) {
+    p->mx.rows = batch;
+    fill_schedule(p->mx, m, msched, ta);
+  } else if (m <= kMaxSinglePass) {
     append_stage_table((int)m, rows_values((int)m), ta);
   } else {
     const int L = ilog2c(m);
@@ -571,13 +602,17 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
     b[(size_t)j] = cb;
     if (j > 0) b[(size_t)(m - j)] = cb;
   }
-  host_fft_f64(b);
+  if (p->bmixed)
+    host_dft_f64(b);
+  else
+    host_fft_f64(b);
   for (int64_t k = 0; k < m; ++k) {
     const std::complex<double> v = b[(size_t)k] / (double)m;
     bh.push_back(make_float2((float)v.real(), (float)v.imag()));
   }
   std::vector<std::vector<float2>*> parts = {&ta, &pre, &pres, &prei, &bh};
-  std::vector<const float2**> slots = {&p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift, &p->bhat};
+  std::vector<const float2**> slots = {p->bmixed ? &p->mx.tw : &p->tw_a, &p->chirp, &p->chirp_shift, &p->chirp_ishift,
+                                       &p->bhat};
   if (p->fourstep) {
     // the row pass between the transforms reads bhat row by row: k2*n1 + k1
     for (int64_t k2 = 0; k2 < p->n2; ++k2)
@@ -993,6 +1028,14 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     a.pre = p->shift == 1 ? p->mx_shift : p->shift == 2 ? p->mx_ishift : nullptr;
     const RaderArgs rd{p->rd_conv, reinterpret_cast<const int2*>(p->rd_perm), (int)p->n};
     e = launch_rader(a, rd, stream);
+  } else if (p->bmixed) {
+    MixedArgs a = p->mx;
+    a.in = src;
+    a.out = dst;
+    a.flip = 0;
+    a.pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
+    const ChirpMixedArgs c{p->bhat, p->chirp, (int)p->n};
+    e = launch_bluestein_mixed(a, c, stream);
   } else if (p->bluestein && p->fourstep) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
     const int64_t m = p->bm;

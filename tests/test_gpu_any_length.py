@@ -3,7 +3,8 @@ oracle's DFT by the definition: mixed-radix Stockham stages (radices 2..8,
 10..16) for the lengths with no prime factor above 13, Rader's convolution of
 length p - 1 on those stages for primes p whose p - 1 has a schedule, p x 2^k
 (p in 3, 5, 7, 9, 15, 25) in registers above 8192, Bluestein's chirp
-transform for the rest.
+transform for the rest (on a mixed-radix convolution length where that is
+much shorter than the power of two).
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -67,6 +68,31 @@ def test_primes(n, sign):
         say(f"prime c2c n={n} batch={batch} sign={sign}")
         x = W.uniform_c64((batch, n), np.random.default_rng(n * 13 + batch))
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+# the chirp transform on a convolution length with a mixed-radix schedule
+# (about half the power of two, used where that is 4096 or more):
+# 1034: 2080 = 16 13 10; 2053: 4116 = 12 7 7 7; 2111: 4224 = 11 8 8 6;
+# 263 and 521 keep the power of two (1024, 2048)
+CHIRP_MIXED = [263, 521, 1031, 1034, 1049, 2053, 2063, 2111]
+
+
+@pytest.mark.parametrize("n", CHIRP_MIXED)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_chirp_mixed_length(n, sign):
+    for batch in (1, 7, 65):
+        say(f"chirp (mixed-radix m) c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 17 + batch))
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n,shift", [(1034, 1), (1034, 2), (2053, 1), (2111, 2)])
+def test_chirp_mixed_length_shift_and_in_place(n, shift):
+    say(f"chirp (mixed-radix m) shift={shift} n={n}, in place")
+    x = W.uniform_c64((3, n), np.random.default_rng(n + shift + 5))
+    idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
+    want = oracle.dft(x, -1)[:, idx]
+    assert rel_l2(c2c(x, -1, shift=shift, inplace=True), want) <= TOL
 
 
 @pytest.mark.parametrize("n", [7, 1000, 1009, 4097])
