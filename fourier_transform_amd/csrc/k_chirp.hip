@@ -172,19 +172,24 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   run_stages<N2, E, 1, false, L, SPLIT>(v, lds, a.tw, u, line);
   __builtin_amdgcn_sched_barrier(0);  // keep the post loads below the stages (VGPR budget)
   float2* dst = a.out + b * a.out_stride + c0;
+  // The store offsets are recomputed from an opaque copy of off: reusing the
+  // load offsets kept 64 of them live across the stages (spilled).
+  uint32_t off2 = off;
+  asm volatile("" : "+v"(off2));
   // Outputs j >= out_len are dropped.  With 64 values per thread a branch per
   // store costs many VGPRs spilled, so those tiles write the dropped outputs
   // to a.sink instead (a scratch row that nothing reads any more).
 #pragma unroll
   for (int m = 0; m < E; ++m) {
-    const uint32_t j = c0 + off + step * m;
+    const uint32_t o = off2 + step * m;
+    const uint32_t j = c0 + o;
     const bool keep = j < (uint32_t)a.out_len;
     if constexpr (E > 16) {
-      float2* q = keep ? dst + (off + step * m) : a.sink + tid;
+      float2* q = keep ? dst + o : a.sink + tid;
       gstore_nt(q, 0u, cmul(v[m], gload(a.post, keep ? j : 0u)));
       if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     } else if (keep) {
-      gstore_nt(dst, off + step * m, cmul(v[m], gload(a.post, j)));
+      gstore_nt(dst, o, cmul(v[m], gload(a.post, j)));
     }
   }
 }
