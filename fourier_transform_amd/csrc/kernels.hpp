@@ -542,15 +542,20 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
     run_stages<N2, E, S, false, L, SPLIT>(v, lds, a.tw, u, line);
   }
   if (valid) {
-    const uint32_t eu = c1 * (uint32_t)u;
+    // line, u and c1 again from an opaque copy of the thread index: kept live
+    // across the stages they cost VGPRs (spills)
+    int tid2 = tid;
+    asm volatile("" : "+v"(tid2));
+    const int line2 = tid2 % C, u2 = tid2 / C;
+    const uint32_t eu = (c0 + (uint32_t)line2) * (uint32_t)u2;
     const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
     // the block layout, relative to the first block column of this group
     float2* dst = a.out + b * (int64_t)n1 * N2 + c0 * BK;
 #pragma unroll
     for (int m = 0; m < E; ++m) {
-      const uint32_t k2 = (uint32_t)(u + T * m);
-      const float2 w = cmul(wu, ftab[line * FP + m]);
-      gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line, n1), apply_tw<S>(v[m], w));
+      const uint32_t k2 = (uint32_t)(u2 + T * m);
+      const float2 w = cmul(wu, ftab[line2 * FP + m]);
+      gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line2, n1), apply_tw<S>(v[m], w));
       if constexpr (E > 16) {
         if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
