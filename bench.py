@@ -1,11 +1,14 @@
 """Throughput of the batched fp32 FFT on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload w2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload w2] [--configs all|none]
+    python bench.py --summarize-trace KERNEL_TRACE.csv
 
 One step is one pass of the whole hot path over one batch: for the default
 workload (w2: 16384 rows of N = 4096 complex64, U[-1,1]) a forward transform
 followed by the inverse of its output, two kernel launches.  Inputs are
-resident in HBM before timing starts.  Prints ONE JSON line.
+resident in HBM before timing starts.  Each workload first runs for 200 ms
+(settle, untimed, reported), then W warm-up steps, then the K timed steps.
+Prints ONE JSON line.
 
 value     = 5 N log2(N) * rows * directions / time  (GFLOP/s, the pages'
             flop convention)
@@ -14,6 +17,19 @@ roofline  = algorithmic HBM bytes of one launch (read + write of every
             on the stream the kernels run on, against the 8 TB/s HBM peak
 cpu_baseline = the f64 oracle (untuned reference) on a bounded sample of the
             same workload on the host cores
+configs   = (default run) every configuration of the metric measured in the
+            same run: c1 1024 x 8, c2 4096 x 16384 forward + inverse (the
+            headline above), c3 2^22 x 32 (four-step), c4 real rows 1024 x 2048
+            (C2R then R2C, mmax 682), c5 8192^2 2D with the fused shift.  Each
+            with its time per exec over the timed region, GFLOP/s, algorithmic
+            GB/s and fraction of HBM peak, the median and geometric mean of
+            per-exec event timings, 100 back-to-back steps for c1 and c4, the
+            relative L2 error against the oracle over the whole output, and
+            the oracle's own time on that reference (the CPU baseline)
+--summarize-trace: per-kernel durations of a rocprofv3 kernel trace taken
+            with --selected-regions: the bench opens the profiler only around
+            its timed regions (roctxProfilerResume/Pause), so the trace holds
+            exactly the timed launches
 """
 import argparse
 import hashlib
@@ -174,12 +190,313 @@ def cpu_baseline(spec, x_host, reps=3, direct=False):
     return out
 
 
+# configurations of the metric (c1..c5) and the workloads that implement them
+CONFIGS = (("c1", "w1"), ("c2", "w2"), ("c3", "w3"), ("c4", "w4"), ("c5", "w5"))
+BAR = 0.60              # fraction of HBM peak the large batched C2C and 2D configs must sustain
+BAR_CONFIGS = ("c2", "c3", "c5")
+BACK_TO_BACK = 100      # c1 and c4 (launch-bound) are also timed as this many back-to-back steps
+TRAFFIC_KEY = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22", "w4": "real_2048",
+               "w5": "2d_8192x8192"}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def make_plans(F, spec, direct=False, real_pairs=False):
+    n, batch = spec["n"], spec["batch"]
+    plans = []
+    for s in spec["dirs"]:
+        if spec["kind"] == "real":
+            if direct:
+                kind = F.FFT_C2R_DIRECT if s > 0 else F.FFT_R2C_DIRECT
+            else:
+                kind = F.FFT_C2R if s > 0 else F.FFT_R2C
+            p = F.fft_plan_create(n, batch, kind, s)
+            F.fft_plan_set(p, F.FFT_OPT_MMAX, spec["mmax"])
+            F.fft_plan_set(p, F.FFT_OPT_SPEC_LAYOUT, 1)
+            if real_pairs:
+                F.fft_plan_set(p, F.FFT_OPT_REAL_PAIRS, 1)
+        elif spec["kind"] == "2d":
+            p = F.fft_plan_create_2d(spec["ny"], spec["nx"], batch, F.FFT_C2C, s)
+            F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
+        else:
+            p = F.fft_plan_create(n, batch, F.FFT_C2C, s)
+        plans.append(p)
+    return plans
+
+
+SETTLE_MS = 200.0       # the workload runs this long before its warm-up steps (see time_workload)
+
+
+class _Roctx:
+    """roctxProfilerResume/Pause around each timed region, so that
+    `rocprofv3 --selected-regions` traces exactly the timed launches.  Without
+    a profiler attached the calls do nothing; without the library, neither
+    does this."""
+
+    def __init__(self):
+        self.lib = None
+        try:
+            import ctypes
+            self.lib = ctypes.CDLL("librocprofiler-sdk-roctx.so")
+        except OSError:
+            try:
+                import ctypes
+                self.lib = ctypes.CDLL("/opt/rocm/lib/librocprofiler-sdk-roctx.so")
+            except OSError:
+                self.lib = None
+
+    def resume(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerResume(0)
+
+    def pause(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerPause(0)
+
+
+ROCTX = _Roctx()
+
+
+def time_workload(F, torch, plans, xd, bufs, stream, steps, warmup, back_to_back=0, settle_ms=SETTLE_MS):
+    """Settle, warm-up steps, then `steps` steps between one pair of HIP
+    events on the exec stream (no events between launches), then the same
+    steps with an event before every exec (median and geometric mean per exec
+    and plan), then optionally `back_to_back` steps between one event pair.
+
+    Settle: the workload itself runs for `settle_ms` of wall time before the
+    warm-up steps.  Measured on MI355X, a process's first ~100 launches of the
+    4096-point pass take 213-215 us and later ones 190 us, whatever the
+    launch order (the GPU ramping up from idle); the settle keeps that ramp
+    out of the timed region, which then measures the steady state."""
+    def step():
+        src = xd
+        for p, dst in zip(plans, bufs):
+            F.fft_exec(p, src, dst, stream.cuda_stream)
+            src = dst
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    settle_steps = 0
+    while True:
+        step()
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+                break
+    settle = {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": settle_steps}
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ROCTX.resume()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ROCTX.pause()
+    out = {"ms_per_step": ev0.elapsed_time(ev1) / steps, "wall_ms_per_step": wall * 1e3 / steps, "settle": settle}
+    out["ms_per_exec"] = out["ms_per_step"] / len(plans)
+
+    # an event before every exec: per-exec durations (the events themselves
+    # add a little between launches)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps * len(plans) + 1)]
+    k = 0
+    for _ in range(steps):
+        src = xd
+        for p, dst in zip(plans, bufs):
+            evs[k].record(stream)
+            F.fft_exec(p, src, dst, stream.cuda_stream)
+            src = dst
+            k += 1
+    evs[k].record(stream)
+    torch.cuda.synchronize()
+    d = [evs[i].elapsed_time(evs[i + 1]) for i in range(k)]
+    per_plan = []
+    for j in range(len(plans)):
+        dj = sorted(d[j::len(plans)])
+        per_plan.append({"median_ms": round(dj[len(dj) // 2], 5),
+                         "geomean_ms": round(math.exp(sum(math.log(max(v, 1e-9)) for v in dj) / len(dj)), 5)})
+    out["per_exec_events"] = per_plan
+    if back_to_back:
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(back_to_back):
+            step()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        out["back_to_back"] = {"steps": back_to_back,
+                               "ms_per_exec": round(b0.elapsed_time(b1) / (back_to_back * len(plans)), 5)}
+    return out
+
+
+def work_per_exec(spec):
+    """(flops, algorithmic HBM bytes) of one exec (one direction)."""
+    n, batch = spec["n"], spec["batch"]
+    if spec["kind"] == "real":
+        # 2.5 N log2 N per row and direction; the real rows (4 B) once and the kept bins (8 B) once
+        return 2.5 * n * math.log2(n) * batch, batch * n * 4 + (spec["mmax"] + 1) * batch * 8
+    return 5.0 * n * math.log2(n) * batch, 2 * spec["passes"] * batch * n * 8   # read + write per HBM pass
+
+
+def rel(got, want):
+    import numpy as np
+    d = np.asarray(got, np.complex128) - np.asarray(want, np.complex128)
+    return float(np.linalg.norm(d.ravel()) / np.linalg.norm(np.asarray(want, np.complex128).ravel()))
+
+
+def parity_and_oracle(spec, x_host, outs):
+    """Relative L2 error of the GPU outputs against the oracle over the whole
+    output of the configuration, and the oracle's own time on that work (one
+    run, all host threads; the widening to f64 is not timed)."""
+    import numpy as np
+    import oracle
+    n = spec["n"]
+    res = {}
+    t_oracle = 0.0
+    flops = 0.0
+
+    def timed(fn, *a):
+        nonlocal t_oracle
+        t0 = time.perf_counter()
+        r = fn(*a)
+        t_oracle += time.perf_counter() - t0
+        return r
+
+    if spec["kind"] == "real":
+        mmax = spec["mmax"]
+        xs = np.ascontiguousarray(x_host.T).astype(np.complex128)        # [rows][mmax+1]
+        rows_gpu = outs[0]                                                 # C2R output [rows][n]
+        res["synthesis"] = rel(rows_gpu, timed(oracle.c2r, xs, n, mmax))
+        xr = rows_gpu.astype(np.float64)
+        res["analysis"] = rel(outs[1].T, timed(oracle.r2c, xr, mmax))      # same rows the GPU analysed
+        res["closed_form_r2c_c2r_eq_nF"] = rel(outs[1] / n, x_host)
+        flops = 2.5 * n * math.log2(n) * spec["batch"] * 2
+        sample = "whole output: C2R against the oracle's synthesis of F, R2C against the oracle's analysis " \
+                 "of the GPU's rows, and R2C(C2R(F)) = n F"
+    elif spec["kind"] == "2d":
+        want = timed(lambda v: oracle.fftshift_2d(oracle.c2c_2d(v, -1)), x_host)
+        res["forward_shifted"] = rel(outs[0], want)
+        flops = 5.0 * n * math.log2(n)
+        sample = "whole image, against the oracle's 2D transform followed by the index rotation"
+    elif len(spec["dirs"]) == 2:
+        res["forward"] = rel(outs[0], timed(oracle.c2c, x_host, -1))
+        res["inverse"] = rel(outs[1], timed(oracle.c2c, outs[0], +1))
+        res["round_trip"] = rel(outs[1] / n, x_host)
+        flops = 5.0 * n * math.log2(n) * spec["batch"] * 2
+        sample = "whole output: forward against the oracle, inverse against the oracle on the GPU's forward " \
+                 "output, and the round trip"
+    else:
+        # row chunks (16 rows each: one oracle thread per row)
+        err2 = ref2 = 0.0
+        for r0 in range(0, x_host.shape[0], 16):
+            want = timed(oracle.c2c, x_host[r0:r0 + 16], spec["dirs"][0])
+            d = outs[0][r0:r0 + 16].astype(np.complex128) - want
+            err2 += float(np.sum(np.abs(d) ** 2))
+            ref2 += float(np.sum(np.abs(want) ** 2))
+        res["forward"] = math.sqrt(err2 / ref2)
+        flops = 5.0 * n * math.log2(n) * spec["batch"]
+        sample = "whole output (all rows), oracle on chunks of 16 rows"
+    res = {k: float(f"{v:.4g}") for k, v in res.items()}
+    cpu = {"value": round(flops / t_oracle / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.threads(0),
+           "kind": "oracle", "sample": f"the parity reference: {sample}; one run, {t_oracle:.3f} s"}
+    return res, sample, cpu
+
+
+def measure_config(F, torch, name, steps, warmup):
+    """One configuration end to end: inputs, plans, timing, parity, oracle time."""
+    spec = workload_spec(name)
+    x_host = spec["gen"]()
+    xd = torch.from_numpy(x_host).cuda()
+    if spec["kind"] == "real":
+        bufs = [torch.empty((spec["batch"], spec["n"]), dtype=torch.float32, device="cuda"), torch.empty_like(xd)]
+    else:
+        bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
+    plans = make_plans(F, spec)
+    stream = torch.cuda.current_stream()
+    try:
+        tm = time_workload(F, torch, plans, xd, bufs, stream, steps, warmup,
+                           back_to_back=BACK_TO_BACK if name in ("w1", "w4") else 0)
+        torch.cuda.synchronize()
+        outs = [b.cpu().numpy() for b in bufs]
+    finally:
+        for p in plans:
+            F.fft_plan_destroy(p)
+    del xd, bufs
+    torch.cuda.empty_cache()
+    flops, nbytes = work_per_exec(spec)
+    ms = tm["ms_per_exec"]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    entry = {
+        "workload": spec["label"],
+        "ms_per_exec": round(ms, 5),
+        "ms_per_step": round(tm["ms_per_step"], 5),
+        "execs_per_step": len(plans),
+        "gflops": round(flops / (ms * 1e-3) / 1e9, 2),
+        "flop_convention": "2.5 N log2 N per real row" if spec["kind"] == "real" else "5 N log2 N",
+        "algorithmic_bytes_per_exec": nbytes,
+        "hbm_passes": spec["passes"],
+        "algorithmic_gbps": round(gbps, 1),
+        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "traffic": stored_traffic(TRAFFIC_KEY[name]),
+        "per_exec_events": tm["per_exec_events"],
+        "settle": tm["settle"],
+    }
+    if "back_to_back" in tm:
+        entry["back_to_back"] = tm["back_to_back"]
+    rl2, sample, cpu = parity_and_oracle(spec, x_host, outs)
+    entry["rel_l2"] = rl2
+    entry["rel_l2_sample"] = sample
+    entry["cpu_baseline"] = cpu
+    return entry
+
+
+def summarize_trace(path, out=sys.stdout):
+    """Per-kernel durations of a rocprofv3 kernel trace (CSV) of a bench run
+    under `rocprofv3 --kernel-trace --selected-regions`: the trace then holds
+    only the launches of the timed regions.  Prints a markdown table:
+    dispatches, median, mean, min and max duration (us), VGPRs, LDS."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(r)
+    print("| kernel | dispatches | median us | mean us | min us | max us | VGPR | AGPR | LDS B | scratch B |",
+          file=out)
+    print("|---|---|---|---|---|---|---|---|---|---|", file=out)
+    for name, rs in by.items():
+        d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs)
+        r0 = rs[0]
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{short}` | {len(d)} | {d[len(d) // 2]:.1f} | {sum(d) / len(d):.1f} | {d[0]:.1f} | "
+              f"{d[-1]:.1f} | {r0.get('VGPR_Count', r0.get('Arch_VGPR_Count', ''))} | "
+              f"{r0.get('Accum_VGPR_Count', '')} | {r0.get('LDS_Block_Size', r0.get('Group_Segment_Size', ''))} | "
+              f"{r0.get('Scratch_Size', r0.get('Private_Segment_Size', ''))} |", file=out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="w2", choices=["w1", "w2", "w3", "w4", "w5", "w6"])
+    ap.add_argument("--configs", choices=["all", "none"], default=None,
+                    help="also measure configurations c1-c5 (default: all with the w2 headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--real-pairs", action="store_true",
                     help="w4: two real rows per complex transform of length n")
@@ -187,7 +504,13 @@ def main():
                     help="w6 only: the row length (default 1000; rows scaled to keep ~512 MiB)")
     ap.add_argument("--direct", action="store_true",
                     help="w4: the band-limited direct sums on the matrix cores instead of the FFT")
+    ap.add_argument("--summarize-trace", metavar="CSV", default=None,
+                    help="print the per-kernel durations of a rocprofv3 kernel trace taken with "
+                         "--selected-regions (the timed launches only) and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the transforms are not sharded across devices", file=sys.stderr)
@@ -200,6 +523,8 @@ def main():
         raise SystemExit("--n applies to the any-length workload w6")
     if args.n is not None and (args.n < 3 or args.n & (args.n - 1) == 0):
         raise SystemExit("--n takes a length >= 3 that is not a power of two")
+    plain_headline = args.workload == "w2" and not (args.direct or args.real_pairs or args.n)
+    configs = args.configs or ("all" if plain_headline else "none")
 
     import numpy as np
     import torch
@@ -217,50 +542,10 @@ def main():
         bufs = [torch.empty((batch, n), dtype=torch.float32, device="cuda"), torch.empty_like(xd)]
     else:
         bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
-    plans = []
-    for s in spec["dirs"]:
-        if spec["kind"] == "real":
-            if args.direct:
-                kind = F.FFT_C2R_DIRECT if s > 0 else F.FFT_R2C_DIRECT
-            else:
-                kind = F.FFT_C2R if s > 0 else F.FFT_R2C
-            p = F.fft_plan_create(n, batch, kind, s)
-            F.fft_plan_set(p, F.FFT_OPT_MMAX, spec["mmax"])
-            F.fft_plan_set(p, F.FFT_OPT_SPEC_LAYOUT, 1)
-            if args.real_pairs:
-                F.fft_plan_set(p, F.FFT_OPT_REAL_PAIRS, 1)
-        elif spec["kind"] == "2d":
-            p = F.fft_plan_create_2d(spec["ny"], spec["nx"], batch, F.FFT_C2C, s)
-            F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
-        else:
-            p = F.fft_plan_create(n, batch, F.FFT_C2C, s)
-        plans.append(p)
+    plans = make_plans(F, spec, direct=args.direct, real_pairs=args.real_pairs)
     stream = torch.cuda.current_stream()
-
-    def step():
-        src = xd
-        for p, dst in zip(plans, bufs):
-            F.fft_exec(p, src, dst, stream.cuda_stream)
-            src = dst
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K steps between two synchronisations, bracketed by HIP
-    # events on the stream the kernels are launched on (no events between
-    # launches, which would insert gaps)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_exec_ms = ev0.elapsed_time(ev1) / (args.steps * len(plans))
+    tm = time_workload(F, torch, plans, xd, bufs, stream, args.steps, args.warmup)
+    avg_exec_ms = tm["ms_per_exec"]
 
     # each direction on its own (same buffers), outside the timed region
     per_dir = None
@@ -280,7 +565,7 @@ def main():
 
     # correctness guard for the numbers: the round trip must return N x
     check = None
-    if len(spec["dirs"]) == 2:
+    if len(spec["dirs"]) == 2 and spec["kind"] != "real":
         z = bufs[-1]
         check = float(torch.linalg.vector_norm(z / n - xd) / torch.linalg.vector_norm(xd))
 
@@ -298,28 +583,20 @@ def main():
     copy_gbps = 10 * 2 * a.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del a, b
 
-    ms_per_step = wall * 1e3 / args.steps
-    if spec["kind"] == "real":
-        # real transforms: 2.5 N log2 N per row and direction; bytes per exec:
-        # the real rows (4 B) once and the kept bins (8 B) once
-        flops_step = 2.5 * n * math.log2(n) * batch * len(spec["dirs"])
-        bytes_per_exec = batch * n * 4 + (spec["mmax"] + 1) * batch * 8
-    else:
-        flops_step = 5.0 * n * math.log2(n) * batch * len(spec["dirs"])
-        bytes_per_exec = 2 * spec["passes"] * x_host.nbytes      # read + write per HBM pass
-    value = flops_step / (ms_per_step * 1e-3) / 1e9
-    key = {"w1": "c2c_rows_1024", "w2": "c2c_rows_4096", "w3": "fourstep_2^22",
-           "w4": "real_2048", "w5": "2d_8192x8192", "w6": f"any_{n}"}[args.workload]
+    ms_per_step = tm["wall_ms_per_step"]
+    flops_exec, bytes_per_exec = work_per_exec(spec)
+    value = flops_exec * len(plans) / (ms_per_step * 1e-3) / 1e9
+    key = TRAFFIC_KEY.get(args.workload, f"any_{n}")
     if args.direct:
         # a real matrix product of batch x n x 2(mmax+1) per launch, on the
         # fp32 matrix cores
         key = "direct_2048"
-        flops_exec = 2.0 * batch * n * 2 * (spec["mmax"] + 1)
-        achieved = flops_exec / (avg_exec_ms * 1e-3) / 1e12
+        flops_mm = 2.0 * batch * n * 2 * (spec["mmax"] + 1)
+        achieved = flops_mm / (avg_exec_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
                 "traffic": stored_traffic(key), "kernel": key, "avg_launch_ms": round(avg_exec_ms, 5),
-                "algorithmic_flops_per_launch": flops_exec,
+                "algorithmic_flops_per_launch": flops_mm,
                 "algorithmic_bytes_per_launch": bytes_per_exec}
     else:
         achieved = bytes_per_exec / (avg_exec_ms * 1e-3) / 1e9
@@ -352,17 +629,51 @@ def main():
                    else "interleaved complex64"},
         "roofline": roof,
         "copy_gbps": round(copy_gbps, 1),
+        "per_exec_events": tm["per_exec_events"],
+        "settle": dict(tm["settle"], note="the workload ran this long before the warm-up steps, so that "
+                                          "the timed region sees the GPU's steady state, not its ramp from idle"),
     }
     if check is not None:
         out["round_trip_rel_l2"] = check
     if per_dir is not None:
         out["ms_per_direction"] = per_dir
+    outs = [b.cpu().numpy() for b in bufs] if configs == "all" else None
     for p in plans:
         F.fft_plan_destroy(p)
     del xd, bufs
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, x_host, direct=args.direct)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+
+    if configs == "all":
+        # every configuration of the metric in the same run; c2 is the
+        # headline measurement above (its timed region, parity on its outputs)
+        recs = {}
+        for cname, wname in CONFIGS:
+            print(f"[bench] {cname} ({wname})", file=sys.stderr, flush=True)
+            if wname == args.workload:
+                rl2, sample, cpu = parity_and_oracle(spec, x_host, outs)
+                flops, nbytes = work_per_exec(spec)
+                gbps = nbytes / (avg_exec_ms * 1e-3) / 1e9
+                recs[cname] = {"workload": spec["label"], "ms_per_exec": round(avg_exec_ms, 5),
+                               "ms_per_step": round(tm["ms_per_step"], 5), "execs_per_step": len(plans),
+                               "gflops": round(flops / (avg_exec_ms * 1e-3) / 1e9, 2),
+                               "flop_convention": "5 N log2 N", "algorithmic_bytes_per_exec": nbytes,
+                               "hbm_passes": spec["passes"], "algorithmic_gbps": round(gbps, 1),
+                               "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "traffic": roof["traffic"],
+                               "per_exec_events": tm["per_exec_events"], "settle": tm["settle"], "rel_l2": rl2,
+                               "rel_l2_sample": sample, "cpu_baseline": cpu}
+            else:
+                recs[cname] = measure_config(F, torch, wname, args.steps, args.warmup)
+            if cname in BAR_CONFIGS:
+                recs[cname]["bar_frac"] = BAR
+                recs[cname]["meets_bar"] = recs[cname]["frac_of_hbm_peak"] >= BAR
+            else:
+                recs[cname]["bar_frac"] = None      # launch-bound parity configurations
+            recs[cname]["parity_ok"] = all(v <= 1e-5 for v in recs[cname]["rel_l2"].values())
+            recs[cname]["cpu_baseline"]["cpu_model"] = cpu_model()
+        out["configs"] = recs
     print(json.dumps(out), flush=True)
 
 

@@ -26,6 +26,7 @@ __global__ __launch_bounds__(rows_threads(M) * C) void k_bluestein(BluesteinArgs
   using L = RowLds<M, SPLIT, E>;
   static_assert(row_lds_bytes(M, C, SPLIT, E) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -62,7 +63,7 @@ struct BluesteinOp {
     uint32_t grid;
     hipError_t e = grid_of(a.rows, C, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_bluestein<M, C>), dim3(grid), dim3(rows_threads(M) * C), 0, st, a);
+    FFTAMD_LAUNCH((k_bluestein<M, C>), dim3(grid), dim3(rows_threads(M) * C), 0, st, a);
     return hipGetLastError();
   }
 };

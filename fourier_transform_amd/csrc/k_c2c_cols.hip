@@ -12,7 +12,7 @@ struct ColsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.images * a.nx, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_c2c_cols<N, S>), dim3(grid), dim3(C * (N / tile_e(N, false))), 0, st, a);
+      FFTAMD_LAUNCH((k_c2c_cols<N, S>), dim3(grid), dim3(C * (N / tile_e(N, false))), 0, st, a);
       return hipGetLastError();
     }
   };

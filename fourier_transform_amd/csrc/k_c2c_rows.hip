@@ -12,7 +12,7 @@ struct RowsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.rows, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_c2c_rows<N, S, C>), dim3(grid), dim3(rows_threads(N) * C), 0, st, a);
+      FFTAMD_LAUNCH((k_c2c_rows<N, S, C>), dim3(grid), dim3(rows_threads(N) * C), 0, st, a);
       return hipGetLastError();
     }
   };

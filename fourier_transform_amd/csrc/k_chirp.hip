@@ -44,6 +44,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
   __shared__ float2 ftab[C * FP];
   __shared__ float2 twl[LTW ? TW1 : 1];
+  lds_poison(lds, ftab, twl);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -154,6 +155,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   using L = ColLds<N2, C, SPLIT>;
   static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -205,7 +207,7 @@ struct ChirpMidOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_chirp_mid<N1, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
+      FFTAMD_LAUNCH((k_chirp_mid<N1, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
@@ -225,7 +227,7 @@ struct ChirpOutOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_chirp_out<N2>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
+      FFTAMD_LAUNCH((k_chirp_out<N2>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
       return hipGetLastError();
     }
   };

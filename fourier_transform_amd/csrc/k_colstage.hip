@@ -15,6 +15,7 @@ __global__ __launch_bounds__(colstage_lines(L) * (L / colstage_values(L))) void 
   using L_ = ColLds<L, C, false>;
   static_assert(L_::size(C) * sizeof(float2) <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L_::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -54,7 +55,7 @@ struct ColStageOp {
       hipError_t e = grid_of(a.nlines, C, &grid);
       if (e != hipSuccess) return e;
       if (a.images < 1 || a.images > 65535) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL((k_col_stage<L, S, TW>), dim3(grid, a.images), dim3(C * (L / colstage_values(L))), 0, st, a);
+      FFTAMD_LAUNCH((k_col_stage<L, S, TW>), dim3(grid, a.images), dim3(C * (L / colstage_values(L))), 0, st, a);
       return hipGetLastError();
     }
   };

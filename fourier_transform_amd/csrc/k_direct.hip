@@ -131,6 +131,7 @@ template <bool SYN, bool MMAJOR, bool VEC>
 __global__ __launch_bounds__(kDirThreads) void k_direct(DirectArgs a) {
   extern __shared__ float4 smem4[];
   float* smem = reinterpret_cast<float*>(smem4);
+  lds_poison_dynamic(smem, (uint32_t)direct_lds_bytes(a.n));
   const uint32_t n = (uint32_t)a.n, half = n / 2;
   float* T = smem;                                    // (cos, -sin)(2 pi u/n), u <= n/2
   float* As = smem + direct_table_floats((int)n);     // A slice [128][kDirPitch]
@@ -308,6 +309,7 @@ template <bool SYN, bool MMAJOR, bool VEC, int RB>
 __global__ __launch_bounds__(kDirThreads) void k_direct_small(DirectArgs a) {
   extern __shared__ float4 smem4[];
   float* smem = reinterpret_cast<float*>(smem4);
+  lds_poison_dynamic(smem, (uint32_t)(direct_table_floats(a.n) + 4 * RB * 1024) * 4u);
   const uint32_t n = (uint32_t)a.n, half = n / 2;
   float* T = smem;
   float* red = smem + direct_table_floats((int)n);  // [4 waves][RB][16][64 lanes]
@@ -428,26 +430,26 @@ hipError_t launch_direct_as(const DirectArgs& a, hipStream_t st, int64_t N, bool
     if (big > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)big);
     if (a.mmajor && (SYN || !vec))
-      hipLaunchKernelGGL((k_direct<SYN, true, false>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct<SYN, true, false>), grid, block, lds, st, a);
     else if (a.mmajor)
-      hipLaunchKernelGGL((k_direct<SYN, true, true>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct<SYN, true, true>), grid, block, lds, st, a);
     else if (vec)
-      hipLaunchKernelGGL((k_direct<SYN, false, true>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct<SYN, false, true>), grid, block, lds, st, a);
     else
-      hipLaunchKernelGGL((k_direct<SYN, false, false>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct<SYN, false, false>), grid, block, lds, st, a);
   } else {
     constexpr int RB = 1;
     const int64_t blocks = ((a.rows + 32 * RB - 1) / (32 * RB)) * ((N + 31) / 32);
     const size_t lds = (size_t)(direct_table_floats(a.n) + 4 * RB * 1024) * 4;
     const dim3 grid((uint32_t)blocks);
     if (a.mmajor && (SYN || !vec))
-      hipLaunchKernelGGL((k_direct_small<SYN, true, false, RB>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct_small<SYN, true, false, RB>), grid, block, lds, st, a);
     else if (a.mmajor)
-      hipLaunchKernelGGL((k_direct_small<SYN, true, true, RB>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct_small<SYN, true, true, RB>), grid, block, lds, st, a);
     else if (vec)
-      hipLaunchKernelGGL((k_direct_small<SYN, false, true, RB>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct_small<SYN, false, true, RB>), grid, block, lds, st, a);
     else
-      hipLaunchKernelGGL((k_direct_small<SYN, false, false, RB>), grid, block, lds, st, a);
+      FFTAMD_LAUNCH((k_direct_small<SYN, false, false, RB>), grid, block, lds, st, a);
   }
   return hipGetLastError();
 }

@@ -47,6 +47,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   __shared__ float lds[L::size(NA)];
   __shared__ float2 twl[LTW ? TW1 : 1];
+  lds_poison(lds, twl);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
   constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   __shared__ float lds[L::size(C)];
   __shared__ float2 twl[LTW ? TW1 : 1];
+  lds_poison(lds, twl);
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -216,12 +218,12 @@ hipError_t run_fold(const FoldArgs& a, hipStream_t st) {
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FoldArgs p1 = a;
   p1.out = a.scratch;
-  hipLaunchKernelGGL((k_rows_fold<NX, NA, E1, S>), dim3((uint32_t)g1), dim3(NA * NX / E1), 0, st, p1);
+  FFTAMD_LAUNCH((k_rows_fold<NX, NA, E1, S>), dim3((uint32_t)g1), dim3(NA * NX / E1), 0, st, p1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   FoldArgs p2 = a;
   p2.in = a.scratch;
-  hipLaunchKernelGGL((k_fold_cols<NB, C, E2, S>), dim3((uint32_t)g2), dim3(C * NB / E2), 0, st, p2);
+  FFTAMD_LAUNCH((k_fold_cols<NB, C, E2, S>), dim3((uint32_t)g2), dim3(C * NB / E2), 0, st, p2);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
-// Instantiations and launchers of the two four-step passes (lengths beyond one
-// workgroup): strided column transforms with the inter-pass twiddle, then row
-// transforms with a transposing store.
+// Instantiations and launcher of four-step pass 1 (lengths beyond one
+// workgroup): strided column transforms with the inter-pass twiddle fused
+// into their block-layout store.  Pass 2 is in k_fourstep_rows.hip.
 #include "kernels.hpp"
 
 namespace fftamd {
@@ -22,33 +22,12 @@ struct FsColsOp {
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_cols<N2, S, BK, HOOK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
+      FFTAMD_LAUNCH((k_fs_cols<N2, S, BK, HOOK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
       if (a.n1 == N2) return go<tile_lines(N2, true)>(a, st);
       if (2 * a.n1 == N2) return go<tile_lines(N2 / 2, true)>(a, st);
-      return hipErrorInvalidValue;
-    }
-  };
-};
-template <int S>
-struct FsRowsOp {
-  template <int N1>
-  struct At {
-    template <int BC>
-    static hipError_t go(const FourStepArgs& a, hipStream_t st) {
-      constexpr int C = tile_lines(N1, true);
-      if ((a.batch * a.n2) % C != 0) return hipErrorInvalidValue;  // the kernel loads whole groups
-      uint32_t grid;
-      hipError_t e = grid_of(a.batch * a.n2, C, &grid);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((k_fs_rows<N1, S, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
-      return hipGetLastError();
-    }
-    static hipError_t run(const FourStepArgs& a, hipStream_t st) {
-      if (a.n2 == N1) return go<tile_lines(N1, false)>(a, st);
-      if (a.n2 == 2 * N1) return go<tile_lines(2 * N1, false)>(a, st);
       return hipErrorInvalidValue;
     }
   };
@@ -62,9 +41,5 @@ hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStre
   }
   if (sign < 0) return dispatch_pow2<FsColsOp<-1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
   return dispatch_pow2<FsColsOp<1, false>::At, kFourStepMin, kMaxSinglePass>(n2, a, st);
-}
-hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t st) {
-  if (sign < 0) return dispatch_pow2<FsRowsOp<-1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
-  return dispatch_pow2<FsRowsOp<1>::At, kFourStepMin, kMaxSinglePass>(n1, a, st);
 }
 }  // namespace fftamd

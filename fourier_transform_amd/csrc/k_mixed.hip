@@ -320,6 +320,7 @@ template <int S, int KB, int RMAX, bool PAD>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
+  lds_poison_dynamic(smem, (uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) * sizeof(float2));
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -341,6 +342,7 @@ template <bool PAD>
 __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
+  lds_poison_dynamic(smem, (uint32_t)a.lines * rader_line((uint32_t)a.n, PAD) * sizeof(float2));
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -390,6 +392,7 @@ template <bool PAD>
 __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixedArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
+  lds_poison_dynamic(smem, (uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) * sizeof(float2));
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -445,20 +448,20 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   if (rmax > 8) {
     if (a.pad) {
       if (sign < 0)
-        hipLaunchKernelGGL((k_mixed<-1, 1, 16, true>), dim3(grid), block, lds, st, a);
+        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true>), dim3(grid), block, lds, st, a);
       else
-        hipLaunchKernelGGL((k_mixed<1, 1, 16, true>), dim3(grid), block, lds, st, a);
+        FFTAMD_LAUNCH((k_mixed<1, 1, 16, true>), dim3(grid), block, lds, st, a);
     } else if (sign < 0) {
-      hipLaunchKernelGGL((k_mixed<-1, 1, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false>), dim3(grid), block, lds, st, a);
     } else {
-      hipLaunchKernelGGL((k_mixed<1, 1, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<1, 1, 16, false>), dim3(grid), block, lds, st, a);
     }
   } else if (a.pad) {
     return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    hipLaunchKernelGGL((k_mixed<-1, 2, 8, false>), dim3(grid), block, lds, st, a);
+    FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false>), dim3(grid), block, lds, st, a);
   } else {
-    hipLaunchKernelGGL((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
+    FFTAMD_LAUNCH((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
   }
   return hipGetLastError();
 }
@@ -474,9 +477,9 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
   if (a.pad)
-    hipLaunchKernelGGL((k_rader<true>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<true>), dim3(grid), block, lds, st, a, rd);
   else
-    hipLaunchKernelGGL((k_rader<false>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<false>), dim3(grid), block, lds, st, a, rd);
   return hipGetLastError();
 }
 
@@ -492,9 +495,9 @@ hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, h
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
   if (a.pad)
-    hipLaunchKernelGGL((k_bluestein_mixed<true>), dim3(grid), block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_bluestein_mixed<true>), dim3(grid), block, lds, st, a, c);
   else
-    hipLaunchKernelGGL((k_bluestein_mixed<false>), dim3(grid), block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_bluestein_mixed<false>), dim3(grid), block, lds, st, a, c);
   return hipGetLastError();
 }
 

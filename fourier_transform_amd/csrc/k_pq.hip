@@ -219,6 +219,7 @@ __global__ __launch_bounds__(rows_threads(Q) * P * C) void k_c2c_pq(PqArgs a) {
   using L = RowLds<Q>;
   static_assert(row_lds_bytes(Q, C * P) <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C * P)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid - line * T;  // line = c P + p
@@ -278,7 +279,7 @@ struct PqOp {
         uint32_t grid;
         hipError_t e = grid_of(a.rows, C, &grid);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((k_c2c_pq<Q, P, S, C>), dim3(grid), dim3(rows_threads(Q) * P * C), 0, st, a);
+        FFTAMD_LAUNCH((k_c2c_pq<Q, P, S, C>), dim3(grid), dim3(rows_threads(Q) * P * C), 0, st, a);
         return hipGetLastError();
       }
     }

@@ -24,7 +24,7 @@ int real_split(int64_t rows) {
       uint32_t grid;                                                                              \
       hipError_t e = grid_of(ROWS, C, &grid);                                                     \
       if (e != hipSuccess) return e;                                                              \
-      hipLaunchKernelGGL((KERNEL<LEN, C>), dim3(grid), dim3(threads_per_line(LEN) * C), 0, st, a); \
+      FFTAMD_LAUNCH((KERNEL<LEN, C>), dim3(grid), dim3(threads_per_line(LEN) * C), 0, st, a); \
       return hipGetLastError();                                                                   \
     }                                                                                             \
     static hipError_t run(const RealArgs& a, hipStream_t st) {                                    \

@@ -130,7 +130,7 @@ hipError_t launch_items(void (*k)(RealAnyArgs), int64_t total, const RealAnyArgs
   uint32_t grid;
   hipError_t e = grid_of(total, kRealAnyThreads, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(grid), dim3(kRealAnyThreads), 0, st, a);
+  FFTAMD_LAUNCH(k, dim3(grid), dim3(kRealAnyThreads), 0, st, a);
   return hipGetLastError();
 }
 bool args_ok(const RealAnyArgs& a) {

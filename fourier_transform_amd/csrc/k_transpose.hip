@@ -14,6 +14,7 @@ __global__ __launch_bounds__(kTile * kTileRows) void k_transpose(const float2* _
                                                               float2* __restrict__ out, int64_t rows,
                                                               int64_t cols, int64_t tiles_c) {
   __shared__ float2 tile[kTile][kTile + 1];
+  lds_poison(tile);
   const int64_t img = blockIdx.y;
   const int64_t tr = (int64_t)blockIdx.x / tiles_c, tc = (int64_t)blockIdx.x % tiles_c;
   const int tx = threadIdx.x, ty = threadIdx.y;
@@ -38,7 +39,7 @@ hipError_t launch_transpose(const float2* in, float2* out, int64_t rows, int64_t
   if (rows < 1 || cols < 1 || images < 1 || images > 65535) return hipErrorInvalidValue;
   const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
   if (tiles_r * tiles_c > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_transpose, dim3((uint32_t)(tiles_r * tiles_c), (uint32_t)images),
+  FFTAMD_LAUNCH(k_transpose, dim3((uint32_t)(tiles_r * tiles_c), (uint32_t)images),
                      dim3(kTile, kTileRows), 0, st, in, out, rows, cols, tiles_c);
   return hipGetLastError();
 }

@@ -11,8 +11,12 @@ namespace fftamd {
 template <bool SPLIT>
 using lds_elem_t = typename std::conditional<SPLIT, float, float2>::type;
 
-// Real transforms: whole rows, >= 8 rows per workgroup so that m-major
-// spectrum accesses form 64 B runs.
+// Real transforms: whole rows, the largest rows-per-workgroup count (8 where
+// a line is short) that fits the thread and LDS limits, so that m-major
+// spectrum accesses form 64 B runs on large batches.  The launchers
+// (k_real.hip, real_split) run a half or a quarter of this count per
+// workgroup while the full count would leave fewer workgroups than CUs
+// (w4's 1024 rows of 2048: 4 rows per workgroup, 32 B runs).
 constexpr int real_rows_per_wg(int h) {
   int c = rows_per_wg(h) < 8 ? 8 : rows_per_wg(h);
   while (c > 1 && (c * threads_per_line(h) > kMaxThreads || row_lds_bytes(h, c) + c * 8 > kLdsBudgetBytes)) c /= 2;
@@ -31,6 +35,7 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   using L = RowLds<N, SPLIT, E>;
   static_assert(row_lds_bytes(N, C, SPLIT, E) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -79,6 +84,7 @@ __global__ __launch_bounds__(tile_lines(N, false) * (N / tile_e(N, false))) void
   using L = ColLds<N, C, SPLIT>;
   static_assert(L::size(C) * sizeof(lds_elem_t<SPLIT>) <= kLdsBudgetBytes, "LDS budget");
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -124,6 +130,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
   using L = RowLds<H>;
   static_assert(row_lds_bytes(H, C) <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -184,6 +191,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
   static_assert(row_lds_bytes(H, C) + C * 8 <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C)];
   __shared__ float2 nyq[C];
+  lds_poison(lds, nyq);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -259,6 +267,7 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_r2c_pairs(RealArgs 
   using L = RowLds<N>;
   static_assert(row_lds_bytes(N, C) <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C)];
+  lds_poison(lds);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -325,6 +334,7 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2r_pairs(RealArgs 
   static_assert(row_lds_bytes(N, C) + 2 * C * 8 <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C)];
   __shared__ float2 nyq[2 * C];
+  lds_poison(lds, nyq);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;
@@ -458,6 +468,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
   __shared__ float2 ftab[C * FP];
   __shared__ float2 twl[LTW ? TW1 : 1];
+  lds_poison(lds, ftab, twl);
 
   const int tid = threadIdx.x;
   const int line = tid % C, u = tid / C;
@@ -585,6 +596,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
                        L::size(C) * sizeof(lds_elem_t<SPLIT>) + TW1 * sizeof(float2) <= kLdsBudgetBytes;
   __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
   __shared__ float2 twl[LTW ? TW1 : 1];
+  lds_poison(lds, twl);
 
   const int tid = threadIdx.x;
   const int line = tid / T, u = tid % T;

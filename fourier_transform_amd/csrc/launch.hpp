@@ -6,10 +6,23 @@
 // and returns the launch status.  Pointers are device pointers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fftamd {
+
+// Completion event of the plan whose kernels are being enqueued: set by
+// fft_exec around a plan's launch sequence (outside graph capture), null
+// otherwise (thread-local).  Every launch binds it to the completion of its
+// own dispatch (the stop event of hipExtLaunchKernel), so after an exec it
+// stands for the end of the exec's last kernel without a separate marker
+// command in the stream (a marker per exec measured 1-2 us of idle GPU time
+// between launches).
+hipEvent_t& exec_done_event();
+#define FFTAMD_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                   \
+  hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, nullptr, ::fftamd::exec_done_event(), 0, \
+                        __VA_ARGS__)
 
 // Whole rows of length n (contiguous), one transform per row.
 // shift_mode: 0 none; 1 multiply element j by (-1)^j; 2 multiply element j of

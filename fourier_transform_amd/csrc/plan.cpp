@@ -24,6 +24,11 @@
 
 using namespace fftamd;
 
+hipEvent_t& fftamd::exec_done_event() {
+  thread_local hipEvent_t e = nullptr;
+  return e;
+}
+
 namespace {
 
 constexpr int kFourStepMaxLog = 2 * ilog2c(kMaxSinglePass);  // 2^28
@@ -242,6 +247,12 @@ struct fft_plan {
   bool any2d = false;
   fft_plan* inner2 = nullptr;
   float2* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  // completion of the plan's last exec outside graph capture (destroy waits
+  // for it; an exec on another stream first waits for it)
+  hipEvent_t done = nullptr;
+  bool recorded = false;
+  hipStream_t last_stream = nullptr;
 };
 
 namespace {
@@ -274,7 +285,18 @@ void free_plan(fft_plan* p) {
   if (p->inner2) free_plan(p->inner2);
   if (p->tables) (void)hipFree(p->tables);
   if (p->scratch) (void)hipFree(p->scratch);
+  if (p->done) (void)hipEventDestroy(p->done);
   delete p;
+}
+
+// wait for the last recorded exec of the plan and of its inner plans (an
+// inner plan records its own event, and the outer exec may have failed after
+// the inner one was enqueued)
+void wait_plan(fft_plan* p) {
+  if (!p) return;
+  if (p->recorded) (void)hipEventSynchronize(p->done);
+  wait_plan(p->inner);
+  wait_plan(p->inner2);
 }
 
 // allocate and upload the tables (called after every argument check passed)
@@ -297,7 +319,10 @@ int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
   if (scratch_bytes) {
     e = hipMalloc((void**)&p->scratch, scratch_bytes);
     if (e != hipSuccess) return hip_err(e, "hipMalloc(scratch)");
+    p->scratch_bytes = scratch_bytes;
   }
+  e = hipEventCreateWithFlags(&p->done, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_err(e, "hipEventCreateWithFlags");
   return FFT_OK;
 }
 
@@ -954,38 +979,39 @@ int fft_plan_get_sizes(const fft_plan* p, int64_t* in_bytes, int64_t* out_bytes)
   return ok();
 }
 
-int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
+}  // extern "C"
+
+namespace {
+
+int check_exec_args(const fft_plan* p, const void* in, const void* out) {
   if (!p) return set_err(FFT_EINVAL, "plan is NULL");
   if (!in || !out) return set_err(FFT_EINVAL, "in and out must be device pointers");
   if (((uintptr_t)in & 7) || ((uintptr_t)out & 7)) return set_err(FFT_EINVAL, "buffers must be 8-byte aligned");
   if (p->kind != FFT_C2C && in == out) return set_err(FFT_EINVAL, "R2C/C2R cannot run in place");
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return FFT_OK;
+}
 
-  int cur = 0;
-  hipError_t e = hipGetDevice(&cur);
-  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
-  if (cur != p->device) {
-    e = hipSetDevice(p->device);
-    if (e != hipSuccess) return hip_err(e, "hipSetDevice");
-  }
-  p->executed = true;
+// The launch sequence of plan p on `stream` (device already current), with
+// `sc` as the plan's scratch.  Inner plans run through fft_exec.
+int run_plan(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float2* sc) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  hipError_t e = hipSuccess;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
   if (p->any2d) {
     int rc = fft_exec(p->inner, in, out, stream_);
-    if (rc == FFT_OK) e = launch_transpose(dst, p->scratch, p->ny, p->nx, p->batch, stream);
-    if (rc == FFT_OK && e == hipSuccess) rc = fft_exec(p->inner2, p->scratch, p->scratch, stream_);
-    if (rc == FFT_OK && e == hipSuccess) e = launch_transpose(p->scratch, dst, p->nx, p->ny, p->batch, stream);
-    if (cur != p->device) (void)hipSetDevice(cur);
+    if (rc == FFT_OK) e = launch_transpose(dst, sc, p->ny, p->nx, p->batch, stream);
+    if (rc == FFT_OK && e == hipSuccess) rc = fft_exec(p->inner2, sc, sc, stream_);
+    if (rc == FFT_OK && e == hipSuccess) e = launch_transpose(sc, dst, p->nx, p->ny, p->batch, stream);
     if (rc != FFT_OK) return rc;
     if (e != hipSuccess) return hip_err(e, "kernel launch");
-    return ok();
+    return FFT_OK;
   }
   if (p->real_any) {
     const bool even = p->n % 2 == 0;
     const int64_t len = even ? p->n / 2 : p->n;
-    float2* s1 = p->scratch;
-    float2* s2 = p->scratch + p->batch * len;
+    float2* s1 = sc;
+    float2* s2 = sc + p->batch * len;
     RealAnyArgs ra{nullptr, nullptr, p->rt, p->batch, (int)p->n, (int)len, (int)p->mmax, p->spec_layout};
     int rc = FFT_OK;
     if (p->kind == FFT_R2C && even) {
@@ -1003,10 +1029,9 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       if (e == hipSuccess) rc = fft_exec(p->inner, s1, s2, stream_);
       if (e == hipSuccess && rc == FFT_OK) ra.in = s2, ra.out = out, e = launch_real_part(ra, stream);
     }
-    if (cur != p->device) (void)hipSetDevice(cur);
     if (rc != FFT_OK) return rc;
     if (e != hipSuccess) return hip_err(e, "kernel launch");
-    return ok();
+    return FFT_OK;
   }
   if (p->pq) {
     PqArgs a{src, dst, p->tw_a, p->wn, p->batch, p->shift ? 1 : 0};
@@ -1039,8 +1064,8 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
   } else if (p->bluestein && p->fourstep) {
     const float2* pre = p->shift == 1 ? p->chirp_shift : p->shift == 2 ? p->chirp_ishift : p->chirp;
     const int64_t m = p->bm;
-    float2* s1 = p->scratch;
-    float2* s2 = p->scratch + m * p->batch;
+    float2* s1 = sc;
+    float2* s2 = sc + m * p->batch;
     // pass 1: the chirped row (zero beyond n), forward n2-point column
     // transforms with the four-step factor, into s1
     FourStepArgs f1{src, s1, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0,
@@ -1066,10 +1091,10 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     RowsArgs a{src, dst, p->tw_a, p->batch, p->shift ? 1 : 0, 1, 1};
     e = launch_c2c_rows((int)p->n, p->sign, a, stream);
   } else if (p->kind == FFT_C2C && p->dims == 1) {
-    FourStepArgs a{src, p->scratch, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, p->shift};
+    FourStepArgs a{src, sc, p->tw_b, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, p->shift};
     e = launch_fourstep_cols(p->n2, p->sign, a, stream);
     if (e == hipSuccess) {
-      FourStepArgs b{p->scratch, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
+      FourStepArgs b{sc, dst, p->tw_a, p->thi, p->tlo, p->batch, p->n1, p->n2, p->bits, 0};
       e = launch_fourstep_rows(p->n1, p->sign, b, stream);
     }
   } else if (p->kind == FFT_C2C && !p->tall) {
@@ -1081,20 +1106,20 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
     }
   } else if (p->kind == FFT_C2C && p->fold) {
     // rows and the first column factor: in -> scratch; columns: scratch -> out
-    FoldArgs a{src, dst, p->scratch, p->tw_ca, p->tw_cb, p->wt, p->batch, p->ny, p->nx, p->shift ? 1 : 0};
+    FoldArgs a{src, dst, sc, p->tw_ca, p->tw_cb, p->wt, p->batch, p->ny, p->nx, p->shift ? 1 : 0};
     e = launch_fold_2d(p->sign, a, stream);
   } else if (p->kind == FFT_C2C) {
     // rows: in -> scratch; column step A in place on scratch; step B scratch -> out
     const uint32_t nx = (uint32_t)p->nx, na = kTallSplit, nb = (uint32_t)(p->ny / kTallSplit);
-    RowsArgs a{src, p->scratch, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny, 0};
+    RowsArgs a{src, sc, p->tw_a, p->batch * p->ny, p->shift ? 2 : 0, p->ny, 0};
     e = launch_c2c_rows((int)p->nx, p->sign, a, stream);
     if (e == hipSuccess) {
-      ColStageArgs ca{p->scratch, p->scratch, p->tw_ca, p->wt, (int64_t)na * nx, p->ny * p->nx, (int)p->batch,
+      ColStageArgs ca{sc, sc, p->tw_ca, p->wt, (int64_t)na * nx, p->ny * p->nx, (int)p->batch,
                       nx, (uint32_t)ilog2c(nx), nx, na * nx, nx, na * nx};
       e = launch_col_stage((int)nb, p->sign, true, ca, stream);
     }
     if (e == hipSuccess) {
-      ColStageArgs cb{p->scratch, dst, p->tw_cb, p->wt, (int64_t)nb * nx, p->ny * p->nx, (int)p->batch,
+      ColStageArgs cb{sc, dst, p->tw_cb, p->wt, (int64_t)nb * nx, p->ny * p->nx, (int)p->batch,
                       nx, (uint32_t)ilog2c(nx), na * nx, nx, nx, nb * nx};
       e = launch_col_stage((int)na, p->sign, false, cb, stream);
     }
@@ -1110,9 +1135,64 @@ int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream_) {
       e = p->kind == FFT_R2C ? launch_r2c((int)(p->n / 2), a, stream) : launch_c2r((int)(p->n / 2), a, stream);
     }
   }
-  if (cur != p->device) (void)hipSetDevice(cur);
   if (e != hipSuccess) return hip_err(e, "kernel launch");
-  return ok();
+  return FFT_OK;
+}
+
+// fft_exec and fft_exec_noalloc after their argument checks: the plan's
+// device made current, ordering against the plan's previous exec, the
+// launches, and the completion event.  Outside graph capture every kernel of
+// the exec binds the plan's event to its own completion (exec_done_event,
+// FFTAMD_LAUNCH), so the event ends up standing for the exec's last kernel;
+// fft_plan_destroy waits for it, and an exec on another stream than the
+// plan's last one first waits for it (both would use the plan's scratch).
+// The inner plans of an exec (any-length 2D and real plans) bind the outer
+// plan's event.  Inside a capture none of this is done (an event bound
+// outside the capture cannot be waited on inside it): the caller orders
+// captured work and finishes the graph's launches before destroying the
+// plan.
+int exec_common(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float2* sc) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+  if (cur != p->device) {
+    e = hipSetDevice(p->device);
+    if (e != hipSuccess) return hip_err(e, "hipSetDevice");
+  }
+  hipEvent_t& bound = exec_done_event();
+  const hipEvent_t outer = bound;  // non-null while an outer plan's exec runs this one
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+  const bool track = !capturing && !outer;
+  int rc = FFT_OK;
+  if (track && p->recorded && p->last_stream != stream) {
+    e = hipStreamWaitEvent(stream, p->done, 0);
+    if (e != hipSuccess) rc = hip_err(e, "hipStreamWaitEvent");
+  }
+  if (rc == FFT_OK) {
+    if (track) bound = p->done;
+    rc = run_plan(p, in, out, stream_, sc);
+    bound = outer;
+    if (track) {
+      // also after a failed sequence: its first kernels may have been
+      // enqueued (an event nothing was bound to completes at once)
+      p->recorded = true;
+      p->last_stream = stream;
+    }
+  }
+  if (rc == FFT_OK) p->executed = true;  // only once a launch sequence went through
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return rc == FFT_OK ? ok() : rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream) {
+  if (check_exec_args(p, in, out) != FFT_OK) return g_err.code;
+  return exec_common(p, in, out, stream, p->scratch);
 }
 
 void fft_plan_destroy(fft_plan* p) {
@@ -1121,12 +1201,13 @@ void fft_plan_destroy(fft_plan* p) {
     return;
   }
   // work enqueued with this plan may still read its tables and scratch: wait
-  // for the plan's device, then free (restoring the caller's device)
+  // for its last recorded exec (not for the rest of the device), then free
+  // on the plan's device (restoring the caller's)
+  wait_plan(p);
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
   const bool other = have_cur && cur != p->device;
   if (other) (void)hipSetDevice(p->device);
-  if (p->executed) (void)hipDeviceSynchronize();
   free_plan(p);
   if (other) (void)hipSetDevice(cur);
   ok();

@@ -377,6 +377,42 @@ struct StageIdx {
   }
 };
 
+// LDS-poison debug build (compiled with -DFFTAMD_LDS_POISON=1, the library
+// libfft_amd_poison.so): every kernel first fills its LDS arrays with quiet
+// NaNs and synchronises, so that a read of LDS that no thread of the
+// workgroup has written in this kernel -- a missing barrier, a wrong index, a
+// read of a pad element -- turns the output into NaNs instead of reusing a
+// stale value left by an earlier workgroup.  (The hazard: the radix-2 kernel
+// of the "Fast Fourier Transform on CPU and GPU" page loads shared memory and
+// stores back into it with no barrier in between.)  In the default build the
+// calls compile to nothing.
+#ifndef FFTAMD_LDS_POISON
+#define FFTAMD_LDS_POISON 0
+#endif
+__device__ __forceinline__ void lds_poison_bytes(void* p, uint32_t bytes) {
+  if constexpr (FFTAMD_LDS_POISON != 0) {
+    uint32_t* w = static_cast<uint32_t*>(p);
+    const uint32_t nt = blockDim.x * blockDim.y * blockDim.z;
+    const uint32_t t = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+    for (uint32_t i = t; i < bytes / 4; i += nt) w[i] = 0x7fc00000u;
+  }
+}
+// static __shared__ arrays (sizes from their types), then a workgroup barrier
+template <class... A>
+__device__ __forceinline__ void lds_poison(A&... arrays) {
+  if constexpr (FFTAMD_LDS_POISON != 0) {
+    (lds_poison_bytes(static_cast<void*>(&arrays), (uint32_t)sizeof(arrays)), ...);
+    __syncthreads();
+  }
+}
+// dynamic LDS of `bytes` bytes, then a workgroup barrier
+__device__ __forceinline__ void lds_poison_dynamic(void* p, uint32_t bytes) {
+  if constexpr (FFTAMD_LDS_POISON != 0) {
+    lds_poison_bytes(p, bytes);
+    __syncthreads();
+  }
+}
+
 // Barrier between the LDS writes and reads of one exchange.  The fences are
 // restricted to LDS ("local" address space), so the barrier waits for LDS
 // traffic only and leaves global loads in flight (prefetching kernels rely on

@@ -39,32 +39,37 @@ class FFTError(RuntimeError):
 _lib = None
 
 
+def load_library(path):
+    """Open one build of the library (the default one, or the LDS-poison
+    debug build) with the argument types of include/fft.h."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m fourier_transform_amd.build`")
+    L = ctypes.CDLL(path)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.fft_plan_create.argtypes = [i64, i64, ci, ci]
+    L.fft_plan_create.restype = vp
+    L.fft_plan_create_2d.argtypes = [i64, i64, i64, ci, ci]
+    L.fft_plan_create_2d.restype = vp
+    L.fft_plan_set.argtypes = [vp, ci, i64]
+    L.fft_plan_set.restype = ci
+    L.fft_plan_get_sizes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    L.fft_plan_get_sizes.restype = ci
+    L.fft_exec.argtypes = [vp, vp, vp, vp]
+    L.fft_exec.restype = ci
+    L.fft_plan_destroy.argtypes = [vp]
+    L.fft_plan_destroy.restype = None
+    L.fft_last_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
+    L.fft_last_error.restype = ci
+    L.fft_max_single_pass_length.argtypes = []
+    L.fft_max_single_pass_length.restype = i64
+    return L
+
+
 def lib():
     """Load libfft_amd.so (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(
-                f"{LIB_PATH} is missing: build it with `python -m fourier_transform_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        L.fft_plan_create.argtypes = [i64, i64, ci, ci]
-        L.fft_plan_create.restype = vp
-        L.fft_plan_create_2d.argtypes = [i64, i64, i64, ci, ci]
-        L.fft_plan_create_2d.restype = vp
-        L.fft_plan_set.argtypes = [vp, ci, i64]
-        L.fft_plan_set.restype = ci
-        L.fft_plan_get_sizes.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64)]
-        L.fft_plan_get_sizes.restype = ci
-        L.fft_exec.argtypes = [vp, vp, vp, vp]
-        L.fft_exec.restype = ci
-        L.fft_plan_destroy.argtypes = [vp]
-        L.fft_plan_destroy.restype = None
-        L.fft_last_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
-        L.fft_last_error.restype = ci
-        L.fft_max_single_pass_length.argtypes = []
-        L.fft_max_single_pass_length.restype = i64
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
 
 
@@ -129,6 +134,11 @@ def fft_exec(plan, x, y, stream=None):
     x, y: contiguous device tensors (or raw device pointers as ints).  Tensor
     sizes are checked against fft_plan_get_sizes before the call.
     """
+    px, py, stream = _exec_args(plan, x, y, stream)
+    return _check(lib().fft_exec(plan, px, py, stream))
+
+
+def _exec_args(plan, x, y, stream):
     px, bx = _ptr_and_bytes(x)
     py, by = _ptr_and_bytes(y)
     need_in, need_out = fft_plan_get_sizes(plan)
@@ -141,7 +151,7 @@ def fft_exec(plan, x, y, stream=None):
         stream = torch.cuda.current_stream().cuda_stream
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
-    return _check(lib().fft_exec(plan, px, py, stream))
+    return px, py, stream
 
 
 def fft_plan_destroy(plan):

@@ -154,7 +154,16 @@ enum fft_option {
  * chirp tables of n entries and one of m entries, all built in f64 on the
  * host.
  * Direct plans own a table of n/2 + 1 (cos, -sin) pairs.
- * Uses the current HIP device.  Returns NULL on error (see fft_last_error).
+ * The implementation is chosen here, at plan creation, from the length and
+ * the kind, and a length a path cannot take is refused here rather than at
+ * execution (the WGSL Fourier-stage source, turing-sphere fourier.ts, header
+ * comment: its 'fft' and 'dft' implementations are selected at plan creation,
+ * the 'fft' one only for power-of-two lengths whose two workgroup buffers fit
+ * the device's workgroup storage; its stockham() throws for other lengths).
+ * Here the single-pass limit of 16384 points is what fits the 160 KiB of LDS
+ * of one gfx950 workgroup.
+ * Uses the current HIP device; the plan stays bound to it.  Returns NULL on
+ * error (see fft_last_error).
  */
 fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);
 
@@ -188,16 +197,31 @@ int fft_plan_get_sizes(const fft_plan* plan, int64_t* in_bytes,
 
 /*
  * Enqueue the transform on `stream` and return (asynchronous).  `in` is read,
- * `out` written; out-of-place execution never writes `in`.  Calls of one plan
- * on two streams at once are undefined (they share the plan's scratch).
+ * `out` written, both caller-owned device pointers; out-of-place execution
+ * never writes `in` (the out-of-place kernel signature (data, out, N) of the
+ * "Fast Fourier Transform on CPU and GPU" page, CUDA Kernel: Radix-2 FFT).
+ * The direction is the plan's sign, +1 or -1, which flips the exponent of
+ * every twiddle factor (the fft_dir uniform of "High Performance Fourier
+ * Transforms on GPUs with GLSL", section 3.1, Listing 3.4).
+ * The plan's device is made current for the launches and restored after.
+ * Outside HIP graph capture, each exec binds a plan-owned event to the
+ * completion of its last kernel (no extra command in the stream), and an
+ * exec on a different stream than the plan's previous one first makes
+ * `stream` wait for that event, so execs of one plan on several streams run
+ * one after the other (they share the plan's scratch).  Inside a capture
+ * neither is done: the caller orders the captured work and must not replay
+ * the graph concurrently with other execs of the plan.
  * Returns FFT_OK, FFT_EINVAL (NULL plan or buffer, misaligned, in == out for
- * R2C/C2R) or FFT_EHIP (launch failure).
+ * R2C/C2R) or FFT_EHIP (launch failure).  The options are locked by the
+ * first exec that succeeds; a failed exec leaves them settable.
  */
 int fft_exec(fft_plan* plan, const void* in, void* out, fft_stream_t stream);
 
-/* Free the plan.  If it has been executed, first waits for all work on the
- * device (hipDeviceSynchronize), since enqueued transforms may still read its
- * tables and scratch.  NULL is a no-op. */
+/* Free the plan.  First waits (hipEventSynchronize) for the event of the
+ * plan's last exec outside graph capture, since that work may still read its
+ * tables and scratch; work of other plans and streams is not waited for.
+ * A graph that captured an exec of the plan must have finished its launches
+ * before the plan is destroyed.  NULL is a no-op. */
 void fft_plan_destroy(fft_plan* plan);
 
 /* Code of the last call on this host thread; *msg (if msg is not NULL) points

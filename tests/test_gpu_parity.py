@@ -165,20 +165,26 @@ def test_deterministic_fourstep_and_tall_2d():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_w3_full_size_sampled_rows():
-    """Workload 3 at full size (32 x 2^22): every row is an independent
-    transform; rows 0, 17 and 31 are compared with the oracle in full."""
-    say("w3 n=2^22 batch=32 forward")
+def test_w3_full_size_all_rows():
+    """Workload 3 at full size (32 x 2^22), compared with the oracle element
+    by element over the whole output: the oracle runs on chunks of 4 rows and
+    the squared error and reference norms are summed over all 32."""
+    say("w3 n=2^22 batch=32 forward, whole output")
     x = W.workload3()
     y = c2c(x, -1)
-    rows = [0, 17, 31]
-    e = rel_l2(y[rows], oracle.c2c(x[rows], -1))
-    say(f"w3 rel_l2 rows {rows}: {e:.3e}")
-    assert e <= TOL
-    # Parseval on every row (a property at any size)
-    px = np.sum(np.abs(x.astype(np.complex128)) ** 2, axis=1) * x.shape[1]
-    py = np.sum(np.abs(y.astype(np.complex128)) ** 2, axis=1)
-    assert np.max(np.abs(py / px - 1)) < 1e-5
+    err2 = ref2 = 0.0
+    worst = 0.0
+    for r0 in range(0, x.shape[0], 4):
+        want = oracle.c2c(x[r0:r0 + 4], -1)
+        d = y[r0:r0 + 4].astype(np.complex128) - want
+        e2 = np.sum(np.abs(d) ** 2, axis=1)
+        w2 = np.sum(np.abs(want) ** 2, axis=1)
+        err2 += float(e2.sum())
+        ref2 += float(w2.sum())
+        worst = max(worst, float(np.sqrt(np.max(e2 / w2))))
+    e = float(np.sqrt(err2 / ref2))
+    say(f"w3 rel_l2 over all 32 rows: {e:.3e} (worst row {worst:.3e})")
+    assert e <= TOL and worst <= TOL
 
 
 # --------------------------------------------------------------------------
@@ -555,3 +561,94 @@ def test_exec_errors_and_state():
     finally:
         F.fft_plan_destroy(plan)
     assert F.fft_plan_get_sizes is not None
+
+
+def test_destroy_waits_for_its_own_work_only():
+    """fft_plan_destroy waits for the plan's last exec (its event), not for
+    the device: it returns while an unrelated stream still has queued work,
+    and by then the plan's own transform has finished and is correct."""
+    import time
+
+    import torch
+    say("destroy: own work done, unrelated stream still busy")
+    n, batch = 4096, 2048
+    x = W.uniform_c64((batch, n), np.random.default_rng(41))
+    xd = dev(x)
+    yd = torch.empty_like(xd)
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.randn(4096, 4096, device="cuda")
+    torch.mm(a, b)                                   # library start-up outside the timing
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(4):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    per_mm = (time.perf_counter() - t0) / 4
+    reps = int(min(4000, max(8, 1.0 / max(per_mm, 1e-5))))  # about a second of queued work
+    # Two created streams (work on the legacy null stream would wait for the
+    # side stream by itself).  The transform is enqueued first: streams may
+    # share a hardware queue, and then later side work cannot delay it; a
+    # destroy that waited for the device would return only after the side
+    # work, one that waits for the plan's own exec returns before.
+    side, own = torch.cuda.Stream(), torch.cuda.Stream()
+    plan = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    destroyed = False
+    try:
+        F.fft_exec(plan, xd, yd, own)
+        with torch.cuda.stream(side):
+            for _ in range(reps):
+                torch.mm(a, b)
+        F.fft_plan_destroy(plan)
+        destroyed = True
+        side_busy = not side.query()
+        own_done = own.query()
+    finally:
+        if not destroyed:
+            F.fft_plan_destroy(plan)
+    say(f"destroy returned with the side stream busy={side_busy} ({reps} products queued), own work done={own_done}")
+    side.synchronize()
+    assert side_busy
+    assert own_done
+    assert rel_l2(host(yd), oracle.c2c(x, -1)) <= TOL
+
+
+def test_exec_on_two_streams_is_ordered():
+    """Execs of one plan on two streams run one after the other (the second
+    waits for the first's event), so a four-step plan, whose execs share the
+    plan's scratch, gives both results correctly."""
+    import torch
+    say("one four-step plan on two streams")
+    n, batch = 1 << 20, 4
+    xs = [W.normal_c64((batch, n), np.random.default_rng(50 + i)) for i in range(2)]
+    plan = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    try:
+        xd = [dev(x) for x in xs]
+        yd = [torch.empty_like(v) for v in xd]
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        F.fft_exec(plan, xd[0], yd[0], s1)
+        F.fft_exec(plan, xd[1], yd[1], s2)
+        torch.cuda.synchronize()
+        for x, y in zip(xs, yd):
+            assert rel_l2(host(y), oracle.c2c(x, -1)) <= TOL
+    finally:
+        F.fft_plan_destroy(plan)
+
+
+def test_failed_exec_leaves_options_settable():
+    """An exec that fails its checks does not lock the plan's options."""
+    import torch
+    say("failed exec keeps options settable")
+    plan = F.fft_plan_create(64, 4, F.FFT_C2C, F.FFT_FORWARD)
+    try:
+        x = torch.zeros(4 * 64, dtype=torch.complex64, device="cuda")
+        lib = F.lib()
+        assert lib.fft_exec(plan, x.data_ptr() + 4, x.data_ptr(), None) == F.FFT_EINVAL
+        F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 1)          # still before the first successful exec
+        F.fft_exec(plan, x, x)
+        with pytest.raises(F.FFTError) as e:
+            F.fft_plan_set(plan, F.FFT_OPT_SHIFT, 0)
+        assert e.value.code == F.FFT_ESTATE
+        torch.cuda.synchronize()
+    finally:
+        F.fft_plan_destroy(plan)
