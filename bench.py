@@ -1,7 +1,7 @@
 """Throughput of the batched fp32 FFT on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload w2] [--configs all|none]
-    python bench.py --summarize-trace KERNEL_TRACE.csv
+    python bench.py --summarize-trace KERNEL_TRACE.csv [--windows WINDOWS.jsonl]
 
 One step is one pass of the whole hot path over one batch: for the default
 workload (w2: 16384 rows of N = 4096 complex64, U[-1,1]) a forward transform
@@ -26,12 +26,13 @@ configs   = (default run) every configuration of the metric measured in the
             per-exec event timings, 100 back-to-back steps for c1 and c4, the
             relative L2 error against the oracle over the whole output, and
             the oracle's own time on that reference (the CPU baseline)
---summarize-trace: per-kernel durations of a rocprofv3 kernel trace taken
-            with --selected-regions: the bench opens the profiler only around
-            its timed regions (roctxProfilerResume/Pause), so the trace holds
-            exactly the timed launches
+--summarize-trace: per-kernel durations of a rocprofv3 kernel trace of a
+            bench run; with --windows (the --timed-windows file the traced run
+            wrote: host CLOCK_MONOTONIC windows around its timed regions, the
+            clock of the trace's timestamps) only the timed launches
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -237,34 +238,29 @@ def make_plans(F, spec, direct=False, real_pairs=False):
 SETTLE_MS = 200.0       # the workload runs this long before its warm-up steps (see time_workload)
 
 
-class _Roctx:
-    """roctxProfilerResume/Pause around each timed region, so that
-    `rocprofv3 --selected-regions` traces exactly the timed launches.  Without
-    a profiler attached the calls do nothing; without the library, neither
-    does this."""
+class _Windows:
+    """Host-clock windows (CLOCK_MONOTONIC, ns: the clock of rocprofv3's
+    kernel timestamps) around each timed region, appended to a JSON-lines
+    file when --timed-windows is given.  The device is idle when a window
+    opens and has finished when it closes, so the launches whose start lies
+    inside it are exactly the timed ones (--summarize-trace --windows)."""
 
     def __init__(self):
-        self.lib = None
-        try:
-            import ctypes
-            self.lib = ctypes.CDLL("librocprofiler-sdk-roctx.so")
-        except OSError:
-            try:
-                import ctypes
-                self.lib = ctypes.CDLL("/opt/rocm/lib/librocprofiler-sdk-roctx.so")
-            except OSError:
-                self.lib = None
+        self.path = None
+        self.label = ""
+        self.t0 = None
 
-    def resume(self):
-        if self.lib is not None:
-            self.lib.roctxProfilerResume(0)
+    def open(self):
+        self.t0 = time.clock_gettime_ns(time.CLOCK_MONOTONIC)
 
-    def pause(self):
-        if self.lib is not None:
-            self.lib.roctxProfilerPause(0)
+    def close(self):
+        t1 = time.clock_gettime_ns(time.CLOCK_MONOTONIC)
+        if self.path:
+            with open(self.path, "a") as f:
+                f.write(json.dumps({"label": self.label, "t0_ns": self.t0, "t1_ns": t1}) + "\n")
 
 
-ROCTX = _Roctx()
+WINDOWS = _Windows()
 
 
 def time_workload(F, torch, plans, xd, bufs, stream, steps, warmup, back_to_back=0, settle_ms=SETTLE_MS):
@@ -300,7 +296,7 @@ def time_workload(F, torch, plans, xd, bufs, stream, steps, warmup, back_to_back
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    ROCTX.resume()
+    WINDOWS.open()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(steps):
@@ -308,7 +304,7 @@ def time_workload(F, torch, plans, xd, bufs, stream, steps, warmup, back_to_back
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ROCTX.pause()
+    WINDOWS.close()
     out = {"ms_per_step": ev0.elapsed_time(ev1) / steps, "wall_ms_per_step": wall * 1e3 / steps, "settle": settle}
     out["ms_per_exec"] = out["ms_per_step"] / len(plans)
 
@@ -429,6 +425,7 @@ def measure_config(F, torch, name, steps, warmup):
         bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
     plans = make_plans(F, spec)
     stream = torch.cuda.current_stream()
+    WINDOWS.label = name
     try:
         tm = time_workload(F, torch, plans, xd, bufs, stream, steps, warmup,
                            back_to_back=BACK_TO_BACK if name in ("w1", "w4") else 0)
@@ -466,13 +463,16 @@ def measure_config(F, torch, name, steps, warmup):
     return entry
 
 
-def summarize_trace(path, out=sys.stdout):
-    """Per-kernel durations of a rocprofv3 kernel trace (CSV) of a bench run
-    under `rocprofv3 --kernel-trace --selected-regions`: the trace then holds
-    only the launches of the timed regions.  Prints a markdown table:
+def summarize_trace(path, windows=None, out=sys.stdout):
+    """Per-kernel durations of a rocprofv3 kernel trace (CSV) of a bench run:
+    with `windows` (the --timed-windows file of that run) only the launches
+    that started inside a timed region.  Prints a markdown table:
     dispatches, median, mean, min and max duration (us), VGPRs, LDS."""
     import csv
     rows = list(csv.DictReader(open(path)))
+    if windows:
+        wins = [json.loads(l) for l in open(windows) if l.strip()]
+        rows = [r for r in rows if any(w["t0_ns"] <= int(r["Start_Timestamp"]) <= w["t1_ns"] for w in wins)]
     by = {}
     for r in rows:
         by.setdefault(r["Kernel_Name"], []).append(r)
@@ -487,6 +487,80 @@ def summarize_trace(path, out=sys.stdout):
               f"{d[-1]:.1f} | {r0.get('VGPR_Count', r0.get('Arch_VGPR_Count', ''))} | "
               f"{r0.get('Accum_VGPR_Count', '')} | {r0.get('LDS_Block_Size', r0.get('Group_Segment_Size', ''))} | "
               f"{r0.get('Scratch_Size', r0.get('Private_Segment_Size', ''))} |", file=out)
+
+
+# kernels of each stored traffic record: (name prefix, launches per record)
+TRAFFIC_KERNELS = {
+    "c2c_rows_1024": [("fftamd::k_c2c_rows<1024,", 1.0)],
+    "c2c_rows_4096": [("fftamd::k_c2c_rows<4096,", 1.0)],      # per launch (both directions averaged)
+    "fourstep_2^22": [("fftamd::k_fs_cols<2048,", 1.0), ("fftamd::k_fs_rows<2048,", 1.0)],
+    "real_2048": [("fftamd::k_c2r<1024,", 0.5), ("fftamd::k_r2c<1024,", 0.5)],   # per exec (one direction)
+    "2d_8192x8192": [("fftamd::k_rows_fold<8192,", 1.0), ("fftamd::k_fold_cols<2048,", 1.0)],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 29     # the bench's reference copy: 512 MiB read and 512 MiB written
+
+
+def summarize_counters(fetch_csv, write_csv, out=sys.stdout, write_traffic=False):
+    """HBM bytes per dispatch from two rocprofv3 --pmc runs of the bench
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, --selected-regions),
+    each scaled by what the same counter reads for the bench's 512 MiB
+    reference copy.  Prints a markdown table per kernel and the bytes of each
+    stored traffic record; with write_traffic, stores them in
+    profiles/traffic.json under the current kernel-source hash."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        for k in acc:
+            if k.startswith(COPY_KERNEL):
+                # the copy kernel also serves torch's small staging copies:
+                # keep the dispatches of the 512 MiB reference copy (the largest)
+                top = max(acc[k])
+                acc[k] = [v for v in acc[k] if v >= 0.9 * top]
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if k.startswith(COPY_KERNEL))
+    fscale = COPY_BYTES / (fetch[copy_name] * 1024)
+    wscale = COPY_BYTES / (write[copy_name] * 1024)
+    print(f"Calibration: `{copy_name}` of {COPY_BYTES >> 20} MiB reads FETCH_SIZE {fetch[copy_name]:.0f} KiB and "
+          f"WRITE_SIZE {write[copy_name]:.0f} KiB per dispatch: scale x{fscale:.3f} and x{wscale:.3f}.\n", file=out)
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes |", file=out)
+    print("|---|---|---|---|---|", file=out)
+    scaled = {}
+    for k in fetch:
+        if k not in write:
+            continue
+        scaled[k] = fetch[k] * 1024 * fscale + write[k] * 1024 * wscale
+        short = k if len(k) <= 90 else k[:87] + "..."
+        print(f"| `{short}` | {nf[k]} / {nw[k]} | {fetch[k]:.0f} | {write[k]:.0f} | {scaled[k]:.4g} |", file=out)
+    print("", file=out)
+    rec = {}
+    for key, parts in TRAFFIC_KERNELS.items():
+        total, ok = 0.0, True
+        for prefix, w in parts:
+            ks = [k for k in scaled if k.split("(")[0].replace("void ", "").startswith(prefix)]
+            if not ks:
+                ok = False
+                break
+            total += w * sum(scaled[k] for k in ks) / len(ks)
+        if ok:
+            rec[key] = int(round(total))
+            print(f"- `{key}`: {rec[key]} bytes per record ({' + '.join(p for p, _ in parts)})", file=out)
+    if write_traffic:
+        path = os.path.join(PROFILES, "traffic.json")
+        h = kernel_source_hash()
+        d = {key: {"source_hash": h, "bytes_per_launch": v,
+                   "evidence": "profiles/hbm_traffic_counters.md",
+                   "kernels": [p for p, _ in TRAFFIC_KERNELS[key]]} for key, v in rec.items()}
+        json.dump(d, open(path, "w"), indent=1)
+    return rec
 
 
 def main():
@@ -504,12 +578,24 @@ def main():
                     help="w6 only: the row length (default 1000; rows scaled to keep ~512 MiB)")
     ap.add_argument("--direct", action="store_true",
                     help="w4: the band-limited direct sums on the matrix cores instead of the FFT")
+    ap.add_argument("--summarize-counters", metavar=("FETCH_CSV", "WRITE_CSV"), nargs=2, default=None,
+                    help="HBM bytes per kernel from two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, then WRITE_SIZE) of a bench run, calibrated on the reference copy")
+    ap.add_argument("--write-traffic", action="store_true",
+                    help="with --summarize-counters: store the records in profiles/traffic.json")
     ap.add_argument("--summarize-trace", metavar="CSV", default=None,
-                    help="print the per-kernel durations of a rocprofv3 kernel trace taken with "
-                         "--selected-regions (the timed launches only) and exit")
+                    help="print the per-kernel durations of a rocprofv3 kernel trace of a bench run and exit "
+                         "(with --windows: only the launches of its timed regions)")
+    ap.add_argument("--windows", metavar="JSONL", default=None,
+                    help="with --summarize-trace: the --timed-windows file of the traced run")
+    ap.add_argument("--timed-windows", metavar="JSONL", default=None,
+                    help="append the host-clock window of every timed region to this file")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.windows)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, write_traffic=args.write_traffic)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -524,6 +610,7 @@ def main():
     if args.n is not None and (args.n < 3 or args.n & (args.n - 1) == 0):
         raise SystemExit("--n takes a length >= 3 that is not a power of two")
     plain_headline = args.workload == "w2" and not (args.direct or args.real_pairs or args.n)
+    WINDOWS.path = args.timed_windows
     configs = args.configs or ("all" if plain_headline else "none")
 
     import numpy as np
@@ -544,6 +631,7 @@ def main():
         bufs = [torch.empty_like(xd) for _ in spec["dirs"]]
     plans = make_plans(F, spec, direct=args.direct, real_pairs=args.real_pairs)
     stream = torch.cuda.current_stream()
+    WINDOWS.label = args.workload
     tm = time_workload(F, torch, plans, xd, bufs, stream, args.steps, args.warmup)
     avg_exec_ms = tm["ms_per_exec"]
 
@@ -575,11 +663,14 @@ def main():
     b.copy_(a)
     torch.cuda.synchronize()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    WINDOWS.label = "copy 512 MiB"
+    WINDOWS.open()     # the calibration of the HBM byte counters
     c0.record(stream)
     for _ in range(10):
         b.copy_(a)
     c1.record(stream)
     torch.cuda.synchronize()
+    WINDOWS.close()
     copy_gbps = 10 * 2 * a.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del a, b
 

@@ -283,8 +283,9 @@ void free_plan(fft_plan* p) {
   if (!p) return;
   if (p->inner) free_plan(p->inner);
   if (p->inner2) free_plan(p->inner2);
-  if (p->tables) (void)hipFree(p->tables);
-  if (p->scratch) (void)hipFree(p->scratch);
+  // returned in stream order on the null stream (see finish_plan)
+  if (p->tables) (void)hipFreeAsync(p->tables, nullptr);
+  if (p->scratch) (void)hipFreeAsync(p->scratch, nullptr);
   if (p->done) (void)hipEventDestroy(p->done);
   delete p;
 }
@@ -311,16 +312,22 @@ int finish_plan(fft_plan* p, const std::vector<std::vector<float2>*>& parts,
   }
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) return hip_err(e, "hipGetDevice");
-  e = hipMalloc((void**)&p->tables, all.size() * sizeof(float2));
-  if (e != hipSuccess) return hip_err(e, "hipMalloc(twiddle tables)");
+  // Plan memory comes from the device's stream-ordered pool (allocated on
+  // the null stream, then synchronised, so every stream may use it) and is
+  // returned with hipFreeAsync: hipFree synchronises the whole device, which
+  // would make fft_plan_destroy wait for unrelated streams.
+  e = hipMallocAsync((void**)&p->tables, all.size() * sizeof(float2), nullptr);
+  if (e != hipSuccess) return hip_err(e, "hipMallocAsync(twiddle tables)");
   e = hipMemcpy(p->tables, all.data(), all.size() * sizeof(float2), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_err(e, "hipMemcpy(twiddle tables)");
   for (size_t i = 0; i < slots.size(); ++i) *slots[i] = p->tables + offs[i];
   if (scratch_bytes) {
-    e = hipMalloc((void**)&p->scratch, scratch_bytes);
-    if (e != hipSuccess) return hip_err(e, "hipMalloc(scratch)");
+    e = hipMallocAsync((void**)&p->scratch, scratch_bytes, nullptr);
+    if (e != hipSuccess) return hip_err(e, "hipMallocAsync(scratch)");
     p->scratch_bytes = scratch_bytes;
   }
+  e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_err(e, "hipStreamSynchronize");
   e = hipEventCreateWithFlags(&p->done, hipEventDisableTiming);
   if (e != hipSuccess) return hip_err(e, "hipEventCreateWithFlags");
   return FFT_OK;

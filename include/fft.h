@@ -220,6 +220,9 @@ int fft_exec(fft_plan* plan, const void* in, void* out, fft_stream_t stream);
 /* Free the plan.  First waits (hipEventSynchronize) for the event of the
  * plan's last exec outside graph capture, since that work may still read its
  * tables and scratch; work of other plans and streams is not waited for.
+ * The plan's device memory comes from the device's stream-ordered pool and
+ * goes back to it with hipFreeAsync on the null stream (hipFree would wait
+ * for the whole device).
  * A graph that captured an exec of the plan must have finished its launches
  * before the plan is destroyed.  NULL is a no-op. */
 void fft_plan_destroy(fft_plan* plan);

@@ -106,3 +106,42 @@ def test_summarize_trace(tmp_path):
     assert [x.strip() for x in a[2:7]] == ["3", "3.0", "3.0", "2.0", "4.0"]
     b = next(l for l in lines if "`k_b`" in l).split("|")
     assert [x.strip() for x in b[2:9]] == ["1", "10.0", "10.0", "10.0", "10.0", "128", "4"]
+
+
+def test_summarize_counters(tmp_path, monkeypatch):
+    """Counter summary: calibration on the copy kernel, per-record sums."""
+    cols = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+
+    def write(path, counter, vals):
+        rows = [cols] + [[k, counter, v] for k, v in vals]
+        path.write_text("\n".join(",".join(f'"{x}"' for x in r) for r in rows) + "\n")
+    f = tmp_path / "f.csv"
+    w = tmp_path / "w.csv"
+    half = (1 << 29) // 2048        # the copy reads half its bytes in FETCH_SIZE KiB
+    write(f, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", half),
+                            ("void fftamd::k_c2c_rows<4096, -1, 1>(fftamd::RowsArgs)", 262144),
+                            ("void fftamd::k_c2c_rows<4096, 1, 1>(fftamd::RowsArgs)", 262144)])
+    write(w, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", (1 << 29) // 1024),
+                            ("void fftamd::k_c2c_rows<4096, -1, 1>(fftamd::RowsArgs)", 524288),
+                            ("void fftamd::k_c2c_rows<4096, 1, 1>(fftamd::RowsArgs)", 524288)])
+    import io
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = bench.summarize_counters(str(f), str(w), out=io.StringIO(), write_traffic=True)
+    assert rec["c2c_rows_4096"] == 2 * 512 * 1024 * 1024       # 512 MiB read + 512 MiB written
+    stored = json.load(open(tmp_path / "traffic.json"))
+    assert stored["c2c_rows_4096"]["source_hash"] == bench.kernel_source_hash()
+    assert "fourstep_2^22" not in rec                            # no counters for its kernels
+
+
+def test_summarize_trace_keeps_the_timed_windows(tmp_path):
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    rows = [["k_a", 100, 200], ["k_a", 1000, 1100], ["k_a", 1200, 1500], ["k_a", 5000, 9000]]
+    p = tmp_path / "t.csv"
+    p.write_text("\n".join(",".join(f'"{v}"' for v in r) for r in [cols] + rows) + "\n")
+    w = tmp_path / "w.jsonl"
+    w.write_text(json.dumps({"label": "w2", "t0_ns": 900, "t1_ns": 2000}) + "\n")
+    import io
+    buf = io.StringIO()
+    bench.summarize_trace(str(p), str(w), out=buf)
+    a = next(l for l in buf.getvalue().splitlines() if "`k_a`" in l).split("|")
+    assert [x.strip() for x in a[2:7]] == ["2", "0.3", "0.2", "0.1", "0.3"]
