@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1193,6 +1194,54 @@ int exec_common(fft_plan* p, const void* in, void* out, fft_stream_t stream_, fl
   return rc == FFT_OK ? ok() : rc;
 }
 
+// Scratch the inner plans of p own (an any-length 2D or real plan runs its
+// complex transforms through inner plans).
+size_t inner_scratch_bytes(const fft_plan* p) {
+  size_t b = 0;
+  for (const fft_plan* q : {p->inner, p->inner2})
+    if (q) b += q->scratch_bytes + inner_scratch_bytes(q);
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of fft_exec_noalloc: one array per device, part of the
+// library's device code (allocated when the code object is loaded on a
+// device, held until the process ends).  Host code never uses the array's
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = FFT_NOALLOC_MAX_SCRATCH_BYTES;
+constexpr int kStaticScratchDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) float2 scratch[kStaticScratchBytes / sizeof(float2)];
+
+namespace {
+
+std::mutex g_static_mu;
+float2* g_static_ptr[kStaticScratchDevices] = {};
+
+int static_scratch(int dev, float2** out) {
+  if (dev < 0 || dev >= kStaticScratchDevices)
+    return set_err(FFT_ENOTSUP, "fft_exec_noalloc supports device ordinals below 64");
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_err(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_err(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_err(e, "hipGetSymbolAddress(static scratch)");
+    if (!ptr) return set_err(FFT_EHIP, "hipGetSymbolAddress(static scratch) returned NULL");
+    g_static_ptr[dev] = static_cast<float2*>(ptr);
+  }
+  *out = g_static_ptr[dev];
+  return FFT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1200,6 +1249,19 @@ extern "C" {
 int fft_exec(fft_plan* p, const void* in, void* out, fft_stream_t stream) {
   if (check_exec_args(p, in, out) != FFT_OK) return g_err.code;
   return exec_common(p, in, out, stream, p->scratch);
+}
+
+int fft_exec_noalloc(fft_plan* p, const void* in, void* out, fft_stream_t stream) {
+  if (check_exec_args(p, in, out) != FFT_OK) return g_err.code;
+  if (inner_scratch_bytes(p))
+    return set_err(FFT_ENOTSUP, "fft_exec_noalloc: the plan's inner transforms own scratch of their own");
+  if (p->scratch_bytes > kStaticScratchBytes)
+    return set_err(FFT_ENOTSUP, "fft_exec_noalloc: the plan needs " + std::to_string(p->scratch_bytes) +
+                                    " bytes of scratch, the static buffer holds " +
+                                    std::to_string(kStaticScratchBytes));
+  float2* sc = nullptr;
+  if (p->scratch_bytes && static_scratch(p->device, &sc) != FFT_OK) return g_err.code;
+  return exec_common(p, in, out, stream, sc);
 }
 
 void fft_plan_destroy(fft_plan* p) {

@@ -25,7 +25,9 @@ _NAMES = {0: "FFT_OK", -1: "FFT_EINVAL", -2: "FFT_ENOTSUP", -3: "FFT_ENOMEM",
 
 # every symbol include/fft.h declares
 EXPORTS = ("fft_plan_create", "fft_plan_create_2d", "fft_plan_set", "fft_plan_get_sizes",
-           "fft_exec", "fft_plan_destroy", "fft_last_error", "fft_max_single_pass_length")
+           "fft_exec", "fft_plan_destroy", "fft_last_error", "fft_max_single_pass_length",
+           "fft_exec_noalloc")
+FFT_NOALLOC_MAX_SCRATCH_BYTES = 256 << 20
 
 
 class FFTError(RuntimeError):
@@ -56,6 +58,8 @@ def load_library(path):
     L.fft_plan_get_sizes.restype = ci
     L.fft_exec.argtypes = [vp, vp, vp, vp]
     L.fft_exec.restype = ci
+    L.fft_exec_noalloc.argtypes = [vp, vp, vp, vp]
+    L.fft_exec_noalloc.restype = ci
     L.fft_plan_destroy.argtypes = [vp]
     L.fft_plan_destroy.restype = None
     L.fft_last_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
@@ -152,6 +156,14 @@ def _exec_args(plan, x, y, stream):
     elif not isinstance(stream, int):
         stream = stream.cuda_stream
     return px, py, stream
+
+
+def fft_exec_noalloc(plan, x, y, stream=None):
+    """fft_exec with the library's static per-device scratch instead of the
+    plan's (include/fft.h): no device allocation; calls on one device that
+    overlap in time race on that buffer."""
+    px, py, stream = _exec_args(plan, x, y, stream)
+    return _check(lib().fft_exec_noalloc(plan, px, py, stream))
 
 
 def fft_plan_destroy(plan):

@@ -234,6 +234,33 @@ int fft_last_error(const char** msg);
 /* Longest length run as a single kernel (one workgroup per row). */
 int64_t fft_max_single_pass_length(void);
 
+/* Size of the static per-device scratch buffer of fft_exec_noalloc, bytes. */
+#define FFT_NOALLOC_MAX_SCRATCH_BYTES 268435456
+
+/*
+ * fft_exec for callers that cannot allocate device memory at execution time
+ * or while capturing a HIP graph, and do not want to keep a scratch buffer
+ * per plan: the same kernels and results as fft_exec(plan, in, out, stream),
+ * with the plan's intermediate results kept in a buffer of
+ * FFT_NOALLOC_MAX_SCRATCH_BYTES (256 MiB) per device that is part of the
+ * library's device code (held from the first call on a device until the
+ * process ends) instead of the plan's own scratch.  Plans without scratch
+ * (single-pass lengths) run as with fft_exec.  It calls no allocating
+ * routine: the buffer's device address is looked up once per device, on
+ * the first call there.
+ * Errors: those of fft_exec, and FFT_ENOTSUP when the plan's scratch
+ * (four-step C2C: batch*n*8 bytes; tall 2D and chirp plans: see
+ * fft_plan_create and fft_plan_create_2d) exceeds the buffer, or when the
+ * plan runs inner plans with scratch of their own (any-length 2D and real
+ * plans whose complex transforms need scratch).  Checked before any launch.
+ * Every call on one device shares that device's buffer, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that may
+ * overlap in time on one device -- on different streams, or on one stream
+ * with other work that uses the buffer in between -- race; callers serialise
+ * them.
+ */
+int fft_exec_noalloc(fft_plan* plan, const void* in, void* out, fft_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
