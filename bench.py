@@ -256,6 +256,7 @@ class _Windows:
     def close(self):
         t1 = time.clock_gettime_ns(time.CLOCK_MONOTONIC)
         if self.path:
+            os.makedirs(os.path.dirname(os.path.abspath(self.path)), exist_ok=True)
             with open(self.path, "a") as f:
                 f.write(json.dumps({"label": self.label, "t0_ns": self.t0, "t1_ns": t1}) + "\n")
 

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   float2 v[E];
   static_for<0, E>([&](auto ic) {
     constexpr int m = load_slot<N, E>(decltype(ic)::value);
-    v[m] = gload_nt(src, off + T * m);
+    v[m] = gload_nt(src + T * m, off);
   });
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (LTW) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
     const uint32_t off = (uint32_t)line + (uint32_t)u * gp;
     static_for<0, E>([&](auto ic) {
       constexpr int m = load_slot<N, E>(decltype(ic)::value);
-      v[m] = gload_nt(src, off + (uint32_t)T * gp * m);
+      v[m] = gload_nt(src + (size_t)T * gp * m, off);
     });
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -193,11 +193,11 @@ __global__ __launch_bounds__(C * N / E) void k_fold_cols(FoldArgs a) {
     run_stages<N, E, S, false, L, true>(v, lds, a.tw2, u, line);
   }
   const uint32_t off = (uint32_t)line + (uint32_t)u * pitch;
-  const uint32_t step = (uint32_t)T * pitch;
+  const size_t step = (size_t)T * pitch;
   float2* dst = a.out + (img * a.ny + ka) * (int64_t)nx + x0;
 #pragma unroll
   for (int m = 0; m < E; ++m) {
-    gstore_nt(dst, off + step * m, v[m]);
+    gstore_nt(dst + step * m, off, v[m]);
     if constexpr (E > 16) {
       if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }

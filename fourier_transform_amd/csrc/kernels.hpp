@@ -47,7 +47,7 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   if (valid) {
     const float2* src = a.in + row0 * N;
 #pragma unroll
-    for (int m = 0; m < E; ++m) v[m] = gload_nt(src, off + T * m);
+    for (int m = 0; m < E; ++m) v[m] = gload_nt(src + T * m, off);
     if (a.shift_mode) {
       const int par = a.shift_mode == 2 ? (int)(row & (a.rows_per_image - 1)) : 0;
 #pragma unroll
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
     float2* dst = a.out + row0 * N;
     if (a.stream_store) {
 #pragma unroll
-      for (int m = 0; m < E; ++m) gstore_nt(dst, off + T * m, v[m]);
+      for (int m = 0; m < E; ++m) gstore_nt(dst + T * m, off, v[m]);
     } else {
 #pragma unroll
       for (int m = 0; m < E; ++m) gstore(dst, off + T * m, v[m]);
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
       const uint32_t j = c0 + off + step * m;
       v[m] = make_float2(0.f, 0.f);
       if (j < (uint32_t)a.in_len) {
-        v[m] = gload_nt(src, off + step * m);
+        v[m] = gload_nt(src + (size_t)step * m, off);
         if (a.pre) v[m] = cmul(v[m], gload(a.pre, j));
       }
     }
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
     const float2* src = a.in + base;
     static_for<0, E>([&](auto ic) {
       constexpr int m = load_slot<N2, E>(decltype(ic)::value);
-      v[m] = gload_nt(src, off + step * m);
+      v[m] = gload_nt(src + (size_t)step * m, off);
     });
   } else {
 #pragma unroll
@@ -562,13 +562,28 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
     const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
     // the block layout, relative to the first block column of this group
     float2* dst = a.out + b * (int64_t)n1 * N2 + c0 * BK;
+    if constexpr (T % BK == 0) {
+      // k2 = u2 + T*m with T a multiple of BK: the block index is a
+      // per-thread base plus m*T*n1 (whole block rows), a uniform stride
+      const uint32_t base = fs_block_index<BK, C>((uint32_t)u2, (uint32_t)line2, n1);
+      const size_t row_step = (size_t)T * n1;
 #pragma unroll
-    for (int m = 0; m < E; ++m) {
-      const uint32_t k2 = (uint32_t)(u2 + T * m);
-      const float2 w = cmul(wu, ftab[line2 * FP + m]);
-      gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line2, n1), apply_tw<S>(v[m], w));
-      if constexpr (E > 16) {
-        if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < E; ++m) {
+        const float2 w = cmul(wu, ftab[line2 * FP + m]);
+        gstore_nt(dst + row_step * m, base, apply_tw<S>(v[m], w));
+        if constexpr (E > 16) {
+          if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < E; ++m) {
+        const uint32_t k2 = (uint32_t)(u2 + T * m);
+        const float2 w = cmul(wu, ftab[line2 * FP + m]);
+        gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line2, n1), apply_tw<S>(v[m], w));
+        if constexpr (E > 16) {
+          if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   }
@@ -616,10 +631,19 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
     // starting at (b*n2 + k20)*N1 (k20 is a multiple of C).  Unconditional:
     // every launched group is whole (batch*n2 is a multiple of C).
     const float2* src = a.in + g0 * N1;
-    static_for<0, E>([&](auto ic) {
-      constexpr int m = load_slot<N1, E>(decltype(ic)::value);
-      v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
-    });
+    if constexpr (T % BC == 0) {
+      // slot m adds T/BC whole blocks: a compile-time step of the base
+      const uint32_t off = fs_block_index<C, BC>((uint32_t)line, (uint32_t)u, N1);
+      static_for<0, E>([&](auto ic) {
+        constexpr int m = load_slot<N1, E>(decltype(ic)::value);
+        v[m] = gload_nt(src + (T / BC) * C * BC * m, off);
+      });
+    } else {
+      static_for<0, E>([&](auto ic) {
+        constexpr int m = load_slot<N1, E>(decltype(ic)::value);
+        v[m] = gload_nt(src, fs_block_index<C, BC>((uint32_t)line, (uint32_t)(u + T * m), N1));
+      });
+    }
   }
   if constexpr (LTW) {
     __builtin_amdgcn_sched_barrier(0);
@@ -675,10 +699,10 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
     const int64_t k20 = g0 - b * n2;
     float2* dst = a.out + b * n2 * N1 + k20;
     const uint32_t off = (uint32_t)ln + (uint32_t)(tid / C) * (uint32_t)n2;
-    const uint32_t step = (uint32_t)(NT / C) * (uint32_t)n2;
+    const size_t step = (size_t)(NT / C) * (size_t)n2;
 #pragma unroll
     for (int p = 0; p < E; ++p) {
-      gstore_nt(dst, off + step * p, v[p]);
+      gstore_nt(dst + step * p, off, v[p]);
       if constexpr (E > 16) {
         if ((p & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }

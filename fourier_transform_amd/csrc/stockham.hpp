@@ -105,6 +105,11 @@ __device__ __forceinline__ float2 apply_tw(float2 v, float2 w) {
 // element offset: the compiler then uses the SGPR-base form of the global
 // memory instructions (one 32-bit VGPR per address instead of a 64-bit pair
 // built with 64-bit multiply-adds).  Offsets must stay below 2^29 elements.
+// Where an unrolled loop steps by a compile-time or wave-uniform stride, the
+// callers add the stride to the base pointer (scalar arithmetic) and keep one
+// per-thread offset for every access: the instruction's immediate offset
+// only reaches 4 KiB, so folding the stride into the offset costs one or
+// two vector adds per access.
 __device__ __forceinline__ float2 gload(const float2* __restrict__ base, uint32_t i) {
   return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(base) + (i << 3));
 }
@@ -476,16 +481,18 @@ struct TwLdsStage {
   const float2* l;
   uint32_t off;
 };
+// entry k + j of the table: k compile-time (folded into the base pointer),
+// j per thread
 template <int s>
-__device__ __forceinline__ float2 tw_at(const float2* __restrict__ t, uint32_t i) {
-  return gload(t, i);
+__device__ __forceinline__ float2 tw_at(const float2* __restrict__ t, uint32_t k, uint32_t j) {
+  return gload(t + k, j);
 }
 template <int s, int LS>
-__device__ __forceinline__ float2 tw_at(const TwLdsStage<LS>& t, uint32_t i) {
+__device__ __forceinline__ float2 tw_at(const TwLdsStage<LS>& t, uint32_t k, uint32_t j) {
   if constexpr (s == LS) {
-    return t.l[i - t.off];
+    return t.l[k - t.off + j];
   } else {
-    return gload(t.g, i);
+    return gload(t.g + k, j);
   }
 }
 
@@ -510,7 +517,7 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, in
     if constexpr (s > 0) {
 #pragma unroll
       for (int r = 1; r < R; ++r) {
-        x[r] = apply_tw<S>(x[r], tw_at<s>(tw, (uint32_t)(OFF + (r - 1) * NS + j)));
+        x[r] = apply_tw<S>(x[r], tw_at<s>(tw, (uint32_t)(OFF + (r - 1) * NS), (uint32_t)j));
         // bound the twiddle loads in flight for large radices (VGPR budget)
         if constexpr (R > 16) {
           if ((r & 15) == 15) __builtin_amdgcn_sched_barrier(0);
