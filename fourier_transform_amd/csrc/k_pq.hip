@@ -203,19 +203,18 @@ __device__ __forceinline__ void dft_odd(float2* x) {
 
 // lines of length Q per workgroup: C rows of P lines each
 constexpr int pq_rows(int q, int p) {
-  const int t = rows_threads(q) * p;
+  const int t = pq_threads(q) * p;
   return t >= 256 ? 1 : 256 / t;
 }
 }  // namespace
 
 template <int Q, int P, int S, int C>
-__global__ __launch_bounds__(rows_threads(Q) * P * C) void k_c2c_pq(PqArgs a) {
-  constexpr int E = rows_values(Q);
+__global__ __launch_bounds__(pq_threads(Q) * P * C) void k_c2c_pq(PqArgs a) {
+  constexpr int E = pq_values(Q);
   constexpr int T = Q / E;
   constexpr int N = P * Q;
   constexpr int NT = C * P * T;
   constexpr bool WL = T <= 64 && (64 % T) == 0;  // each line inside one wavefront
-  static_assert(!rows_split(Q), "the power-of-two part uses the complex LDS exchange");
   using L = RowLds<Q>;
   static_assert(row_lds_bytes(Q, C * P) <= kLdsBudgetBytes, "LDS budget");
   __shared__ float2 lds[L::size(C * P)];
@@ -279,7 +278,7 @@ struct PqOp {
         uint32_t grid;
         hipError_t e = grid_of(a.rows, C, &grid);
         if (e != hipSuccess) return e;
-        FFTAMD_LAUNCH((k_c2c_pq<Q, P, S, C>), dim3(grid), dim3(rows_threads(Q) * P * C), 0, st, a);
+        FFTAMD_LAUNCH((k_c2c_pq<Q, P, S, C>), dim3(grid), dim3(pq_threads(Q) * P * C), 0, st, a);
         return hipGetLastError();
       }
     }

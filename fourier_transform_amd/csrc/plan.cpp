@@ -682,7 +682,7 @@ fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
   p->pq_p = pf;
   p->pq_q = (int)(n / pf);
   std::vector<float2> ta, wn;
-  append_stage_table(p->pq_q, rows_values(p->pq_q), ta);
+  append_stage_table(p->pq_q, pq_values(p->pq_q), ta);
   for (int64_t e = 0; e < n; ++e) wn.push_back(root(e, n));
   if (finish_plan(p, {&ta, &wn}, {&p->tw_a, &p->wn}, 0) != FFT_OK) {
     free_plan(p);

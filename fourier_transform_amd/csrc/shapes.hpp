@@ -25,13 +25,24 @@ constexpr int rows_per_wg(int n) {
   return threads_per_line(n) >= 256 ? 1 : 256 / threads_per_line(n);
 }
 // The C2C row kernel: 16 values per thread and a complex LDS exchange, except
-// for rows of 8192 and more, which take 32 values per thread (one stage fewer)
-// and the split exchange (half the LDS, so four workgroups fit a CU).
-constexpr int kRowsWideMin = 8192;
+// for rows of 4096 and more, which take 32 values per thread and the split
+// exchange (half the LDS per line).  For 4096 points that keeps two rows of
+// 128 threads per workgroup and eight rows in flight per CU instead of four:
+// measured on MI355X (steady state, forward + inverse of 16384 rows) 185.9 -
+// 188.0 against 189 - 194 us per launch; 16 values with the split exchange
+// (192.9 - 194.5), 32 with the complex one (194.8 - 198.1), 32 with four
+// rows per workgroup (255.5) and 64 with one wavefront per row (195.9 -
+// 196.3) were slower.  Rows of 8192 and more: one stage fewer, and four
+// workgroups fit a CU.
+constexpr int kRowsWideMin = 4096;
 constexpr int rows_values(int n) { return n >= kRowsWideMin ? 32 : sched_e(n); }
 constexpr bool rows_split(int n) { return n >= kRowsWideMin; }
 constexpr int rows_threads(int n) { return n / rows_values(n); }
 constexpr int rows_lines(int n) { return rows_threads(n) >= 256 ? 1 : 256 / rows_threads(n); }
+// The power-of-two part of the p * 2^k kernel (k_pq.hip): 16 values per
+// thread and the complex exchange at every length it takes (q <= 4096)
+constexpr int pq_values(int q) { return sched_e(q); }
+constexpr int pq_threads(int q) { return q / pq_values(q); }
 // Workgroups whose lines are read with a stride (column lanes) or stored
 // transposed (row lanes + transposing store) hold up to 16 adjacent lines, so
 // every strided access is a run of 16 x 8 B = 128 B.  When 16 values per
