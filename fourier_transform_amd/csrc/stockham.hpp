@@ -496,6 +496,67 @@ __device__ __forceinline__ float2 tw_at(const TwLdsStage<LS>& t, uint32_t k, uin
   }
 }
 
+// Exchanges inside a wavefront without LDS (gfx950 v_permlane32_swap and
+// v_permlane16_swap).  After a radix-16 stage with NS = 16 and one 16-value
+// butterfly per thread on a line of T = 64 (or 32) threads, thread
+// u = 16c + j holds outputs q of element 256c + 16q + j.  The next stage wants
+// element e on lane e mod T, slot e / T: lane 16(q mod 4) + j, slot 4c + q/4
+// for T = 64 (lane 16(q mod 2) + j, slot 8c + q/2 for T = 32).  So the
+// exchange only swaps the lane bits above 3 (c) with the low register bits
+// (q mod 4, or q mod 2) and relabels the registers: permlane32_swap swaps
+// lanes 32-63 of one register with lanes 0-31 of another (lane bit 5),
+// permlane16_swap the odd 16-lane rows of one with the even rows of another
+// (lane bit 4).  Lines of 32 threads are half-waves, so each swap stays
+// inside its line.  Two (or one) rounds of 16 swaps replace 32 LDS accesses,
+// their address arithmetic and a barrier.  Measured on MI355X against the
+// LDS exchange: LDS instructions -58 % (1024-point rows) and -25 % (1024-point
+// real transforms), VALU instructions +1.5 %, time equal or lower (1024 x 8:
+// 4.2 against 4.5-5.1 us; real 2048 x 1024: 9.97 against 10.15 us per exec).
+// The first exchange of these lines (NS = 1) also rotates the lane bits, so
+// it stays in LDS: as swaps it would need six or more rounds, four of them at
+// lane distances below 16 (DPP moves and selects, two to three instructions
+// per value) or cross-lane permutes through the LDS crossbar.
+// (row lanes only: WAVE_LOCAL lines, thread u of a line on lane u mod T)
+template <int N, int E, int s, bool WAVE_LOCAL>
+constexpr bool swap_exchange() {
+  return WAVE_LOCAL && E == 16 && (N / E == 64 || N / E == 32) &&
+         s + 1 < sched_stages(N, E) && sched_radix(N, E, s) == 16 && sched_ns(N, E, s) == 16;
+}
+__device__ __forceinline__ void swap32(float2& a, float2& b) {
+  const auto rx = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.x), __float_as_uint(b.x), false, false);
+  const auto ry = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.y), __float_as_uint(b.y), false, false);
+  a = make_float2(__uint_as_float(rx[0]), __uint_as_float(ry[0]));
+  b = make_float2(__uint_as_float(rx[1]), __uint_as_float(ry[1]));
+}
+__device__ __forceinline__ void swap16(float2& a, float2& b) {
+  const auto rx = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.x), __float_as_uint(b.x), false, false);
+  const auto ry = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.y), __float_as_uint(b.y), false, false);
+  a = make_float2(__uint_as_float(rx[0]), __uint_as_float(ry[0]));
+  b = make_float2(__uint_as_float(rx[1]), __uint_as_float(ry[1]));
+}
+// x: the 16 outputs of the thread's butterfly; v: the next stage's slots
+template <int T>
+__device__ __forceinline__ void swap_exchange_16(float2* x, float2* v) {
+  if constexpr (T == 64) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if ((q & 2) == 0) swap32(x[q], x[q | 2]);  // lane bit 5 <-> register bit 1
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if ((q & 1) == 0) swap16(x[q], x[q | 1]);  // lane bit 4 <-> register bit 0
+    // register r = (q/4, c): slot m = 4c + q/4
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = x[((m & 3) << 2) | (m >> 2)];
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if ((q & 1) == 0) swap16(x[q], x[q | 1]);  // lane bit 4 <-> register bit 0
+    // register r = (q/2, c): slot m = 8c + q/2
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = x[((m & 7) << 1) | (m >> 3)];
+  }
+}
+
 template <int N, int E, int S, bool WAVE_LOCAL, class Lds, bool SPLIT, int s, class LdsT, class TW>
 __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, int u, int line) {
   static_assert(SPLIT == std::is_same<LdsT, float>::value, "LDS element type");
@@ -528,6 +589,9 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, in
     if constexpr (last || SPLIT) {
 #pragma unroll
       for (int r = 0; r < R; ++r) v[k + r * KB] = x[r];
+    } else if constexpr (swap_exchange<N, E, s, WAVE_LOCAL>()) {
+      static_assert(WAVE_LOCAL && !SPLIT && KB == 1, "lane-swap exchange shape");
+      swap_exchange_16<T>(x, v);
     } else {
       using I = StageIdx<T, R, NS, k>;
       const int base = I::base(u);
@@ -540,13 +604,14 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, in
     // above this one: with many values per thread that would exhaust VGPRs
     if constexpr (KB > 1 && E > 16) __builtin_amdgcn_sched_barrier(0);
   });
-  if constexpr (!last && !SPLIT) {
+  if constexpr (!last && !SPLIT && !swap_exchange<N, E, s, WAVE_LOCAL>()) {
     lds_sync<WAVE_LOCAL>();
     static_for<0, E>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       v[m] = lds[Lds::template at_k<T * m>(line, u)];
     });
-    if constexpr (s + 1 < NST - 1) lds_sync<WAVE_LOCAL>();
+    // the next stage writes LDS again (unless its exchange is a lane swap)
+    if constexpr (s + 1 < NST - 1 && !swap_exchange<N, E, s + 1, WAVE_LOCAL>()) lds_sync<WAVE_LOCAL>();
   } else if constexpr (!last && SPLIT) {
     // real parts, then imaginary parts (v[.].y still hold the butterfly
     // outputs meanwhile).  For the second half the empty asm hides that the

@@ -652,3 +652,33 @@ def test_failed_exec_leaves_options_settable():
         torch.cuda.synchronize()
     finally:
         F.fft_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_lane_swap_exchange_lines(sign):
+    """Lines of 64 and 32 threads whose second exchange is a lane swap
+    (v_permlane32_swap / v_permlane16_swap instead of LDS): 512- and
+    1024-point rows, the 2D row pass on 1024-point rows with the shift, real
+    transforms with 512- and 1024-point halves, the chirp transform on a
+    1024-point convolution and p * 2^k with 512- and 1024-point parts."""
+    g = np.random.default_rng(500 + sign)
+    for n in (512, 1024):
+        for batch in (1, 2, 5, 64):
+            say(f"lane swap: c2c n={n} batch={batch} sign={sign}")
+            x = W.uniform_c64((batch, n), g)
+            assert rel_l2(c2c(x, sign), oracle.c2c(x, sign)) <= TOL, (n, batch)
+    x = W.normal_c64((1, 64, 1024), g)
+    say("lane swap: 2d 64x1024 shift")
+    y = c2c_2d(x, sign, shift=1)
+    assert rel_l2(y, oracle.fftshift_2d(oracle.c2c_2d(x, sign))) <= TOL
+    for n in (500, 12800, 15360):          # chirp on m = 1024; 25 x 512; 15 x 1024
+        say(f"lane swap: c2c n={n} sign={sign}")
+        x = W.uniform_c64((3, n), g)
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, n
+    if sign < 0:
+        for n in (1024, 2048):
+            say(f"lane swap: real n={n}")
+            xr = g.uniform(-1, 1, (7, n)).astype(np.float32)
+            Z = r2c(xr, n // 3, mmajor=True)
+            assert rel_l2(Z.T, oracle.r2c(xr, n // 3)) <= TOL
+            assert rel_l2(c2r(Z, n, 7, n // 3, mmajor=True), oracle.c2r(Z.T, n, n // 3)) <= TOL
