@@ -24,14 +24,14 @@ namespace fftamd {
 namespace {
 constexpr int kRealAnyThreads = 256;
 
+// (row, bin) of work item t: bins fastest (row-major spectrum) or rows
+// fastest (m-major).  One division by the selected extent, then value
+// selects (selecting between two output pointers put them in scratch).
 __device__ __forceinline__ void item(const RealAnyArgs& a, int64_t t, int64_t nk, int64_t* row, int64_t* k) {
-  if (a.mmajor) {
-    *k = t / a.rows;
-    *row = t - *k * a.rows;
-  } else {
-    *row = t / nk;
-    *k = t - *row * nk;
-  }
+  const int64_t d = a.mmajor ? a.rows : nk;
+  const int64_t q = t / d, r = t - q * d;
+  *row = a.mmajor ? r : q;
+  *k = a.mmajor ? q : r;
 }
 __device__ __forceinline__ int64_t spec_at(const RealAnyArgs& a, int64_t row, int64_t k) {
   return a.mmajor ? k * a.rows + row : row * (a.mmax + 1) + k;

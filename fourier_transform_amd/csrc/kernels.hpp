@@ -379,14 +379,18 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2r_pairs(RealArgs 
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       float2 t;
+      // value selects (a select between an LDS and a private lvalue put
+      // the zero in scratch)
       if (k == 0) {
         t = make_float2(lds[L::at(line, w * H)].x, 0.f);
       } else if (k == H) {
-        t = mmax >= H ? make_float2(nyq[2 * line + w].x, 0.f) : zero;
+        t = make_float2(mmax >= H ? nyq[2 * line + w].x : 0.f, 0.f);
       } else if (k < H) {
-        t = k <= mmax ? lds[L::at(line, w * H + k)] : zero;
+        const float2 l = lds[L::at(line, w * H + k)];
+        t = k <= mmax ? l : zero;
       } else {
-        t = N - k <= mmax ? cconj(lds[L::at(line, w * H + N - k)]) : zero;
+        const float2 l = cconj(lds[L::at(line, w * H + N - k)]);
+        t = N - k <= mmax ? l : zero;
       }
       x[w] = t;
     }

@@ -636,7 +636,12 @@ __device__ __forceinline__ void run_stage(float2* v, LdsT* lds, const TW& tw, in
         if constexpr (IM) v[m].y = w; else v[m].x = w;
       });
     };
-    exchange(std::integral_constant<bool, false>{}, u, line);
+    // Each half (and each stage) takes an opaque copy of the indices: the
+    // read addresses are the same in every exchange, and kept live from one
+    // exchange to the next they spilled (k_fs_cols<4096>: 6 VGPRs).
+    int u1 = u, line1 = line;
+    asm volatile("" : "+v"(u1), "+v"(line1));
+    exchange(std::integral_constant<bool, false>{}, u1, line1);
     lds_sync<WAVE_LOCAL>();
     int u2 = u, line2 = line;
     asm volatile("" : "+v"(u2), "+v"(line2));
