@@ -417,6 +417,66 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
     for (uint32_t j = t; j < n; j += tpl) gstore_nt(dst, j, cmul(L[mixed_pad<PAD>(j)], gload(c.post, j)));
 }
 
+// Column transforms of a mixed-radix length over [images][n][nx] (see
+// launch.hpp, launch_mixed_cols): CT adjacent columns of the flattened
+// images x nx column index per workgroup.  Load: consecutive threads on
+// consecutive columns, so each row of the tile is one run of CT values,
+// into line `column` of LDS at the row's position (the shift applied on
+// load); then the stages with the line in LDS (IO = 3: the first stage
+// reads it, the last writes it back in natural order), G lines at a time
+// with tpl threads each (threads beyond the group's lines take no butterfly
+// but join every barrier); then the columns are stored back.
+constexpr int kColBatch = 16;
+template <int S, int KB, int RMAX, bool PAD>
+__global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
+  extern __shared__ float4 smem4[];
+  float2* smem = reinterpret_cast<float2*>(smem4);
+  const uint32_t n = (uint32_t)a.n, tpl = (uint32_t)a.tpl, nt = blockDim.x, tid = threadIdx.x;
+  const uint32_t CT = (uint32_t)a.lines;  // columns per workgroup (set by the launcher)
+  const uint32_t pitch = mixed_pad<PAD>(n) + 1;
+  lds_poison_dynamic(smem, CT * pitch * (uint32_t)sizeof(float2));
+  // thread tid takes column tid % CT of the tile and rows tid / CT + RS*i
+  // (nt is a multiple of 64, so of CT): one division per thread, and
+  // kColBatch loads in flight before their LDS writes
+  const uint32_t col = tid % CT, RS = nt / CT;
+  const int64_t g = (int64_t)blockIdx.x * CT + col;
+  const bool has_col = g < c.images * c.nx;
+  const int64_t img = g / c.nx;
+  const float2* src = a.in + img * (int64_t)n * c.nx + (g - img * c.nx);
+  float2* L0 = smem + col * pitch;
+  for (uint32_t r0 = tid / CT; r0 < n; r0 += kColBatch * RS) {
+    float2 v[kColBatch];
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i) {
+      const uint32_t r = r0 + RS * i;
+      v[i] = make_float2(0.f, 0.f);
+      if (has_col && r < n) {
+        v[i] = gload(src, r * (uint32_t)c.nx);
+        if (a.pre) v[i] = cmul(v[i], gload(a.pre, r));
+        if (a.flip && (r & 1)) v[i] = negate_bits(v[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kColBatch; ++i) {
+      const uint32_t r = r0 + RS * i;
+      if (r < n) L0[mixed_pad<PAD>(r)] = v[i];
+    }
+  }
+  lds_barrier();
+  const uint32_t G = nt / tpl;  // lines per group
+  for (uint32_t l0 = 0; l0 < CT; l0 += G) {
+    const uint32_t line = l0 + tid / tpl;
+    const bool active = tid < G * tpl && line < CT;
+    // an inactive thread's butterfly index is past every stage's count
+    mixed_stages<S, KB, RMAX, PAD, 3>(a, active ? tid % tpl : 0x40000000u, tpl, active, nullptr, nullptr,
+                                      smem + (active ? line : 0u) * pitch);
+  }
+  if (has_col) {
+    float2* dst = a.out + img * (int64_t)n * c.nx + (g - img * c.nx);
+    for (uint32_t r = tid / CT; r < n; r += RS) gstore(dst, r * (uint32_t)c.nx, L0[mixed_pad<PAD>(r)]);
+  }
+}
+
 namespace {
 // the checks every launch of a schedule needs (host side, before any HIP call)
 bool mixed_schedule_ok(const MixedArgs& a, int* rmax_out) {
@@ -462,6 +522,56 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
     FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false>), dim3(grid), block, lds, st, a);
   } else {
     FFTAMD_LAUNCH((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+int mixed_cols_tile(const MixedArgs& a) {
+  const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
+  for (int ct : {16, 8})
+    if ((size_t)ct * pitch * sizeof(float2) <= (size_t)kLdsBudgetBytes) return ct;
+  return 0;
+}
+
+hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs& c, hipStream_t st) {
+  int rmax = 0;
+  MixedArgs a = a0;
+  a.rows = 1;
+  a.lines = 1;
+  if (!mixed_schedule_ok(a, &rmax) || c.nx < 1 || c.images < 1 || !a.in || !a.out) return hipErrorInvalidValue;
+  const int ct = mixed_cols_tile(a);
+  if (ct == 0) return hipErrorInvalidValue;
+  a.lines = ct;
+  const int64_t cols = c.images * c.nx;
+  // element offsets r * nx within an image: below 2^29 (gload's 32-bit byte offsets)
+  if ((int64_t)a.n * c.nx > (int64_t(1) << 29)) return hipErrorInvalidValue;
+  const int64_t blocks = (cols + ct - 1) / ct;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // lines per group: as many as 1024 threads hold, at least 256 threads
+  int g = 1024 / a.tpl;
+  if (g > ct) g = ct;
+  int threads = g * a.tpl;
+  threads = (threads + 63) / 64 * 64;
+  const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
+  const size_t lds = (size_t)ct * pitch * sizeof(float2);
+  const dim3 grid((uint32_t)blocks), block((uint32_t)threads);
+  if (rmax > 8) {
+    if (a.pad) {
+      if (sign < 0)
+        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true>), grid, block, lds, st, a, c);
+      else
+        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true>), grid, block, lds, st, a, c);
+    } else if (sign < 0) {
+      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false>), grid, block, lds, st, a, c);
+    } else {
+      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false>), grid, block, lds, st, a, c);
+    }
+  } else if (a.pad) {
+    return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
+  } else if (sign < 0) {
+    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false>), grid, block, lds, st, a, c);
+  } else {
+    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false>), grid, block, lds, st, a, c);
   }
   return hipGetLastError();
 }

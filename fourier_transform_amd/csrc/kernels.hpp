@@ -104,6 +104,11 @@ __global__ __launch_bounds__(tile_lines(N, false) * (N / tile_e(N, false))) void
     const float2* src = a.in + base;
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = gload(src, off + step * m);
+    if (a.shift) {  // slot m holds row u + T*m: (-1)^row
+#pragma unroll
+      for (int m = 0; m < E; ++m)
+        if ((u + T * m) & 1) v[m] = negate_bits(v[m]);
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);

@@ -45,6 +45,7 @@ struct ColsArgs {
   float2* out;
   const float2* tw;  // single-pass stage table for ny
   int64_t ny, nx, images;
+  int shift;  // 1: multiply row i by (-1)^i on load (the shift along y; ny even)
 };
 hipError_t launch_c2c_cols(int ny, int sign, const ColsArgs& a, hipStream_t stream);
 
@@ -201,6 +202,24 @@ struct MixedArgs {
   uint32_t ns_magic[kMixedMaxStages];
 };
 hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
+
+// Column transforms of a mixed-radix length n = a.n over [images][n][nx]
+// (the column pass of 2D plans whose ny has a mixed-radix schedule):
+// a.in / a.out hold the images (in place allowed: a workgroup reads its whole
+// tile before writing it), a.pre / a.flip the shift along y on load; the
+// schedule, tables and threads per line of `a` as for launch_mixed (a.rows
+// unused; a.lines is set by the launcher to the columns per workgroup).
+// n * nx must stay below 2^29 (32-bit element offsets within an image).  mixed_cols_tile(a) adjacent columns per workgroup
+// are staged in LDS (rows of the tile are runs of 8 * columns bytes), the
+// stages run on the lines in LDS a group of lines at a time, and the columns
+// are stored back.
+struct MixedColsArgs {
+  int64_t nx, images;
+};
+// columns per workgroup (16 or 8, the most that fit the LDS), or 0 when not
+// even 8 fit (the caller then transposes instead)
+int mixed_cols_tile(const MixedArgs& a);
+hipError_t launch_mixed_cols(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t stream);
 
 // C2C rows of a prime length p by Rader's algorithm ("High Performance
 // Fourier Transforms on GPUs with GLSL", section 2.3, names it beside

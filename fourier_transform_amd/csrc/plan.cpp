@@ -246,6 +246,11 @@ struct fft_plan {
   // 2D plans with an axis that is not a power of two: row plans of nx (inner)
   // and of ny (inner2, run on the transposed image)
   bool any2d = false;
+  // column pass of those plans: 0 = transpose, row plan of ny, transpose
+  // back (four HBM passes with the rows); 1 = k_c2c_cols in place (ny a power
+  // of two, tw_b its table); 2 = k_mixed_cols in place (ny has a mixed-radix
+  // schedule, inner2 holds it)
+  int cols2d = 0;
   fft_plan* inner2 = nullptr;
   float2* scratch = nullptr;
   size_t scratch_bytes = 0;
@@ -855,12 +860,31 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
     if (batch > 65535)
       return set_err(FFT_ENOTSUP, "2D plans with a size that is not a power of two take at most 65535 images"),
              nullptr;
+    // The column pass runs in place on the columns (two HBM passes with the
+    // rows) when ny is a power of two whose column tile holds at least 8
+    // columns (64 B runs), or has a mixed-radix schedule whose tile does;
+    // else the image is transposed, transformed as rows and transposed back.
     fft_plan* rows = fft_plan_create(nx, batch * ny, FFT_C2C, sign);
     if (!rows) return nullptr;
-    fft_plan* cols = fft_plan_create(ny, batch * nx, FFT_C2C, sign);
-    if (!cols) {
-      free_plan(rows);
-      return nullptr;
+    int cols2d = 0;
+    fft_plan* cols = nullptr;
+    if (is_pow2(ny) && ny <= kMaxSinglePass && tile_lines((int)ny, false) >= 8) {
+      cols2d = 1;
+    } else {
+      cols = fft_plan_create(ny, is_pow2(ny) ? 1 : batch * nx, FFT_C2C, sign);
+      if (!cols) {
+        free_plan(rows);
+        return nullptr;
+      }
+      if (cols->mixed && mixed_cols_tile(cols->mx) >= 8 && ny * nx <= (int64_t(1) << 29)) cols2d = 2;
+      if (cols2d == 0 && is_pow2(ny)) {  // the transposed rows need a plan of the full batch
+        free_plan(cols);
+        cols = fft_plan_create(ny, batch * nx, FFT_C2C, sign);
+        if (!cols) {
+          free_plan(rows);
+          return nullptr;
+        }
+      }
     }
     fft_plan* p = new (std::nothrow) fft_plan();
     if (!p) {
@@ -876,10 +900,16 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
     p->kind = kind;
     p->sign = sign;
     p->any2d = true;
+    p->cols2d = cols2d;
     p->inner = rows;
     p->inner2 = cols;
-    std::vector<float2> none(1, make_float2(0.f, 0.f));
-    if (finish_plan(p, {&none}, {&p->tw_a}, (size_t)(ny * nx * batch) * sizeof(float2)) != FFT_OK) {
+    std::vector<float2> tcols;
+    if (cols2d == 1)
+      append_stage_table((int)ny, cols_values((int)ny), tcols);
+    else
+      tcols.push_back(make_float2(0.f, 0.f));
+    const size_t scratch = cols2d ? 0 : (size_t)(ny * nx * batch) * sizeof(float2);
+    if (finish_plan(p, {&tcols}, {&p->tw_b}, scratch) != FFT_OK) {
       free_plan(p);
       return nullptr;
     }
@@ -942,9 +972,9 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
       if (value && !p->bluestein && !p->mixed && !p->rader && !p->any2d &&
           ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
-      if (p->any2d) {  // the shift of each axis, in its row plan
+      if (p->any2d) {  // the shift of each axis: in its row plan, or in the column pass
         if (fft_plan_set(p->inner, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
-        if (fft_plan_set(p->inner2, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
+        if (p->inner2 && fft_plan_set(p->inner2, FFT_OPT_SHIFT, value) != FFT_OK) return g_err.code;
       }
       p->shift = (int)value;
       return ok();
@@ -1006,6 +1036,28 @@ int run_plan(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float
   hipError_t e = hipSuccess;
   const float2* src = static_cast<const float2*>(in);
   float2* dst = static_cast<float2*>(out);
+  if (p->any2d && p->cols2d) {
+    // rows (with the shift along x), then the columns in place on out (with
+    // the shift along y)
+    int rc = fft_exec(p->inner, in, out, stream_);
+    if (rc != FFT_OK) return rc;
+    if (p->cols2d == 1) {
+      const ColsArgs c{dst, dst, p->tw_b, p->ny, p->nx, p->batch, p->shift ? 1 : 0};
+      e = launch_c2c_cols((int)p->ny, p->sign, c, stream);
+    } else {
+      MixedArgs a = p->inner2->mx;
+      a.in = dst;
+      a.out = dst;
+      // even ny: the exact sign flip of odd rows for either shift; odd ny: the ramps
+      const bool even = p->ny % 2 == 0;
+      a.flip = even && p->shift ? 1 : 0;
+      a.pre = even ? nullptr
+                   : p->shift == 1 ? p->inner2->mx_shift : p->shift == 2 ? p->inner2->mx_ishift : nullptr;
+      e = launch_mixed_cols(p->sign, a, MixedColsArgs{p->nx, p->batch}, stream);
+    }
+    if (e != hipSuccess) return hip_err(e, "kernel launch");
+    return FFT_OK;
+  }
   if (p->any2d) {
     int rc = fft_exec(p->inner, in, out, stream_);
     if (rc == FFT_OK) e = launch_transpose(dst, sc, p->ny, p->nx, p->batch, stream);

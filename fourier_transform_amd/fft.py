@@ -111,7 +111,14 @@ def fft_plan_create_2d(ny, nx, batch=1, kind=FFT_C2C, sign=FFT_FORWARD):
     return p
 
 
+# (in_bytes, out_bytes) per plan handle, for the size checks of fft_exec
+# without a library call per exec; dropped when an option changes or the plan
+# is destroyed
+_sizes = {}
+
+
 def fft_plan_set(plan, option, value):
+    _sizes.pop(plan, None)
     return _check(lib().fft_plan_set(plan, int(option), int(value)))
 
 
@@ -145,7 +152,10 @@ def fft_exec(plan, x, y, stream=None):
 def _exec_args(plan, x, y, stream):
     px, bx = _ptr_and_bytes(x)
     py, by = _ptr_and_bytes(y)
-    need_in, need_out = fft_plan_get_sizes(plan)
+    sizes = _sizes.get(plan)
+    if sizes is None:
+        sizes = _sizes[plan] = fft_plan_get_sizes(plan)
+    need_in, need_out = sizes
     if bx is not None and bx < need_in:
         raise ValueError(f"input holds {bx} bytes, plan reads {need_in}")
     if by is not None and by < need_out:
@@ -167,6 +177,7 @@ def fft_exec_noalloc(plan, x, y, stream=None):
 
 
 def fft_plan_destroy(plan):
+    _sizes.pop(plan, None)
     lib().fft_plan_destroy(plan)
 
 

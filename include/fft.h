@@ -36,9 +36,13 @@
  *    of n values for odd n, through a plan-owned scratch buffer of
  *    batch * n * 4 bytes (even n) or 2 * batch * n * 8 bytes (odd n)).
  *  - 2D sizes: powers of two from 2 to 16384 (row pass, then column pass),
- *    or any sizes from 2 to 2^22 (row transforms, a tiled transpose, row
- *    transforms of the transposed image, a transpose back; at most 65535
- *    images; plan-owned scratch of batch * ny * nx * 8 bytes).
+ *    or any sizes from 2 to 2^22 (at most 65535 images): row transforms,
+ *    then the column transforms in place on `out` when ny is a power of two
+ *    up to 4096, or has a mixed-radix schedule (see C2C lengths) whose
+ *    column tile of 8 or more columns fits the LDS (ny up to about 2560)
+ *    and ny * nx <= 2^29; otherwise a tiled transpose, row transforms of the
+ *    transposed image and a transpose back, through a plan-owned scratch of
+ *    batch * ny * nx * 8 bytes.
  *    The direct kinds below take any length from 2 to 16384.
  *  - Buffers: `in` and `out` are DEVICE pointers owned by the caller, 8-byte
  *    aligned.  The plan owns its twiddle tables and scratch (allocated at

@@ -258,11 +258,17 @@ def test_real_any_length_options():
 
 
 # --------------------------------------------------------------------------
-# 2D plans with an axis that is not a power of two (rows, transpose, rows,
-# transpose back); the shift is the shift of each axis
+# 2D plans with an axis that is not a power of two: the row plan, then the
+# columns in place (power-of-two ny: the column kernel; a mixed-radix ny: its
+# stages on column tiles in LDS) where a tile holds 8 or more columns, else
+# rows, transpose, rows, transpose back; the shift is the shift of each axis
 # --------------------------------------------------------------------------
 SIZES_2D = [(3, 5, 2), (6, 10, 3), (100, 64, 2), (64, 100, 2), (360, 180, 1), (1000, 999, 1), (17, 1024, 2),
-            (97, 331, 1), (10001, 6, 1)]
+            (97, 331, 1), (10001, 6, 1),
+            # column pass in place: power-of-two ny (16 and 8 columns per tile), mixed-radix ny (16 and 8,
+            # one and two butterflies per thread, odd), then the transposing fallback (8192, 6000)
+            (1024, 100, 2), (2048, 60, 1), (4096, 12, 1), (1000, 64, 1), (2000, 30, 1), (7776, 7, 1),
+            (105, 64, 2), (64, 1000, 3), (8192, 20, 1), (6000, 20, 1)]
 
 
 @pytest.mark.parametrize("ny,nx,batch", SIZES_2D)
@@ -273,7 +279,8 @@ def test_2d_any_size(ny, nx, batch, sign):
     assert rel_l2(c2c_2d(x, sign), oracle.c2c_2d(x, sign)) <= TOL
 
 
-@pytest.mark.parametrize("ny,nx", [(3, 5), (7, 8), (100, 99)])
+@pytest.mark.parametrize("ny,nx", [(3, 5), (7, 8), (100, 99), (64, 100), (1024, 30), (1000, 64), (105, 60),
+                                   (2000, 30)])
 @pytest.mark.parametrize("shift", [1, 2])
 def test_2d_any_size_shift_and_in_place(ny, nx, shift):
     say(f"2D any size {ny}x{nx} shift={shift}, in place")
