@@ -19,10 +19,16 @@ struct FsRowsOp {
     static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N1, true);
       if ((a.batch * a.n2) % C != 0) return hipErrorInvalidValue;  // the kernel loads whole groups
-      uint32_t grid;
+      constexpr int threads = C * (N1 / tile_e(N1, true));
+      uint32_t grid, resident = 0;
       hipError_t e = grid_of(a.batch * a.n2, C, &grid);
       if (e != hipSuccess) return e;
-      FFTAMD_LAUNCH((k_fs_rows<N1, S, BC>), dim3(grid), dim3(C * (N1 / tile_e(N1, true))), 0, st, a);
+      if constexpr (fs_rows_persistent<N1>()) {
+        // at most as many workgroups as run at once, each looping over tiles
+        if ((e = resident_workgroups<k_fs_rows<N1, S, BC>>(threads, &resident)) != hipSuccess) return e;
+        if (grid > resident) grid = resident;
+      }
+      FFTAMD_LAUNCH((k_fs_rows<N1, S, BC>), dim3(grid), dim3(threads), 0, st, a);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {
