@@ -30,7 +30,16 @@ namespace fftamd {
 
 // ---------------------------------------------------------------------------
 // pass 1: N = nx, NA rows per workgroup, EF values per thread
+//
+// Tiles of 64 values per thread (one workgroup holds the CU) are persistent,
+// as in four-step pass 2: one wave of workgroups, each looping over (image,
+// yb) tiles.  Measured per launch: 16384 x 4096 265 -> 250 us, 8192 x 8192
+// 272 us either way; the same loop in pass 2 was slower (269 -> 277 us).
 // ---------------------------------------------------------------------------
+template <int EF>
+constexpr bool fold_rows_persistent() {
+  return EF == kSplitValues;
+}
 template <int N, int NA, int EF, int S>
 __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   constexpr int E = EF;
@@ -49,18 +58,30 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
   __shared__ float2 twl[LTW ? TW1 : 1];
   lds_poison(lds, twl);
 
-  const int tid = threadIdx.x;
-  const int line = tid / T, u = tid % T;
+  constexpr bool PERSIST = fold_rows_persistent<EF>();
+  if constexpr (LTW && PERSIST) {  // the stage-1 twiddles once per workgroup
+    float2 tq[TQ];
+    fs_fetch_tw1<N, E, NT, TQ>(tq, a.tw, threadIdx.x);
+    fs_store_tw1<N, E, NT, TQ>(twl, tq, threadIdx.x);
+    lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
+  }
   const uint32_t nb = (uint32_t)(a.ny / NA);
-  const int64_t img = (int64_t)(blockIdx.x / nb);
-  const uint32_t yb = blockIdx.x - (uint32_t)img * nb;
+  const uint32_t ntiles = (uint32_t)(a.images * nb);
+  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // a per-tile opaque copy of the thread index: what derives from it is
+  // recomputed per tile rather than kept live across the loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int line = tid / T, u = tid % T;
+  const int64_t img = (int64_t)(tile / nb);
+  const uint32_t yb = tile - (uint32_t)img * nb;
   // the small loads first (see k_fs_cols): W_ny^{yb*ka}, one factor per
   // output row (yb*ka < ny), and the stage-1 twiddles
   float2 w[NA];
 #pragma unroll
   for (int ka = 1; ka < NA; ++ka) w[ka] = gload(a.wy, yb * (uint32_t)ka);
   float2 tq[TQ];
-  if constexpr (LTW) fs_fetch_tw1<N, E, NT, TQ>(tq, a.tw, tid);
+  if constexpr (LTW && !PERSIST) fs_fetch_tw1<N, E, NT, TQ>(tq, a.tw, tid);
   __builtin_amdgcn_sched_barrier(0);
   // rows yb + nb*line of the image; 32-bit offsets from a uniform base
   const float2* src = a.in + (img * a.ny + yb) * N;
@@ -71,7 +92,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
     v[m] = gload_nt(src + T * m, off);
   });
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (LTW) {
+  if constexpr (LTW && !PERSIST) {
     fs_store_tw1<N, E, NT, TQ>(twl, tq, tid);
     lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
   }
@@ -132,6 +153,8 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
       const float2 y = ka == 0 ? x[0] : apply_tw<S>(x[ka], w[ka]);
       gstore_nt(dst, (uint32_t)(ka * N + i0 + T * i), y);
     }
+  }
+  lds_barrier();  // the next tile's exchanges overwrite LDS
   }
 }
 
@@ -218,9 +241,15 @@ hipError_t run_fold(const FoldArgs& a, hipStream_t st) {
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FoldArgs p1 = a;
   p1.out = a.scratch;
-  FFTAMD_LAUNCH((k_rows_fold<NX, NA, E1, S>), dim3((uint32_t)g1), dim3(NA * NX / E1), 0, st, p1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  uint32_t grid1 = (uint32_t)g1;
+  hipError_t e;
+  if constexpr (fold_rows_persistent<E1>()) {
+    uint32_t resident = 0;
+    if ((e = resident_workgroups<k_rows_fold<NX, NA, E1, S>>(NA * NX / E1, &resident)) != hipSuccess) return e;
+    if (grid1 > resident) grid1 = resident;
+  }
+  FFTAMD_LAUNCH((k_rows_fold<NX, NA, E1, S>), dim3(grid1), dim3(NA * NX / E1), 0, st, p1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   FoldArgs p2 = a;
   p2.in = a.scratch;
   FFTAMD_LAUNCH((k_fold_cols<NB, C, E2, S>), dim3((uint32_t)g2), dim3(C * NB / E2), 0, st, p2);
