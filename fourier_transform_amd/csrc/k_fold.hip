@@ -139,7 +139,9 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
     });
   });
 
-  // scratch: group yb of image img, its NA rows adjacent
+  // scratch: group yb of image img, its NA rows adjacent.  Ordinary (not
+  // streaming) stores, so that pass 2 finds part of it in the caches
+  // (8192 x 8192: 549.6 -> 546.8 us, 16384 x 4096: 529.9 -> 523.1 us per exec)
   constexpr int64_t GP = fold_group_pitch(N, NA);
   float2* dst = a.out + (img * nb + yb) * GP;
 #pragma unroll
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
 #pragma unroll
     for (int ka = 0; ka < NA; ++ka) {
       const float2 y = ka == 0 ? x[0] : apply_tw<S>(x[ka], w[ka]);
-      gstore_nt(dst, (uint32_t)(ka * N + i0 + T * i), y);
+      gstore(dst, (uint32_t)(ka * N + i0 + T * i), y);
     }
   }
   lds_barrier();  // the next tile's exchanges overwrite LDS

@@ -571,7 +571,10 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
     const int line2 = tid2 % C, u2 = tid2 / C;
     const uint32_t eu = (c0 + (uint32_t)line2) * (uint32_t)u2;
     const float2 wu = cmul(gload(a.thi, eu >> a.bits), gload(a.tlo, eu & mask));
-    // the block layout, relative to the first block column of this group
+    // the block layout, relative to the first block column of this group.
+    // Ordinary (not streaming) stores: pass 2 finds part of the scratch still
+    // in the caches (2^22 x 32: 906 -> 891 us per exec; streaming loads or
+    // ordinary stores in pass 2 were slower, 945 and 952 us)
     float2* dst = a.out + b * (int64_t)n1 * N2 + c0 * BK;
     if constexpr (T % BK == 0) {
       // k2 = u2 + T*m with T a multiple of BK: the block index is a
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 #pragma unroll
       for (int m = 0; m < E; ++m) {
         const float2 w = cmul(wu, ftab[line2 * FP + m]);
-        gstore_nt(dst + row_step * m, base, apply_tw<S>(v[m], w));
+        gstore(dst + row_step * m, base, apply_tw<S>(v[m], w));
         if constexpr (E > 16) {
           if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
         }
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
       for (int m = 0; m < E; ++m) {
         const uint32_t k2 = (uint32_t)(u2 + T * m);
         const float2 w = cmul(wu, ftab[line2 * FP + m]);
-        gstore_nt(dst, fs_block_index<BK, C>(k2, (uint32_t)line2, n1), apply_tw<S>(v[m], w));
+        gstore(dst, fs_block_index<BK, C>(k2, (uint32_t)line2, n1), apply_tw<S>(v[m], w));
         if constexpr (E > 16) {
           if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
         }
