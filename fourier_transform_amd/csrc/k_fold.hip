@@ -33,8 +33,10 @@ namespace fftamd {
 //
 // Tiles of 64 values per thread (one workgroup holds the CU) are persistent,
 // as in four-step pass 2: one wave of workgroups, each looping over (image,
-// yb) tiles.  Measured per launch: 16384 x 4096 265 -> 250 us, 8192 x 8192
-// 272 us either way; the same loop in pass 2 was slower (269 -> 277 us).
+// yb) tiles, half of them starting 13 us late (stagger_start).  Measured per
+// launch: 8192 x 8192 277 -> 243-248 us (6 us late: 270, 9: 264, 18: 273;
+// persistent without the stagger: 272), 16384 x 4096 265 -> 236-239 us.  The
+// same loop in pass 2 was slower (269 -> 277 us).
 // ---------------------------------------------------------------------------
 template <int EF>
 constexpr bool fold_rows_persistent() {
@@ -65,13 +67,14 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
     fs_store_tw1<N, E, NT, TQ>(twl, tq, threadIdx.x);
     lds_barrier();  // the stage exchanges may be wave-local: publish the copy here
   }
+  if constexpr (PERSIST) stagger_start(a.stagger);
   const uint32_t nb = (uint32_t)(a.ny / NA);
   const uint32_t ntiles = (uint32_t)(a.images * nb);
   for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
   // a per-tile opaque copy of the thread index: what derives from it is
   // recomputed per tile rather than kept live across the loop
   int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int line = tid / T, u = tid % T;
   const int64_t img = (int64_t)(tile / nb);
   const uint32_t yb = tile - (uint32_t)img * nb;
@@ -156,6 +159,7 @@ __global__ __launch_bounds__(NA * N / EF) void k_rows_fold(FoldArgs a) {
       gstore(dst, (uint32_t)(ka * N + i0 + T * i), y);
     }
   }
+  if constexpr (!PERSIST) break;  // one tile per workgroup
   lds_barrier();  // the next tile's exchanges overwrite LDS
   }
 }
@@ -243,17 +247,20 @@ hipError_t run_fold(const FoldArgs& a, hipStream_t st) {
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FoldArgs p1 = a;
   p1.out = a.scratch;
+  p1.stagger = 0;
   uint32_t grid1 = (uint32_t)g1;
   hipError_t e;
   if constexpr (fold_rows_persistent<E1>()) {
     uint32_t resident = 0;
     if ((e = resident_workgroups<k_rows_fold<NX, NA, E1, S>>(NA * NX / E1, &resident)) != hipSuccess) return e;
     if (grid1 > resident) grid1 = resident;
+    if ((e = stagger_ticks(13.0, (uint32_t)g1, grid1, &p1.stagger)) != hipSuccess) return e;
   }
   FFTAMD_LAUNCH((k_rows_fold<NX, NA, E1, S>), dim3(grid1), dim3(NA * NX / E1), 0, st, p1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   FoldArgs p2 = a;
   p2.in = a.scratch;
+  p2.stagger = 0;
   FFTAMD_LAUNCH((k_fold_cols<NB, C, E2, S>), dim3((uint32_t)g2), dim3(C * NB / E2), 0, st, p2);
   return hipGetLastError();
 }

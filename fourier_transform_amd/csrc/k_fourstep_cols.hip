@@ -18,11 +18,23 @@ struct FsColsOp {
     template <int BK>
     static hipError_t go(const FourStepArgs& a, hipStream_t st) {
       constexpr int C = tile_lines(N2, false);
+      constexpr int threads = C * (N2 / tile_e(N2, false));
       if ((a.batch * a.n1) % C != 0) return hipErrorInvalidValue;  // the kernel loads whole groups
       uint32_t grid;
       hipError_t e = grid_of(a.batch * a.n1, C, &grid);
       if (e != hipSuccess) return e;
-      FFTAMD_LAUNCH((k_fs_cols<N2, S, BK, HOOK>), dim3(grid), dim3(C * (N2 / tile_e(N2, false))), 0, st, a);
+      FourStepArgs b = a;
+      b.stagger = 0;
+      if constexpr (fs_cols_persistent<N2, HOOK>()) {
+        // at most as many workgroups as run at once, each looping over
+        // tiles, half of them 7 us late
+        const uint32_t tiles = grid;
+        uint32_t resident = 0;
+        if ((e = resident_workgroups<k_fs_cols<N2, S, BK, HOOK>>(threads, &resident)) != hipSuccess) return e;
+        if (grid > resident) grid = resident;
+        if ((e = stagger_ticks(7.0, tiles, grid, &b.stagger)) != hipSuccess) return e;
+      }
+      FFTAMD_LAUNCH((k_fs_cols<N2, S, BK, HOOK>), dim3(grid), dim3(threads), 0, st, b);
       return hipGetLastError();
     }
     static hipError_t run(const FourStepArgs& a, hipStream_t st) {

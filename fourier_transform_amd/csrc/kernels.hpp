@@ -461,7 +461,18 @@ __device__ __forceinline__ void fs_store_tw1(float2* twl, const float2* tq, int 
 // Four-step pass 1: column transforms of length N2 over stride n1, each
 // output multiplied by W_n^{n1*k2}, stored to scratch in the block layout
 // above (BK: rows per pass-2 workgroup)
+//
+// Tiles of 64 values per thread (N2 >= 2048) are persistent, with a
+// staggered start (stagger_start): 2^22 x 32 pass 1 456 -> 439-441 us per
+// launch with half of the workgroups 6-8 us late (4: 443, 10: 443, 12: 453;
+// persistent without the stagger: no change).  The smaller tiles, and the
+// hooked pass of the chirp transform (its extra live values spill in the
+// loop), launch one workgroup per tile and run the loop once.
 // ---------------------------------------------------------------------------
+template <int N2, bool HOOK>
+constexpr bool fs_cols_persistent() {
+  return !HOOK && tile_e(N2, false) == kSplitValues;
+}
 template <int N2, int S, int BK, bool HOOK>
 __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) void k_fs_cols(FourStepArgs a) {
   constexpr int E = tile_e(N2, false);
@@ -481,14 +492,34 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   __shared__ float2 twl[LTW ? TW1 : 1];
   lds_poison(lds, ftab, twl);
 
-  const int tid = threadIdx.x;
+  constexpr bool PERSIST = fs_cols_persistent<N2, HOOK>();
+  constexpr int NT = C * T;
+  // stage-1 twiddles: copied to LDS once per workgroup when persistent; else
+  // fetched with the small loads below and stored after the line's loads.
+  // Stage 0's exchange barriers order the copy before its reads.
+  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
+  if constexpr (LTW && PERSIST) {
+    float2 tq[TQ];
+    fs_fetch_tw1<N2, E, NT, TQ>(tq, a.tw, threadIdx.x);
+    fs_store_tw1<N2, E, NT, TQ>(twl, tq, threadIdx.x);
+  }
+  if constexpr (PERSIST) stagger_start(a.stagger);
+  const uint32_t ntiles = (uint32_t)(a.batch * a.n1 / C);  // whole groups (checked by the launcher)
+  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // a per-tile opaque copy of the thread index: what derives from it is
+  // recomputed per tile rather than kept live across the loop (spills)
+  int tid = threadIdx.x;
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int line = tid % C, u = tid / C;
-  // n1 >= 128 > C: the group's columns belong to one transform b
-  const int64_t g0 = (int64_t)xcd_grouped_block(blockIdx.x, gridDim.x) * C;
+  // n1 >= 128 > C: the group's columns belong to one transform b.  n1 is a
+  // power of two: shifts, not a 64-bit division (whose reciprocal the
+  // compiler would keep live across the tile loop)
+  const int64_t g0 = (int64_t)xcd_grouped_block(tile, ntiles) * C;
   const uint32_t n1 = (uint32_t)a.n1;
   const bool valid = g0 + line < a.batch * (int64_t)n1;
-  const int64_t b = g0 / n1;
-  const uint32_t c1 = (uint32_t)(g0 - b * n1) + line;
+  const uint32_t n1_log2 = (uint32_t)__builtin_ctz(n1);
+  const int64_t b = g0 >> n1_log2;
+  const uint32_t c1 = (uint32_t)(g0 & (int64_t)(n1 - 1)) + line;
   const int64_t base = (HOOK ? b * a.in_stride : b * (int64_t)n1 * N2) + (c1 - line);
   const uint32_t off = (uint32_t)line + (uint32_t)u * n1;
   const uint32_t step = (uint32_t)T * n1;
@@ -503,21 +534,19 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
   // twiddles) are issued first and consumed only after the line's loads have
   // been issued: loads complete in issue order, so waiting for them then does
   // not wait for the line.
-  constexpr int NT = C * T;
   constexpr int FQ = (C * E + NT - 1) / NT;
   float2 fh[FQ], fl[FQ];
 #pragma unroll
   for (int i = 0; i < FQ; ++i) {
     const int q = tid + NT * i;
-    if (q < C * E) {
+    if ((C * E) % NT == 0 || q < C * E) {
       const uint32_t e = (c0 + (uint32_t)(q / E)) * (uint32_t)(T * (q % E));
       fh[i] = gload(a.thi, e >> a.bits);
       fl[i] = gload(a.tlo, e & mask);
     }
   }
-  constexpr int TQ = LTW ? (TW1 + NT - 1) / NT : 1;
   float2 tq[TQ];
-  if constexpr (LTW) fs_fetch_tw1<N2, E, NT, TQ>(tq, a.tw, tid);
+  if constexpr (LTW && !PERSIST) fs_fetch_tw1<N2, E, NT, TQ>(tq, a.tw, tid);
   __builtin_amdgcn_sched_barrier(0);
   float2 v[E];
   if (valid && HOOK) {
@@ -550,9 +579,9 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 #pragma unroll
   for (int i = 0; i < FQ; ++i) {
     const int q = tid + NT * i;
-    if (q < C * E) ftab[(q / E) * FP + q % E] = cmul(fh[i], fl[i]);
+    if ((C * E) % NT == 0 || q < C * E) ftab[(q / E) * FP + q % E] = cmul(fh[i], fl[i]);
   }
-  if constexpr (LTW) fs_store_tw1<N2, E, NT, TQ>(twl, tq, tid);
+  if constexpr (LTW && !PERSIST) fs_store_tw1<N2, E, NT, TQ>(twl, tq, tid);
   if (valid && !HOOK && a.shift && (c1 & 1)) {  // element index c1 + n1*k has the parity of c1 (n1 even)
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = negate_bits(v[m]);
@@ -601,6 +630,9 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
       }
     }
   }
+  if constexpr (!PERSIST) break;  // one tile per workgroup
+  lds_barrier();  // the next tile's factor table and exchanges overwrite LDS
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -619,7 +651,8 @@ __global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) v
 // (512 MiB): 2^22 x 32 pass 2 459 -> 418 us, 2^22 x 16 493 -> 477 us, 2^24 x 4
 // 764 -> 745 us, 2^28 14.63 -> 14.08 ms; the same loop in pass 1 no change.
 // The smaller tiles (2^15 .. 2^20: 0.85x .. 0.99x when persistent) launch one
-// workgroup per tile and run the loop once.
+// workgroup per tile and run the loop once.  A staggered start as in pass 1
+// made this pass slower (428 -> 428-441 us for 6-18 us).
 // ---------------------------------------------------------------------------
 template <int N1>
 constexpr bool fs_rows_persistent() {
@@ -660,7 +693,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
   // a per-tile opaque copy of the thread index: what derives from it is
   // recomputed per tile rather than kept live across the loop (spills)
   int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  if constexpr (PERSIST) asm volatile("" : "+v"(tid));
   const int line = tid / T, u = tid % T;
   float2 tq[TQ];
   if constexpr (LTW && !PERSIST) fs_fetch_tw1<N1, E, NT, TQ>(tq, a.tw, tid);
@@ -754,6 +787,7 @@ __global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) voi
       }
     }
   }
+  if constexpr (!PERSIST) break;  // one tile per workgroup
   lds_barrier();  // the next tile's exchanges overwrite LDS
   }
 }
@@ -793,6 +827,26 @@ hipError_t resident_workgroups(int threads, uint32_t* out) {
   const uint32_t r = (uint32_t)per_cu * (uint32_t)cus;
   if (cacheable) cache[dev].store(r, std::memory_order_relaxed);
   *out = r;
+  return hipSuccess;
+}
+
+// The stagger of a persistent launch: `us` microseconds in wall-clock ticks
+// of the current device, when each workgroup runs at least 4 tiles (else 0:
+// a delayed workgroup would only lengthen the launch).
+inline hipError_t stagger_ticks(double us, uint32_t tiles, uint32_t grid, int64_t* out) {
+  static std::atomic<int> rate_khz[kResidentDevices];
+  *out = 0;
+  if ((uint64_t)tiles < 4ull * grid) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int khz = dev >= 0 && dev < kResidentDevices ? rate_khz[dev].load(std::memory_order_relaxed) : 0;
+  if (khz == 0) {
+    if ((e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+    if (khz <= 0) return hipSuccess;  // no wall clock: no stagger
+    if (dev >= 0 && dev < kResidentDevices) rate_khz[dev].store(khz, std::memory_order_relaxed);
+  }
+  *out = (int64_t)(us * khz / 1000.0);
   return hipSuccess;
 }
 

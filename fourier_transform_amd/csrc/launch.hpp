@@ -95,6 +95,7 @@ struct FourStepArgs {
   int64_t in_stride, out_stride;
   int in_len, out_len;
   float2* sink;  // launch_chirp_out: >= 1024 elements nothing else reads (dropped outputs land there)
+  int64_t stagger;  // set by the launcher: wall-clock ticks by which half of the workgroups start late
 };
 hipError_t launch_fourstep_cols(int n2, int sign, const FourStepArgs& a, hipStream_t stream, bool hook = false);
 hipError_t launch_fourstep_rows(int n1, int sign, const FourStepArgs& a, hipStream_t stream);
@@ -150,6 +151,7 @@ struct FoldArgs {
   int64_t images;
   int64_t ny, nx;
   int shift;          // 1: (-1)^(y + x) on the load (fftshift of both axes)
+  int64_t stagger;    // set by the launcher: wall-clock ticks by which half of the workgroups start late
 };
 bool fold_supported(int64_t ny, int64_t nx);
 hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t stream);

@@ -667,4 +667,19 @@ __device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t b, uint32_t nbloc
   return (b & 7u) * (full >> 3) + (b >> 3);
 }
 
+
+// Persistent passes whose workgroup holds a CU alone start in lockstep:
+// every CU loads its first tile at once and then computes while HBM idles,
+// and tiles of equal work keep them in step.  Half of each XCD's workgroups
+// (blocks are dealt to the 8 XCDs round-robin, so index bit 3 halves each
+// XCD's set) therefore start `ticks` of the constant-rate wall clock late,
+// which puts the two halves' load and compute phases out of step for the
+// rest of the launch.  The wait is bounded by the clock.
+__device__ __forceinline__ void stagger_start(int64_t ticks) {
+  if (ticks > 0 && ((blockIdx.x >> 3) & 1u)) {
+    const long long t0 = wall_clock64();
+    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(4);
+  }
+}
+
 }  // namespace fftamd
