@@ -502,11 +502,50 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 29     # the bench's reference copy: 512 MiB read and 512 MiB written
 
 
+NUM_CUS = 256  # MI355X compute units
+XCDS = 8   # GRBM_GUI_ACTIVE is summed over the XCDs' instances in rocprofv3's counter CSV
+
+
+def summarize_pmc(paths, out=sys.stdout):
+    """LDS and VALU activity per kernel from rocprofv3 --pmc counter CSVs of a
+    bench run (one counter group per run; the files are merged by kernel
+    name).  Per dispatch, each counter is summed over its instances (one CSV
+    row per dispatch and counter); the table gives the mean over dispatches
+    and, where their counters are present, the conflict share
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE, VALUBusy = 100 *
+    SQ_ACTIVE_INST_VALU / CUs / (GRBM_GUI_ACTIVE / XCDs) and VALUUtilization =
+    100 * SQ_THREAD_CYCLES_VALU / (64 * SQ_ACTIVE_INST_VALU)."""
+    import csv
+    acc = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "fftamd::" not in name:
+                continue
+            acc.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cols = ["SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU"]
+    print("| kernel | dispatches | LDS instructions | LDS-active clocks | bank-conflict clocks | conflict share | "
+          "VALU instructions | VALUBusy % | VALUUtilization % |", file=out)
+    print("|---|---|---|---|---|---|---|---|---|", file=out)
+    for name, cs in acc.items():
+        mean = {k: sum(v) / len(v) for k, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        cell = [f"{mean[c]:.4g}" if c in mean else "-" for c in cols]
+        share = (f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_LDS_IDX_ACTIVE']:.3f}"
+                 if mean.get("SQ_LDS_IDX_ACTIVE") else "-")
+        busy = (f"{100 * mean['SQ_ACTIVE_INST_VALU'] / NUM_CUS / (mean['GRBM_GUI_ACTIVE'] / XCDS):.1f}"
+                if mean.get("SQ_ACTIVE_INST_VALU") and mean.get("GRBM_GUI_ACTIVE") else "-")
+        util = (f"{100 * mean['SQ_THREAD_CYCLES_VALU'] / (64 * mean['SQ_ACTIVE_INST_VALU']):.1f}"
+                if mean.get("SQ_ACTIVE_INST_VALU") and "SQ_THREAD_CYCLES_VALU" in mean else "-")
+        short = name.replace("void ", "").split("(")[0]
+        print(f"| `{short}` | {n} | {cell[0]} | {cell[1]} | {cell[2]} | {share} | {cell[3]} | {busy} | {util} |",
+              file=out)
+
+
 def summarize_counters(fetch_csv, write_csv, out=sys.stdout, write_traffic=False):
     """HBM bytes per dispatch from two rocprofv3 --pmc runs of the bench
-    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, --selected-regions),
-    each scaled by what the same counter reads for the bench's 512 MiB
-    reference copy.  Prints a markdown table per kernel and the bytes of each
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the bench's 512 MiB reference copy.  Prints a markdown table per kernel and the bytes of each
     stored traffic record; with write_traffic, stores them in
     profiles/traffic.json under the current kernel-source hash."""
     import csv
@@ -582,6 +621,9 @@ def main():
     ap.add_argument("--summarize-counters", metavar=("FETCH_CSV", "WRITE_CSV"), nargs=2, default=None,
                     help="HBM bytes per kernel from two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, then WRITE_SIZE) of a bench run, calibrated on the reference copy")
+    ap.add_argument("--summarize-pmc", metavar="CSV", nargs="+", default=None,
+                    help="LDS and VALU activity per kernel from rocprofv3 --pmc counter_collection.csv files "
+                         "of a bench run (one counter group per file)")
     ap.add_argument("--write-traffic", action="store_true",
                     help="with --summarize-counters: store the records in profiles/traffic.json")
     ap.add_argument("--summarize-trace", metavar="CSV", default=None,
@@ -597,6 +639,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, write_traffic=args.write_traffic)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "

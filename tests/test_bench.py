@@ -145,3 +145,30 @@ def test_summarize_trace_keeps_the_timed_windows(tmp_path):
     bench.summarize_trace(str(p), str(w), out=buf)
     a = next(l for l in buf.getvalue().splitlines() if "`k_a`" in l).split("|")
     assert [x.strip() for x in a[2:7]] == ["2", "0.3", "0.2", "0.1", "0.3"]
+
+
+def test_summarize_pmc_merges_groups_and_derives_ratios(tmp_path):
+    """LDS/VALU summary: two counter groups merged by kernel, mean per
+    dispatch, conflict share, VALUBusy over per-XCD clocks, VALUUtilization."""
+    cols = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    k = "void fftamd::k_fs_cols<2048, -1, 16, false>(fftamd::FourStepArgs)"
+
+    def write(path, rows):
+        path.write_text("\n".join(",".join(f'"{x}"' for x in r) for r in [cols] + rows) + "\n")
+    lds, valu = tmp_path / "lds.csv", tmp_path / "valu.csv"
+    write(lds, [[k, "SQ_LDS_IDX_ACTIVE", 1000], [k, "SQ_LDS_BANK_CONFLICT", 250], [k, "SQ_INSTS_LDS", 10],
+                [k, "SQ_LDS_IDX_ACTIVE", 3000], [k, "SQ_LDS_BANK_CONFLICT", 750], [k, "SQ_INSTS_LDS", 30],
+                ["__amd_rocclr_copyBuffer", "SQ_INSTS_LDS", 5]])
+    # 256 CUs busy half of the per-XCD clocks; 48 of 64 lanes active
+    write(valu, [[k, "SQ_ACTIVE_INST_VALU", 256 * 500], [k, "GRBM_GUI_ACTIVE", 8 * 1000],
+                 [k, "SQ_THREAD_CYCLES_VALU", 48 * 256 * 500], [k, "SQ_INSTS_VALU", 77]])
+    import io
+    buf = io.StringIO()
+    bench.summarize_pmc([str(lds), str(valu)], out=buf)
+    lines = [l for l in buf.getvalue().splitlines() if l.startswith("| `")]
+    assert len(lines) == 1                                       # torch's and the copy's kernels left out
+    c = [x.strip() for x in lines[0].split("|")[1:-1]]
+    assert c[0] == "`fftamd::k_fs_cols<2048, -1, 16, false>`"
+    assert c[1] == "2"                                           # dispatches
+    assert c[2:6] == ["20", "2000", "500", "0.250"]              # means per dispatch and the share
+    assert c[6:9] == ["77", "50.0", "75.0"]
