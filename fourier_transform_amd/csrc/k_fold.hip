@@ -1,4 +1,4 @@
-// Tall 2D images in two passes over HBM.
+// 2D images of 4096, 8192 and 16384 rows in two passes over HBM.
 //
 // A 2D transform is the row transforms followed by the column transforms
 // (Mota, section 2.7, Equation 19).  Here the column transform of length
@@ -23,7 +23,8 @@
 // power of two; its writes keep the output's power-of-two row pitch.
 //
 // Against rows + two column steps this moves each element through HBM twice
-// instead of three times.
+// instead of three times; against rows + a 4096-point column pass (whose
+// tiles hold 8 columns: 64 B runs) it keeps 128 B runs on both sides.
 #include "kernels.hpp"
 
 namespace fftamd {
@@ -265,30 +266,49 @@ hipError_t run_fold(const FoldArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int NY, int S>
+hipError_t fold_ny(const FoldArgs& a, hipStream_t st) {
+  switch (a.nx) {
+    case 512:
+      return run_fold<NY, 512, S>(a, st);
+    case 1024:
+      return run_fold<NY, 1024, S>(a, st);
+    case 2048:
+      return run_fold<NY, 2048, S>(a, st);
+    case 4096:
+      return run_fold<NY, 4096, S>(a, st);
+    case 8192:
+      if constexpr (fold_fits(NY, 8192)) return run_fold<NY, 8192, S>(a, st);
+      break;
+    case 16384:
+      if constexpr (fold_fits(NY, 16384)) return run_fold<NY, 16384, S>(a, st);
+      break;
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int S>
 hipError_t fold_sign(const FoldArgs& a, hipStream_t st) {
-  if (a.ny == 8192) {
-    if (a.nx == 8192) return run_fold<8192, 8192, S>(a, st);
-    if (a.nx == 4096) return run_fold<8192, 4096, S>(a, st);
-    if (a.nx == 2048) return run_fold<8192, 2048, S>(a, st);
-  } else if (a.ny == 16384) {
-    if (a.nx == 4096) return run_fold<16384, 4096, S>(a, st);
-    if (a.nx == 2048) return run_fold<16384, 2048, S>(a, st);
-    if (a.nx == 1024) return run_fold<16384, 1024, S>(a, st);
-  }
+  if (a.ny == 4096) return fold_ny<4096, S>(a, st);
+  if (a.ny == 8192) return fold_ny<8192, S>(a, st);
+  if (a.ny == 16384) return fold_ny<16384, S>(a, st);
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-// The shapes with a pass-1 tile of at most 32768 points and pass-2 columns
-// of 2048.  On MI355X the two passes beat rows + two column steps on each of
-// them (8192 x 8192: 566 against 650 us; 16384 x 4096: 551 against 606 us;
-// 8192 x 4096: 295 against 303 us; 16384 x 2048: 285 against 297 us; 8192 x
-// 2048 and 16384 x 1024: 115-120 against 150 us).
-bool fold_supported(int64_t ny, int64_t nx) {
-  return (ny == 8192 && (nx == 8192 || nx == 4096 || nx == 2048)) ||
-         (ny == 16384 && (nx == 4096 || nx == 2048 || nx == 1024));
-}
+// The two passes against the other forms, per exec on MI355X (512 MiB per
+// exec where the image allows): against rows + two column steps (images of
+// 8192 rows and more) 8192 x 8192 566 against 650 us, 16384 x 4096 551
+// against 606, 8192 x 4096 295 against 303, 16384 x 2048 285 against 297,
+// 8192 x 2048 and 16384 x 1024 115-120 against 150, 8192 x 1024 390 against
+// 606, 8192 x 512 394 against 624, 16384 x 512 396 against 609; against rows
+// + the 4096-point column pass (8 columns per workgroup, 64 B runs) 4096 x
+// 4096 431 against 522, 4096 x 2048 405 against 511, 4096 x 1024 388 against
+// 526, 4096 x 512 404 against 503, 4096 x 8192 548 against 574, 4096 x 16384
+// 514 against 641.
+bool fold_supported(int64_t ny, int64_t nx) { return fold_fits(ny, nx); }
 
 hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t st) {
   return sign < 0 ? fold_sign<-1>(a, st) : fold_sign<1>(a, st);

@@ -207,9 +207,10 @@ struct fft_plan {
   const float2* tw_full = nullptr;  // real transforms, pair mode: stage table for n
   const float2* thi = nullptr;
   const float2* tlo = nullptr;
-  // tall 2D images: column steps A (length ny/64) and B (length 64), W_ny table;
-  // fold: the two-pass form instead (tw_ca: rows of nx for the fold kernel,
-  // tw_cb: columns of kFoldColLength)
+  // 2D images through a scratch (8192 rows and more, and the 4096-row images
+  // of the two-pass form): column steps A (length ny/64) and B (length 64),
+  // W_ny table; fold: the two-pass form instead (tw_ca: rows of nx for the
+  // fold kernel, tw_cb: the 2048-point columns)
   bool tall = false;
   bool fold = false;
   const float2* tw_ca = nullptr;
@@ -934,7 +935,10 @@ fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind, in
   std::vector<float2> ta, tb, tca, tcb, wt;
   append_stage_table((int)nx, rows_values((int)nx), ta);
   int rc;
-  if (ny >= kTallRows) {
+  // Images of 8192 rows and more, and the 4096-row images the two-pass form
+  // takes (faster than rows + the 4096-point column pass, whose tiles hold
+  // only 8 columns), go through a scratch; the others transform in place.
+  if (ny >= kTallRows || fold_supported(ny, nx)) {
     p->tall = true;
     p->fold = fold_supported(ny, nx);
     if (p->fold) {

@@ -88,6 +88,12 @@ constexpr int colstage_values(int n) { return sched_e(n); }       // k_col_stage
 // adjacent columns per workgroup (128 B runs), and the values per thread of
 // each pass (64 for 32K-point tiles: 512 threads of up to 256 VGPRs).
 constexpr int fold_na(int64_t ny, int64_t nx) { return (void)nx, (int)(ny / 2048); }
+// The two-pass form: ny in {4096, 8192, 16384} and nx a power of two from
+// 512 with a pass-1 tile (fold_na rows of nx) of at most 32768 points
+constexpr bool fold_fits(int64_t ny, int64_t nx) {
+  return (ny == 4096 || ny == 8192 || ny == 16384) && nx >= 512 && (nx & (nx - 1)) == 0 &&
+         fold_na(ny, nx) * nx <= 32768;
+}
 constexpr int fold_c(int nb) { return (void)nb, 16; }
 constexpr int fold_row_values(int nx, int na) { return nx * na >= 32768 ? 64 : 32; }
 constexpr int fold_col_values(int nb, int c) { return (void)nb, (void)c, 64; }

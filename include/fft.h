@@ -176,14 +176,15 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign);
  * (Mota, section 2.7, Equation 19).  ny, nx: powers of two in [2, 16384], or
  * any sizes in [2, 2^22] (then at most 65535 images; the shift options act
  * on each axis).
- * Only kind = FFT_C2C.  Images with ny >= 8192 rows own a scratch buffer and
- * take at most 65535 images.  For ny = 8192 with nx in {2048, 4096, 8192} and
- * ny = 16384 with nx in {1024, 2048, 4096} they take two passes over HBM:
- * na = ny/2048 rows per workgroup transformed along x with the first factor
- * of the column transform fused, then 2048-point column tiles (scratch of
- * batch*(ny/na)*(na*nx + 16)*8 bytes).  Other tall images run the column
- * transform as two steps of 64 x ny/64 points (three passes, scratch of
- * batch*ny*nx*8 bytes).  Returns NULL on error.
+ * Only kind = FFT_C2C.  For ny in {4096, 8192, 16384} and nx a power of two
+ * from 512 with (ny/2048)*nx <= 32768 the transform takes two passes over
+ * HBM: na = ny/2048 rows per workgroup transformed along x with the first
+ * factor of the column transform fused, then 2048-point column tiles
+ * (plan-owned scratch of batch*(ny/na)*(na*nx + 16)*8 bytes).  Other images
+ * of 8192 rows and more run the column transform as two steps of
+ * 64 x ny/64 points (three passes, scratch of batch*ny*nx*8 bytes); images
+ * of 8192 rows and more take at most 65535 images.  The rest transform in
+ * place on `out` without scratch.  Returns NULL on error.
  */
 fft_plan* fft_plan_create_2d(int64_t ny, int64_t nx, int64_t batch, int kind,
                              int sign);

@@ -79,7 +79,8 @@ def test_poison_c2c_shift_in_place(n, shift):
 # per thread, power-of-two columns of a non-power-of-two image (64 x 1000),
 # and the transposing form (1009 rows: a Rader length)
 @pytest.mark.parametrize("ny,nx,batch", [(256, 512, 2), (1024, 1024, 1), (8192, 2048, 1), (8192, 64, 1),
-                                         (100, 60, 2), (7776, 6, 1), (64, 1000, 1), (1009, 30, 1)])
+                                         (100, 60, 2), (7776, 6, 1), (64, 1000, 1), (1009, 30, 1),
+                                         (4096, 512, 1)])
 def test_poison_2d(ny, nx, batch):
     say(f"poison build: 2d {ny}x{nx} batch={batch}")
     x = W.normal_c64((batch, ny, nx), np.random.default_rng(ny + nx))

@@ -398,10 +398,12 @@ def test_2d_sweep(ny, nx, shift):
 
 
 @pytest.mark.parametrize("ny,nx,batch", [(8192, 8192, 1), (8192, 2048, 2), (16384, 1024, 2), (16384, 4096, 1),
-                                         (8192, 4096, 1), (16384, 2048, 1)])
+                                         (8192, 4096, 1), (16384, 2048, 1), (4096, 4096, 1), (4096, 1024, 2),
+                                         (4096, 512, 3), (4096, 16384, 1), (8192, 1024, 1), (8192, 512, 2),
+                                         (16384, 512, 1)])
 def test_2d_tall(ny, nx, batch):
-    """Tall images on the two-pass form (rows with the first column factor,
-    then columns of 2048).  Forward with the shift out of place, inverse in
+    """Images on the two-pass form (rows with the first column factor, then
+    columns of 2048): 4096, 8192 and 16384 rows, 512 to 16384 columns.  Forward with the shift out of place, inverse in
     place, against the oracle; the shift bit for bit against the
     chessboard-negated input."""
     say(f"2d two-pass {ny}x{nx} batch={batch}")
