@@ -226,7 +226,33 @@ __global__ __launch_bounds__(pq_threads(Q) * P * C) void k_c2c_pq(PqArgs a) {
   const int64_t row = (int64_t)blockIdx.x * C + c;
   const bool valid = row < a.rows;
   float2 v[E];
-  if (valid) {
+  if constexpr (P >= 7) {
+    // Line p reads elements P apart, so a wavefront's loads would touch P *
+    // 512 B.  Instead the group's C rows are loaded coalesced and put into
+    // the line layout through LDS (element j of row cc: line cc P + j % P,
+    // position j / P).  Per 512 MiB: 15360 801 -> 392 us, 12800 583 -> 434,
+    // 14336 541 -> 400, 9216 501 -> 443; 10240 (P = 5) equal, 12288 (P = 3)
+    // 403 -> 412, so those keep the direct loads.
+    static_assert((C * N) % NT == 0 && (C * N) / NT == E, "one value per slot");
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const uint32_t e = (uint32_t)tid + (uint32_t)NT * i;
+      const uint32_t cc = e / N, j = e - cc * N;
+      const int64_t r = (int64_t)blockIdx.x * C + cc;
+      float2 x = make_float2(0.f, 0.f);
+      if (r < a.rows) {
+        x = gload_nt(a.in + r * N, j);
+        if (a.shift && (j & 1)) x = negate_bits(x);  // (-1)^j
+      }
+      lds[L::at((int)(cc * P + j % P), (int)(j / P))] = x;
+    }
+    lds_barrier();
+    static_for<0, E>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      v[m] = lds[L::template at_k<T * m>(line, u)];
+    });
+    lds_barrier();  // stage 0 writes LDS again
+  } else if (valid) {
     const float2* src = a.in + row * N;
 #pragma unroll
     for (int m = 0; m < E; ++m) {

@@ -50,9 +50,11 @@ C2C_CASES = [
     (2, 3), (16, 5), (64, 7), (1024, 8), (4096, 33), (8192, 3), (16384, 2),
     # four-step
     (1 << 15, 3), (1 << 20, 2),
-    # mixed radix (one butterfly of <= 16, two of <= 8), Rader, p * 2^k, chirp (one kernel
-    # on a power of two, one on a mixed-radix length, three passes)
-    (1000, 9), (360, 11), (7776, 3), (1009, 5), (97, 13), (12288, 2), (1019, 4), (1034, 3), (10001, 2),
+    # mixed radix (one butterfly of <= 16, two of <= 8), Rader, p * 2^k (direct and
+    # staged loads), chirp (one kernel on a power of two, one on a mixed-radix length,
+    # three passes)
+    (1000, 9), (360, 11), (7776, 3), (1009, 5), (97, 13), (12288, 2), (15360, 3), (1019, 4), (1034, 3),
+    (10001, 2),
 ]
 
 
