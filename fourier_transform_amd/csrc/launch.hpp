@@ -261,7 +261,7 @@ hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, h
 // with zeros to m >= 2n - 1 and b = conj(c) wrapped around; the convolution
 // is inverse_FFT_m(forward_FFT_m(a) * bhat) with bhat = forward_FFT_m(b)/m.
 // Rows of n complex64 values, contiguous; in place allowed.
-constexpr int kMaxBluesteinLength = 8192;
+constexpr int kMaxBluesteinLength = 16384;  // m <= 32768: one workgroup per row
 // longer lengths run the same computation in three passes (the hooked
 // launch_fourstep_cols, launch_chirp_mid, launch_chirp_out), up to this length
 constexpr int64_t kMaxBluesteinLengthLarge = int64_t(1) << 22;

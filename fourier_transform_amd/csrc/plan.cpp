@@ -567,7 +567,7 @@ fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector
 
 // C2C of a length that is not a power of two, 2 <= n <= kMaxBluesteinLengthLarge.
 // The transforms of length m >= 2n - 1 run inside one kernel per row batch
-// while m <= kMaxSinglePass; above, in three passes over batch x m values
+// while m <= 2 * kMaxBluesteinLength; above, in three passes over batch x m values
 // through two plan-owned scratch buffers: the forward transform's column
 // pass with the chirp applied on load, one row pass for the forward row
 // factor, the product with bhat and the inverse row factor, and the inverse
@@ -607,8 +607,8 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   if (p->bmixed) {
     p->mx.rows = batch;
     fill_schedule(p->mx, m, msched, ta);
-  } else if (m <= kMaxSinglePass) {
-    append_stage_table((int)m, rows_values((int)m), ta);
+  } else if (m <= 2 * (int64_t)kMaxBluesteinLength) {  // one kernel (k_bluestein.hip)
+    append_stage_table((int)m, m > kMaxSinglePass ? kSplitValues : rows_values((int)m), ta);
   } else {
     const int L = ilog2c(m);
     p->fourstep = true;

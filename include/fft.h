@@ -26,7 +26,7 @@
  *    chirp transform: two transforms of length m >= 2n - 1 (a power of two,
  *    or a length with a mixed-radix schedule below 1/1.3 of that power of
  *    two when it is 4096 or more and n <= 4096), inside one kernel while
- *    m <= 16384, else in three passes (the second
+ *    m <= 32768 (n <= 16384), else in three passes (the second
  *    holds the inner factors of both transforms) through a scratch buffer of
  *    2 * batch * m * 8 bytes.
  *  - R2C/C2R lengths: powers of two from 4 to 32768 (one kernel), and any

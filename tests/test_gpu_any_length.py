@@ -180,14 +180,14 @@ def test_any_length_shift_option_and_sizes():
 
 
 # --------------------------------------------------------------------------
-# lengths above 8192: the chirp transform in three passes over m >= 2n - 1
-# points (the hooked four-step column pass, the fused row pass, the inverse
-# column pass)
+# lengths above 8192: the chirp transform over m >= 2n - 1 points, in one
+# kernel up to n = 16384 (m = 32768), above in three passes (the hooked
+# four-step column pass, the fused row pass, the inverse column pass)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("n", [8193, 10000, 12289, 20000])
+@pytest.mark.parametrize("n", [8193, 10000, 12289, 16383, 16385, 20000, 30001])
 @pytest.mark.parametrize("sign", [-1, 1])
 def test_any_length_large_full(n, sign):
-    say(f"any-length (four-step chirp) n={n} sign={sign}")
+    say(f"any-length (chirp, {'one kernel' if n <= 16384 else 'three passes'}) n={n} sign={sign}")
     x = W.uniform_c64((3, n), np.random.default_rng(n + 21))
     assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL
 
@@ -211,9 +211,9 @@ def test_any_length_large_sampled_bins(n):
     assert e <= 1e-5
 
 
-@pytest.mark.parametrize("n,shift", [(10001, 1), (10001, 2), (16000, 1)])
+@pytest.mark.parametrize("n,shift", [(10001, 1), (10001, 2), (16000, 1), (20011, 1), (20011, 2)])
 def test_any_length_large_shift_and_in_place(n, shift):
-    say(f"any-length (four-step chirp) shift={shift} n={n}, in place")
+    say(f"any-length (chirp) shift={shift} n={n}, in place")
     x = W.uniform_c64((2, n), np.random.default_rng(n + shift))
     idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
     want = oracle.dft(x, -1)[:, idx]

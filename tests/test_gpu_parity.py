@@ -488,10 +488,10 @@ def test_graph_capture_replays():
     every replay, with eager work in between, matches the eager result."""
     import torch
     say("graph capture: 1D n=4096, four-step 2^16 and 2^22 x 8, 2D 512x512 and 8192x8192, mixed radix 1000, "
-        "Rader 1009, chirp 1019 and 10001")
+        "Rader 1009, chirp 1019, 10001 (one kernel) and 20011 (three passes)")
     # 2^22 x 8 and 8192 x 8192 run the persistent passes with a staggered start
     cases = [(4096, 64, None), (1 << 16, 4, None), (1 << 22, 8, None), (512, 512, 2), (8192, 1, 8192),
-             (1000, 16, None), (1009, 8, None), (1019, 8, None), (10001, 2, None)]
+             (1000, 16, None), (1009, 8, None), (1019, 8, None), (10001, 2, None), (20011, 2, None)]
     for n, b, ny in cases:
         if ny is None:
             plan = F.fft_plan_create(n, b, F.FFT_C2C, F.FFT_FORWARD)
