@@ -486,7 +486,7 @@ bool mixed_schedule_ok(const MixedArgs& a, int* rmax_out) {
   int rmax = 0;
   for (int s = 0; s < a.nstages; ++s) {
     const int R = a.radix[s];
-    if (R < 2 || R > 16 || (R > 8 && a.kb != 1) || R == 9) return false;
+    if (R < 2 || R > 16 || R == 9) return false;
     if ((int64_t)a.tpl * a.kb < a.m[s]) return false;  // every butterfly has a thread
     rmax = R > rmax ? R : rmax;
   }
@@ -505,7 +505,14 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
       (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  if (rmax > 8) {
+  if (rmax > 8 && a.kb == 2) {
+    // lengths above 8192: two butterflies of up to 16 values per thread
+    if (a.pad) return hipErrorInvalidValue;
+    if (sign < 0)
+      FFTAMD_LAUNCH((k_mixed<-1, 2, 16, false>), dim3(grid), block, lds, st, a);
+    else
+      FFTAMD_LAUNCH((k_mixed<1, 2, 16, false>), dim3(grid), block, lds, st, a);
+  } else if (rmax > 8) {
     if (a.pad) {
       if (sign < 0)
         FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true>), dim3(grid), block, lds, st, a);
@@ -539,6 +546,7 @@ hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs&
   a.rows = 1;
   a.lines = 1;
   if (!mixed_schedule_ok(a, &rmax) || c.nx < 1 || c.images < 1 || !a.in || !a.out) return hipErrorInvalidValue;
+  if (rmax > 8 && a.kb != 1) return hipErrorInvalidValue;  // no column-tile kernel of this shape
   const int ct = mixed_cols_tile(a);
   if (ct == 0) return hipErrorInvalidValue;
   a.lines = ct;

@@ -156,24 +156,6 @@ struct FoldArgs {
 bool fold_supported(int64_t ny, int64_t nx);
 hipError_t launch_fold_2d(int sign, const FoldArgs& a, hipStream_t stream);
 
-// C2C rows of length n = p * q, p in {3, 5, 7, 9, 15, 25}, q a power of two,
-// kMinPqLength <= n <= kMaxPqLength (shorter lengths of this form take the
-// mixed-radix kernel): p power-of-two transforms of length q in registers
-// (interleaved sub-rows), the twiddle W_n^{p k} (wn: e^{-2 pi i e/n}, e < n),
-// and p-point DFTs through LDS.  shift: multiply element j by (-1)^j (n is
-// even).  In place allowed.
-constexpr int kMinPqLength = 8193;
-constexpr int kMaxPqLength = 16384;
-struct PqArgs {
-  const float2* in;
-  float2* out;
-  const float2* tw;  // stage table of q (row-kernel schedule)
-  const float2* wn;
-  int64_t rows;
-  int shift;
-};
-hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream);
-
 // C2C rows whose length n <= kMaxMixedLength has no prime factor above 13:
 // mixed-radix Stockham stages of radix 2, 3, 4, 5, 7 or 8 (schedule chosen at
 // plan time), the line resident in LDS between stages.  Stage s has radix
@@ -182,10 +164,11 @@ hipError_t launch_pq(int q, int p, int sign, const PqArgs& a, hipStream_t stream
 // ns_magic[s] = ceil(2^32 / ns[s]), so that b / ns = umulhi(b, ns_magic) for
 // b < 2^16.  pre: n factors applied on load (the shift ramps), or null.
 // Threads: tpl per line, lines per workgroup; each thread takes butterflies
-// t, t + tpl, ..., at most kb per stage (2 when every radix is at most 8,
-// kMixedButterflies; 1 when radices go up to 16: 2..8, 10..16),
-// so tpl * kb >= m[s] and every stage needs m[s] <= 1024 * kb.
-constexpr int kMaxMixedLength = 8192;
+// t, t + tpl, ..., at most kb per stage (kb = 2, kMixedButterflies, with
+// radices up to 8 for n <= 8192 and up to 16 above; kb = 1 with radices up
+// to 16: 2..8, 10..16), so tpl * kb >= m[s] and every stage needs
+// m[s] <= 1024 * kb.  One line of n <= 16384 complex values fits the LDS.
+constexpr int kMaxMixedLength = 16384;
 constexpr int kMixedMaxStages = 16;
 constexpr int kMixedButterflies = 2;
 struct MixedArgs {

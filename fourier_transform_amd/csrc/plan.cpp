@@ -36,6 +36,9 @@ constexpr int kFourStepMaxLog = 2 * ilog2c(kMaxSinglePass);  // 2^28
 // 2D images with at least this many rows split their column transform in two
 // steps (64 x ny/64), each with long runs (see ColStageArgs)
 constexpr int64_t kTallRows = 8192;
+// longest mixed-radix convolution the one-kernel chirp transform searches
+// (its measured gains were for n <= 4096, c <= 8192)
+constexpr int64_t kMaxChirpMixedLength = 8192;
 constexpr int kTallSplit = 64;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
@@ -230,9 +233,6 @@ struct fft_plan {
   // C2C lengths with no prime factor above 13 (mixed radix): the schedule, and
   // the load factors of the two shifts
   // C2C lengths p * q (p in {3, 5, 7, 9, 15, 25}, q a power of two >= 16)
-  bool pq = false;
-  int pq_p = 0, pq_q = 0;
-  const float2* wn = nullptr;
   bool mixed = false;
   bool rader = false;  // mx holds the schedule of n - 1
   MixedArgs mx{};
@@ -455,7 +455,7 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
   // first radix 16 (1280, 1536, 1792, 2560, 3072, 3584) 3-8 % faster with the
   // pad; first radix 8, 10, 12, 14 (48 ... 7168) equal or up to 7.6 % faster
   // without it (6400 383.7 -> 357.7 us, 7168 379.9 -> 351.2 us per 512 MiB).
-  a.pad = rad[0] == 16 ? 1 : 0;
+  a.pad = rad[0] == 16 && kb == 1 ? 1 : 0;
   a.tpl = (int)((maxm + a.kb - 1) / a.kb);
   // 256 threads per workgroup where a line has fewer.  Filling the last
   // wavefront with more lines per workgroup (n = 1000: 7 lines, 700 of 704
@@ -594,7 +594,7 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   if (m >= 4096) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     int64_t best_cost = INT64_MAX, best_c = 0;
-    for (int64_t c = 2 * n - 1; c <= kMaxMixedLength && 13 * c < 10 * m && 2 * c < best_cost; ++c) {
+    for (int64_t c = 2 * n - 1; c <= kMaxChirpMixedLength && 13 * c < 10 * m && 2 * c < best_cost; ++c) {
       const std::vector<int> w = mixed_radices(c, wide, (int)((c + 1023) / 1024));
       if (w.empty() || (int)w.size() > kMixedMaxStages) continue;
       if (c * (int64_t)w.size() < best_cost) best_cost = c * (int64_t)w.size(), best_c = c, msched = w;
@@ -667,74 +667,54 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   return p;
 }
 
-// n = p * q with p in {3, 5, 7, 9, 15, 25} and q a power of two, kMinPqLength
-// <= n <= kMaxPqLength: the odd factor p, else 0
-int pq_factor(int64_t n) {
-  if (n < kMinPqLength || n > kMaxPqLength) return 0;
-  for (int p : {25, 15, 9, 7, 5, 3})
-    if (n % p == 0 && is_pow2(n / p)) return p;
-  return 0;
-}
-
-fft_plan* create_pq(int64_t n, int64_t batch, int sign, int pf) {
-  fft_plan* p = new (std::nothrow) fft_plan();
-  if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
-  p->n = n;
-  p->nx = n;
-  p->batch = batch;
-  p->kind = FFT_C2C;
-  p->sign = sign;
-  p->pq = true;
-  p->pq_p = pf;
-  p->pq_q = (int)(n / pf);
-  std::vector<float2> ta, wn;
-  append_stage_table(p->pq_q, pq_values(p->pq_q), ta);
-  for (int64_t e = 0; e < n; ++e) wn.push_back(root(e, n));
-  if (finish_plan(p, {&ta, &wn}, {&p->tw_a, &p->wn}, 0) != FFT_OK) {
-    free_plan(p);
-    return nullptr;
-  }
-  ok();
-  return p;
-}
-
-// any-length C2C plan: mixed radix when possible, then p * 2^k in registers,
+// any-length C2C plan: mixed radix when possible, then Rader for primes,
 // else the chirp transform
 fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
-  // Up to 8192 points the mixed-radix kernel, above that p * 2^k in
-  // registers (with each mixed-radix stage compiled for its radix it beat
-  // the p * 2^k kernel on most lengths it shares, e.g. 3072: 216 against
-  // 310 us, 6144: 266 against 312 us; 384 and 768 were 5 % slower), else the
-  // chirp transform.  Mixed-radix schedules, in order:
+  // The mixed-radix kernel up to 16384 points, else Rader (primes), else the
+  // chirp transform.  (An earlier p * 2^k kernel for n = p * 2^k, p in {3,
+  // 5, 7, 9, 15, 25}, lost to mixed radix on every length it took: 3072 216
+  // against 310 us, 6144 266 against 312, 15360 372 against 392 per 512 MiB.)
+  // Mixed-radix schedules, in order:
   //  1. radices up to 16, one butterfly per thread (1000: 10 10 10, three
   //     stages).  Measured against the fixed order of step 2 on MI355X with
   //     each stage compiled for its radix: better or equal for 1000, 2000,
   //     2500 (253 against 330 us per 512 MiB), 3000, 3500, 4500, 6000, 8000,
   //     worse for 4000 and 5000 (325 against 291, 289 against 280 us);
-  //  2. radices up to 8 in a fixed order, two butterflies per thread;
-  //  3. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
-  //  4. the chirp transform.
+  //  2. above 8192 points, radices up to 16 with two butterflies per thread;
+  //  3. radices up to 8 in a fixed order, two butterflies per thread;
+  //  4. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
+  //  5. Rader's algorithm, then the chirp transform.
   if (n <= kMaxMixedLength) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
     const std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
     if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_mixed(n, batch, sign, w, 1);
     const int rlo2 = (int)((n + 2 * 1024 - 1) / (2 * 1024));
+    // above 8192 points: two butterflies of up to 16 values per thread (one
+    // would need every radix >= n/1024).  Per 512 MiB against the chirp
+    // transform: 10000 1331 -> 313 us, 9000 1440 -> 408, 12000 1133 -> 401,
+    // 16000 954 -> 416; against the p * 2^k kernel it replaced: 9216 444 ->
+    // 414, 10240 445 -> 429, 12288 404 -> 399, 12800 433 -> 394, 14336 399 ->
+    // 370, 15360 392 -> 372
+    if (n > 8192) {
+      const std::vector<int> w2 = mixed_radices(n, wide, rlo2);
+      if (!w2.empty() && (int)w2.size() <= kMixedMaxStages)
+        return create_mixed(n, batch, sign, w2, kMixedButterflies);
+    }
     for (const std::vector<int>& r : {mixed_radices_fixed(n), mixed_radices(n, narrow, rlo2)}) {
       if (r.empty() || (int)r.size() > kMixedMaxStages) continue;
       if (n / *std::min_element(r.begin(), r.end()) <= 1024 * kMixedButterflies)
         return create_mixed(n, batch, sign, r, kMixedButterflies);
     }
   }
-  // primes up to 8193 whose p - 1 has a schedule: Rader's convolution of
-  // length p - 1 in one kernel (1009: two 1008-point transforms instead of
-  // the chirp transform's two of 2048)
+  // primes up to 16385 whose p - 1 has a one-butterfly schedule: Rader's
+  // convolution of length p - 1 in one kernel (1009: two 1008-point
+  // transforms instead of the chirp transform's two of 2048)
   if (n <= kMaxMixedLength + 1 && is_prime(n)) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     const std::vector<int> w = mixed_radices(n - 1, wide, (int)((n - 1 + 1023) / 1024));
     if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_rader(n, batch, sign, w);
   }
-  if (const int pf = pq_factor(n)) return create_pq(n, batch, sign, pf);
   return create_bluestein(n, batch, sign);
 }
 
@@ -781,9 +761,9 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
   if (kind == FFT_C2C && n > 1 && !is_pow2(n)) {
     if (n > kMaxBluesteinLengthLarge)
       return set_err(FFT_ENOTSUP, "C2C lengths that are not powers of two must be <= 2^22"), nullptr;
-    // p * 2^k in registers, else mixed radix when every prime factor is at
-    // most 13 and every stage has at most 1024 butterflies per thread slot,
-    // else the chirp transform
+    // mixed radix when every prime factor is at most 13 and every stage has
+    // at most 1024 butterflies per thread slot, Rader for primes, else the
+    // chirp transform
     return create_c2c_any(n, batch, sign);
   }
   if (kind != FFT_C2C && n > 2 && !is_pow2(n)) {
@@ -1097,10 +1077,7 @@ int run_plan(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float
     if (e != hipSuccess) return hip_err(e, "kernel launch");
     return FFT_OK;
   }
-  if (p->pq) {
-    PqArgs a{src, dst, p->tw_a, p->wn, p->batch, p->shift ? 1 : 0};
-    e = launch_pq(p->pq_q, p->pq_p, p->sign, a, stream);
-  } else if (p->mixed) {
+  if (p->mixed) {
     MixedArgs a = p->mx;
     a.in = src;
     a.out = dst;

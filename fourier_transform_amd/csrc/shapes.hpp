@@ -39,10 +39,6 @@ constexpr int rows_values(int n) { return n >= kRowsWideMin ? 32 : sched_e(n); }
 constexpr bool rows_split(int n) { return n >= kRowsWideMin; }
 constexpr int rows_threads(int n) { return n / rows_values(n); }
 constexpr int rows_lines(int n) { return rows_threads(n) >= 256 ? 1 : 256 / rows_threads(n); }
-// The power-of-two part of the p * 2^k kernel (k_pq.hip): 16 values per
-// thread and the complex exchange at every length it takes (q <= 4096)
-constexpr int pq_values(int q) { return sched_e(q); }
-constexpr int pq_threads(int q) { return q / pq_values(q); }
 // Workgroups whose lines are read with a stride (column lanes) or stored
 // transposed (row lanes + transposing store) hold up to 16 adjacent lines, so
 // every strided access is a run of 16 x 8 B = 128 B.  When 16 values per

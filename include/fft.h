@@ -16,13 +16,12 @@
  *  - C2C lengths: powers of two (single pass up to 16384, four-step up to
  *    2^28), and any other length from 3 to 2^22 (the GLSL dissertation,
  *    section 2.3, names mixed radices and other lengths as the extension of
- *    its radix-2 transforms): lengths with no prime factor above 13 by
- *    mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every stage
- *    has at most 2048 butterflies (n <= 8192); primes p <= 8193 whose p - 1
- *    has such a schedule by Rader's algorithm (a cyclic convolution of length
- *    p - 1 on those stages, in one kernel); n = p * 2^k (p in 3, 5, 7, 9,
- *    15, 25, 8192 < n <= 16384) in one register-resident kernel (p
- *    power-of-two transforms, twiddles, p-point DFTs); the others by Bluestein's
+ *    its radix-2 transforms): lengths up to 16384 with no prime factor above
+ *    13 by mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every
+ *    stage has at most 2048 butterflies (one or two per thread); primes
+ *    p <= 16385 whose p - 1 has a one-butterfly schedule by Rader's algorithm
+ *    (a cyclic convolution of length p - 1 on those stages, in one kernel);
+ *    the others by Bluestein's
  *    chirp transform: two transforms of length m >= 2n - 1 (a power of two,
  *    or a length with a mixed-radix schedule below 1/1.3 of that power of
  *    two when it is 4096 or more and n <= 4096), inside one kernel while

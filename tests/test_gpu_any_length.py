@@ -1,10 +1,10 @@
 """GPU parity for C2C lengths that are not powers of two, against the
 oracle's DFT by the definition: mixed-radix Stockham stages (radices 2..8,
-10..16) for the lengths with no prime factor above 13, Rader's convolution of
-length p - 1 on those stages for primes p whose p - 1 has a schedule, p x 2^k
-(p in 3, 5, 7, 9, 15, 25) in registers above 8192, Bluestein's chirp
-transform for the rest (on a mixed-radix convolution length where that is
-much shorter than the power of two).
+10..16) for the lengths up to 16384 with no prime factor above 13 and a
+schedule, Rader's convolution of length p - 1 on those stages for primes p
+whose p - 1 has a schedule, Bluestein's chirp transform for the rest (on a
+mixed-radix convolution length where that is much shorter than the power of
+two).
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -318,18 +318,19 @@ def test_beyond_2p31_elements(n, batch):
 
 
 # --------------------------------------------------------------------------
-# p x 2^k (p in 3, 5, 7, 9, 15, 25): above 8192 points in one
-# register-resident kernel, up to 8192 in the mixed-radix kernel
+# p x 2^k (p in 3, 5, 7, 9, 15, 25) and other smooth lengths above 8192: the
+# mixed-radix kernel, with two butterflies of up to 16 values per thread above
+# 8192 points (15625 = 5^6 has no such schedule: the chirp transform)
 # --------------------------------------------------------------------------
 PQ_N = [48, 80, 240, 400, 576, 960, 1792, 2304, 2560, 3840, 4608, 6400, 9216, 10240, 12288, 12800,
-        14336, 15360]
+        14336, 15360, 9000, 10000, 12000, 16000, 15625]
 
 
 @pytest.mark.parametrize("n", PQ_N)
 @pytest.mark.parametrize("sign", [-1, 1])
-def test_pq_sweep(n, sign):
+def test_smooth_length_sweep(n, sign):
     for batch in (1, 7):
-        say(f"p x 2^k c2c n={n} batch={batch} sign={sign}")
+        say(f"smooth length c2c n={n} batch={batch} sign={sign}")
         x = W.uniform_c64((batch, n), np.random.default_rng(n * 3 + batch))
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
 
@@ -337,8 +338,9 @@ def test_pq_sweep(n, sign):
 @pytest.mark.parametrize("n", [6, 48, 1000, 1536, 2002, 15360])
 def test_even_shift_bit_exact_and_in_place(n):
     """The shift is the exact sign flip of (-1)^j (n even): bitwise the
-    transform of the negated input; and the rotation of the oracle's.  Up to
-    2002 the mixed-radix kernel, 15360 the p x 2^k kernel."""
+    transform of the negated input; and the rotation of the oracle's.  The
+    mixed-radix kernel, 15360 with two butterflies of up to 16 values per
+    thread."""
     from gpu_helpers import negate_odd
     x = W.uniform_c64((3, n), np.random.default_rng(n + 9))
     ys = c2c(x, -1, shift=1)

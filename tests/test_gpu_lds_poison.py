@@ -50,11 +50,11 @@ C2C_CASES = [
     (2, 3), (16, 5), (64, 7), (1024, 8), (4096, 33), (8192, 3), (16384, 2),
     # four-step
     (1 << 15, 3), (1 << 20, 2),
-    # mixed radix (one butterfly of <= 16, two of <= 8), Rader, p * 2^k (direct and
-    # staged loads), chirp (one kernel on a power of two up to 16384 and at 32768, one
-    # on a mixed-radix length, three passes)
-    (1000, 9), (360, 11), (7776, 3), (1009, 5), (97, 13), (12288, 2), (15360, 3), (1019, 4), (10001, 2),
-    (1034, 3), (20011, 2),
+    # mixed radix (one butterfly of <= 16, two of <= 8, two of <= 16 above 8192), Rader,
+    # chirp (one kernel on a power of two up to 16384 and at 32768, one on a mixed-radix
+    # length, three passes)
+    (1000, 9), (360, 11), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (97, 13), (1019, 4),
+    (10001, 2), (1034, 3), (20011, 2),
 ]
 
 

@@ -663,8 +663,8 @@ def test_lane_swap_exchange_lines(sign):
     """Lines of 64 and 32 threads whose second exchange is a lane swap
     (v_permlane32_swap / v_permlane16_swap instead of LDS): 512- and
     1024-point rows, the 2D row pass on 1024-point rows with the shift, real
-    transforms with 512- and 1024-point halves, the chirp transform on a
-    1024-point convolution and p * 2^k with 512- and 1024-point parts."""
+    transforms with 512- and 1024-point halves and the chirp transform on a
+    1024-point convolution."""
     g = np.random.default_rng(500 + sign)
     for n in (512, 1024):
         for batch in (1, 2, 5, 64):
@@ -675,7 +675,7 @@ def test_lane_swap_exchange_lines(sign):
     say("lane swap: 2d 64x1024 shift")
     y = c2c_2d(x, sign, shift=1)
     assert rel_l2(y, oracle.fftshift_2d(oracle.c2c_2d(x, sign))) <= TOL
-    for n in (500, 12800, 15360):          # chirp on m = 1024; 25 x 512; 15 x 1024
+    for n in (500,):                       # chirp on m = 1024
         say(f"lane swap: c2c n={n} sign={sign}")
         x = W.uniform_c64((3, n), g)
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, n
