@@ -338,7 +338,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
 // product with conv (A_0 = sum of x_j, j >= 1, kept aside), the inverse
 // N-point transform, then X_0 = x_0 + A_0 and X_j = x_0 + c_(ind j), stored
 // coalesced.  The pre factors (the shift of odd lengths) apply on load.
-template <bool PAD>
+template <int KB, int RMAX, bool PAD>
 __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -367,14 +367,14 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
     }
   }
   lds_barrier();
-  mixed_stages<-1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<-1, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
   for (uint32_t k = t; k < N; k += tpl) {
     const float2 A = L[mixed_pad<PAD>(k)];
     if (k == 0) x0s[1] = A;
     L[mixed_pad<PAD>(k)] = cmul(A, gload(rd.conv, k));
   }
   lds_barrier();
-  mixed_stages<1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<1, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
   if (valid) {
     const float2 x0 = x0s[0];
     for (uint32_t j = t; j < p; j += tpl) {
@@ -586,7 +586,7 @@ hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs&
 
 hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st) {
   int rmax = 0;
-  if (!mixed_schedule_ok(a, &rmax) || a.kb != 1 || rd.p != a.n + 1 || !rd.conv || !rd.perm)
+  if (!mixed_schedule_ok(a, &rmax) || rd.p != a.n + 1 || !rd.conv || !rd.perm || (a.kb == 2 && a.pad))
     return hipErrorInvalidValue;
   uint32_t grid;
   hipError_t e = grid_of(a.rows, a.lines, &grid);
@@ -594,10 +594,12 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
   const size_t lds = (size_t)a.lines * rader_line((uint32_t)a.n, a.pad != 0) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  if (a.pad)
-    FFTAMD_LAUNCH((k_rader<true>), dim3(grid), block, lds, st, a, rd);
+  if (a.kb == 2)  // p - 1 above 8192: two butterflies of up to 16 values per thread
+    FFTAMD_LAUNCH((k_rader<2, 16, false>), dim3(grid), block, lds, st, a, rd);
+  else if (a.pad)
+    FFTAMD_LAUNCH((k_rader<1, 16, true>), dim3(grid), block, lds, st, a, rd);
   else
-    FFTAMD_LAUNCH((k_rader<false>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<1, 16, false>), dim3(grid), block, lds, st, a, rd);
   return hipGetLastError();
 }
 

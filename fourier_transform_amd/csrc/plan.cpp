@@ -485,7 +485,7 @@ fft_plan* create_mixed(int64_t n, int64_t batch, int sign, const std::vector<int
 // its stage twiddles appended to tw; lines per workgroup and padding as for
 // the mixed-radix plans.  Used by the transforms whose N-point stages run on
 // a line in LDS (Rader, Bluestein on a mixed-radix length).
-void fill_schedule(MixedArgs& a, int64_t N, const std::vector<int>& rad, std::vector<float2>& tw) {
+void fill_schedule(MixedArgs& a, int64_t N, const std::vector<int>& rad, std::vector<float2>& tw, int kb = 1) {
   a.n = (int)N;
   a.nstages = (int)rad.size();
   int64_t ns = 1, maxm = 0;
@@ -503,18 +503,18 @@ void fill_schedule(MixedArgs& a, int64_t N, const std::vector<int>& rad, std::ve
     ns *= R;
   }
   if (tw.empty()) tw.push_back(make_float2(1.f, 0.f));
-  a.kb = 1;
-  a.pad = rad[0] == 16 ? 1 : 0;
-  a.tpl = (int)maxm;
+  a.kb = kb;
+  a.pad = rad[0] == 16 && kb == 1 ? 1 : 0;
+  a.tpl = (int)((maxm + kb - 1) / kb);
   a.lines = a.tpl >= 256 ? 1 : 256 / a.tpl;
 }
 
 // C2C of a prime length p by Rader's algorithm: a cyclic convolution of
-// length N = p - 1 on the mixed-radix schedule rad of N (one butterfly per
+// length N = p - 1 on the mixed-radix schedule rad of N (kb butterflies per
 // thread, radices up to 16).  Tables: the stage twiddles of N, conv (the f64
 // transform of b_m = e^{sign 2 pi i g^m/p}, divided by N), the index pairs
 // of each j, and the shift ramps.
-fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector<int>& rad) {
+fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector<int>& rad, int kb = 1) {
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
   const int64_t n = p_len, N = n - 1;
@@ -527,7 +527,7 @@ fft_plan* create_rader(int64_t p_len, int64_t batch, int sign, const std::vector
   MixedArgs& a = p->mx;
   a.rows = batch;
   std::vector<float2> tw, conv, perm, sh, ish;
-  fill_schedule(a, N, rad, tw);
+  fill_schedule(a, N, rad, tw, kb);
   // generator powers and discrete logarithms
   const int64_t g = primitive_root(n);
   std::vector<int64_t> ind(n, 0);
@@ -707,13 +707,18 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
         return create_mixed(n, batch, sign, r, kMixedButterflies);
     }
   }
-  // primes up to 16385 whose p - 1 has a one-butterfly schedule: Rader's
-  // convolution of length p - 1 in one kernel (1009: two 1008-point
-  // transforms instead of the chirp transform's two of 2048)
+  // primes up to 16385 whose p - 1 has a schedule: Rader's convolution of
+  // length p - 1 in one kernel (1009: two 1008-point transforms instead of
+  // the chirp transform's two of 2048)
   if (n <= kMaxMixedLength + 1 && is_prime(n)) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     const std::vector<int> w = mixed_radices(n - 1, wide, (int)((n - 1 + 1023) / 1024));
     if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_rader(n, batch, sign, w);
+    if (n - 1 > 8192) {  // two butterflies per thread, as for the mixed-radix lengths above 8192
+      const std::vector<int> w2 = mixed_radices(n - 1, wide, (int)((n - 1 + 2047) / 2048));
+      if (!w2.empty() && (int)w2.size() <= kMixedMaxStages)
+        return create_rader(n, batch, sign, w2, kMixedButterflies);
+    }
   }
   return create_bluestein(n, batch, sign);
 }

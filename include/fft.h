@@ -19,8 +19,8 @@
  *    its radix-2 transforms): lengths up to 16384 with no prime factor above
  *    13 by mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every
  *    stage has at most 2048 butterflies (one or two per thread); primes
- *    p <= 16385 whose p - 1 has a one-butterfly schedule by Rader's algorithm
- *    (a cyclic convolution of length p - 1 on those stages, in one kernel);
+ *    p <= 16385 whose p - 1 has such a schedule by Rader's algorithm (a
+ *    cyclic convolution of length p - 1 on those stages, in one kernel);
  *    the others by Bluestein's
  *    chirp transform: two transforms of length m >= 2n - 1 (a power of two,
  *    or a length with a mixed-radix schedule below 1/1.3 of that power of

@@ -2,7 +2,7 @@
 oracle's DFT by the definition: mixed-radix Stockham stages (radices 2..8,
 10..16) for the lengths up to 16384 with no prime factor above 13 and a
 schedule, Rader's convolution of length p - 1 on those stages for primes p
-whose p - 1 has a schedule, Bluestein's chirp transform for the rest (on a
+up to 16385 whose p - 1 has a schedule, Bluestein's chirp transform for the rest (on a
 mixed-radix convolution length where that is much shorter than the power of
 two).
 
@@ -68,6 +68,30 @@ def test_primes(n, sign):
         say(f"prime c2c n={n} batch={batch} sign={sign}")
         x = W.uniform_c64((batch, n), np.random.default_rng(n * 13 + batch))
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+# primes above 8193 by Rader's algorithm with two butterflies of up to 16
+# values per thread (p - 1 above 8192): 8233: 14 14 7 6; 9001: 15 15 8 5;
+# 12289: 16 16 8 6; 15361: 16 15 8 8; 14401: 15 15 8 8
+RADER_WIDE = [8233, 9001, 12289, 14401, 15361]
+
+
+@pytest.mark.parametrize("n", RADER_WIDE)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_primes_two_butterflies(n, sign):
+    for batch in (1, 3):
+        say(f"prime c2c (Rader, two butterflies) n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 19 + batch))
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n,shift", [(9001, 1), (12289, 2)])
+def test_primes_two_butterflies_shift_in_place(n, shift):
+    say(f"prime c2c (Rader, two butterflies) shift={shift} n={n}, in place")
+    x = W.uniform_c64((2, n), np.random.default_rng(n + shift + 3))
+    idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
+    want = oracle.dft(x, 1)[:, idx]
+    assert rel_l2(c2c(x, 1, shift=shift, inplace=True), want) <= TOL
 
 
 # the chirp transform on a convolution length with a mixed-radix schedule
@@ -180,11 +204,13 @@ def test_any_length_shift_option_and_sizes():
 
 
 # --------------------------------------------------------------------------
-# lengths above 8192: the chirp transform over m >= 2n - 1 points, in one
-# kernel up to n = 16384 (m = 32768), above in three passes (the hooked
-# four-step column pass, the fused row pass, the inverse column pass)
+# lengths above 8192 with a prime factor above 13: the chirp transform over
+# m >= 2n - 1 points, in one kernel up to n = 16384 (m = 32768), above in
+# three passes (the hooked four-step column pass, the fused row pass, the
+# inverse column pass).  10007 and 12281 are primes whose p - 1 has no
+# schedule.
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("n", [8193, 10000, 12289, 16383, 16385, 20000, 30001])
+@pytest.mark.parametrize("n", [8193, 10007, 12281, 16383, 16385, 20000, 30001])
 @pytest.mark.parametrize("sign", [-1, 1])
 def test_any_length_large_full(n, sign):
     say(f"any-length (chirp, {'one kernel' if n <= 16384 else 'three passes'}) n={n} sign={sign}")

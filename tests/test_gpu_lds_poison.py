@@ -53,7 +53,7 @@ C2C_CASES = [
     # mixed radix (one butterfly of <= 16, two of <= 8, two of <= 16 above 8192), Rader,
     # chirp (one kernel on a power of two up to 16384 and at 32768, one on a mixed-radix
     # length, three passes)
-    (1000, 9), (360, 11), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (97, 13), (1019, 4),
+    (1000, 9), (360, 11), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (1019, 4),
     (10001, 2), (1034, 3), (20011, 2),
 ]
 
