@@ -9,10 +9,13 @@
 // and writes output q to (b - j) R + j + q ns.
 //
 // One kernel handles every such length: the schedule is plan data, each
-// thread holds up to 2 butterflies of at most 8 values in registers, and the line lives in LDS between stages (read, barrier,
-// compute, write, barrier).  The first stage reads HBM directly and the last
-// one writes it, both coalesced (consecutive butterflies, consecutive
-// addresses).
+// thread holds one butterfly of up to 16 values or two of up to 8 (above 8192
+// points two of up to 16) in registers, and the line lives in LDS between
+// stages (read, barrier, compute, write, barrier).  The first stage reads HBM
+// directly and the last one writes it (consecutive butterflies, consecutive
+// addresses); lines of fewer than 128 threads, whose butterflies would read
+// runs of a few elements, move the workgroup's block of rows through LDS in
+// order instead.
 #include "kernels.hpp"
 
 namespace fftamd {
@@ -315,8 +318,9 @@ __device__ __forceinline__ void mixed_stages(const MixedArgs& a, uint32_t t, uin
 }
 
 // KB butterflies of at most RMAX values per thread and stage (2 x 8 or
-// 1 x 16), up to 1024 threads (so at most 128 VGPRs).
-template <int S, int KB, int RMAX, bool PAD>
+// 1 x 16), up to 1024 threads (so at most 128 VGPRs).  STG: HBM accessed
+// through the LDS lines in the block's order (lines of few threads).
+template <int S, int KB, int RMAX, bool PAD, bool STG>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -328,8 +332,46 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   const int64_t row = (int64_t)blockIdx.x * a.lines + line;
   const bool valid = row < a.rows;
   const uint32_t n = (uint32_t)a.n;
-  float2* L = smem + (size_t)line * (mixed_pad<PAD>(n) + 1);
-  mixed_stages<S, KB, RMAX, PAD, 0>(a, t, tpl, valid, a.in + row * n, a.out + row * n, L);
+  const uint32_t lp = mixed_pad<PAD>(n) + 1;
+  float2* L = smem + (size_t)line * lp;
+  if constexpr (STG) {
+    // short lines: the workgroup's rows (one contiguous block) are read and
+    // written in order through the lines in LDS; the shift factors apply as
+    // the values enter LDS, and the stages run with IO = 3 (line in, line out)
+    const int64_t row0 = (int64_t)blockIdx.x * a.lines;
+    const int64_t left = a.rows - row0;
+    const uint32_t nblk = (uint32_t)(left < a.lines ? left : a.lines) * n;
+    const uint32_t NT = tpl * (uint32_t)a.lines;
+    const uint32_t magic = 0xffffffffu / n + 1u;  // e / n for e < 2^32 / n
+    const float2* src = a.in + row0 * n;
+    constexpr int U = 8;
+    for (uint32_t e0 = (uint32_t)tid; e0 < nblk; e0 += U * NT) {
+      float2 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (e0 + k * NT < nblk) v[k] = gload_nt(src, e0 + k * NT);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const uint32_t e = e0 + k * NT;
+        if (e < nblk) {
+          const uint32_t q = __umulhi(e, magic), j = e - q * n;
+          float2 x = v[k];
+          if (a.pre) x = cmul(x, gload(a.pre, j));
+          if (a.flip && (j & 1)) x = negate_bits(x);
+          smem[q * lp + mixed_pad<PAD>(j)] = x;
+        }
+      }
+    }
+    lds_barrier();
+    mixed_stages<S, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+    float2* dst = a.out + row0 * n;
+    for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
+      const uint32_t q = __umulhi(e, magic), j = e - q * n;
+      gstore_nt(dst, e, smem[q * lp + mixed_pad<PAD>(j)]);
+    }
+  } else {
+    mixed_stages<S, KB, RMAX, PAD, 0>(a, t, tpl, valid, a.in + row * n, a.out + row * n, L);
+  }
 }
 
 // Rader's transform of a prime length p (see launch.hpp), one line of
@@ -338,7 +380,7 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
 // product with conv (A_0 = sum of x_j, j >= 1, kept aside), the inverse
 // N-point transform, then X_0 = x_0 + A_0 and X_j = x_0 + c_(ind j), stored
 // coalesced.  The pre factors (the shift of odd lengths) apply on load.
-template <int KB, int RMAX, bool PAD>
+template <int KB, int RMAX, bool PAD, bool STG>
 __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -353,9 +395,35 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   const uint32_t lp = rader_line(N, PAD);
   float2* L = smem + (size_t)line * lp;
   float2* x0s = L + (lp - 2);  // x_0, then A_0
-  const float2* src = a.in + row * (int64_t)p;
-  float2* dst = a.out + row * (int64_t)p;
-  if (valid) {
+  // STG (lines of few threads): the workgroup's rows, one contiguous block,
+  // read and written in order; element e is x_j of line e / p
+  const int64_t row0 = (int64_t)blockIdx.x * a.lines;
+  const int64_t left = a.rows - row0;
+  const uint32_t nblk = (uint32_t)(left < a.lines ? left : a.lines) * p;
+  const uint32_t NT = tpl * (uint32_t)a.lines;
+  const uint32_t magic = 0xffffffffu / p + 1u;  // e / p for e < 2^32 / p
+  if constexpr (STG) {
+    const float2* src = a.in + row0 * p;
+    constexpr int U = 8;
+    for (uint32_t e0 = (uint32_t)tid; e0 < nblk; e0 += U * NT) {
+      float2 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (e0 + k * NT < nblk) v[k] = gload_nt(src, e0 + k * NT);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const uint32_t e = e0 + k * NT;
+        if (e < nblk) {
+          const uint32_t q = __umulhi(e, magic), j = e - q * p;
+          float2 x = v[k];
+          if (a.pre) x = cmul(x, gload(a.pre, j));
+          float2* Lq = smem + (size_t)q * lp;
+          Lq[j == 0 ? lp - 2 : mixed_pad<PAD>((uint32_t)rd.perm[j].x)] = x;
+        }
+      }
+    }
+  } else if (valid) {
+    const float2* src = a.in + row * (int64_t)p;
     for (uint32_t j = t; j < p; j += tpl) {
       float2 v = gload_nt(src, j);
       if (a.pre) v = cmul(v, gload(a.pre, j));
@@ -375,7 +443,17 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   }
   lds_barrier();
   mixed_stages<1, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
-  if (valid) {
+  if constexpr (STG) {
+    float2* dst = a.out + row0 * p;
+    for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
+      const uint32_t q = __umulhi(e, magic), j = e - q * p;
+      const float2* Lq = smem + (size_t)q * lp;
+      const float2 x0 = Lq[lp - 2];
+      const float2 c = Lq[j == 0 ? lp - 1 : mixed_pad<PAD>((uint32_t)rd.perm[j].y)];
+      gstore_nt(dst, e, make_float2(x0.x + c.x, x0.y + c.y));
+    }
+  } else if (valid) {
+    float2* dst = a.out + row * (int64_t)p;
     const float2 x0 = x0s[0];
     for (uint32_t j = t; j < p; j += tpl) {
       const float2 c = j == 0 ? x0s[1] : L[mixed_pad<PAD>((uint32_t)rd.perm[j].y)];
@@ -387,8 +465,8 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
 // Bluestein's chirp transform on a convolution length m with a mixed-radix
 // schedule: the row times pre, zero beyond n, as a line of m values in LDS;
 // the forward m-point stages; the product with bhat; the inverse stages; the
-// outputs j < n times post.
-template <bool PAD>
+// outputs j < n times post.  STG: the rows read and written as one block.
+template <bool PAD, bool STG>
 __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixedArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -400,21 +478,56 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
   const int64_t row = (int64_t)blockIdx.x * a.lines + line;
   const bool valid = row < a.rows;
   const uint32_t m = (uint32_t)a.n, n = (uint32_t)c.n;
-  float2* L = smem + (size_t)line * (mixed_pad<PAD>(m) + 1);
-  const float2* src = a.in + row * (int64_t)n;
-  float2* dst = a.out + row * (int64_t)n;
-  for (uint32_t j = t; j < m; j += tpl) {
-    float2 v = make_float2(0.f, 0.f);
-    if (valid && j < n) v = cmul(gload_nt(src, j), gload(a.pre, j));
-    L[mixed_pad<PAD>(j)] = v;
+  const uint32_t lp = mixed_pad<PAD>(m) + 1;
+  float2* L = smem + (size_t)line * lp;
+  // STG (lines of few threads): the workgroup's rows, one contiguous block of
+  // n-value rows, read and written in order; element e is x_j of line e / n
+  const int64_t row0 = (int64_t)blockIdx.x * a.lines;
+  const int64_t left = a.rows - row0;
+  const uint32_t nblk = (uint32_t)(left < a.lines ? left : a.lines) * n;
+  const uint32_t NT = tpl * (uint32_t)a.lines;
+  const uint32_t magic = 0xffffffffu / n + 1u;  // e / n for e < 2^32 / n
+  if constexpr (STG) {
+    const float2* src = a.in + row0 * n;
+    constexpr int U = 8;
+    for (uint32_t e0 = (uint32_t)tid; e0 < nblk; e0 += U * NT) {
+      float2 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (e0 + k * NT < nblk) v[k] = gload_nt(src, e0 + k * NT);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const uint32_t e = e0 + k * NT;
+        if (e < nblk) {
+          const uint32_t q = __umulhi(e, magic), j = e - q * n;
+          smem[q * lp + mixed_pad<PAD>(j)] = cmul(v[k], gload(a.pre, j));
+        }
+      }
+    }
+    for (uint32_t j = n + t; j < m; j += tpl) L[mixed_pad<PAD>(j)] = make_float2(0.f, 0.f);
+  } else {
+    const float2* src = a.in + row * (int64_t)n;
+    for (uint32_t j = t; j < m; j += tpl) {
+      float2 v = make_float2(0.f, 0.f);
+      if (valid && j < n) v = cmul(gload_nt(src, j), gload(a.pre, j));
+      L[mixed_pad<PAD>(j)] = v;
+    }
   }
   lds_barrier();
   mixed_stages<-1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
   for (uint32_t k = t; k < m; k += tpl) L[mixed_pad<PAD>(k)] = cmul(L[mixed_pad<PAD>(k)], gload(c.bhat, k));
   lds_barrier();
   mixed_stages<1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
-  if (valid)
+  if constexpr (STG) {
+    float2* dst = a.out + row0 * n;
+    for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
+      const uint32_t q = __umulhi(e, magic), j = e - q * n;
+      gstore_nt(dst, e, cmul(smem[q * lp + mixed_pad<PAD>(j)], gload(c.post, j)));
+    }
+  } else if (valid) {
+    float2* dst = a.out + row * (int64_t)n;
     for (uint32_t j = t; j < n; j += tpl) gstore_nt(dst, j, cmul(L[mixed_pad<PAD>(j)], gload(c.post, j)));
+  }
 }
 
 // Column transforms of a mixed-radix length over [images][n][nx] (see
@@ -505,30 +618,56 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
       (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
+  // Lines of fewer than 128 threads read and write HBM through LDS (STG): a
+  // butterfly's direct loads are runs of m[0] elements, as short as one.
+  // Per 512 MiB: n = 3 261 -> 166 us, 6 1124 -> 171, 12 2799 -> 174, 15 3566
+  // -> 228, 24 383 -> 183, 48 267 -> 173, 100 300 -> 187, 360 233 -> 207,
+  // 1000 232 -> 225; 1296 (216 threads) was 2 % slower staged.
+  if (a.tpl < 128 && a.n <= 4096) {  // n <= 4096: two butterflies only with radices up to 8
+    if (rmax > 8) {
+      if (a.pad) {
+        if (sign < 0)
+          FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true, true>), dim3(grid), block, lds, st, a);
+        else
+          FFTAMD_LAUNCH((k_mixed<1, 1, 16, true, true>), dim3(grid), block, lds, st, a);
+      } else if (sign < 0) {
+        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false, true>), dim3(grid), block, lds, st, a);
+      } else {
+        FFTAMD_LAUNCH((k_mixed<1, 1, 16, false, true>), dim3(grid), block, lds, st, a);
+      }
+    } else if (a.pad) {
+      return hipErrorInvalidValue;
+    } else if (sign < 0) {
+      FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false, true>), dim3(grid), block, lds, st, a);
+    } else {
+      FFTAMD_LAUNCH((k_mixed<1, 2, 8, false, true>), dim3(grid), block, lds, st, a);
+    }
+    return hipGetLastError();
+  }
   if (rmax > 8 && a.kb == 2) {
     // lengths above 8192: two butterflies of up to 16 values per thread
     if (a.pad) return hipErrorInvalidValue;
     if (sign < 0)
-      FFTAMD_LAUNCH((k_mixed<-1, 2, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<-1, 2, 16, false, false>), dim3(grid), block, lds, st, a);
     else
-      FFTAMD_LAUNCH((k_mixed<1, 2, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<1, 2, 16, false, false>), dim3(grid), block, lds, st, a);
   } else if (rmax > 8) {
     if (a.pad) {
       if (sign < 0)
-        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true>), dim3(grid), block, lds, st, a);
+        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true, false>), dim3(grid), block, lds, st, a);
       else
-        FFTAMD_LAUNCH((k_mixed<1, 1, 16, true>), dim3(grid), block, lds, st, a);
+        FFTAMD_LAUNCH((k_mixed<1, 1, 16, true, false>), dim3(grid), block, lds, st, a);
     } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false, false>), dim3(grid), block, lds, st, a);
     } else {
-      FFTAMD_LAUNCH((k_mixed<1, 1, 16, false>), dim3(grid), block, lds, st, a);
+      FFTAMD_LAUNCH((k_mixed<1, 1, 16, false, false>), dim3(grid), block, lds, st, a);
     }
   } else if (a.pad) {
     return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false>), dim3(grid), block, lds, st, a);
+    FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false, false>), dim3(grid), block, lds, st, a);
   } else {
-    FFTAMD_LAUNCH((k_mixed<1, 2, 8, false>), dim3(grid), block, lds, st, a);
+    FFTAMD_LAUNCH((k_mixed<1, 2, 8, false, false>), dim3(grid), block, lds, st, a);
   }
   return hipGetLastError();
 }
@@ -594,12 +733,20 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
   const size_t lds = (size_t)a.lines * rader_line((uint32_t)a.n, a.pad != 0) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
+  // short lines: block IO through LDS, as in k_mixed.  Per 512 MiB: p = 5
+  // 906 -> 170 us, 13 2962 -> 175, 17 4158 -> 318, 37 862 -> 326, 97 510 ->
+  // 335, 257 720 -> 405, 641 481 -> 398 (1009: 144 threads, unstaged)
+  const bool stg = a.tpl < 128 && rd.p <= 4096;
   if (a.kb == 2)  // p - 1 above 8192: two butterflies of up to 16 values per thread
-    FFTAMD_LAUNCH((k_rader<2, 16, false>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<2, 16, false, false>), dim3(grid), block, lds, st, a, rd);
+  else if (a.pad && stg)
+    FFTAMD_LAUNCH((k_rader<1, 16, true, true>), dim3(grid), block, lds, st, a, rd);
   else if (a.pad)
-    FFTAMD_LAUNCH((k_rader<1, 16, true>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<1, 16, true, false>), dim3(grid), block, lds, st, a, rd);
+  else if (stg)
+    FFTAMD_LAUNCH((k_rader<1, 16, false, true>), dim3(grid), block, lds, st, a, rd);
   else
-    FFTAMD_LAUNCH((k_rader<1, 16, false>), dim3(grid), block, lds, st, a, rd);
+    FFTAMD_LAUNCH((k_rader<1, 16, false, false>), dim3(grid), block, lds, st, a, rd);
   return hipGetLastError();
 }
 
@@ -614,10 +761,15 @@ hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, h
       (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  if (a.pad)
-    FFTAMD_LAUNCH((k_bluestein_mixed<true>), dim3(grid), block, lds, st, a, c);
+  const bool stg = a.tpl < 128 && c.n <= 4096;  // short lines: block IO through LDS, as in k_mixed
+  if (a.pad && stg)
+    FFTAMD_LAUNCH((k_bluestein_mixed<true, true>), dim3(grid), block, lds, st, a, c);
+  else if (a.pad)
+    FFTAMD_LAUNCH((k_bluestein_mixed<true, false>), dim3(grid), block, lds, st, a, c);
+  else if (stg)
+    FFTAMD_LAUNCH((k_bluestein_mixed<false, true>), dim3(grid), block, lds, st, a, c);
   else
-    FFTAMD_LAUNCH((k_bluestein_mixed<false>), dim3(grid), block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_bluestein_mixed<false, false>), dim3(grid), block, lds, st, a, c);
   return hipGetLastError();
 }
 

@@ -34,9 +34,23 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   constexpr bool SPLIT = rows_split(N);
   constexpr int T = N / E;
   constexpr bool WL = T <= 64;  // every line inside one wavefront
+  // the wave's priority raised while it issues its row loads: per 512 MiB
+  // 64 points 249 -> 237 us, 512 188 -> 177, 1024 191 -> 184, 2048 191 ->
+  // 183, 16384 273 -> 265; no change at 4096, slower at 8192 (195 -> 207)
+  constexpr bool LPRIO = N >= 64 && N != 4096 && N != 8192;
   using L = RowLds<N, SPLIT, E>;
   static_assert(row_lds_bytes(N, C, SPLIT, E) <= kLdsBudgetBytes, "LDS budget");
-  __shared__ lds_elem_t<SPLIT> lds[L::size(C)];
+  // Rows of 4 to 32 points (one or two threads per row): a wavefront's loads
+  // and stores would each touch up to 64 rows, so the workgroup's block of C
+  // rows (contiguous) is read and written in order through LDS, rows SP =
+  // N + 1 elements apart.  Per 512 MiB on MI355X: 8 points 370 -> 178 us,
+  // 16 points 619 -> 230, 32 points 401 -> 252, 4 points 187 -> 169; 2 points
+  // (163 -> 177) and 64 (249 -> 273) are faster unstaged.
+  constexpr bool STAGE = T < 4 && N >= 4;
+  constexpr int SP = N + 1;
+  constexpr int LX = T > 1 ? L::size(C) : 1;  // lines of one thread exchange nothing
+  constexpr int LE = STAGE && C * SP > LX ? C * SP : LX;
+  __shared__ lds_elem_t<SPLIT> lds[LE];
   lds_poison(lds);
 
   const int tid = threadIdx.x;
@@ -45,11 +59,37 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
   const int64_t row = row0 + line;
   const bool valid = row < a.rows;
   const uint32_t off = (uint32_t)(line * N + u);
+  constexpr uint32_t NT = (uint32_t)(C * T);
+  const int64_t left = (a.rows - row0) * N;
+  const uint32_t lim = left < (int64_t)C * N ? (uint32_t)left : (uint32_t)(C * N);
   float2 v[E];
-  if (valid) {
+  if constexpr (STAGE) {
+    static_assert(!SPLIT, "staged rows use the complex exchange");
     const float2* src = a.in + row0 * N;
+    if constexpr (LPRIO) __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const uint32_t i = (uint32_t)tid + NT * m;
+      const float2 x = i < lim ? gload_nt(src, i) : make_float2(0.f, 0.f);
+      lds[(i / N) * SP + i % N] = x;
+    }
+    if constexpr (LPRIO) __builtin_amdgcn_s_setprio(0);
+    lds_barrier();
+#pragma unroll
+    for (int m = 0; m < E; ++m) v[m] = lds[line * SP + u + T * m];
+    if (valid && a.shift_mode) {
+      const int par = a.shift_mode == 2 ? (int)(row & (a.rows_per_image - 1)) : 0;
+#pragma unroll
+      for (int m = 0; m < E; ++m)
+        if ((par + u + T * m) & 1) v[m] = negate_bits(v[m]);
+    }
+    lds_barrier();  // the stages reuse the buffer
+  } else if (valid) {
+    const float2* src = a.in + row0 * N;
+    if constexpr (LPRIO) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int m = 0; m < E; ++m) v[m] = gload_nt(src + T * m, off);
+    if constexpr (LPRIO) __builtin_amdgcn_s_setprio(0);
     if (a.shift_mode) {
       const int par = a.shift_mode == 2 ? (int)(row & (a.rows_per_image - 1)) : 0;
 #pragma unroll
@@ -61,7 +101,24 @@ __global__ __launch_bounds__(rows_threads(N) * C) void k_c2c_rows(RowsArgs a) {
     for (int m = 0; m < E; ++m) v[m] = make_float2(0.f, 0.f);
   }
   run_stages<N, E, S, WL, L, SPLIT>(v, lds, a.tw, u, line);
-  if (valid) {
+  if constexpr (STAGE) {
+    lds_barrier();  // the last stage's exchange reads are done
+#pragma unroll
+    for (int m = 0; m < E; ++m) lds[line * SP + u + T * m] = v[m];
+    lds_barrier();
+    float2* dst = a.out + row0 * N;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const uint32_t i = (uint32_t)tid + NT * m;
+      if (i < lim) {
+        const float2 x = lds[(i / N) * SP + i % N];
+        if (a.stream_store)
+          gstore_nt(dst, i, x);
+        else
+          gstore(dst, i, x);
+      }
+    }
+  } else if (valid) {
     float2* dst = a.out + row0 * N;
     if (a.stream_store) {
 #pragma unroll

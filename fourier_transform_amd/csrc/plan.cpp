@@ -586,12 +586,13 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
   // A convolution length with a mixed-radix schedule where it is much
   // shorter than the power of two (n just above a power of two: 1034 can use
   // 2080 = 16 x 13 x 10 instead of 4096).  Among the lengths c >= 2n - 1 with
-  // 1.3 c < m, the one with the smallest c x stages, when m >= 4096.
-  // Measured on MI355X per 512 MiB: 1034 973 -> 908 us, 1049 966 -> 863 us,
-  // 2053 1325 -> 1139 us, 2111 1298 -> 1044 us; with m <= 2048 the
-  // power-of-two kernel is as fast or faster (263: 885 against 914 us).
+  // 1.3 c < m, the one with the smallest c x stages.  Measured on MI355X per
+  // 512 MiB: 1034 973 -> 908 us, 1049 966 -> 863 us, 2053 1325 -> 1139 us,
+  // 2111 1298 -> 1044 us; with the short lines read and written through LDS
+  // also below 4096: 34 (70 = 10 x 7) 797 -> 473 us, 47 (96) 663 -> 462, 83
+  // (168) 686 -> 464, 167 728 -> 696, 263 (525) 871 -> 790.
   std::vector<int> msched;
-  if (m >= 4096) {
+  if (m >= 64) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
     int64_t best_cost = INT64_MAX, best_c = 0;
     for (int64_t c = 2 * n - 1; c <= kMaxChirpMixedLength && 13 * c < 10 * m && 2 * c < best_cost; ++c) {

@@ -95,10 +95,11 @@ def test_primes_two_butterflies_shift_in_place(n, shift):
 
 
 # the chirp transform on a convolution length with a mixed-radix schedule
-# (about half the power of two, used where that is 4096 or more):
+# (used where it is at least 1.3 times shorter than the power of two):
+# 34: 70 = 10 7; 47: 96 = 16 6; 83: 165 = 15 11; 263: 525 = 15 7 5;
 # 1034: 2080 = 16 13 10; 2053: 4116 = 12 7 7 7; 2111: 4224 = 11 8 8 6;
-# 263 and 521 keep the power of two (1024, 2048)
-CHIRP_MIXED = [263, 521, 1031, 1034, 1049, 2053, 2063, 2111]
+# 59 and 107 keep the power of two (128, 256)
+CHIRP_MIXED = [34, 47, 59, 83, 107, 263, 1031, 1034, 1049, 2053, 2063, 2111]
 
 
 @pytest.mark.parametrize("n", CHIRP_MIXED)
@@ -110,13 +111,28 @@ def test_chirp_mixed_length(n, sign):
         assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
 
 
-@pytest.mark.parametrize("n,shift", [(1034, 1), (1034, 2), (2053, 1), (2111, 2)])
+@pytest.mark.parametrize("n,shift", [(34, 1), (83, 2), (1034, 1), (1034, 2), (2053, 1), (2111, 2)])
 def test_chirp_mixed_length_shift_and_in_place(n, shift):
     say(f"chirp (mixed-radix m) shift={shift} n={n}, in place")
     x = W.uniform_c64((3, n), np.random.default_rng(n + shift + 5))
     idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
     want = oracle.dft(x, -1)[:, idx]
     assert rel_l2(c2c(x, -1, shift=shift, inplace=True), want) <= TOL
+
+
+@pytest.mark.parametrize("n", [3, 12, 15, 100, 360, 5, 17, 97, 257, 34, 83])
+def test_short_lines_several_workgroups(n):
+    """Lines of fewer than 128 threads (mixed radix, Rader, the chirp on a
+    mixed-radix length) read and write their workgroup's rows as one block
+    through LDS: many workgroups and a ragged last one, in place, and the
+    shift (the sign flip of even n, the ramp of odd n)."""
+    batch = 2000 + n % 7
+    say(f"short lines n={n} batch={batch}")
+    x = W.uniform_c64((batch, n), np.random.default_rng(n + 31))
+    assert rel_l2(c2c(x, -1), oracle.dft(x, -1)) <= TOL
+    assert rel_l2(c2c(x, 1, inplace=True), oracle.dft(x, 1)) <= TOL
+    want = oracle.dft(x, -1)[:, oracle.fftshift_index(n)]
+    assert rel_l2(c2c(x, -1, shift=1), want) <= TOL
 
 
 @pytest.mark.parametrize("n", [7, 1000, 1009, 4097])

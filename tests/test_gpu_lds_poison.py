@@ -46,14 +46,15 @@ def _twice(fn):
 
 
 C2C_CASES = [
-    # single-pass rows (complex and split exchanges, wave-local and workgroup lines)
-    (2, 3), (16, 5), (64, 7), (1024, 8), (4096, 33), (8192, 3), (16384, 2),
+    # single-pass rows (complex and split exchanges, wave-local and workgroup lines, rows
+    # of 4-32 points staged through LDS)
+    (2, 3), (16, 5), (8, 300), (32, 200), (64, 7), (1024, 8), (4096, 33), (8192, 3), (16384, 2),
     # four-step
     (1 << 15, 3), (1 << 20, 2),
     # mixed radix (one butterfly of <= 16, two of <= 8, two of <= 16 above 8192), Rader,
     # chirp (one kernel on a power of two up to 16384 and at 32768, one on a mixed-radix
     # length, three passes)
-    (1000, 9), (360, 11), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (1019, 4),
+    (1000, 9), (360, 11), (12, 700), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (17, 600), (1019, 4), (34, 300),
     (10001, 2), (1034, 3), (20011, 2),
 ]
 

@@ -54,6 +54,22 @@ def test_c2c_single_pass_sweep(logn, sign):
         assert rel_l2(y, oracle.c2c(x, sign)) <= TOL, (n, batch)
 
 
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
+def test_c2c_short_rows_several_workgroups(n):
+    """Short rows: 4 to 32 points are read and written through LDS in the
+    workgroup's order (256 or 128 rows per workgroup).  Several workgroups and
+    a ragged last one, in place, and the shift, bitwise the transform of the
+    negated input."""
+    batch = 3 * 256 + 37
+    say(f"c2c short rows n={n} batch={batch}")
+    x = W.uniform_c64((batch, n), np.random.default_rng(n + 500))
+    assert rel_l2(c2c(x, -1), oracle.c2c(x, -1)) <= TOL
+    assert rel_l2(c2c(x, 1, inplace=True), oracle.c2c(x, 1)) <= TOL
+    ys = c2c(x, -1, shift=1)
+    xn = negate_odd(x, np.broadcast_to(np.arange(n), x.shape))
+    assert np.array_equal(ys.view(np.uint32), c2c(xn, -1).view(np.uint32))
+
+
 @pytest.mark.parametrize("n", [2, 64, 4096])
 def test_c2c_in_place(n):
     say(f"c2c in place n={n}")
