@@ -180,6 +180,13 @@ __global__ __launch_bounds__(tile_lines(N, false) * (N / tile_e(N, false))) void
   }
 }
 
+// q / d for q * d < 2^32 by a multiply-high with floor((2^32 - 1) / d) + 1
+struct FastDiv {
+  uint32_t d, magic;
+  __device__ explicit FastDiv(uint32_t d_) : d(d_), magic(0xffffffffu / d_ + 1u) {}
+  __device__ __forceinline__ uint32_t div(uint32_t q) const { return d == 1 ? q : __umulhi(q, magic); }
+};
+
 // ---------------------------------------------------------------------------
 // Real analysis (R2C) of rows of n = 2H reals: z_m = x_{2m} + i x_{2m+1},
 // Z = forward FFT_H(z), X_k = Xe + e^{-2 pi i k/n} Xo with
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
   lds_barrier();
 
   const int kout = a.mmax + 1;
+  const FastDiv dk((uint32_t)kout);
   float2* out = static_cast<float2*>(a.out);
   for (int q = tid; q < C * kout; q += C * T) {
     int ln, k;
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_r2c(RealArgs a) {
       ln = q % C;
       k = q / C;
     } else {
-      ln = q / kout;
+      ln = (int)dk.div((uint32_t)q);
       k = q - ln * kout;
     }
     const int64_t r = (int64_t)blockIdx.x * C + ln;
@@ -265,23 +273,36 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
   const int kin = mmax + 1;
   const float2* F = static_cast<const float2*>(a.in);
 
-  // stage the spectra of the workgroup's rows in LDS (coalesced in either layout)
-  for (int q = tid; q < C * kin; q += C * T) {
-    int ln, k;
-    if (a.mmajor) {
-      ln = q % C;
-      k = q / C;
-    } else {
-      ln = q / kin;
-      k = q - ln * kin;
+  // stage the spectra of the workgroup's rows in LDS (coalesced in either
+  // layout), U loads in flight per thread before their LDS stores (one load
+  // at a time, each waited for before its store, took 1.4-1.7x as long: per
+  // 1 GiB of reals 2048 746 -> 524 us, 256 663 -> 469, 8 1667 -> 998)
+  const FastDiv dk((uint32_t)kin);
+  const int tot = C * kin;
+  constexpr int U = 8;
+  for (int q0 = tid; q0 < tot; q0 += U * C * T) {
+    float2 val[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int q = q0 + i * C * T;
+      const int ln = a.mmajor ? q % C : (int)dk.div((uint32_t)q);
+      const int k = a.mmajor ? q / C : q - ln * kin;
+      const int64_t r = (int64_t)blockIdx.x * C + ln;
+      val[i] = make_float2(0.f, 0.f);
+      if (q < tot && r < a.rows) val[i] = F[a.mmajor ? (int64_t)k * a.rows + r : r * kin + k];
     }
-    const int64_t r = (int64_t)blockIdx.x * C + ln;
-    float2 val = make_float2(0.f, 0.f);
-    if (r < a.rows) val = F[a.mmajor ? (int64_t)k * a.rows + r : r * kin + k];
-    if (k < H)
-      lds[L::at(ln, k)] = val;
-    else
-      nyq[ln] = val;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int q = q0 + i * C * T;
+      if (q < tot) {
+        const int ln = a.mmajor ? q % C : (int)dk.div((uint32_t)q);
+        const int k = a.mmajor ? q / C : q - ln * kin;
+        if (k < H)
+          lds[L::at(ln, k)] = val[i];
+        else
+          nyq[ln] = val[i];
+      }
+    }
   }
   lds_barrier();
 
@@ -308,7 +329,23 @@ __global__ __launch_bounds__(threads_per_line(H) * C) void k_c2r(RealArgs a) {
   }
   lds_barrier();
   run_stages<H, E, +1, WL, L, false>(v, lds, a.tw, u, line);
-  if (valid) {
+  // rows of 32 reals (16-value lines of one thread) are stored in order
+  // through LDS: per 1 GiB of reals 495 -> 402 us; the shorter ones were
+  // slower that way (8 reals 997 -> 1093 us, 16 1207 -> 1308)
+  constexpr bool STG = T == 1 && H == 16;
+  if constexpr (STG) {
+#pragma unroll
+    for (int m = 0; m < E; ++m) lds[L::at(line, m)] = v[m];
+    lds_barrier();
+    float2* dst = static_cast<float2*>(a.out) + (int64_t)blockIdx.x * C * H;
+    const int64_t left = (a.rows - (int64_t)blockIdx.x * C) * H;
+    const int lim = left < C * H ? (int)left : C * H;
+#pragma unroll
+    for (int m = 0; m < E; ++m) {
+      const int i = tid + C * m;
+      if (i < lim) dst[i] = lds[L::at(i / H, i % H)];
+    }
+  } else if (valid) {
     float2* dst = static_cast<float2*>(a.out) + row * H;
 #pragma unroll
     for (int m = 0; m < E; ++m) dst[u + T * m] = v[m];
@@ -358,6 +395,7 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_r2c_pairs(RealArgs 
   // outputs: (line, row of the pair, bin k); consecutive threads take
   // consecutive bins (row-major) or consecutive rows (m-major)
   const int kout = a.mmax + 1;
+  const FastDiv dk((uint32_t)kout);
   float2* out = static_cast<float2*>(a.out);
   for (int q = tid; q < C * 2 * kout; q += C * T) {
     int ln, which, k;
@@ -367,7 +405,7 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_r2c_pairs(RealArgs 
       which = r & 1;
       k = q / (2 * C);
     } else {
-      const int r = q / kout;
+      const int r = (int)dk.div((uint32_t)q);
       ln = r >> 1;
       which = r & 1;
       k = q - r * kout;
@@ -408,28 +446,41 @@ __global__ __launch_bounds__(threads_per_line(N) * C) void k_c2r_pairs(RealArgs 
   const int kin = mmax + 1;
   const float2* F = static_cast<const float2*>(a.in);
 
-  // stage both spectra: row 2p at [0, H), row 2p+1 at [H, N); bin H apart
-  for (int q = tid; q < C * 2 * kin; q += C * T) {
-    int ln, which, k;
-    if (a.mmajor) {
-      const int r = q % (2 * C);
-      ln = r >> 1;
-      which = r & 1;
-      k = q / (2 * C);
-    } else {
-      const int r = q / kin;
-      ln = r >> 1;
-      which = r & 1;
-      k = q - r * kin;
+  // stage both spectra: row 2p at [0, H), row 2p+1 at [H, N); bin H apart;
+  // U loads in flight per thread before their LDS stores
+  const FastDiv dk((uint32_t)kin);
+  const int tot = C * 2 * kin;
+  constexpr int U = 8;
+  auto decode = [&](int q, int& ln, int& which, int& k) {
+    const int r = a.mmajor ? q % (2 * C) : (int)dk.div((uint32_t)q);
+    ln = r >> 1;
+    which = r & 1;
+    k = a.mmajor ? q / (2 * C) : q - r * kin;
+  };
+  for (int q0 = tid; q0 < tot; q0 += U * C * T) {
+    float2 val[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int q = q0 + i * C * T;
+      int ln, which, k;
+      decode(q, ln, which, k);
+      const int64_t p = (int64_t)blockIdx.x * C + ln;
+      const int64_t row = 2 * p + which;
+      val[i] = make_float2(0.f, 0.f);
+      if (q < tot && p < pairs) val[i] = F[a.mmajor ? (int64_t)k * a.rows + row : row * kin + k];
     }
-    const int64_t p = (int64_t)blockIdx.x * C + ln;
-    float2 val = make_float2(0.f, 0.f);
-    const int64_t row = 2 * p + which;
-    if (p < pairs) val = F[a.mmajor ? (int64_t)k * a.rows + row : row * kin + k];
-    if (k < H)
-      lds[L::at(ln, which * H + k)] = val;
-    else
-      nyq[2 * ln + which] = val;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+      const int q = q0 + i * C * T;
+      if (q < tot) {
+        int ln, which, k;
+        decode(q, ln, which, k);
+        if (k < H)
+          lds[L::at(ln, which * H + k)] = val[i];
+        else
+          nyq[2 * ln + which] = val[i];
+      }
+    }
   }
   lds_barrier();
 

@@ -288,8 +288,11 @@ __device__ __forceinline__ void dft(float2* x) {
 //   row lanes:            line * P + p(i),  p(i) = i + i/G.
 //                         8-byte: G = 32, so 32 consecutive elements stay in
 //                         one block of the 64 banks.  P = T mod 32 for lines
-//                         of T < 32 threads, so the lines that share a clock
-//                         tile the banks.  Lines that are also read across
+//                         of 1 < T < 32 threads, so the lines that share a
+//                         clock tile the banks; lines of one thread exchange
+//                         nothing and take P = p(N) + 1 (real rows of 32:
+//                         per 1 GiB of reals R2C 508 -> 420 us, C2R 618 ->
+//                         495, from the LDS no longer limiting occupancy).  Lines that are also read across
 //                         (the transposed read-back of the four-step row
 //                         pass: 16 lines at two neighbouring indices per
 //                         clock) take P = 6 mod 32, best for every T there.
@@ -315,6 +318,7 @@ constexpr int row_pad(int i, bool split, int e) { return i + i / row_pad_g(split
 constexpr int row_pitch(int n, bool split, int e, bool xread) {
   const int p = row_pad(n, split, e) + 1;
   const int t = n / e;
+  if (t == 1) return p;  // lines of one thread: no exchange, the pitch only separates them
   const int target = split ? 2 : xread ? 6 : t < 32 ? t : 1;
   return p + ((target - p % 32) % 32 + 32) % 32;
 }

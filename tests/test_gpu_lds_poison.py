@@ -91,7 +91,7 @@ def test_poison_2d(ny, nx, batch):
     assert rel_l2(y, oracle.c2c_2d(x, -1)) <= TOL
 
 
-@pytest.mark.parametrize("n,mmax,pairs", [(64, 32, False), (2048, 682, False), (2048, 682, True), (1000, 300, False),
+@pytest.mark.parametrize("n,mmax,pairs", [(32, 16, False), (8, 4, True), (64, 32, False), (2048, 682, False), (2048, 682, True), (1000, 300, False),
                                           (999, 499, False)])
 def test_poison_real(n, mmax, pairs):
     say(f"poison build: real n={n} mmax={mmax} pairs={pairs}")

@@ -224,6 +224,24 @@ def test_real_sweep(logn):
         assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
 
 
+@pytest.mark.parametrize("n", [8, 32, 64, 2048])
+@pytest.mark.parametrize("pairs", [False, True])
+def test_real_several_workgroups(n, pairs):
+    """Batches of several workgroups with a ragged last one (the spectrum
+    staging loop runs several rounds of loads per thread; rows of 32 reals
+    are stored through LDS), both spectrum layouts, full and cut band."""
+    g = np.random.default_rng(n + 77)
+    batch = 602 if n < 2048 else 42
+    for mmax, mmajor in ((n // 2, False), (n // 3, True)):
+        say(f"r2c/c2r n={n} batch={batch} mmax={mmax} mmajor={mmajor} pairs={pairs}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = r2c(x, mmax, mmajor, pairs=pairs)
+        assert rel_l2(Fg.T if mmajor else Fg, oracle.r2c(x, mmax)) <= TOL
+        S = (g.normal(size=(batch, mmax + 1)) + 1j * g.normal(size=(batch, mmax + 1))).astype(np.complex64)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        assert rel_l2(c2r(Sin, n, batch, mmax, mmajor, pairs=pairs), oracle.c2r(S, n, mmax)) <= TOL
+
+
 @pytest.mark.parametrize("logn", range(2, 15))
 def test_real_pairs_sweep(logn):
     """Two real rows per complex transform (Mota, section 2.6, Eq. 17-18)."""
