@@ -539,7 +539,11 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
 // reads it, the last writes it back in natural order), G lines at a time
 // with tpl threads each (threads beyond the group's lines take no butterfly
 // but join every barrier); then the columns are stored back.
-constexpr int kColBatch = 16;
+// 8 loads (and 8 twiddle pairs) in flight per thread: 60-64 VGPRs, 8 waves
+// per SIMD; with 16, 108-123 VGPRs and 4 waves cost per 512 MiB: 2D 360 x
+// 360 494 against 652 us, 125 x 160 460 against 595, 12 x 4096 369 against
+// 473; the four-step of 20000 794 against 965, 6561 997 against 1279
+constexpr int kColBatch = 8;
 template <int S, int KB, int RMAX, bool PAD>
 __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
   extern __shared__ float4 smem4[];
@@ -584,7 +588,28 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
     mixed_stages<S, KB, RMAX, PAD, 3>(a, active ? tid % tpl : 0x40000000u, tpl, active, nullptr, nullptr,
                                       smem + (active ? line : 0u) * pitch);
   }
-  if (has_col) {
+  if (has_col && c.thi) {
+    // the four-step's W^{x k}: kColBatch pairs of table loads in flight
+    // before their stores
+    float2* dst = a.out + img * (int64_t)n * c.nx + (g - img * c.nx);
+    const uint32_t x = (uint32_t)(g - img * c.nx), mask = (1u << c.bits) - 1u;
+    for (uint32_t r0 = tid / CT; r0 < n; r0 += kColBatch * RS) {
+      float2 wh[kColBatch], wl[kColBatch];
+#pragma unroll
+      for (int i = 0; i < kColBatch; ++i) {
+        const uint32_t r = r0 + RS * i, e = x * r;
+        if (r < n) {
+          wh[i] = gload(c.thi, e >> c.bits);
+          wl[i] = gload(c.tlo, e & mask);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kColBatch; ++i) {
+        const uint32_t r = r0 + RS * i;
+        if (r < n) gstore(dst, r * (uint32_t)c.nx, apply_tw<S>(L0[mixed_pad<PAD>(r)], cmul(wh[i], wl[i])));
+      }
+    }
+  } else if (has_col) {
     float2* dst = a.out + img * (int64_t)n * c.nx + (g - img * c.nx);
     for (uint32_t r = tid / CT; r < n; r += RS) gstore(dst, r * (uint32_t)c.nx, L0[mixed_pad<PAD>(r)]);
   }
@@ -686,6 +711,8 @@ hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs&
   a.lines = 1;
   if (!mixed_schedule_ok(a, &rmax) || c.nx < 1 || c.images < 1 || !a.in || !a.out) return hipErrorInvalidValue;
   if (rmax > 8 && a.kb != 1) return hipErrorInvalidValue;  // no column-tile kernel of this shape
+  if (c.thi && (!c.tlo || c.bits < 1 || c.bits > 16 || (int64_t)a.n * c.nx > (int64_t(1) << 32)))
+    return hipErrorInvalidValue;  // the twiddle exponents x k must fit 32 bits
   const int ct = mixed_cols_tile(a);
   if (ct == 0) return hipErrorInvalidValue;
   a.lines = ct;

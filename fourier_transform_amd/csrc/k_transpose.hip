@@ -12,7 +12,7 @@ constexpr int kTileRows = 8;  // 32 x 8 threads, 4 elements each
 
 __global__ __launch_bounds__(kTile * kTileRows) void k_transpose(const float2* __restrict__ in,
                                                               float2* __restrict__ out, int64_t rows,
-                                                              int64_t cols, int64_t tiles_c) {
+                                                              int64_t cols, int64_t tiles_c, int64_t rot) {
   __shared__ float2 tile[kTile][kTile + 1];
   lds_poison(tile);
   const int64_t img = blockIdx.y;
@@ -29,18 +29,23 @@ __global__ __launch_bounds__(kTile * kTileRows) void k_transpose(const float2* _
 #pragma unroll
   for (int i = 0; i < kTile; i += kTileRows) {
     const int64_t c = tc * kTile + ty + i, r = tr * kTile + tx;  // output row c, column r
-    if (r < rows && c < cols) dst[c * rows + r] = tile[tx][ty + i];
+    if (r < rows && c < cols) {
+      int64_t e = c * rows + r + rot;
+      if (e >= rows * cols) e -= rows * cols;
+      dst[e] = tile[tx][ty + i];
+    }
   }
 }
 }  // namespace
 
 hipError_t launch_transpose(const float2* in, float2* out, int64_t rows, int64_t cols, int64_t images,
-                            hipStream_t st) {
-  if (rows < 1 || cols < 1 || images < 1 || images > 65535) return hipErrorInvalidValue;
+                            hipStream_t st, int64_t rot) {
+  if (rows < 1 || cols < 1 || images < 1 || images > 65535 || rot < 0 || rot >= rows * cols)
+    return hipErrorInvalidValue;
   const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
   if (tiles_r * tiles_c > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   FFTAMD_LAUNCH(k_transpose, dim3((uint32_t)(tiles_r * tiles_c), (uint32_t)images),
-                     dim3(kTile, kTileRows), 0, st, in, out, rows, cols, tiles_c);
+                     dim3(kTile, kTileRows), 0, st, in, out, rows, cols, tiles_c, rot);
   return hipGetLastError();
 }
 

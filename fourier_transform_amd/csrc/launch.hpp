@@ -200,6 +200,12 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t stream);
 // are stored back.
 struct MixedColsArgs {
   int64_t nx, images;
+  // optional (thi non-null): the stored value of row k of column x is
+  // multiplied by W^{x k} = thi[e >> bits] * tlo[e & (2^bits - 1)], e = x k
+  // (x k < 2^32; the four-step of lengths with no prime factor above 13)
+  const float2* thi;
+  const float2* tlo;
+  int bits;
 };
 // columns per workgroup (16 or 8, the most that fit the LDS), or 0 when not
 // even 8 fit (the caller then transposes instead)
@@ -285,9 +291,12 @@ hipError_t launch_real_part(const RealAnyArgs& a, hipStream_t stream);
 
 // Transpose of `images` complex64 matrices [rows][cols] -> [cols][rows]
 // (out must not overlap in), through 32 x 32 LDS tiles so both sides are
-// coalesced.  Used by 2D plans with an axis that is not a power of two.
+// coalesced.  Used by 2D plans with an axis that is not a power of two, and
+// by the four-step of smooth lengths, whose fftshift is the rotation rot
+// (0 <= rot < rows * cols): element e of an output image goes to
+// (e + rot) mod (rows * cols).
 hipError_t launch_transpose(const float2* in, float2* out, int64_t rows, int64_t cols, int64_t images,
-                            hipStream_t stream);
+                            hipStream_t stream, int64_t rot = 0);
 
 // Band-limited direct transforms (any n, 2 <= n <= kMaxDirectLength):
 // analysis reads real rows [rows][n] (float) and writes bins 0..mmax;

@@ -232,8 +232,13 @@ struct fft_plan {
   const float2* bhat_t = nullptr;  // above m = 16384: bhat[k2 + n2*k1] at k2*n1 + k1
   // C2C lengths with no prime factor above 13 (mixed radix): the schedule, and
   // the load factors of the two shifts
-  // C2C lengths p * q (p in {3, 5, 7, 9, 15, 25}, q a power of two >= 16)
   bool mixed = false;
+  // C2C lengths with no prime factor above 13 that no one-kernel schedule
+  // takes: the four-step n = n1 * n2 (n1, n2, bits, thi, tlo as above): the
+  // n2-point column transforms (inner2's schedule) times W_n^{j1 k2} into
+  // the scratch, the n1-point row plan (inner) in place there, and a
+  // transpose to natural order that also applies the shift (a rotation)
+  bool fsany = false;
   bool rader = false;  // mx holds the schedule of n - 1
   MixedArgs mx{};
   const float2* rd_conv = nullptr;
@@ -670,44 +675,118 @@ fft_plan* create_bluestein(int64_t n, int64_t batch, int sign) {
 
 // any-length C2C plan: mixed radix when possible, then Rader for primes,
 // else the chirp transform
-fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
-  // The mixed-radix kernel up to 16384 points, else Rader (primes), else the
-  // chirp transform.  (An earlier p * 2^k kernel for n = p * 2^k, p in {3,
-  // 5, 7, 9, 15, 25}, lost to mixed radix on every length it took: 3072 216
-  // against 310 us, 6144 266 against 312, 15360 372 against 392 per 512 MiB.)
-  // Mixed-radix schedules, in order:
-  //  1. radices up to 16, one butterfly per thread (1000: 10 10 10, three
-  //     stages).  Measured against the fixed order of step 2 on MI355X with
-  //     each stage compiled for its radix: better or equal for 1000, 2000,
-  //     2500 (253 against 330 us per 512 MiB), 3000, 3500, 4500, 6000, 8000,
-  //     worse for 4000 and 5000 (325 against 291, 289 against 280 us);
-  //  2. above 8192 points, radices up to 16 with two butterflies per thread;
-  //  3. radices up to 8 in a fixed order, two butterflies per thread;
-  //  4. the fewest radices up to 8, two butterflies per thread (7776: 6^5);
-  //  5. Rader's algorithm, then the chirp transform.
-  if (n <= kMaxMixedLength) {
-    static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
-    static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
-    const std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
-    if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_mixed(n, batch, sign, w, 1);
-    const int rlo2 = (int)((n + 2 * 1024 - 1) / (2 * 1024));
-    // above 8192 points: two butterflies of up to 16 values per thread (one
-    // would need every radix >= n/1024).  Per 512 MiB against the chirp
-    // transform: 10000 1331 -> 313 us, 9000 1440 -> 408, 12000 1133 -> 401,
-    // 16000 954 -> 416; against the p * 2^k kernel it replaced: 9216 444 ->
-    // 414, 10240 445 -> 429, 12288 404 -> 399, 12800 433 -> 394, 14336 399 ->
-    // 370, 15360 392 -> 372
-    if (n > 8192) {
-      const std::vector<int> w2 = mixed_radices(n, wide, rlo2);
-      if (!w2.empty() && (int)w2.size() <= kMixedMaxStages)
-        return create_mixed(n, batch, sign, w2, kMixedButterflies);
-    }
-    for (const std::vector<int>& r : {mixed_radices_fixed(n), mixed_radices(n, narrow, rlo2)}) {
-      if (r.empty() || (int)r.size() > kMixedMaxStages) continue;
-      if (n / *std::min_element(r.begin(), r.end()) <= 1024 * kMixedButterflies)
-        return create_mixed(n, batch, sign, r, kMixedButterflies);
-    }
+// The one-kernel mixed-radix schedule of n <= kMaxMixedLength (kb: butterflies
+// per thread), or an empty list.  In order:
+//  1. radices up to 16, one butterfly per thread (1000: 10 10 10, three
+//     stages).  Measured against the fixed order of step 3 on MI355X with
+//     each stage compiled for its radix: better or equal for 1000, 2000,
+//     2500 (253 against 330 us per 512 MiB), 3000, 3500, 4500, 6000, 8000,
+//     worse for 4000 and 5000 (325 against 291, 289 against 280 us);
+//  2. above 8192 points, radices up to 16 with two butterflies per thread
+//     (one would need every radix >= n/1024).  Per 512 MiB against the chirp
+//     transform: 10000 1331 -> 313 us, 9000 1440 -> 408, 12000 1133 -> 401,
+//     16000 954 -> 416; against the p * 2^k kernel it replaced: 9216 444 ->
+//     414, 10240 445 -> 429, 12288 404 -> 399, 12800 433 -> 394, 14336 399 ->
+//     370, 15360 392 -> 372;
+//  3. radices up to 8 in a fixed order, two butterflies per thread;
+//  4. the fewest radices up to 8, two butterflies per thread (7776: 6^5).
+std::vector<int> one_kernel_schedule(int64_t n, int* kb) {
+  static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
+  static const std::vector<int> narrow = {8, 7, 6, 5, 4, 3, 2};
+  if (n < 2 || n > kMaxMixedLength) return {};
+  std::vector<int> w = mixed_radices(n, wide, (int)((n + 1023) / 1024));
+  if (!w.empty() && (int)w.size() <= kMixedMaxStages) return *kb = 1, w;
+  const int rlo2 = (int)((n + 2 * 1024 - 1) / (2 * 1024));
+  if (n > 8192) {
+    w = mixed_radices(n, wide, rlo2);
+    if (!w.empty() && (int)w.size() <= kMixedMaxStages) return *kb = kMixedButterflies, w;
   }
+  for (const std::vector<int>& r : {mixed_radices_fixed(n), mixed_radices(n, narrow, rlo2)}) {
+    if (r.empty() || (int)r.size() > kMixedMaxStages) continue;
+    if (n / *std::min_element(r.begin(), r.end()) <= 1024 * kMixedButterflies) return *kb = kMixedButterflies, r;
+  }
+  return {};
+}
+
+bool smooth13(int64_t n) {
+  for (int p : {2, 3, 5, 7, 11, 13})
+    while (n % p == 0) n /= p;
+  return n == 1;
+}
+
+// C2C of a length with no prime factor above 13 and no one-kernel schedule
+// (above 16384 points, and a few below: 15625 = 5^6, 6561 = 3^8), as a
+// four-step split n = n1 * n2 (the decomposition the ctsai page names for
+// transforms that do not fit on chip, with mixed-radix factors): n2 <= 1024
+// (16 columns of a tile fit the LDS) with the one-butterfly schedule, n1 a
+// power of two up to 16384 or a one-kernel length, n2 closest to sqrt(n).
+// Returns nullptr with *split false when no split exists.
+fft_plan* create_fourstep_any(int64_t n, int64_t batch, int sign, bool* split) {
+  *split = false;
+  if (n < 4 || n > kMaxBluesteinLengthLarge || !smooth13(n)) return nullptr;
+  int64_t best = 0;
+  double bestd = 1e300;
+  std::vector<int> w2best;
+  for (int64_t n2 = 2; n2 <= 1024 && n2 < n; ++n2) {
+    if (n % n2) continue;
+    const int64_t n1 = n / n2;
+    int kb1 = 0, kb2 = 0;
+    if (n1 < 2 || n1 > kMaxMixedLength || (!is_pow2(n1) && one_kernel_schedule(n1, &kb1).empty())) continue;
+    const std::vector<int> w2 = one_kernel_schedule(n2, &kb2);
+    if (w2.empty() || kb2 != 1) continue;
+    const double d = std::fabs(std::log((double)n2) - 0.5 * std::log((double)n));
+    if (d < bestd) bestd = d, best = n2, w2best = w2;
+  }
+  if (!best) return nullptr;
+  *split = true;
+  const int64_t n2 = best, n1 = n / n2;
+  fft_plan* rows = fft_plan_create(n1, batch * n2, FFT_C2C, sign);
+  if (!rows) return nullptr;
+  fft_plan* cols = create_mixed(n2, 1, sign, w2best, 1);
+  if (!cols) {
+    free_plan(rows);
+    return nullptr;
+  }
+  fft_plan* p = new (std::nothrow) fft_plan();
+  if (!p) {
+    free_plan(rows);
+    free_plan(cols);
+    return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
+  }
+  p->n = n;
+  p->nx = n;
+  p->batch = batch;
+  p->kind = FFT_C2C;
+  p->sign = sign;
+  p->fsany = true;
+  p->n1 = (int)n1;
+  p->n2 = (int)n2;
+  p->bits = (ilog2c(n) + 1) / 2;
+  p->inner = rows;
+  p->inner2 = cols;
+  std::vector<float2> thi, tlo;
+  for (int64_t h = 0; h <= ((n - 1) >> p->bits); ++h) thi.push_back(root(h << p->bits, n));
+  for (int64_t l = 0; l < (int64_t(1) << p->bits); ++l) tlo.push_back(root(l, n));
+  if (finish_plan(p, {&thi, &tlo}, {&p->thi, &p->tlo}, (size_t)(n * batch) * sizeof(float2)) != FFT_OK) {
+    free_plan(p);
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
+fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
+  // The mixed-radix kernel up to 16384 points (one_kernel_schedule), else
+  // the mixed-radix four-step, else Rader (primes), else the chirp
+  // transform.  (An earlier p * 2^k kernel for n = p * 2^k, p in {3, 5, 7, 9,
+  // 15, 25}, lost to mixed radix on every length it took: 3072 216 against
+  // 310 us, 6144 266 against 312, 15360 372 against 392 per 512 MiB.)
+  int kb = 0;
+  const std::vector<int> w = one_kernel_schedule(n, &kb);
+  if (!w.empty()) return create_mixed(n, batch, sign, w, kb);
+  bool split = false;
+  fft_plan* q = create_fourstep_any(n, batch, sign, &split);
+  if (split) return q;  // nullptr: its plans failed, the error is set
   // primes up to 16385 whose p - 1 has a schedule: Rader's convolution of
   // length p - 1 in one kernel (1009: two 1008-point transforms instead of
   // the chirp transform's two of 2048)
@@ -724,11 +803,12 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
   return create_bluestein(n, batch, sign);
 }
 
-// R2C/C2R of a length that is not a power of two (3 <= n <= kMaxBluesteinLengthLarge)
+// R2C/C2R of a length that is not a power of two (3 <= n <= kMaxBluesteinLengthLarge),
+// or of a power of two above the one-kernel real rows (n/2 on the four-step path)
 fft_plan* create_real_any(int64_t n, int64_t batch, int kind, int sign) {
   const bool even = n % 2 == 0;
   const int64_t len = even ? n / 2 : n;
-  fft_plan* inner = create_c2c_any(len, batch, sign);
+  fft_plan* inner = is_pow2(len) ? fft_plan_create(len, batch, FFT_C2C, sign) : create_c2c_any(len, batch, sign);
   if (!inner) return nullptr;
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) {
@@ -778,11 +858,14 @@ fft_plan* fft_plan_create(int64_t n, int64_t batch, int kind, int sign) {
     return create_real_any(n, batch, kind, sign);
   }
   if (!is_pow2(n)) return set_err(FFT_ENOTSUP, "n out of range"), nullptr;
-  const int64_t max_len = kind == FFT_C2C ? (int64_t(1) << kFourStepMaxLog) : 2 * (int64_t)kMaxSinglePass;
+  const int64_t max_len = int64_t(1) << (kind == FFT_C2C ? kFourStepMaxLog : kFourStepMaxLog + 1);
   const int64_t min_len = kind == FFT_C2C ? 2 : 4;
   if (n < min_len || n > max_len)
-    return set_err(FFT_ENOTSUP, "n out of range: C2C needs 2 <= n <= 2^28, R2C/C2R 4 <= n <= 32768"),
+    return set_err(FFT_ENOTSUP, "n out of range: C2C needs 2 <= n <= 2^28, R2C/C2R 4 <= n <= 2^29"),
            nullptr;
+  // real rows above one kernel's reach: the four-step transform of n/2
+  // complex values, then the Hermitian unpack (pack first for C2R)
+  if (kind != FFT_C2C && n > 2 * (int64_t)kMaxSinglePass) return create_real_any(n, batch, kind, sign);
 
   fft_plan* p = new (std::nothrow) fft_plan();
   if (!p) return set_err(FFT_ENOMEM, "host allocation failed"), nullptr;
@@ -959,7 +1042,7 @@ int fft_plan_set(fft_plan* p, int option, int64_t value) {
     case FFT_OPT_SHIFT:
       if (value < 0 || value > 2) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT takes 0, 1 or 2");
       if (p->kind != FFT_C2C) return set_err(FFT_EINVAL, "FFT_OPT_SHIFT applies to C2C plans only");
-      if (value && !p->bluestein && !p->mixed && !p->rader && !p->any2d &&
+      if (value && !p->bluestein && !p->mixed && !p->rader && !p->any2d && !p->fsany &&
           ((p->nx & 1) || (p->dims == 2 && (p->ny & 1))))
         return set_err(FFT_EINVAL, "FFT_OPT_SHIFT needs even lengths");
       if (p->any2d) {  // the shift of each axis: in its row plan, or in the column pass
@@ -1053,6 +1136,28 @@ int run_plan(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float
     if (rc == FFT_OK) e = launch_transpose(dst, sc, p->ny, p->nx, p->batch, stream);
     if (rc == FFT_OK && e == hipSuccess) rc = fft_exec(p->inner2, sc, sc, stream_);
     if (rc == FFT_OK && e == hipSuccess) e = launch_transpose(sc, dst, p->nx, p->ny, p->batch, stream);
+    if (rc != FFT_OK) return rc;
+    if (e != hipSuccess) return hip_err(e, "kernel launch");
+    return FFT_OK;
+  }
+  if (p->fsany) {
+    // the n2-point columns (stride n1) times W_n^{j1 k2} into the scratch,
+    // the n1-point rows in place there, then [n2][n1] -> [n1][n2] per row of
+    // the batch, rotated by the shift (bin 0 to index n/2, or back)
+    MixedArgs a = p->inner2->mx;
+    a.in = src;
+    a.out = sc;
+    a.flip = 0;
+    a.pre = nullptr;
+    e = launch_mixed_cols(p->sign, a, MixedColsArgs{p->n1, p->batch, p->thi, p->tlo, p->bits}, stream);
+    int rc = FFT_OK;
+    if (e == hipSuccess) rc = fft_exec(p->inner, sc, sc, stream_);
+    const int64_t h = p->n / 2;
+    const int64_t rot = p->shift == 1 ? h : p->shift == 2 ? (p->n - h) % p->n : 0;
+    for (int64_t b0 = 0; b0 < p->batch && e == hipSuccess && rc == FFT_OK; b0 += 65535) {
+      const int64_t nb = std::min<int64_t>(65535, p->batch - b0);
+      e = launch_transpose(sc + b0 * p->n, dst + b0 * p->n, p->n2, p->n1, nb, stream, rot);
+    }
     if (rc != FFT_OK) return rc;
     if (e != hipSuccess) return hip_err(e, "kernel launch");
     return FFT_OK;

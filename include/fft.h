@@ -18,21 +18,24 @@
  *    section 2.3, names mixed radices and other lengths as the extension of
  *    its radix-2 transforms): lengths up to 16384 with no prime factor above
  *    13 by mixed-radix Stockham stages (radices 2 to 8, 10 to 16) when every
- *    stage has at most 2048 butterflies (one or two per thread); primes
- *    p <= 16385 whose p - 1 has such a schedule by Rader's algorithm (a
- *    cyclic convolution of length p - 1 on those stages, in one kernel);
- *    the others by Bluestein's
- *    chirp transform: two transforms of length m >= 2n - 1 (a power of two,
- *    or a length with a mixed-radix schedule below 1/1.3 of that power of
- *    two when it is 4096 or more and n <= 4096), inside one kernel while
- *    m <= 32768 (n <= 16384), else in three passes (the second
- *    holds the inner factors of both transforms) through a scratch buffer of
- *    2 * batch * m * 8 bytes.
- *  - R2C/C2R lengths: powers of two from 4 to 32768 (one kernel), and any
- *    other length from 3 to 2^22 (fourier.ts refuses these for its FFT; here
- *    an any-length complex transform of n/2 values for even n, with the same
- *    Hermitian pack/unpack as the power-of-two path in separate kernels, or
- *    of n values for odd n, through a plan-owned scratch buffer of
+ *    stage has at most 2048 butterflies (one or two per thread); the other
+ *    lengths with no prime factor above 13 by a four-step split n = n1 * n2
+ *    (n2 <= 1024): n2-point column transforms times the twiddles, n1-point
+ *    row transforms, a transpose (three passes through a scratch buffer of
+ *    batch * n * 8 bytes); primes p <= 16385 whose p - 1 has a one-kernel
+ *    schedule by Rader's algorithm (a cyclic convolution of length p - 1 on
+ *    those stages, in one kernel); the others by Bluestein's chirp
+ *    transform: two transforms of length m >= 2n - 1 (a power of two, or a
+ *    length with a mixed-radix schedule below 1/1.3 of that power of two
+ *    when n <= 4096), inside one kernel while m <= 32768 (n <= 16384), else
+ *    in three passes (the second holds the inner factors of both transforms)
+ *    through a scratch buffer of 2 * batch * m * 8 bytes.
+ *  - R2C/C2R lengths: powers of two from 4 to 32768 (one kernel), powers of
+ *    two from 65536 to 2^29 and any other length from 3 to 2^22 (fourier.ts
+ *    refuses the latter for its FFT; here a complex transform of n/2 values
+ *    for even n (the four-step transform for powers of two), with the same
+ *    Hermitian pack/unpack as the one-kernel path in separate kernels, or of
+ *    n values for odd n, through a plan-owned scratch buffer of
  *    batch * n * 4 bytes (even n) or 2 * batch * n * 8 bytes (odd n)).
  *  - 2D sizes: powers of two from 2 to 16384 (row pass, then column pass),
  *    or any sizes from 2 to 2^22 (at most 65535 images): row transforms,
@@ -141,7 +144,7 @@ enum fft_option {
 /*
  * Create a plan for `batch` transforms of length n.
  * n: C2C: a power of two 2 <= n <= 2^28, or any 3 <= n <= 2^22; R2C/C2R: a
- * power of two 4 <= n <= 32768, or any 3 <= n <= 2^22; the direct kinds: any
+ * power of two 4 <= n <= 2^29, or any 3 <= n <= 2^22; the direct kinds: any
  * 2 <= n <= 16384.
  * batch >= 1.
  * kind: enum fft_kind.  sign: FFT_FORWARD or FFT_INVERSE (FFT_FORWARD for the

@@ -55,7 +55,7 @@ def err_of(fn, *args):
     ((1, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),         # too short
     ((2, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),         # real transforms need n >= 4
     ((1 << 29, 1, F.FFT_C2C, -1), F.FFT_ENOTSUP),   # beyond the four-step range
-    ((1 << 16, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),   # real transforms are single-pass
+    ((1 << 30, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),   # real powers of two end at 2^29
     ((1 << 40, 1 << 40, F.FFT_C2C, -1), F.FFT_EINVAL),  # size overflow
     (((1 << 22) + 2, 1, F.FFT_R2C, -1), F.FFT_ENOTSUP),  # R2C beyond 2^22 that is not a power of two
     ((1, 1, F.FFT_R2C_DIRECT, -1), F.FFT_ENOTSUP),  # direct kinds: 2 <= n <= 16384

@@ -1,10 +1,11 @@
 """GPU parity for C2C lengths that are not powers of two, against the
 oracle's DFT by the definition: mixed-radix Stockham stages (radices 2..8,
 10..16) for the lengths up to 16384 with no prime factor above 13 and a
-schedule, Rader's convolution of length p - 1 on those stages for primes p
-up to 16385 whose p - 1 has a schedule, Bluestein's chirp transform for the rest (on a
-mixed-radix convolution length where that is much shorter than the power of
-two).
+schedule, the four-step over two such lengths for the other lengths with no
+prime factor above 13, Rader's convolution of length p - 1 on those stages
+for primes p up to 16385 whose p - 1 has a schedule, Bluestein's chirp
+transform for the rest (on a mixed-radix convolution length where that is
+much shorter than the power of two).
 
 Tolerance: relative L2 error <= 1e-5 over the whole output of a case.
 """
@@ -253,6 +254,52 @@ def test_any_length_large_sampled_bins(n):
     assert e <= 1e-5
 
 
+# --------------------------------------------------------------------------
+# lengths with no prime factor above 13 that no one-kernel schedule takes
+# (above 16384, and 6561 = 3^8, 15625 = 5^6): the four-step n = n1 * n2,
+# n2 <= 1024 closest to sqrt(n) (mixed-radix column tiles times the
+# twiddle, the row plan of n1, a transpose that also applies the shift;
+# 6561 = 81 x 81, 15625 = 125 x 125, 24576 has a power-of-two factor)
+# --------------------------------------------------------------------------
+FOURSTEP_ANY = [6561, 15625, 16896, 20000, 24576, 30000]
+
+
+@pytest.mark.parametrize("n", FOURSTEP_ANY)
+@pytest.mark.parametrize("sign", [-1, 1])
+def test_fourstep_any_full(n, sign):
+    for batch in (1, 2):
+        say(f"four-step (mixed radix) c2c n={n} batch={batch} sign={sign}")
+        x = W.uniform_c64((batch, n), np.random.default_rng(n * 7 + batch))
+        assert rel_l2(c2c(x, sign), oracle.dft(x, sign)) <= TOL, (n, batch)
+
+
+@pytest.mark.parametrize("n,shift", [(6561, 1), (6561, 2), (20000, 1), (24576, 2), (15625, 1)])
+def test_fourstep_any_shift_and_in_place(n, shift):
+    say(f"four-step (mixed radix) shift={shift} n={n}, in place")
+    x = W.uniform_c64((2, n), np.random.default_rng(n + shift + 11))
+    idx = oracle.fftshift_index(n) if shift == 1 else oracle.ifftshift_index(n)
+    want = oracle.dft(x, -1)[:, idx]
+    assert rel_l2(c2c(x, -1, shift=shift, inplace=True), want) <= TOL
+
+
+@pytest.mark.parametrize("n", [49152, 1000000, 3 << 20])
+def test_fourstep_any_large_sampled_bins(n):
+    """Longer smooth rows: 64 sampled bins of every row by the definition,
+    the round trip and Parseval over every value."""
+    batch = 2
+    say(f"four-step (mixed radix) n={n} batch={batch}")
+    x = W.uniform_c64((batch, n), np.random.default_rng(n % 1000 + 9))
+    y = c2c(x, -1)
+    bins = np.unique(np.concatenate([[0, 1, n // 2, n - 1],
+                                     np.random.default_rng(8).integers(0, n, 60)]))
+    for r in range(batch):
+        assert rel_l2(y[r, bins], oracle.dft_bins(x[r], bins, -1)) <= TOL
+    assert rel_l2(c2c(y, +1) / n, x) <= TOL
+    e = np.abs(np.sum(np.abs(y.astype(np.complex128)) ** 2) /
+               (n * np.sum(np.abs(x.astype(np.complex128)) ** 2)) - 1)
+    assert e <= 1e-5
+
+
 @pytest.mark.parametrize("n,shift", [(10001, 1), (10001, 2), (16000, 1), (20011, 1), (20011, 2)])
 def test_any_length_large_shift_and_in_place(n, shift):
     say(f"any-length (chirp) shift={shift} n={n}, in place")
@@ -284,6 +331,22 @@ def test_real_any_length_sweep(n):
         Sin = np.ascontiguousarray(S.T) if mmajor else S
         xg = c2r(Sin, n, batch, m, mmajor)
         assert rel_l2(xg, oracle.c2r(S, n, m)) <= TOL, (n, batch, m)
+
+
+@pytest.mark.parametrize("n", [1 << 16, 1 << 20, 1 << 22])
+def test_real_pow2_four_step(n):
+    """Real rows of a power of two above one kernel's reach (32768): the
+    four-step transform of n/2 complex values between the same pack/unpack
+    kernels; full and cut band, both spectrum layouts, both directions."""
+    g = np.random.default_rng(n % 1000 + 3)
+    for batch, mmax, mmajor in ((2, n // 2, False), (3, n // 5, True)):
+        say(f"pow2 r2c/c2r (four-step) n={n} batch={batch} mmax={mmax} mmajor={mmajor}")
+        x = g.uniform(-1, 1, size=(batch, n)).astype(np.float32)
+        Fg = r2c(x, mmax, mmajor)
+        assert rel_l2(Fg.T if mmajor else Fg, oracle.r2c(x, mmax)) <= TOL, (n, batch, mmax)
+        S = (g.normal(size=(batch, mmax + 1)) + 1j * g.normal(size=(batch, mmax + 1))).astype(np.complex64)
+        Sin = np.ascontiguousarray(S.T) if mmajor else S
+        assert rel_l2(c2r(Sin, n, batch, mmax, mmajor), oracle.c2r(S, n, mmax)) <= TOL, (n, batch, mmax)
 
 
 def test_real_any_length_options():
