@@ -697,10 +697,15 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// 16 columns (128 B runs) while they take at most 80 KiB of LDS (two
+// workgroups per CU), else 8 (64 B runs): one 16-column workgroup per CU was
+// slower (per 512 MiB: 2D 1000 x 1000 575 against 544 us, 720 x 720 616
+// against 564, 640 x 480 590 against 516; the four-step of 10^6 883 against
+// 839; 4 * 10^6 992 against 1029 the exception)
 int mixed_cols_tile(const MixedArgs& a) {
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
-  for (int ct : {16, 8})
-    if ((size_t)ct * pitch * sizeof(float2) <= (size_t)kLdsBudgetBytes) return ct;
+  if (16 * pitch * sizeof(float2) <= 81920) return 16;
+  if (8 * pitch * sizeof(float2) <= (size_t)kLdsBudgetBytes) return 8;
   return 0;
 }
 

@@ -207,8 +207,8 @@ struct MixedColsArgs {
   const float2* tlo;
   int bits;
 };
-// columns per workgroup (16 or 8, the most that fit the LDS), or 0 when not
-// even 8 fit (the caller then transposes instead)
+// columns per workgroup (16 while they take at most 80 KiB of LDS, else 8),
+// or 0 when not even 8 fit (the caller then transposes instead)
 int mixed_cols_tile(const MixedArgs& a);
 hipError_t launch_mixed_cols(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t stream);
 
