@@ -544,7 +544,9 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
 // 360 494 against 652 us, 125 x 160 460 against 595, 12 x 4096 369 against
 // 473; the four-step of 20000 794 against 965, 6561 997 against 1279
 constexpr int kColBatch = 8;
-template <int S, int KB, int RMAX, bool PAD>
+// TROWS: the tile is CT consecutive rows (contiguous, read in order) whose
+// transforms are stored transposed (launch_mixed_rows_t).
+template <int S, int KB, int RMAX, bool PAD, bool TROWS = false>
 __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -559,8 +561,30 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
   const int64_t g = (int64_t)blockIdx.x * CT + col;
   const bool has_col = g < c.images * c.nx;
   const int64_t img = g / c.nx;
-  const float2* src = a.in + img * (int64_t)n * c.nx + (g - img * c.nx);
   float2* L0 = smem + col * pitch;
+  if constexpr (TROWS) {
+    // rows g0 .. g0 + CT - 1, one contiguous block: element e is entry e % n
+    // of line e / n
+    const int64_t g0 = (int64_t)blockIdx.x * CT, left = c.images * c.nx - g0;
+    const uint32_t nblk = (uint32_t)(left < (int64_t)CT ? left : (int64_t)CT) * n;
+    const uint32_t magic = 0xffffffffu / n + 1u;  // e / n for e < 2^32 / n
+    const float2* blk = a.in + g0 * n;
+    for (uint32_t e0 = tid; e0 < nblk; e0 += kColBatch * nt) {
+      float2 v[kColBatch];
+#pragma unroll
+      for (int i = 0; i < kColBatch; ++i)
+        if (e0 + i * nt < nblk) v[i] = gload_nt(blk, e0 + i * nt);
+#pragma unroll
+      for (int i = 0; i < kColBatch; ++i) {
+        const uint32_t e = e0 + i * nt;
+        if (e < nblk) {
+          const uint32_t q = __umulhi(e, magic);
+          smem[q * pitch + mixed_pad<PAD>(e - q * n)] = v[i];
+        }
+      }
+    }
+  } else {
+  const float2* src = a.in + img * (int64_t)n * c.nx + (g - img * c.nx);
   for (uint32_t r0 = tid / CT; r0 < n; r0 += kColBatch * RS) {
     float2 v[kColBatch];
 #pragma unroll
@@ -579,6 +603,7 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
       if (r < n) L0[mixed_pad<PAD>(r)] = v[i];
     }
   }
+  }
   lds_barrier();
   const uint32_t G = nt / tpl;  // lines per group
   for (uint32_t l0 = 0; l0 < CT; l0 += G) {
@@ -588,7 +613,27 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
     mixed_stages<S, KB, RMAX, PAD, 3>(a, active ? tid % tpl : 0x40000000u, tpl, active, nullptr, nullptr,
                                       smem + (active ? line : 0u) * pitch);
   }
-  if (has_col && c.thi) {
+  if constexpr (TROWS) {
+    // line col is row k2 = g - img * nx of image img; entry k1 goes to
+    // (k1 * nx + k2 + rot) mod (n * nx): the CT lines of one k1 are a run
+    // Streaming stores where a run is whole 128 B lines; ordinary ones where
+    // runs straddle lines (nx not a multiple of 16), so that the L2 merges
+    // the halves two workgroups write (n = 20000, runs 1000 B apart: 854 ->
+    // 696 us per 512 MiB; aligned runs 1-5 % slower that way)
+    if (has_col) {
+      const uint32_t k2 = (uint32_t)(g - img * c.nx), nx = (uint32_t)c.nx, len = n * nx;
+      const bool whole = CT == 16 && nx % 16 == 0;
+      float2* dst = a.out + img * (int64_t)len;
+      for (uint32_t k1 = tid / CT; k1 < n; k1 += RS) {
+        uint32_t e = k1 * nx + k2 + (uint32_t)c.rot;
+        if (e >= len) e -= len;
+        if (whole)
+          gstore_nt(dst, e, L0[mixed_pad<PAD>(k1)]);
+        else
+          gstore(dst, e, L0[mixed_pad<PAD>(k1)]);
+      }
+    }
+  } else if (has_col && c.thi) {
     // the four-step's W^{x k}: kColBatch pairs of table loads in flight
     // before their stores
     float2* dst = a.out + img * (int64_t)n * c.nx + (g - img * c.nx);
@@ -709,7 +754,9 @@ int mixed_cols_tile(const MixedArgs& a) {
   return 0;
 }
 
-hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs& c, hipStream_t st) {
+namespace {
+template <bool TROWS>
+hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, hipStream_t st) {
   int rmax = 0;
   MixedArgs a = a0;
   a.rows = 1;
@@ -737,22 +784,32 @@ hipError_t launch_mixed_cols(int sign, const MixedArgs& a0, const MixedColsArgs&
   if (rmax > 8) {
     if (a.pad) {
       if (sign < 0)
-        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS>), grid, block, lds, st, a, c);
       else
-        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS>), grid, block, lds, st, a, c);
     } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS>), grid, block, lds, st, a, c);
     } else {
-      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS>), grid, block, lds, st, a, c);
     }
   } else if (a.pad) {
     return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS>), grid, block, lds, st, a, c);
   } else {
-    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS>), grid, block, lds, st, a, c);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_mixed_cols(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t st) {
+  return launch_tiles<false>(sign, a, c, st);
+}
+
+hipError_t launch_mixed_rows_t(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t st) {
+  if (c.thi || c.rot < 0 || c.rot >= (int64_t)a.n * c.nx || a.in == a.out) return hipErrorInvalidValue;
+  return launch_tiles<true>(sign, a, c, st);
 }
 
 hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st) {

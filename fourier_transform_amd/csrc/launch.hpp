@@ -206,11 +206,20 @@ struct MixedColsArgs {
   const float2* thi;
   const float2* tlo;
   int bits;
+  // launch_mixed_rows_t only: the rotation of the transposed store
+  int64_t rot;
 };
 // columns per workgroup (16 while they take at most 80 KiB of LDS, else 8),
 // or 0 when not even 8 fit (the caller then transposes instead)
 int mixed_cols_tile(const MixedArgs& a);
 hipError_t launch_mixed_cols(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t stream);
+// The same tiles over rows: a.in holds c.images * c.nx contiguous rows of
+// n = a.n values; each image of c.nx rows [c.nx][n] is transformed along
+// its rows and stored transposed, [n][c.nx], rotated by c.rot (0 <= rot <
+// n * nx: element e of an output image goes to (e + rot) mod (n * nx)).
+// The second pass of the four-step of smooth lengths (rows of n1, the
+// output index k1 * n2 + k2).  a.out must not overlap a.in.
+hipError_t launch_mixed_rows_t(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t stream);
 
 // C2C rows of a prime length p by Rader's algorithm ("High Performance
 // Fourier Transforms on GPUs with GLSL", section 2.3, names it beside

@@ -239,6 +239,7 @@ struct fft_plan {
   // the scratch, the n1-point row plan (inner) in place there, and a
   // transpose to natural order that also applies the shift (a rotation)
   bool fsany = false;
+  bool fs2 = false;  // two passes: inner holds the schedule of n1 for row tiles stored transposed
   bool rader = false;  // mx holds the schedule of n - 1
   MixedArgs mx{};
   const float2* rd_conv = nullptr;
@@ -718,29 +719,49 @@ bool smooth13(int64_t n) {
 // (above 16384 points, and a few below: 15625 = 5^6, 6561 = 3^8), as a
 // four-step split n = n1 * n2 (the decomposition the ctsai page names for
 // transforms that do not fit on chip, with mixed-radix factors): n2 <= 1024
-// (16 columns of a tile fit the LDS) with the one-butterfly schedule, n1 a
-// power of two up to 16384 or a one-kernel length, n2 closest to sqrt(n).
-// Returns nullptr with *split false when no split exists.
+// (16 columns of a tile fit the LDS) with the one-butterfly schedule, n2
+// closest to sqrt(n).  Two passes where n1 has a schedule for row tiles of
+// at least 8 rows in LDS (n1 up to about 2540): the column tiles with the
+// twiddle into the scratch, then row tiles stored transposed; else three
+// (n1 a power of two up to 16384 or a one-kernel length): the row plan of
+// n1 in place on the scratch, then the transpose.  Returns nullptr with
+// *split false when no split exists.
+bool tile_schedule(int64_t n, std::vector<int>* w, int* kb) {
+  *w = one_kernel_schedule(n, kb);
+  if (w->empty()) return false;
+  const int rmax = *std::max_element(w->begin(), w->end());
+  if (rmax > 8 && *kb != 1) return false;  // no tile kernel of this shape
+  const bool pad = (*w)[0] == 16 && *kb == 1;
+  const int64_t pitch = (pad ? n + n / 32 : n) + 1;
+  return 8 * pitch * (int64_t)sizeof(float2) <= kLdsBudgetBytes;
+}
+
 fft_plan* create_fourstep_any(int64_t n, int64_t batch, int sign, bool* split) {
   *split = false;
   if (n < 4 || n > kMaxBluesteinLengthLarge || !smooth13(n)) return nullptr;
   int64_t best = 0;
+  bool best2 = false;
   double bestd = 1e300;
-  std::vector<int> w2best;
+  std::vector<int> w2best, w1best;
+  int kb1best = 1;
   for (int64_t n2 = 2; n2 <= 1024 && n2 < n; ++n2) {
     if (n % n2) continue;
     const int64_t n1 = n / n2;
     int kb1 = 0, kb2 = 0;
-    if (n1 < 2 || n1 > kMaxMixedLength || (!is_pow2(n1) && one_kernel_schedule(n1, &kb1).empty())) continue;
+    std::vector<int> w1;
+    const bool two = n1 >= 2 && n1 <= kMaxMixedLength && tile_schedule(n1, &w1, &kb1);
+    if (!two && (n1 < 2 || n1 > kMaxMixedLength || (!is_pow2(n1) && one_kernel_schedule(n1, &kb1).empty())))
+      continue;
     const std::vector<int> w2 = one_kernel_schedule(n2, &kb2);
     if (w2.empty() || kb2 != 1) continue;
     const double d = std::fabs(std::log((double)n2) - 0.5 * std::log((double)n));
-    if (d < bestd) bestd = d, best = n2, w2best = w2;
+    if ((two && !best2) || (two == best2 && d < bestd))
+      bestd = d, best = n2, best2 = two, w2best = w2, w1best = w1, kb1best = kb1;
   }
   if (!best) return nullptr;
   *split = true;
   const int64_t n2 = best, n1 = n / n2;
-  fft_plan* rows = fft_plan_create(n1, batch * n2, FFT_C2C, sign);
+  fft_plan* rows = best2 ? create_mixed(n1, 1, sign, w1best, kb1best) : fft_plan_create(n1, batch * n2, FFT_C2C, sign);
   if (!rows) return nullptr;
   fft_plan* cols = create_mixed(n2, 1, sign, w2best, 1);
   if (!cols) {
@@ -759,6 +780,7 @@ fft_plan* create_fourstep_any(int64_t n, int64_t batch, int sign, bool* split) {
   p->kind = FFT_C2C;
   p->sign = sign;
   p->fsany = true;
+  p->fs2 = best2;
   p->n1 = (int)n1;
   p->n2 = (int)n2;
   p->bits = (ilog2c(n) + 1) / 2;
@@ -1149,11 +1171,22 @@ int run_plan(fft_plan* p, const void* in, void* out, fft_stream_t stream_, float
     a.out = sc;
     a.flip = 0;
     a.pre = nullptr;
-    e = launch_mixed_cols(p->sign, a, MixedColsArgs{p->n1, p->batch, p->thi, p->tlo, p->bits}, stream);
-    int rc = FFT_OK;
-    if (e == hipSuccess) rc = fft_exec(p->inner, sc, sc, stream_);
+    e = launch_mixed_cols(p->sign, a, MixedColsArgs{p->n1, p->batch, p->thi, p->tlo, p->bits, 0}, stream);
     const int64_t h = p->n / 2;
     const int64_t rot = p->shift == 1 ? h : p->shift == 2 ? (p->n - h) % p->n : 0;
+    if (p->fs2) {  // row tiles of n1 stored transposed straight to out
+      MixedArgs r = p->inner->mx;
+      r.in = sc;
+      r.out = dst;
+      r.flip = 0;
+      r.pre = nullptr;
+      if (e == hipSuccess)
+        e = launch_mixed_rows_t(p->sign, r, MixedColsArgs{p->n2, p->batch, nullptr, nullptr, 0, rot}, stream);
+      if (e != hipSuccess) return hip_err(e, "kernel launch");
+      return FFT_OK;
+    }
+    int rc = FFT_OK;
+    if (e == hipSuccess) rc = fft_exec(p->inner, sc, sc, stream_);
     for (int64_t b0 = 0; b0 < p->batch && e == hipSuccess && rc == FFT_OK; b0 += 65535) {
       const int64_t nb = std::min<int64_t>(65535, p->batch - b0);
       e = launch_transpose(sc + b0 * p->n, dst + b0 * p->n, p->n2, p->n1, nb, stream, rot);

@@ -257,9 +257,10 @@ def test_any_length_large_sampled_bins(n):
 # --------------------------------------------------------------------------
 # lengths with no prime factor above 13 that no one-kernel schedule takes
 # (above 16384, and 6561 = 3^8, 15625 = 5^6): the four-step n = n1 * n2,
-# n2 <= 1024 closest to sqrt(n) (mixed-radix column tiles times the
-# twiddle, the row plan of n1, a transpose that also applies the shift;
-# 6561 = 81 x 81, 15625 = 125 x 125, 24576 has a power-of-two factor)
+# n2 <= 1024 closest to sqrt(n): mixed-radix column tiles times the
+# twiddle, then row tiles of n1 stored transposed (n1 up to about 2540), or
+# else the row plan of n1 and a transpose (3 * 2^20 = 3072 x 1024); the
+# shift is a rotation of the output index in the last pass
 # --------------------------------------------------------------------------
 FOURSTEP_ANY = [6561, 15625, 16896, 20000, 24576, 30000]
 
