@@ -374,7 +374,10 @@ SIZES_2D = [(3, 5, 2), (6, 10, 3), (100, 64, 2), (64, 100, 2), (360, 180, 1), (1
             # column pass in place: power-of-two ny (16 and 8 columns per tile), mixed-radix ny (16 and 8,
             # one and two butterflies per thread, odd), then the transposing fallback (8192, 6000)
             (1024, 100, 2), (2048, 60, 1), (4096, 12, 1), (1000, 64, 1), (2000, 30, 1), (7776, 7, 1),
-            (105, 64, 2), (64, 1000, 3), (8192, 20, 1), (6000, 20, 1)]
+            (105, 64, 2), (64, 1000, 3), (8192, 20, 1), (6000, 20, 1),
+            # an axis on the four-step of smooth lengths (rows of 20000; columns of 20000 through
+            # the transposes)
+            (6, 20000, 1), (20000, 6, 1)]
 
 
 @pytest.mark.parametrize("ny,nx,batch", SIZES_2D)
@@ -386,7 +389,7 @@ def test_2d_any_size(ny, nx, batch, sign):
 
 
 @pytest.mark.parametrize("ny,nx", [(3, 5), (7, 8), (100, 99), (64, 100), (1024, 30), (1000, 64), (105, 60),
-                                   (2000, 30)])
+                                   (2000, 30), (6, 20000)])
 @pytest.mark.parametrize("shift", [1, 2])
 def test_2d_any_size_shift_and_in_place(ny, nx, shift):
     say(f"2D any size {ny}x{nx} shift={shift}, in place")

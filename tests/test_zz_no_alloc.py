@@ -75,9 +75,10 @@ def test_noalloc_two_calls_second_smaller():
 
 
 def test_noalloc_chirp_and_single_pass():
-    """The three-pass chirp transform (two scratch buffers) and a plan
-    without scratch, one after the other."""
-    for n, batch in ((20011, 3), (4096, 64)):
+    """The three-pass chirp transform (two scratch buffers), the four-step of
+    a smooth length (two passes through the scratch) and a plan without
+    scratch, one after the other."""
+    for n, batch in ((20011, 3), (20000, 3), (4096, 64)):
         say(f"noalloc: c2c n={n} batch={batch}")
         x = W.uniform_c64((batch, n), np.random.default_rng(n))
         p = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
@@ -87,6 +88,28 @@ def test_noalloc_chirp_and_single_pass():
             F.fft_plan_destroy(p)
         assert rel_l2(b, a) <= TOL
         assert rel_l2(b, oracle.dft(x, -1) if n & (n - 1) else oracle.c2c(x, -1)) <= TOL
+
+
+def test_noalloc_smooth_three_pass():
+    """The four-step of a smooth length whose row factor is too long for row
+    tiles (3 * 2^20 = 3072 x 1024: the row plan of 3072 and a transpose),
+    shifted: the static scratch against fft_exec, and sampled bins of the
+    definition."""
+    n, batch = 3 << 20, 2
+    say(f"noalloc: smooth four-step n={n} batch={batch} shift")
+    x = W.uniform_c64((batch, n), np.random.default_rng(n % 997))
+    p = F.fft_plan_create(n, batch, F.FFT_C2C, F.FFT_FORWARD)
+    try:
+        F.fft_plan_set(p, F.FFT_OPT_SHIFT, 1)
+        a, b = _both(p, x)
+    finally:
+        F.fft_plan_destroy(p)
+    assert rel_l2(b, a) <= TOL
+    bins = np.unique(np.random.default_rng(5).integers(0, n, 48))
+    idx = oracle.fftshift_index(n)
+    for r in range(batch):
+        # output index i holds bin idx[i]
+        assert rel_l2(b[r, bins], oracle.dft_bins(x[r], idx[bins], -1)) <= TOL
 
 
 def test_noalloc_refuses_oversized_scratch():
