@@ -814,12 +814,12 @@ fft_plan* create_c2c_any(int64_t n, int64_t batch, int sign) {
   // the chirp transform's two of 2048)
   if (n <= kMaxMixedLength + 1 && is_prime(n)) {
     static const std::vector<int> wide = {16, 15, 14, 13, 12, 11, 10, 8, 7, 6, 5, 4, 3, 2};
-    const std::vector<int> w = mixed_radices(n - 1, wide, (int)((n - 1 + 1023) / 1024));
-    if (!w.empty() && (int)w.size() <= kMixedMaxStages) return create_rader(n, batch, sign, w);
+    const std::vector<int> wr = mixed_radices(n - 1, wide, (int)((n - 1 + 1023) / 1024));
+    if (!wr.empty() && (int)wr.size() <= kMixedMaxStages) return create_rader(n, batch, sign, wr);
     if (n - 1 > 8192) {  // two butterflies per thread, as for the mixed-radix lengths above 8192
-      const std::vector<int> w2 = mixed_radices(n - 1, wide, (int)((n - 1 + 2047) / 2048));
-      if (!w2.empty() && (int)w2.size() <= kMixedMaxStages)
-        return create_rader(n, batch, sign, w2, kMixedButterflies);
+      const std::vector<int> wr2 = mixed_radices(n - 1, wide, (int)((n - 1 + 2047) / 2048));
+      if (!wr2.empty() && (int)wr2.size() <= kMixedMaxStages)
+        return create_rader(n, batch, sign, wr2, kMixedButterflies);
     }
   }
   return create_bluestein(n, batch, sign);
