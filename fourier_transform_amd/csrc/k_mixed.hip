@@ -743,13 +743,18 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
 }
 
 // 16 columns (128 B runs) while they take at most 80 KiB of LDS (two
-// workgroups per CU), else 8 (64 B runs): one 16-column workgroup per CU was
-// slower (per 512 MiB: 2D 1000 x 1000 575 against 544 us, 720 x 720 616
-// against 564, 640 x 480 590 against 516; the four-step of 10^6 883 against
-// 839; 4 * 10^6 992 against 1029 the exception)
+// workgroups per CU) and 16 lines need at most 384 threads, else 8 (64 B
+// runs).  One 16-column workgroup per CU was slower (per 512 MiB: 2D 1000 x
+// 1000 575 against 544 us, 720 x 720 616 against 564, 640 x 480 590 against
+// 516; the four-step of 10^6 883 against 839; 4 * 10^6 992 against 1029 the
+// exception), and so were workgroups of more than 384 threads (2D 360 x 360,
+// 60 threads per line: 501 against 470 us; 200 x 300 573 against 554; the
+// four-step of 6561 876 against 812, of 100000 894 against 799), while
+// 8-column tiles of short lines lost (24576, 16 threads per line: 617
+// against 448 us; 2D 12 x 4096 519 against 365)
 int mixed_cols_tile(const MixedArgs& a) {
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
-  if (16 * pitch * sizeof(float2) <= 81920) return 16;
+  if (16 * pitch * sizeof(float2) <= 81920 && 16 * a.tpl <= 384) return 16;
   if (8 * pitch * sizeof(float2) <= (size_t)kLdsBudgetBytes) return 8;
   return 0;
 }

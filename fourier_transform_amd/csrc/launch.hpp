@@ -209,8 +209,9 @@ struct MixedColsArgs {
   // launch_mixed_rows_t only: the rotation of the transposed store
   int64_t rot;
 };
-// columns per workgroup (16 while they take at most 80 KiB of LDS, else 8),
-// or 0 when not even 8 fit (the caller then transposes instead)
+// columns per workgroup (16 while they take at most 80 KiB of LDS and 16
+// lines at most 384 threads, else 8), or 0 when not even 8 fit (the caller
+// then transposes instead)
 int mixed_cols_tile(const MixedArgs& a);
 hipError_t launch_mixed_cols(int sign, const MixedArgs& a, const MixedColsArgs& c, hipStream_t stream);
 // The same tiles over rows: a.in holds c.images * c.nx contiguous rows of
