@@ -582,7 +582,8 @@ constexpr bool fs_cols_persistent() {
   return !HOOK && tile_e(N2, false) == kSplitValues;
 }
 template <int N2, int S, int BK, bool HOOK>
-__global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false))) void k_fs_cols(FourStepArgs a) {
+__global__ __launch_bounds__(tile_lines(N2, false) * (N2 / tile_e(N2, false)))
+__attribute__((amdgpu_waves_per_eu(fs_waves(N2)))) void k_fs_cols(FourStepArgs a) {
   constexpr int E = tile_e(N2, false);
   constexpr bool SPLIT = tile_split(N2, false);
   constexpr int C = tile_lines(N2, false);
@@ -767,7 +768,8 @@ constexpr bool fs_rows_persistent() {
   return tile_e(N1, true) == kSplitValues;
 }
 template <int N1, int S, int BC>
-__global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true))) void k_fs_rows(FourStepArgs a) {
+__global__ __launch_bounds__(tile_lines(N1, true) * (N1 / tile_e(N1, true)))
+__attribute__((amdgpu_waves_per_eu(fs_waves(N1)))) void k_fs_rows(FourStepArgs a) {
   constexpr int E = tile_e(N1, true);
   constexpr bool SPLIT = tile_split(N1, true);
   constexpr int C = tile_lines(N1, true);

@@ -55,11 +55,23 @@ constexpr int tile_c(int n, int e, bool split, bool rowlanes) {
   while (c > 1 && !tile_fits(n, e, c, split, rowlanes)) c /= 2;
   return c;
 }
+// 1024-point tiles take 32 values per thread and the split exchange (512
+// threads, 78 KiB of LDS, two workgroups per CU once the kernels keep to 128
+// VGPRs) instead of 16 values and the complex exchange (1024 threads, 130
+// KiB, one workgroup per CU).  Per 512 MiB: the four-step of 2^20 488 ->
+// 393 us, 2^19 402 -> 366, 2^21 445 -> 415; 2D 1024 x 1024 438 -> 420.
+constexpr int kTile1024Values = 32;
 constexpr bool tile_split(int n, bool rowlanes) {
-  return n >= 2 * kSplitValues &&
-         tile_c(n, kSplitValues, true, rowlanes) > tile_c(n, sched_e(n), false, rowlanes);
+  return n == 1024 || (n >= 2 * kSplitValues &&
+                       tile_c(n, kSplitValues, true, rowlanes) > tile_c(n, sched_e(n), false, rowlanes));
 }
-constexpr int tile_e(int n, bool rowlanes) { return tile_split(n, rowlanes) ? kSplitValues : sched_e(n); }
+constexpr int tile_e(int n, bool rowlanes) {
+  return n == 1024 ? kTile1024Values : tile_split(n, rowlanes) ? kSplitValues : sched_e(n);
+}
+// waves per SIMD the four-step tile kernels ask the compiler for: 4 (128
+// VGPRs, 8-16 B of spills) for the 1024-point tiles, so that two 512-thread
+// workgroups share a CU; no bound otherwise
+constexpr int fs_waves(int n) { return n == 1024 ? 4 : 1; }
 constexpr int tile_lines(int n, bool rowlanes) {
   return tile_c(n, tile_e(n, rowlanes), tile_split(n, rowlanes), rowlanes);
 }
