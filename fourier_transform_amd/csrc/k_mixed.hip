@@ -827,10 +827,13 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
   const size_t lds = (size_t)a.lines * rader_line((uint32_t)a.n, a.pad != 0) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  // short lines: block IO through LDS, as in k_mixed.  Per 512 MiB: p = 5
-  // 906 -> 170 us, 13 2962 -> 175, 17 4158 -> 318, 37 862 -> 326, 97 510 ->
-  // 335, 257 720 -> 405, 641 481 -> 398 (1009: 144 threads, unstaged)
-  const bool stg = a.tpl < 128 && rd.p <= 4096;
+  // block IO through LDS, as k_mixed does for short lines, here for every
+  // p <= 4096 (the bound of its exact division).  Per 512 MiB: p = 5 906 ->
+  // 170 us, 13 2962 -> 175, 17 4158 -> 318, 37 862 -> 326, 97 510 -> 335,
+  // 257 720 -> 405, 641 481 -> 398; and with longer lines too, unlike
+  // k_mixed: 1009 (144 threads per line) 600 -> 494, 2017 523 -> 459, 2593
+  // 615 -> 537, 3001 747 -> 678, 4001 730 -> 701
+  const bool stg = rd.p <= 4096;
   if (a.kb == 2)  // p - 1 above 8192: two butterflies of up to 16 values per thread
     FFTAMD_LAUNCH((k_rader<2, 16, false, false>), dim3(grid), block, lds, st, a, rd);
   else if (a.pad && stg)
@@ -855,7 +858,10 @@ hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, h
       (size_t)a.lines * ((a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1) * sizeof(float2);
   if (lds > (size_t)kLdsBudgetBytes) return hipErrorInvalidValue;
   const dim3 block((uint32_t)(a.tpl * a.lines));
-  const bool stg = a.tpl < 128 && c.n <= 4096;  // short lines: block IO through LDS, as in k_mixed
+  // block IO through LDS for every row (n <= 4096 here): per 512 MiB 1034
+  // 851 -> 755 us, 1049 816 -> 658, 2053 1119 -> 1049, 2111 1013 -> 972
+  // beside the short-line gains (34 797 -> 473 with the mixed length)
+  const bool stg = c.n <= 4096;
   if (a.pad && stg)
     FFTAMD_LAUNCH((k_bluestein_mixed<true, true>), dim3(grid), block, lds, st, a, c);
   else if (a.pad)
