@@ -692,8 +692,12 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   // butterfly's direct loads are runs of m[0] elements, as short as one.
   // Per 512 MiB: n = 3 261 -> 166 us, 6 1124 -> 171, 12 2799 -> 174, 15 3566
   // -> 228, 24 383 -> 183, 48 267 -> 173, 100 300 -> 187, 360 233 -> 207,
-  // 1000 232 -> 225; 1296 (216 threads) was 2 % slower staged.
-  if (a.tpl < 128 && a.n <= 4096) {  // n <= 4096: two butterflies only with radices up to 8
+  // 1000 232 -> 225.  So do one-butterfly lines of 800 threads and more (one
+  // line per workgroup): 4000 416 -> 382, 4500 459 -> 359, 5000 380 -> 293,
+  // 6000 361 -> 281, 7000 339 -> 272, 8000 329 -> 263.  Lines of 128 to 768
+  // threads were 3-15 % slower staged (1296, 2000, 2187, 3000, 3125, 3500,
+  // 4200, 4320, 5120, 6144), and so were two-butterfly lines (7200, 7776).
+  if (a.n <= 8192 && (a.tpl < 128 || (a.tpl >= 800 && a.kb == 1))) {
     if (rmax > 8) {
       if (a.pad) {
         if (sign < 0)

@@ -54,7 +54,7 @@ C2C_CASES = [
     # mixed radix (one butterfly of <= 16, two of <= 8, two of <= 16 above 8192), Rader,
     # chirp (one kernel on a power of two up to 16384 and at 32768, one on a mixed-radix
     # length, three passes)
-    (1000, 9), (360, 11), (12, 700), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (17, 600), (1019, 4), (34, 300),
+    (1000, 9), (360, 11), (12, 700), (6000, 3), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (17, 600), (1019, 4), (34, 300),
     (10001, 2), (1034, 3), (20011, 2), (20000, 2),
 ]
 
