@@ -14,14 +14,21 @@ template <bool SPLIT>
 using lds_elem_t = typename std::conditional<SPLIT, float, float2>::type;
 
 // Real transforms: whole rows, the largest rows-per-workgroup count (8 where
-// a line is short) that fits the thread and LDS limits, so that m-major
-// spectrum accesses form 64 B runs on large batches.  The launchers
+// a line is short) that fits the thread and LDS limits (80 KiB from lines of
+// 2048 values), so that m-major spectrum accesses form 64 B runs on large
+// batches.  The launchers
 // (k_real.hip, real_split) run a half or a quarter of this count per
 // workgroup while the full count would leave fewer workgroups than CUs
 // (w4's 1024 rows of 2048: 4 rows per workgroup, 32 B runs).
 constexpr int real_rows_per_wg(int h) {
   int c = rows_per_wg(h) < 8 ? 8 : rows_per_wg(h);
-  while (c > 1 && (c * threads_per_line(h) > kMaxThreads || row_lds_bytes(h, c) + c * 8 > kLdsBudgetBytes)) c /= 2;
+  // lines of 2048 values and more: at most 80 KiB of LDS, so that two
+  // workgroups share a CU (one 8-row workgroup of 2048-point lines held a CU
+  // alone): per 1 GiB of reals R2C / C2R at 4096 589 / 613 -> 497 / 554 us,
+  // 8192 593 / 633 -> 506 / 551, 16384 644 / 687 -> 556 / 591
+  while (c > 1 && (c * threads_per_line(h) > kMaxThreads || row_lds_bytes(h, c) + c * 8 > kLdsBudgetBytes ||
+                   (h >= 2048 && row_lds_bytes(h, c) + c * 8 > 81920)))
+    c /= 2;
   return c;
 }
 
