@@ -279,12 +279,8 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
   }
 }
 
-// KB butterflies of at most RMAX values per thread and stage (2 x 8 or
-// 1 x 16), up to 1024 threads (so at most 128 VGPRs).  The radix of each
-// stage selects a compiled stage (radices of the schedules: 2..8, and with
-// RMAX = 16 also 10 .. 16).
-// every stage of the schedule, each compiled for its radix (a switch on the
-// schedule's radix selects it; radices 2..8, and with RMAX = 16 also 10..16)
+// Every stage of the schedule, each compiled for its radix (a switch on the
+// schedule's radix selects it; radices 2..8, and with RMAX = 16 also 10..16).
 template <int S, int KB, int RMAX, bool PAD, int IO>
 __device__ __forceinline__ void mixed_stages(const MixedArgs& a, uint32_t t, uint32_t tpl, bool valid,
                                              const float2* src, float2* dst, float2* L) {
@@ -546,8 +542,14 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
 constexpr int kColBatch = 8;
 // TROWS: the tile is CT consecutive rows (contiguous, read in order) whose
 // transforms are stored transposed (launch_mixed_rows_t).
-template <int S, int KB, int RMAX, bool PAD, bool TROWS = false>
-__global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
+// LONG (lines of 512 points and more, 8 per workgroup): at most 64 VGPRs (a
+// few spilled dwords in the padded forms) and the loads issued at raised
+// wave priority.  Per 512 MiB: the four-step of 10^6 (1000-point tiles in
+// both passes) 801 -> 718 us, of 3 * 2^20 (1024-point columns) 925 -> 846,
+// 2D 1000 x 1000 546 -> 539; for shorter lines (128-400 points: 24576,
+// 49152, 160000, 2D 360 x 360) the same settings cost up to 3 %.
+template <int S, int KB, int RMAX, bool PAD, bool TROWS, bool LONG>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 : 1))) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
   const uint32_t n = (uint32_t)a.n, tpl = (uint32_t)a.tpl, nt = blockDim.x, tid = threadIdx.x;
@@ -569,6 +571,7 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
     const uint32_t nblk = (uint32_t)(left < (int64_t)CT ? left : (int64_t)CT) * n;
     const uint32_t magic = 0xffffffffu / n + 1u;  // e / n for e < 2^32 / n
     const float2* blk = a.in + g0 * n;
+    if constexpr (LONG) __builtin_amdgcn_s_setprio(3);
     for (uint32_t e0 = tid; e0 < nblk; e0 += kColBatch * nt) {
       float2 v[kColBatch];
 #pragma unroll
@@ -583,8 +586,10 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
         }
       }
     }
+    if constexpr (LONG) __builtin_amdgcn_s_setprio(0);
   } else {
   const float2* src = a.in + img * (int64_t)n * c.nx + (g - img * c.nx);
+  if constexpr (LONG) __builtin_amdgcn_s_setprio(3);
   for (uint32_t r0 = tid / CT; r0 < n; r0 += kColBatch * RS) {
     float2 v[kColBatch];
 #pragma unroll
@@ -603,6 +608,7 @@ __global__ __launch_bounds__(1024) void k_mixed_cols(MixedArgs a, MixedColsArgs 
       if (r < n) L0[mixed_pad<PAD>(r)] = v[i];
     }
   }
+  if constexpr (LONG) __builtin_amdgcn_s_setprio(0);
   }
   lds_barrier();
   const uint32_t G = nt / tpl;  // lines per group
@@ -764,6 +770,31 @@ int mixed_cols_tile(const MixedArgs& a) {
 }
 
 namespace {
+// the compiled tile kernel of one schedule shape
+template <bool TROWS, bool LONG>
+hipError_t launch_tiles_k(int sign, int rmax, bool pad, dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                          const MixedArgs& a, const MixedColsArgs& c) {
+  if (rmax > 8) {
+    if (pad) {
+      if (sign < 0)
+        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS, LONG>), grid, block, lds, st, a, c);
+      else
+        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS, LONG>), grid, block, lds, st, a, c);
+    } else if (sign < 0) {
+      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS, LONG>), grid, block, lds, st, a, c);
+    } else {
+      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS, LONG>), grid, block, lds, st, a, c);
+    }
+  } else if (pad) {
+    return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
+  } else if (sign < 0) {
+    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS, LONG>), grid, block, lds, st, a, c);
+  } else {
+    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS, LONG>), grid, block, lds, st, a, c);
+  }
+  return hipGetLastError();
+}
+
 template <bool TROWS>
 hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, hipStream_t st) {
   int rmax = 0;
@@ -790,25 +821,8 @@ hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, h
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
   const size_t lds = (size_t)ct * pitch * sizeof(float2);
   const dim3 grid((uint32_t)blocks), block((uint32_t)threads);
-  if (rmax > 8) {
-    if (a.pad) {
-      if (sign < 0)
-        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS>), grid, block, lds, st, a, c);
-      else
-        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS>), grid, block, lds, st, a, c);
-    } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS>), grid, block, lds, st, a, c);
-    } else {
-      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS>), grid, block, lds, st, a, c);
-    }
-  } else if (a.pad) {
-    return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
-  } else if (sign < 0) {
-    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS>), grid, block, lds, st, a, c);
-  } else {
-    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS>), grid, block, lds, st, a, c);
-  }
-  return hipGetLastError();
+  if (a.n >= 512) return launch_tiles_k<TROWS, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
+  return launch_tiles_k<TROWS, false>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
 }
 }  // namespace
 
