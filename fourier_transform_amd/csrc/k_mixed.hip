@@ -197,10 +197,12 @@ __host__ __device__ __forceinline__ uint32_t rader_line(uint32_t N, bool pad) {
 // is set), the others from the line in LDS; the last stage stores to HBM,
 // the others back to LDS.  IO bit 1: the first stage reads the line in LDS
 // too; IO bit 2: the last stage writes the line in LDS in natural order
-// (transforms whose input and output stay on chip).
-template <int S, int KB, int R, bool PAD, int IO = 0>
+// (transforms whose input and output stay on chip).  TWL: the twiddles come
+// from twl, the table's copy in LDS, instead of a.tw.
+template <int S, int KB, int R, bool PAD, int IO = 0, bool TWL = false>
 __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last, uint32_t t, uint32_t tpl,
-                                            bool valid, const float2* src, float2* dst, float2* L) {
+                                            bool valid, const float2* src, float2* dst, float2* L,
+                                            const float2* twl) {
   const uint32_t ns = (uint32_t)a.ns[s], m = (uint32_t)a.m[s];
   float2 x[KB][R];
   // gather the inputs of this thread's butterflies: b + r*m
@@ -236,7 +238,7 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
     if (b < m) {
       if (s > 0) {
         const uint32_t j = b - __umulhi(b, a.ns_magic[s]) * ns;
-        const float2* tw = a.tw + a.twoff[s] + j;
+        const float2* tw = (TWL ? twl : a.tw) + a.twoff[s] + j;
 #pragma unroll
         for (int r = 1; r < R; ++r) x[i][r] = apply_tw<S>(x[i][r], tw[(r - 1) * ns]);
       }
@@ -281,12 +283,19 @@ __device__ __forceinline__ void mixed_stage(const MixedArgs& a, int s, bool last
 
 // Every stage of the schedule, each compiled for its radix (a switch on the
 // schedule's radix selects it; radices 2..8, and with RMAX = 16 also 10..16).
-template <int S, int KB, int RMAX, bool PAD, int IO>
+// TWL: the stage twiddles are read from a copy of the table in LDS (twl, the
+// same layout as a.tw) instead of HBM/L2; kernels that run several lines per
+// workgroup copy the table once for all of them.  The twiddle gathers, not
+// the data, kept the texture units busy: with them replaced by register
+// values (a timing copy, wrong results) the 1000-point row kernel ran 218 ->
+// 180 us per 512 MiB and the four-step of 10^6 717 -> 615 us.
+template <int S, int KB, int RMAX, bool PAD, int IO, bool TWL = false>
 __device__ __forceinline__ void mixed_stages(const MixedArgs& a, uint32_t t, uint32_t tpl, bool valid,
-                                             const float2* src, float2* dst, float2* L) {
+                                             const float2* src, float2* dst, float2* L,
+                                             const float2* twl = nullptr) {
   for (int s = 0; s < a.nstages; ++s) {
     const bool last = s + 1 == a.nstages;
-#define FFTAMD_STAGE(R) mixed_stage<S, KB, R, PAD, IO>(a, s, last, t, tpl, valid, src, dst, L)
+#define FFTAMD_STAGE(R) mixed_stage<S, KB, R, PAD, IO, TWL>(a, s, last, t, tpl, valid, src, dst, L, twl)
     switch (a.radix[s]) {
       case 2: FFTAMD_STAGE(2); break;
       case 3: FFTAMD_STAGE(3); break;
@@ -315,12 +324,17 @@ __device__ __forceinline__ void mixed_stages(const MixedArgs& a, uint32_t t, uin
 
 // KB butterflies of at most RMAX values per thread and stage (2 x 8 or
 // 1 x 16), up to 1024 threads (so at most 128 VGPRs).  STG: HBM accessed
-// through the LDS lines in the block's order (lines of few threads).
-template <int S, int KB, int RMAX, bool PAD, bool STG>
+// through the LDS lines in the block's order (lines of few threads).  TWL
+// (with STG): the stage twiddles copied to LDS after the lines, gathered
+// before the rows' loads and written to LDS after them so that the two
+// latencies overlap.
+template <int S, int KB, int RMAX, bool PAD, bool STG, bool TWL = false>
 __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
-  lds_poison_dynamic(smem, (uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) * sizeof(float2));
+  // stage twiddles: (R_s - 1) ns_s entries for every stage s >= 1, n - R_0 in all
+  const uint32_t ntw = TWL ? (uint32_t)(a.n - a.radix[0]) : 0u;
+  lds_poison_dynamic(smem, ((uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) + ntw) * sizeof(float2));
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -340,6 +354,12 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
     const uint32_t NT = tpl * (uint32_t)a.lines;
     const uint32_t magic = 0xffffffffu / n + 1u;  // e / n for e < 2^32 / n
     const float2* src = a.in + row0 * n;
+    float2* twl = smem + (uint32_t)a.lines * lp;
+    float2 tw0 = make_float2(0.f, 0.f), tw1 = tw0;
+    if constexpr (TWL) {
+      if ((uint32_t)tid < ntw) tw0 = gload(a.tw, (uint32_t)tid);
+      if ((uint32_t)tid + NT < ntw) tw1 = gload(a.tw, (uint32_t)tid + NT);
+    }
     constexpr int U = 8;
     for (uint32_t e0 = (uint32_t)tid; e0 < nblk; e0 += U * NT) {
       float2 v[U];
@@ -358,8 +378,13 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
         }
       }
     }
+    if constexpr (TWL) {
+      if ((uint32_t)tid < ntw) twl[tid] = tw0;
+      if ((uint32_t)tid + NT < ntw) twl[tid + NT] = tw1;
+      for (uint32_t e = (uint32_t)tid + 2 * NT; e < ntw; e += NT) twl[e] = gload(a.tw, e);
+    }
     lds_barrier();
-    mixed_stages<S, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+    mixed_stages<S, KB, RMAX, PAD, 3, TWL>(a, t, tpl, valid, nullptr, nullptr, L, twl);
     float2* dst = a.out + row0 * n;
     for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
       const uint32_t q = __umulhi(e, magic), j = e - q * n;
@@ -548,14 +573,25 @@ constexpr int kColBatch = 8;
 // both passes) 801 -> 718 us, of 3 * 2^20 (1024-point columns) 925 -> 846,
 // 2D 1000 x 1000 546 -> 539; for shorter lines (128-400 points: 24576,
 // 49152, 160000, 2D 360 x 360) the same settings cost up to 3 %.
-template <int S, int KB, int RMAX, bool PAD, bool TROWS, bool LONG>
+// TWL: the stage twiddles in LDS after the CT lines (tile_shape decides).
+template <int S, int KB, int RMAX, bool PAD, bool TROWS, bool LONG, bool TWL>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 : 1))) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
   const uint32_t n = (uint32_t)a.n, tpl = (uint32_t)a.tpl, nt = blockDim.x, tid = threadIdx.x;
   const uint32_t CT = (uint32_t)a.lines;  // columns per workgroup (set by the launcher)
   const uint32_t pitch = mixed_pad<PAD>(n) + 1;
-  lds_poison_dynamic(smem, CT * pitch * (uint32_t)sizeof(float2));
+  // stage twiddles: (R_s - 1) ns_s entries for every stage s >= 1, n - R_0 in all
+  const uint32_t ntw = TWL ? (uint32_t)(a.n - a.radix[0]) : 0u;
+  lds_poison_dynamic(smem, (CT * pitch + ntw) * (uint32_t)sizeof(float2));
+  float2* twl = smem + CT * pitch;
+  // the table's first 2 * nt entries are gathered before the tile's loads
+  // and written to LDS after them, so that its latency overlaps theirs
+  float2 tw0 = make_float2(0.f, 0.f), tw1 = tw0;
+  if constexpr (TWL) {
+    if (tid < ntw) tw0 = gload(a.tw, tid);
+    if (tid + nt < ntw) tw1 = gload(a.tw, tid + nt);
+  }
   // thread tid takes column tid % CT of the tile and rows tid / CT + RS*i
   // (nt is a multiple of 64, so of CT): one division per thread, and
   // kColBatch loads in flight before their LDS writes
@@ -610,14 +646,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 :
   }
   if constexpr (LONG) __builtin_amdgcn_s_setprio(0);
   }
+  if constexpr (TWL) {
+    if (tid < ntw) twl[tid] = tw0;
+    if (tid + nt < ntw) twl[tid + nt] = tw1;
+    for (uint32_t e = tid + 2 * nt; e < ntw; e += nt) twl[e] = gload(a.tw, e);
+  }
   lds_barrier();
   const uint32_t G = nt / tpl;  // lines per group
   for (uint32_t l0 = 0; l0 < CT; l0 += G) {
     const uint32_t line = l0 + tid / tpl;
     const bool active = tid < G * tpl && line < CT;
     // an inactive thread's butterfly index is past every stage's count
-    mixed_stages<S, KB, RMAX, PAD, 3>(a, active ? tid % tpl : 0x40000000u, tpl, active, nullptr, nullptr,
-                                      smem + (active ? line : 0u) * pitch);
+    mixed_stages<S, KB, RMAX, PAD, 3, TWL>(a, active ? tid % tpl : 0x40000000u, tpl, active, nullptr, nullptr,
+                                           smem + (active ? line : 0u) * pitch, twl);
   }
   if constexpr (TROWS) {
     // line col is row k2 = g - img * nx of image img; entry k1 goes to
@@ -684,6 +725,31 @@ bool mixed_schedule_ok(const MixedArgs& a, int* rmax_out) {
 }
 }  // namespace
 
+namespace {
+template <bool TWL>
+hipError_t launch_mixed_stg(int sign, int rmax, const MixedArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+  if (rmax > 8) {
+    if (a.pad) {
+      if (sign < 0)
+        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true, true, TWL>), grid, block, lds, st, a);
+      else
+        FFTAMD_LAUNCH((k_mixed<1, 1, 16, true, true, TWL>), grid, block, lds, st, a);
+    } else if (sign < 0) {
+      FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false, true, TWL>), grid, block, lds, st, a);
+    } else {
+      FFTAMD_LAUNCH((k_mixed<1, 1, 16, false, true, TWL>), grid, block, lds, st, a);
+    }
+  } else if (a.pad) {
+    return hipErrorInvalidValue;
+  } else if (sign < 0) {
+    FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false, true, TWL>), grid, block, lds, st, a);
+  } else {
+    FFTAMD_LAUNCH((k_mixed<1, 2, 8, false, true, TWL>), grid, block, lds, st, a);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   int rmax = 0;
   if (!mixed_schedule_ok(a, &rmax)) return hipErrorInvalidValue;
@@ -704,25 +770,14 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
   // threads were 3-15 % slower staged (1296, 2000, 2187, 3000, 3125, 3500,
   // 4200, 4320, 5120, 6144), and so were two-butterfly lines (7200, 7776).
   if (a.n <= 8192 && (a.tpl < 128 || (a.tpl >= 800 && a.kb == 1))) {
-    if (rmax > 8) {
-      if (a.pad) {
-        if (sign < 0)
-          FFTAMD_LAUNCH((k_mixed<-1, 1, 16, true, true>), dim3(grid), block, lds, st, a);
-        else
-          FFTAMD_LAUNCH((k_mixed<1, 1, 16, true, true>), dim3(grid), block, lds, st, a);
-      } else if (sign < 0) {
-        FFTAMD_LAUNCH((k_mixed<-1, 1, 16, false, true>), dim3(grid), block, lds, st, a);
-      } else {
-        FFTAMD_LAUNCH((k_mixed<1, 1, 16, false, true>), dim3(grid), block, lds, st, a);
-      }
-    } else if (a.pad) {
-      return hipErrorInvalidValue;
-    } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed<-1, 2, 8, false, true>), dim3(grid), block, lds, st, a);
-    } else {
-      FFTAMD_LAUNCH((k_mixed<1, 2, 8, false, true>), dim3(grid), block, lds, st, a);
-    }
-    return hipGetLastError();
+    // the stage twiddles in LDS where a workgroup holds 3 lines or more (per
+    // 512 MiB: n = 360 207 -> 183 us, 500 267 -> 232, 100 186 -> 180, 48 173
+    // -> 170, 768 and 2000 unchanged); with 2 lines the larger LDS share costs
+    // more than it saves (1000: 219 -> 231 us)
+    const size_t ldst = lds + (size_t)(a.n - a.radix[0]) * sizeof(float2);
+    if (a.lines >= 3 && ldst <= (size_t)kLdsBudgetBytes)
+      return launch_mixed_stg<true>(sign, rmax, a, dim3(grid), block, ldst, st);
+    return launch_mixed_stg<false>(sign, rmax, a, dim3(grid), block, lds, st);
   }
   if (rmax > 8 && a.kb == 2) {
     // lengths above 8192: two butterflies of up to 16 values per thread
@@ -762,35 +817,53 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
 // four-step of 6561 876 against 812, of 100000 894 against 799), while
 // 8-column tiles of short lines lost (24576, 16 threads per line: 617
 // against 448 us; 2D 12 x 4096 519 against 365)
-int mixed_cols_tile(const MixedArgs& a) {
+namespace {
+// columns per workgroup and whether the stage twiddles (n - R_0 entries)
+// fit in LDS beside the tile.  With the table in LDS, per 512 MiB: the
+// four-step of 100000 795 -> 663 us, 160000 795 -> 655, 10^6 716 -> 643,
+// 2 * 10^6 909 -> 817, 36000 603 -> 542, 49152 499 -> 454, 20000 686 -> 661,
+// 6561 804 -> 736; 2D 640 x 480 521 -> 468, 720 x 720 561 -> 518, 360 x 360
+// 466 -> 448, 1000 x 1000 538 -> 521; 15625 (125-point tiles both ways) the
+// exception, 737 -> 773
+int tile_shape(const MixedArgs& a, bool* twl) {
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
-  if (16 * pitch * sizeof(float2) <= 81920 && 16 * a.tpl <= 384) return 16;
+  const size_t tw = (size_t)(a.n - a.radix[0]);
+  *twl = true;
+  if ((16 * pitch + tw) * sizeof(float2) <= 81920 && 16 * a.tpl <= 384) return 16;
+  if ((8 * pitch + tw) * sizeof(float2) <= (size_t)kLdsBudgetBytes) return 8;
+  *twl = false;
   if (8 * pitch * sizeof(float2) <= (size_t)kLdsBudgetBytes) return 8;
   return 0;
+}
+}  // namespace
+
+int mixed_cols_tile(const MixedArgs& a) {
+  bool twl = false;
+  return tile_shape(a, &twl);
 }
 
 namespace {
 // the compiled tile kernel of one schedule shape
-template <bool TROWS, bool LONG>
+template <bool TROWS, bool LONG, bool TWL>
 hipError_t launch_tiles_k(int sign, int rmax, bool pad, dim3 grid, dim3 block, size_t lds, hipStream_t st,
                           const MixedArgs& a, const MixedColsArgs& c) {
   if (rmax > 8) {
     if (pad) {
       if (sign < 0)
-        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS, LONG>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
       else
-        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS, LONG>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
     } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS, LONG>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
     } else {
-      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS, LONG>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
     }
   } else if (pad) {
     return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS, LONG>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
   } else {
-    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS, LONG>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
   }
   return hipGetLastError();
 }
@@ -805,7 +878,8 @@ hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, h
   if (rmax > 8 && a.kb != 1) return hipErrorInvalidValue;  // no column-tile kernel of this shape
   if (c.thi && (!c.tlo || c.bits < 1 || c.bits > 16 || (int64_t)a.n * c.nx > (int64_t(1) << 32)))
     return hipErrorInvalidValue;  // the twiddle exponents x k must fit 32 bits
-  const int ct = mixed_cols_tile(a);
+  bool twl = false;
+  const int ct = tile_shape(a, &twl);
   if (ct == 0) return hipErrorInvalidValue;
   a.lines = ct;
   const int64_t cols = c.images * c.nx;
@@ -819,10 +893,11 @@ hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, h
   int threads = g * a.tpl;
   threads = (threads + 63) / 64 * 64;
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
-  const size_t lds = (size_t)ct * pitch * sizeof(float2);
+  const size_t lds = ((size_t)ct * pitch + (twl ? (size_t)(a.n - a.radix[0]) : 0)) * sizeof(float2);
   const dim3 grid((uint32_t)blocks), block((uint32_t)threads);
-  if (a.n >= 512) return launch_tiles_k<TROWS, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
-  return launch_tiles_k<TROWS, false>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
+  if (!twl) return launch_tiles_k<TROWS, true, false>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
+  if (a.n >= 512) return launch_tiles_k<TROWS, true, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
+  return launch_tiles_k<TROWS, false, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
 }
 }  // namespace
 
