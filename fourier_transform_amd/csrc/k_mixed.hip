@@ -574,7 +574,9 @@ constexpr int kColBatch = 8;
 // 2D 1000 x 1000 546 -> 539; for shorter lines (128-400 points: 24576,
 // 49152, 160000, 2D 360 x 360) the same settings cost up to 3 %.
 // TWL: the stage twiddles in LDS after the CT lines (tile_shape decides).
-template <int S, int KB, int RMAX, bool PAD, bool TROWS, bool LONG, bool TWL>
+// FSL (with TWL, column tiles of the four-step): thi and tlo in LDS after
+// them, the entries the tile's exponents x k < n nx can reach.
+template <int S, int KB, int RMAX, bool PAD, bool TROWS, bool LONG, bool TWL, bool FSL = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 : 1))) void k_mixed_cols(MixedArgs a, MixedColsArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
@@ -583,8 +585,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 :
   const uint32_t pitch = mixed_pad<PAD>(n) + 1;
   // stage twiddles: (R_s - 1) ns_s entries for every stage s >= 1, n - R_0 in all
   const uint32_t ntw = TWL ? (uint32_t)(a.n - a.radix[0]) : 0u;
-  lds_poison_dynamic(smem, (CT * pitch + ntw) * (uint32_t)sizeof(float2));
+  const uint32_t nhi = FSL ? (((uint32_t)(a.n - 1) * (uint32_t)(c.nx - 1)) >> c.bits) + 1u : 0u;
+  const uint32_t nlo = FSL ? 1u << c.bits : 0u;
+  lds_poison_dynamic(smem, (CT * pitch + ntw + nhi + nlo) * (uint32_t)sizeof(float2));
   float2* twl = smem + CT * pitch;
+  float2* hil = twl + ntw;
+  float2* lol = hil + nhi;
+  float2 th0 = make_float2(0.f, 0.f), tl0 = th0;
+  if constexpr (FSL) {
+    if (tid < nhi) th0 = gload(c.thi, tid);
+    if (tid < nlo) tl0 = gload(c.tlo, tid);
+  }
   // the table's first 2 * nt entries are gathered before the tile's loads
   // and written to LDS after them, so that its latency overlaps theirs
   float2 tw0 = make_float2(0.f, 0.f), tw1 = tw0;
@@ -651,6 +662,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 :
     if (tid + nt < ntw) twl[tid + nt] = tw1;
     for (uint32_t e = tid + 2 * nt; e < ntw; e += nt) twl[e] = gload(a.tw, e);
   }
+  if constexpr (FSL) {
+    if (tid < nhi) hil[tid] = th0;
+    if (tid < nlo) lol[tid] = tl0;
+    for (uint32_t e = tid + nt; e < nhi; e += nt) hil[e] = gload(c.thi, e);
+    for (uint32_t e = tid + nt; e < nlo; e += nt) lol[e] = gload(c.tlo, e);
+  }
   lds_barrier();
   const uint32_t G = nt / tpl;  // lines per group
   for (uint32_t l0 = 0; l0 < CT; l0 += G) {
@@ -691,8 +708,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(LONG ? 8 :
       for (int i = 0; i < kColBatch; ++i) {
         const uint32_t r = r0 + RS * i, e = x * r;
         if (r < n) {
-          wh[i] = gload(c.thi, e >> c.bits);
-          wl[i] = gload(c.tlo, e & mask);
+          if constexpr (FSL) {
+            wh[i] = hil[e >> c.bits];
+            wl[i] = lol[e & mask];
+          } else {
+            wh[i] = gload(c.thi, e >> c.bits);
+            wl[i] = gload(c.tlo, e & mask);
+          }
         }
       }
 #pragma unroll
@@ -773,10 +795,22 @@ hipError_t launch_mixed(int sign, const MixedArgs& a, hipStream_t st) {
     // the stage twiddles in LDS where a workgroup holds 3 lines or more (per
     // 512 MiB: n = 360 207 -> 183 us, 500 267 -> 232, 100 186 -> 180, 48 173
     // -> 170, 768 and 2000 unchanged); with 2 lines the larger LDS share costs
-    // more than it saves (1000: 219 -> 231 us)
+    // more than it saves (1000: 219 -> 231 us), so those run 4 lines
     const size_t ldst = lds + (size_t)(a.n - a.radix[0]) * sizeof(float2);
     if (a.lines >= 3 && ldst <= (size_t)kLdsBudgetBytes)
       return launch_mixed_stg<true>(sign, rmax, a, dim3(grid), block, ldst, st);
+    // two lines per workgroup become four with the table (1000: 220 -> 212
+    // us; 2D 1000 x 1000 522 -> 508, 1000 x 600 544 -> 525; 2000 unchanged)
+    if (a.lines == 2 && a.tpl * 4 <= 1024) {
+      MixedArgs a4 = a;
+      a4.lines = 4;
+      uint32_t grid4;
+      e = grid_of(a4.rows, a4.lines, &grid4);
+      if (e != hipSuccess) return e;
+      const size_t lds4 = 2 * lds + (size_t)(a.n - a.radix[0]) * sizeof(float2);
+      if (lds4 <= (size_t)kLdsBudgetBytes)
+        return launch_mixed_stg<true>(sign, rmax, a4, dim3(grid4), dim3((uint32_t)(a4.tpl * 4)), lds4, st);
+    }
     return launch_mixed_stg<false>(sign, rmax, a, dim3(grid), block, lds, st);
   }
   if (rmax > 8 && a.kb == 2) {
@@ -844,26 +878,26 @@ int mixed_cols_tile(const MixedArgs& a) {
 
 namespace {
 // the compiled tile kernel of one schedule shape
-template <bool TROWS, bool LONG, bool TWL>
+template <bool TROWS, bool LONG, bool TWL, bool FSL = false>
 hipError_t launch_tiles_k(int sign, int rmax, bool pad, dim3 grid, dim3 block, size_t lds, hipStream_t st,
                           const MixedArgs& a, const MixedColsArgs& c) {
   if (rmax > 8) {
     if (pad) {
       if (sign < 0)
-        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, true, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
       else
-        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+        FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, true, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
     } else if (sign < 0) {
-      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<-1, 1, 16, false, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
     } else {
-      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+      FFTAMD_LAUNCH((k_mixed_cols<1, 1, 16, false, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
     }
   } else if (pad) {
     return hipErrorInvalidValue;  // schedules of radices up to 8 run unpadded
   } else if (sign < 0) {
-    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<-1, 2, 8, false, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
   } else {
-    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS, LONG, TWL>), grid, block, lds, st, a, c);
+    FFTAMD_LAUNCH((k_mixed_cols<1, 2, 8, false, TROWS, LONG, TWL, FSL>), grid, block, lds, st, a, c);
   }
   return hipGetLastError();
 }
@@ -895,6 +929,21 @@ hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, h
   const size_t pitch = (size_t)(a.pad ? mixed_pad<true>((uint32_t)a.n) : mixed_pad<false>((uint32_t)a.n)) + 1;
   const size_t lds = ((size_t)ct * pitch + (twl ? (size_t)(a.n - a.radix[0]) : 0)) * sizeof(float2);
   const dim3 grid((uint32_t)blocks), block((uint32_t)threads);
+  if constexpr (!TROWS) {
+    if (twl && c.thi) {
+      // the four-step's tables in LDS too, where copying them costs at most a
+      // quarter of the tile's elements and keeps the workgroups per CU (per 512
+      // MiB: 20000 663 -> 630 us, 24576 443 -> 411, 49152 456 -> 421, 36000
+      // 549 -> 534; 100000 (708 entries for 2000 elements) 667 -> 675 and
+      // 160000 658 -> 669 are left out by the rule, 15625 774 -> 791 is not)
+      const size_t nhi = ((((size_t)a.n - 1) * ((size_t)c.nx - 1)) >> c.bits) + 1, nlo = size_t(1) << c.bits;
+      const size_t ldsf = lds + (nhi + nlo) * sizeof(float2);
+      if (4 * (nhi + nlo) <= (size_t)a.n * ct && ldsf <= (lds <= 81920 ? 81920 : (size_t)kLdsBudgetBytes)) {
+        if (a.n >= 512) return launch_tiles_k<false, true, true, true>(sign, rmax, a.pad != 0, grid, block, ldsf, st, a, c);
+        return launch_tiles_k<false, false, true, true>(sign, rmax, a.pad != 0, grid, block, ldsf, st, a, c);
+      }
+    }
+  }
   if (!twl) return launch_tiles_k<TROWS, true, false>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
   if (a.n >= 512) return launch_tiles_k<TROWS, true, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
   return launch_tiles_k<TROWS, false, true>(sign, rmax, a.pad != 0, grid, block, lds, st, a, c);
