@@ -401,11 +401,20 @@ __global__ __launch_bounds__(1024) void k_mixed(MixedArgs a) {
 // product with conv (A_0 = sum of x_j, j >= 1, kept aside), the inverse
 // N-point transform, then X_0 = x_0 + A_0 and X_j = x_0 + c_(ind j), stored
 // coalesced.  The pre factors (the shift of odd lengths) apply on load.
-template <int KB, int RMAX, bool PAD, bool STG>
+// TWL: the stage twiddles of both transforms from a copy in LDS after the
+// lines (gathered before the rows' loads, written to LDS after them).
+template <int KB, int RMAX, bool PAD, bool STG, bool TWL = false>
 __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
-  lds_poison_dynamic(smem, (uint32_t)a.lines * rader_line((uint32_t)a.n, PAD) * sizeof(float2));
+  const uint32_t ntw = TWL ? (uint32_t)(a.n - a.radix[0]) : 0u;
+  lds_poison_dynamic(smem, ((uint32_t)a.lines * rader_line((uint32_t)a.n, PAD) + ntw) * sizeof(float2));
+  float2* twl = smem + (size_t)a.lines * rader_line((uint32_t)a.n, PAD);
+  float2 tw0 = make_float2(0.f, 0.f), tw1 = tw0;
+  if constexpr (TWL) {
+    if (threadIdx.x < ntw) tw0 = gload(a.tw, threadIdx.x);
+    if (threadIdx.x + blockDim.x < ntw) tw1 = gload(a.tw, threadIdx.x + blockDim.x);
+  }
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -455,15 +464,20 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
       }
     }
   }
+  if constexpr (TWL) {
+    if (threadIdx.x < ntw) twl[threadIdx.x] = tw0;
+    if (threadIdx.x + blockDim.x < ntw) twl[threadIdx.x + blockDim.x] = tw1;
+    for (uint32_t e = threadIdx.x + 2 * blockDim.x; e < ntw; e += blockDim.x) twl[e] = gload(a.tw, e);
+  }
   lds_barrier();
-  mixed_stages<-1, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<-1, KB, RMAX, PAD, 3, TWL>(a, t, tpl, valid, nullptr, nullptr, L, twl);
   for (uint32_t k = t; k < N; k += tpl) {
     const float2 A = L[mixed_pad<PAD>(k)];
     if (k == 0) x0s[1] = A;
     L[mixed_pad<PAD>(k)] = cmul(A, gload(rd.conv, k));
   }
   lds_barrier();
-  mixed_stages<1, KB, RMAX, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<1, KB, RMAX, PAD, 3, TWL>(a, t, tpl, valid, nullptr, nullptr, L, twl);
   if constexpr (STG) {
     float2* dst = a.out + row0 * p;
     for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
@@ -487,11 +501,19 @@ __global__ __launch_bounds__(1024) void k_rader(MixedArgs a, RaderArgs rd) {
 // schedule: the row times pre, zero beyond n, as a line of m values in LDS;
 // the forward m-point stages; the product with bhat; the inverse stages; the
 // outputs j < n times post.  STG: the rows read and written as one block.
-template <bool PAD, bool STG>
+// TWL: the stage twiddles of both transforms from a copy in LDS, as in k_rader.
+template <bool PAD, bool STG, bool TWL = false>
 __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixedArgs c) {
   extern __shared__ float4 smem4[];
   float2* smem = reinterpret_cast<float2*>(smem4);
-  lds_poison_dynamic(smem, (uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) * sizeof(float2));
+  const uint32_t ntw = TWL ? (uint32_t)(a.n - a.radix[0]) : 0u;
+  lds_poison_dynamic(smem, ((uint32_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1) + ntw) * sizeof(float2));
+  float2* twl = smem + (size_t)a.lines * (mixed_pad<PAD>((uint32_t)a.n) + 1);
+  float2 tw0 = make_float2(0.f, 0.f), tw1 = tw0;
+  if constexpr (TWL) {
+    if (threadIdx.x < ntw) tw0 = gload(a.tw, threadIdx.x);
+    if (threadIdx.x + blockDim.x < ntw) tw1 = gload(a.tw, threadIdx.x + blockDim.x);
+  }
   const uint32_t tpl = (uint32_t)a.tpl;
   const int tid = threadIdx.x;
   const int line = tid / (int)tpl;
@@ -534,11 +556,16 @@ __global__ __launch_bounds__(1024) void k_bluestein_mixed(MixedArgs a, ChirpMixe
       L[mixed_pad<PAD>(j)] = v;
     }
   }
+  if constexpr (TWL) {
+    if (threadIdx.x < ntw) twl[threadIdx.x] = tw0;
+    if (threadIdx.x + blockDim.x < ntw) twl[threadIdx.x + blockDim.x] = tw1;
+    for (uint32_t e = threadIdx.x + 2 * blockDim.x; e < ntw; e += blockDim.x) twl[e] = gload(a.tw, e);
+  }
   lds_barrier();
-  mixed_stages<-1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<-1, 1, 16, PAD, 3, TWL>(a, t, tpl, valid, nullptr, nullptr, L, twl);
   for (uint32_t k = t; k < m; k += tpl) L[mixed_pad<PAD>(k)] = cmul(L[mixed_pad<PAD>(k)], gload(c.bhat, k));
   lds_barrier();
-  mixed_stages<1, 1, 16, PAD, 3>(a, t, tpl, valid, nullptr, nullptr, L);
+  mixed_stages<1, 1, 16, PAD, 3, TWL>(a, t, tpl, valid, nullptr, nullptr, L, twl);
   if constexpr (STG) {
     float2* dst = a.out + row0 * n;
     for (uint32_t e = (uint32_t)tid; e < nblk; e += NT) {
@@ -959,6 +986,21 @@ hipError_t launch_mixed_rows_t(int sign, const MixedArgs& a, const MixedColsArgs
   return launch_tiles<true>(sign, a, c, st);
 }
 
+namespace {
+// workgroups per CU that LDS and 8 waves per SIMD allow.  The Rader and
+// chirp kernels run two transforms per line on one stage table, so the copy
+// in LDS pays even with one line per workgroup, but only while it keeps the
+// workgroups per CU (per 512 MiB: Rader p = 97 334 -> 294 us, 257 406 ->
+// 366, 641 394 -> 330, 1009 494 -> 457, 3001 676 -> 625, 4001 699 -> 630;
+// chirp 34 471 -> 435, 2111 972 -> 906; with fewer workgroups 2017 460 ->
+// 618, 6007 540 -> 766, 1034 754 -> 943, 1049 655 -> 857)
+int wg_per_cu(size_t lds, uint32_t threads) {
+  const int by_waves = 32 / (int)((threads + 63) / 64);
+  const int by_lds = lds ? (int)((size_t)kLdsBudgetBytes / lds) : by_waves;
+  return by_waves < by_lds ? by_waves : by_lds;
+}
+}  // namespace
+
 hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st) {
   int rmax = 0;
   if (!mixed_schedule_ok(a, &rmax) || rd.p != a.n + 1 || !rd.conv || !rd.perm || (a.kb == 2 && a.pad))
@@ -976,9 +1018,19 @@ hipError_t launch_rader(const MixedArgs& a, const RaderArgs& rd, hipStream_t st)
   // k_mixed: 1009 (144 threads per line) 600 -> 494, 2017 523 -> 459, 2593
   // 615 -> 537, 3001 747 -> 678, 4001 730 -> 701
   const bool stg = rd.p <= 4096;
+  const size_t ldst = lds + (size_t)(a.n - a.radix[0]) * sizeof(float2);
   if (a.kb == 2)  // p - 1 above 8192: two butterflies of up to 16 values per thread
     FFTAMD_LAUNCH((k_rader<2, 16, false, false>), dim3(grid), block, lds, st, a, rd);
-  else if (a.pad && stg)
+  else if (ldst <= (size_t)kLdsBudgetBytes && wg_per_cu(ldst, block.x) >= wg_per_cu(lds, block.x)) {
+    if (a.pad && stg)
+      FFTAMD_LAUNCH((k_rader<1, 16, true, true, true>), dim3(grid), block, ldst, st, a, rd);
+    else if (a.pad)
+      FFTAMD_LAUNCH((k_rader<1, 16, true, false, true>), dim3(grid), block, ldst, st, a, rd);
+    else if (stg)
+      FFTAMD_LAUNCH((k_rader<1, 16, false, true, true>), dim3(grid), block, ldst, st, a, rd);
+    else
+      FFTAMD_LAUNCH((k_rader<1, 16, false, false, true>), dim3(grid), block, ldst, st, a, rd);
+  } else if (a.pad && stg)
     FFTAMD_LAUNCH((k_rader<1, 16, true, true>), dim3(grid), block, lds, st, a, rd);
   else if (a.pad)
     FFTAMD_LAUNCH((k_rader<1, 16, true, false>), dim3(grid), block, lds, st, a, rd);
@@ -1004,6 +1056,18 @@ hipError_t launch_bluestein_mixed(const MixedArgs& a, const ChirpMixedArgs& c, h
   // 851 -> 755 us, 1049 816 -> 658, 2053 1119 -> 1049, 2111 1013 -> 972
   // beside the short-line gains (34 797 -> 473 with the mixed length)
   const bool stg = c.n <= 4096;
+  const size_t ldst = lds + (size_t)(a.n - a.radix[0]) * sizeof(float2);
+  if (ldst <= (size_t)kLdsBudgetBytes && wg_per_cu(ldst, block.x) >= wg_per_cu(lds, block.x)) {
+    if (a.pad && stg)
+      FFTAMD_LAUNCH((k_bluestein_mixed<true, true, true>), dim3(grid), block, ldst, st, a, c);
+    else if (a.pad)
+      FFTAMD_LAUNCH((k_bluestein_mixed<true, false, true>), dim3(grid), block, ldst, st, a, c);
+    else if (stg)
+      FFTAMD_LAUNCH((k_bluestein_mixed<false, true, true>), dim3(grid), block, ldst, st, a, c);
+    else
+      FFTAMD_LAUNCH((k_bluestein_mixed<false, false, true>), dim3(grid), block, ldst, st, a, c);
+    return hipGetLastError();
+  }
   if (a.pad && stg)
     FFTAMD_LAUNCH((k_bluestein_mixed<true, true>), dim3(grid), block, lds, st, a, c);
   else if (a.pad)
