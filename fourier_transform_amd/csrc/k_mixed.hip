@@ -958,14 +958,14 @@ hipError_t launch_tiles(int sign, const MixedArgs& a0, const MixedColsArgs& c, h
   const dim3 grid((uint32_t)blocks), block((uint32_t)threads);
   if constexpr (!TROWS) {
     if (twl && c.thi) {
-      // the four-step's tables in LDS too, where copying them costs at most a
-      // quarter of the tile's elements and keeps the workgroups per CU (per 512
-      // MiB: 20000 663 -> 630 us, 24576 443 -> 411, 49152 456 -> 421, 36000
-      // 549 -> 534; 100000 (708 entries for 2000 elements) 667 -> 675 and
-      // 160000 658 -> 669 are left out by the rule, 15625 774 -> 791 is not)
+      // the four-step's tables in LDS too for 16-column tiles (the copy shared
+      // by 16 columns, the workgroups per CU kept).  Per 512 MiB: 24576 443
+      // -> 411 us, 49152 456 -> 421, 36000 549 -> 534; with 8-column tiles
+      // the results were mixed (20000 663 -> 630, but 15625 774 -> 791,
+      // 100000 667 -> 675, 160000 658 -> 669), so those keep them in HBM
       const size_t nhi = ((((size_t)a.n - 1) * ((size_t)c.nx - 1)) >> c.bits) + 1, nlo = size_t(1) << c.bits;
       const size_t ldsf = lds + (nhi + nlo) * sizeof(float2);
-      if (4 * (nhi + nlo) <= (size_t)a.n * ct && ldsf <= (lds <= 81920 ? 81920 : (size_t)kLdsBudgetBytes)) {
+      if (ct == 16 && ldsf <= (lds <= 81920 ? 81920 : (size_t)kLdsBudgetBytes)) {
         if (a.n >= 512) return launch_tiles_k<false, true, true, true>(sign, rmax, a.pad != 0, grid, block, ldsf, st, a, c);
         return launch_tiles_k<false, false, true, true>(sign, rmax, a.pad != 0, grid, block, ldsf, st, a, c);
       }
