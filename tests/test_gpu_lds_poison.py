@@ -53,9 +53,11 @@ C2C_CASES = [
     (1 << 15, 3), (1 << 20, 2),
     # mixed radix (one butterfly of <= 16, two of <= 8, two of <= 16 above 8192), Rader,
     # chirp (one kernel on a power of two up to 16384 and at 32768, one on a mixed-radix
-    # length, three passes)
+    # length, three passes); the stage twiddles in LDS: rows of 3+ and 4 lines per
+    # workgroup (360, 1000), Rader (1009), chirp on a mixed length (34), the four-step's
+    # 8-column tiles (20000) and 16-column tiles with the two-level table in LDS (24576)
     (1000, 9), (360, 11), (12, 700), (6000, 3), (7776, 3), (12000, 2), (15360, 3), (1009, 5), (9001, 2), (97, 13), (17, 600), (1019, 4), (34, 300),
-    (10001, 2), (1034, 3), (20011, 2), (20000, 2),
+    (10001, 2), (1034, 3), (20011, 2), (20000, 2), (24576, 2),
 ]
 
 
